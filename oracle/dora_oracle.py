@@ -1,0 +1,100 @@
+"""CPU fp64 oracle of the DoRA hot path.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The product path (the HIP library and its Python binding)
+never calls it, and it shares no code with that path.
+
+Source of truth: the press summary of arXiv:2603.22276 ("AI training
+breakthrough: Anthropic team cracks the memory bottleneck of large-model
+fine-tuning", techwalker.com/2026/0401/3182870).  The page prints no equations
+with numbers; it names the operations:
+
+* the DoRA weight norm, taken per output row of W0 + s*B*A (paragraph on the
+  "factored norm", and the Q&A on why DoRA needs so much memory).  The factored
+  method splits it into base, cross and Gram terms and reaches *the same result*
+  by algebra, so the oracle is the plain definition: form W0 + s*B*A densely in
+  fp64 and take Euclidean row norms.
+* the magnitude compose in its stable form (g - 1) * base + g * s * lora, with
+  g = m / n per output feature (paragraph on numerical stability near g = 1).
+  The formula is the adapter's delta; ``add_base`` adds base to it.
+* the backward of that compose, including the magnitude gradient, which is a
+  reduction over tokens (paragraph on the convergence study: the dmag reduction
+  order).  The norm n is treated as a constant in the backward.
+
+Everything is computed in fp64 from the exact values of the inputs: bf16/fp16
+tensors and fp32 vectors convert to fp64 without rounding, and ``s`` is the fp32
+scale the kernels receive.  numpy's matmul, sum and sqrt are the only library
+steps.  No blocking, fusion or reordering beyond the definitions.
+
+Readings of points the page leaves open (also listed in the design notes):
+W0 is [out x in], A [r x in], B [out x r] (nn.Linear orientation); the norm is
+L2 over the input axis; g = m / n with m, n fp32 per output feature; the
+compose output is the delta unless add_base; n is detached in the backward.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def as_f64(t) -> np.ndarray:
+    """Exact fp64 copy of a torch tensor (bf16, fp16, fp32) or numpy array."""
+    if hasattr(t, "detach"):
+        return t.detach().cpu().double().numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def weight_norm(W0, A, B, s) -> np.ndarray:
+    """n_i = || W0_i + s * (B A)_i ||_2 for every output row i.
+
+    The dense definition of the DoRA weight norm (summary page, paragraph on the
+    factored norm: base + cross + Gram terms give the same value as this).
+    Shapes: W0 [out x in], A [r x in], B [out x r]; returns fp64 [out].
+    Passing a row subset of W0 and B gives the norms of those rows.
+    """
+    W0, A, B = as_f64(W0), as_f64(A), as_f64(B)
+    s = float(s)
+    V = W0 + s * (B @ A)  # the out x in matrix the GPU path never forms
+    return np.sqrt(np.sum(V * V, axis=1))
+
+
+def scale_factor(m, n) -> np.ndarray:
+    """g = m / n per output feature (summary page, paragraph on stability near g = 1)."""
+    return as_f64(m) / as_f64(n)
+
+
+def compose_fwd(base, lora, m, n, s, add_base: bool = False) -> np.ndarray:
+    """y = (g - 1) * base + g * s * lora, g = m / n broadcast over tokens.
+
+    The stable compose form of the summary page (paragraph on numerical
+    stability).  With ``add_base`` the output is base + that delta, which is
+    the full DoRA layer output g * (base + s * lora).
+    base, lora: [T x out]; m, n: [out].  Returns fp64 [T x out], unrounded.
+    """
+    base, lora = as_f64(base), as_f64(lora)
+    g = scale_factor(m, n)
+    s = float(s)
+    y = (g - 1.0) * base + g * s * lora
+    if add_base:
+        y = y + base
+    return y
+
+
+def compose_bwd(dy, base, lora, m, n, s, add_base: bool = False):
+    """Gradients of L = sum(dy * y) for the compose above, with n held fixed.
+
+    d_lora = g * s * dy
+    d_base = (g - 1) * dy, or g * dy with add_base
+    d_mag_j = sum_t dy_tj * (base_tj + s * lora_tj) / n_j   (reduction over tokens)
+
+    The magnitude gradient is the token reduction the summary page mentions in
+    its convergence paragraph.  Returns fp64 (d_lora [T x out], d_base [T x out],
+    d_mag [out]).
+    """
+    dy, base, lora = as_f64(dy), as_f64(base), as_f64(lora)
+    n = as_f64(n)
+    g = scale_factor(m, n)
+    s = float(s)
+    d_lora = g * s * dy
+    d_base = (g if add_base else (g - 1.0)) * dy
+    d_mag = np.sum(dy * (base + s * lora), axis=0) / n
+    return d_lora, d_base, d_mag

@@ -1,0 +1,267 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each ``pin_*`` takes an object with the oracle's three functions
+(``weight_norm``, ``compose_fwd``, ``compose_bwd``) and raises AssertionError
+when the oracle disagrees with:
+
+* exact rational arithmetic on tiny inputs (brute force, using the factored
+  base + cross + Gram expansion, a different formula from the oracle's dense one),
+* special cases that reduce to a library routine (``numpy.linalg.norm``),
+* closed forms (rank one, orthonormal A, exact cancellation, g = 1, m = 0),
+* hand-worked examples stored under ``golden/`` with their derivation,
+* central finite differences and fp64 autograd for the backward.
+
+The mutation tests run every pin against planted mistakes to show that each
+plausible error (a dropped term, a wrong sign, a transposed operand, a missing
+division) fails at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16_exact(rng, shape, sigma):
+    """Random values exactly representable in bf16 (so fp64 and Fraction agree)."""
+    a = (rng.standard_normal(shape) * sigma).astype(np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16).double().numpy()
+
+
+# --------------------------------------------------------------------------- norm
+
+
+def _norm_sq_fraction_factored(W0, A, B, s):
+    """n_i^2 = ||W_i||^2 + 2 s B_i (A W_i^T) + s^2 B_i (A A^T) B_i^T, exactly."""
+    out, inn = W0.shape
+    r = A.shape[0]
+    W = [[Fraction(float(v)) for v in row] for row in W0]
+    Af = [[Fraction(float(v)) for v in row] for row in A]
+    Bf = [[Fraction(float(v)) for v in row] for row in B]
+    sf = Fraction(float(s))
+    G = [[sum(Af[j][k] * Af[l][k] for k in range(inn)) for l in range(r)] for j in range(r)]
+    res = []
+    for i in range(out):
+        base = sum(w * w for w in W[i])
+        U = [sum(W[i][k] * Af[j][k] for k in range(inn)) for j in range(r)]
+        cross = 2 * sf * sum(Bf[i][j] * U[j] for j in range(r))
+        gram = sf * sf * sum(Bf[i][j] * G[j][l] * Bf[i][l] for j in range(r) for l in range(r))
+        res.append(base + cross + gram)
+    return res
+
+
+def pin_norm_exact_bruteforce(o, seed=0, trials=6):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        out, inn, r = int(rng.integers(1, 7)), int(rng.integers(1, 11)), int(rng.integers(1, 5))
+        W0 = _bf16_exact(rng, (out, inn), 0.5)
+        A = _bf16_exact(rng, (r, inn), 1.0)
+        B = _bf16_exact(rng, (out, r), 0.5)
+        s = float(np.float32(rng.uniform(0.3, 3.0)))
+        exact = _norm_sq_fraction_factored(W0, A, B, s)
+        got = np.asarray(o.weight_norm(W0, A, B, s), dtype=np.float64)
+        assert got.shape == (out,), got.shape
+        for i in range(out):
+            want = math.sqrt(float(exact[i]))
+            assert abs(got[i] - want) <= 1e-12 * max(want, 1e-300) + 1e-300, (t, i, got[i], want)
+
+
+def pin_norm_special_cases(o, seed=1):
+    rng = np.random.default_rng(seed)
+    out, inn, r = 9, 13, 3
+    W0 = _bf16_exact(rng, (out, inn), 0.02)
+    A = _bf16_exact(rng, (r, inn), 0.3)
+    B = _bf16_exact(rng, (out, r), 0.01)
+    ref = np.linalg.norm(W0, axis=1)
+    # B = 0 and A = 0 reduce to plain row norms of W0
+    np.testing.assert_allclose(o.weight_norm(W0, A, np.zeros_like(B), 1.7), ref, rtol=1e-14)
+    np.testing.assert_allclose(o.weight_norm(W0, np.zeros_like(A), B, 1.7), ref, rtol=1e-14)
+    # s = 0 also drops the adapter
+    np.testing.assert_allclose(o.weight_norm(W0, A, B, 0.0), ref, rtol=1e-14)
+    # W0 = 0, rank one: n_i = |s b_i| ||a||
+    a = A[:1]
+    b = B[:, :1]
+    got = o.weight_norm(np.zeros_like(W0), a, b, 2.5)
+    np.testing.assert_allclose(got, np.abs(2.5 * b[:, 0]) * np.linalg.norm(a[0]), rtol=1e-14)
+    # orthonormal rows of A (unit basis vectors) and W0 orthogonal to them:
+    # n_i^2 = ||W0_i||^2 + s^2 ||B_i||^2 (Pythagoras)
+    Aon = np.zeros((r, inn))
+    for j in range(r):
+        Aon[j, 2 * j + 1] = 1.0
+    W0p = W0.copy()
+    W0p[:, [2 * j + 1 for j in range(r)]] = 0.0
+    s = 1.25
+    want = np.sqrt(np.sum(W0p**2, axis=1) + s * s * np.sum(B**2, axis=1))
+    np.testing.assert_allclose(o.weight_norm(W0p, Aon, B, s), want, rtol=1e-14)
+    # orthonormal A with W0 along A: n_i = || W0_i A^T + s B_i || (the coefficients add)
+    W0a = (B[:, ::-1].copy() * 3.0) @ Aon
+    want = np.linalg.norm(B[:, ::-1] * 3.0 + s * B, axis=1)
+    np.testing.assert_allclose(o.weight_norm(W0a, Aon, B, s), want, rtol=1e-14)
+    # exact cancellation W0 = -s B A: the norm is exactly zero
+    Bi = np.array([[1.0, -2.0], [0.5, 0.0], [0.0, 0.25]])
+    Ai = np.array([[1.0, 2.0, 0.0, -1.0], [0.0, 1.0, 4.0, 0.5]])
+    s = 2.0
+    W0c = -s * (Bi @ Ai)
+    assert np.all(o.weight_norm(W0c, Ai, Bi, s) == 0.0)
+    # non-negativity and per-row independence (rows can be evaluated alone)
+    full = o.weight_norm(W0, A, B, 1.3)
+    assert np.all(full >= 0)
+    rows = [7, 0, 4]
+    np.testing.assert_allclose(o.weight_norm(W0[rows], A, B[rows], 1.3), full[rows], rtol=0, atol=0)
+
+
+def pin_norm_golden(o):
+    for ex in _golden("worked_examples.json")["norm"]:
+        got = np.asarray(o.weight_norm(np.array(ex["W0"], float), np.array(ex["A"], float),
+                                       np.array(ex["B"], float), ex["s"]))
+        want = np.sqrt(np.array(ex["expected_norm_sq"], float))
+        np.testing.assert_allclose(got, want, rtol=1e-15, atol=0, err_msg=ex["name"])
+
+
+def pin_norm_invariances(o, seed=2):
+    """Invariances fixed by the mathematics: sign flips, scaling, permutations."""
+    rng = np.random.default_rng(seed)
+    out, inn, r = 6, 10, 4
+    W0 = _bf16_exact(rng, (out, inn), 0.1)
+    A = _bf16_exact(rng, (r, inn), 0.5)
+    B = _bf16_exact(rng, (out, r), 0.2)
+    s = 1.5
+    ref = o.weight_norm(W0, A, B, s)
+    # (B, s) -> (-B, -s) leaves s*B*A unchanged; (B, A) -> (2B, A/2) as well
+    np.testing.assert_allclose(o.weight_norm(W0, A, -B, -s), ref, rtol=1e-14)
+    np.testing.assert_allclose(o.weight_norm(W0, A / 2, 2 * B, s), ref, rtol=1e-14)
+    # scaling W0 and B together scales the norm
+    np.testing.assert_allclose(o.weight_norm(4 * W0, A, 4 * B, s), 4 * ref, rtol=1e-14)
+    # permuting the input axis of W0 and A, or the rank axis of A and B, changes nothing
+    p = rng.permutation(inn)
+    np.testing.assert_allclose(o.weight_norm(W0[:, p], A[:, p], B, s), ref, rtol=1e-13)
+    q = rng.permutation(r)
+    np.testing.assert_allclose(o.weight_norm(W0, A[q], B[:, q], s), ref, rtol=1e-13)
+    # the norm changes when the adapter changes sign relative to W0 (detects a
+    # dropped cross term, which is the only term odd in s)
+    flipped = o.weight_norm(W0, A, B, -s)
+    assert np.max(np.abs(flipped - ref)) > 1e-6
+
+
+# ----------------------------------------------------------------------- compose
+
+
+def pin_compose_golden(o):
+    for ex in _golden("worked_examples.json")["compose"]:
+        args = [np.array(ex[k], float) for k in ("base", "lora", "m", "n")]
+        s = ex["s"]
+        np.testing.assert_allclose(o.compose_fwd(*args, s, add_base=False), ex["expected_delta"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(o.compose_fwd(*args, s, add_base=True), ex["expected_full"], rtol=0, atol=1e-15)
+        dy = np.array(ex["dy"], float)
+        dl, db, dm = o.compose_bwd(dy, *args, s, add_base=False)
+        np.testing.assert_allclose(dl, ex["expected_d_lora"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(db, ex["expected_d_base_delta"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(dm, ex["expected_d_mag"], rtol=0, atol=1e-15)
+        dl, db, dm = o.compose_bwd(dy, *args, s, add_base=True)
+        np.testing.assert_allclose(db, ex["expected_d_base_full"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(dm, ex["expected_d_mag"], rtol=0, atol=1e-15)
+
+
+def _compose_inputs(seed, T=7, out=5):
+    rng = np.random.default_rng(seed)
+    base = _bf16_exact(rng, (T, out), 1.0)
+    lora = _bf16_exact(rng, (T, out), 0.3)
+    n = rng.uniform(0.5, 2.0, out).astype(np.float32).astype(np.float64)
+    m = (n * (1 + rng.standard_normal(out) * 0.05)).astype(np.float32).astype(np.float64)
+    return base, lora, m, n
+
+
+def pin_compose_closed_forms(o, seed=3):
+    base, lora, m, n = _compose_inputs(seed)
+    s = 1.75
+    # m == n: g = 1, the delta is exactly s * lora and the full output base + s * lora
+    np.testing.assert_array_equal(o.compose_fwd(base, lora, n, n, s), s * lora)
+    np.testing.assert_array_equal(o.compose_fwd(base, np.zeros_like(lora), n, n, s, add_base=True), base)
+    # m == 0: the layer output vanishes, the delta is -base
+    np.testing.assert_allclose(o.compose_fwd(base, lora, np.zeros_like(m), n, s, add_base=True), 0.0, atol=1e-15)
+    np.testing.assert_allclose(o.compose_fwd(base, lora, np.zeros_like(m), n, s), -base, atol=1e-15)
+    # the stable form equals the direct DoRA output g * (base + s * lora) (and minus base for the delta)
+    g = m / n
+    full = g * (base + s * lora)
+    np.testing.assert_allclose(o.compose_fwd(base, lora, m, n, s, add_base=True), full, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o.compose_fwd(base, lora, m, n, s), full - base, rtol=1e-12, atol=1e-14)
+    # the correction term alone: with lora = 0 the delta is (g - 1) * base, nonzero where m != n
+    corr = o.compose_fwd(base, np.zeros_like(lora), m, n, s)
+    assert np.all((corr != 0) == ((m != n)[None, :] & (base != 0)))
+    # column scaling: doubling m doubles the full output
+    np.testing.assert_allclose(o.compose_fwd(base, lora, 2 * m, n, s, add_base=True), 2 * full, rtol=1e-13)
+
+
+def pin_compose_bwd_finite_differences(o, seed=4):
+    """Central differences of L = sum(dy * y); y is affine in m, base and lora, so
+    the differences are exact up to rounding."""
+    base, lora, m, n = _compose_inputs(seed)
+    s = 1.25
+    rng = np.random.default_rng(seed + 100)
+    dy = _bf16_exact(rng, base.shape, 1.0)
+    for add_base in (False, True):
+        dl, db, dm = o.compose_bwd(dy, base, lora, m, n, s, add_base=add_base)
+
+        def L(mm=m, bb=base, ll=lora):
+            return float(np.sum(dy * o.compose_fwd(bb, ll, mm, n, s, add_base=add_base)))
+
+        h = 1e-3
+        for j in range(len(m)):
+            e = np.zeros_like(m)
+            e[j] = h
+            fd = (L(mm=m + e) - L(mm=m - e)) / (2 * h)
+            assert abs(fd - dm[j]) <= 1e-9 * (1 + abs(fd)), (add_base, j, fd, dm[j])
+        for (t, j) in [(0, 0), (3, 2), (6, 4), (2, 1)]:
+            e = np.zeros_like(base)
+            e[t, j] = h
+            fd_b = (L(bb=base + e) - L(bb=base - e)) / (2 * h)
+            fd_l = (L(ll=lora + e) - L(ll=lora - e)) / (2 * h)
+            assert abs(fd_b - db[t, j]) <= 1e-9 * (1 + abs(fd_b)), (add_base, t, j, fd_b, db[t, j])
+            assert abs(fd_l - dl[t, j]) <= 1e-9 * (1 + abs(fd_l)), (add_base, t, j, fd_l, dl[t, j])
+
+
+def pin_compose_bwd_autograd(o, seed=5):
+    """torch.autograd in fp64 through g * (base + s * lora) (n detached)."""
+    base, lora, m, n = _compose_inputs(seed, T=11, out=6)
+    s = 0.875
+    rng = np.random.default_rng(seed + 7)
+    dy = _bf16_exact(rng, base.shape, 1.0)
+    for add_base in (False, True):
+        tb = torch.tensor(base, requires_grad=True)
+        tl = torch.tensor(lora, requires_grad=True)
+        tm = torch.tensor(m, requires_grad=True)
+        tn = torch.tensor(n)
+        y = (tm / tn) * (tb + s * tl)
+        if not add_base:
+            y = y - tb
+        (y * torch.tensor(dy)).sum().backward()
+        dl, db, dm = o.compose_bwd(dy, base, lora, m, n, s, add_base=add_base)
+        np.testing.assert_allclose(dl, tl.grad.numpy(), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(db, tb.grad.numpy(), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(dm, tm.grad.numpy(), rtol=1e-12, atol=1e-14)
+    # no tokens: the magnitude gradient is an empty sum
+    dl, db, dm = o.compose_bwd(dy[:0], base[:0], lora[:0], m, n, s)
+    assert dl.shape == (0, 6) and np.all(dm == 0)
+
+
+ALL_PINS = [
+    pin_norm_exact_bruteforce,
+    pin_norm_special_cases,
+    pin_norm_golden,
+    pin_norm_invariances,
+    pin_compose_golden,
+    pin_compose_closed_forms,
+    pin_compose_bwd_finite_differences,
+    pin_compose_bwd_autograd,
+]

@@ -1,0 +1,108 @@
+"""The CPU oracle against its pins (exact arithmetic, closed forms, golden
+examples, finite differences, autograd), and the pins against planted mistakes."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import dora_oracle as O
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(O)
+
+
+def _mutant(**overrides):
+    ns = types.SimpleNamespace(weight_norm=O.weight_norm, compose_fwd=O.compose_fwd, compose_bwd=O.compose_bwd)
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def _f(x):
+    return O.as_f64(x)
+
+
+def _norm_dense(W0, A, B, s, *, sign=1.0, s_pow=1, axis=1, root=True):
+    W0, A, B = _f(W0), _f(A), _f(B)
+    V = W0 + sign * (float(s) ** s_pow) * (B @ A)
+    sq = np.sum(V * V, axis=axis)
+    return np.sqrt(sq) if root else sq
+
+
+def _fwd(base, lora, m, n, s, add_base=False, *, corr_one=True, s_on_lora=True, invert=False, honour_add=True):
+    base, lora, m, n = _f(base), _f(lora), _f(m), _f(n)
+    g = n / m if invert else m / n
+    y = ((g - 1.0) if corr_one else g) * base + g * (float(s) if s_on_lora else 1.0) * lora
+    if add_base and honour_add:
+        y = y + base
+    return y
+
+
+def _bwd(dy, base, lora, m, n, s, add_base=False, *, div_n=True, lora_sign=1.0, dbase_g=False,
+         dlora_s=True, extra_g=False):
+    dy, base, lora, m, n = _f(dy), _f(base), _f(lora), _f(m), _f(n)
+    g = m / n
+    s = float(s)
+    d_lora = g * (s if dlora_s else 1.0) * dy
+    d_base = (g if (add_base or dbase_g) else (g - 1.0)) * dy
+    d_mag = np.sum(dy * (base + lora_sign * s * lora), axis=0)
+    if div_n:
+        d_mag = d_mag / n
+    if extra_g:
+        d_mag = d_mag * g
+    return d_lora, d_base, d_mag
+
+
+MUTANTS = {
+    "norm_drops_s": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, 1.0)),
+    "norm_minus_adapter": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, s, sign=-1.0)),
+    "norm_s_squared": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, s, s_pow=2)),
+    "norm_no_sqrt": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, s, root=False)),
+    "norm_column_axis": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, s, axis=0)),
+    "norm_base_only": _mutant(weight_norm=lambda W0, A, B, s: np.linalg.norm(_f(W0), axis=1)),
+    "norm_drops_cross": _mutant(weight_norm=lambda W0, A, B, s: np.sqrt(
+        np.sum(_f(W0) ** 2, axis=1) + float(s) ** 2 * np.sum((_f(B) @ _f(A)) ** 2, axis=1))),
+    "norm_drops_gram": _mutant(weight_norm=lambda W0, A, B, s: np.sqrt(np.maximum(
+        np.sum(_f(W0) ** 2, axis=1) + 2 * float(s) * np.sum(_f(B) * (_f(W0) @ _f(A).T), axis=1), 0))),
+    "norm_transposed_gram": _mutant(weight_norm=lambda W0, A, B, s: np.sqrt(np.maximum(
+        np.sum(_f(W0) ** 2, axis=1) + 2 * float(s) * np.sum(_f(B) * (_f(W0) @ _f(A).T), axis=1)
+        + float(s) ** 2 * np.sum((_f(B) @ (_f(A) @ _f(A).T)[::-1, ::-1]) * _f(B), axis=1), 0))),
+    "fwd_no_minus_one": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, corr_one=False)),
+    "fwd_drops_s": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, s_on_lora=False)),
+    "fwd_inverted_g": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, invert=True)),
+    "fwd_ignores_add_base": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, honour_add=False)),
+    "bwd_no_div_n": _mutant(compose_bwd=lambda *a, add_base=False: _bwd(*a, add_base=add_base, div_n=False)),
+    "bwd_lora_sign": _mutant(compose_bwd=lambda *a, add_base=False: _bwd(*a, add_base=add_base, lora_sign=-1.0)),
+    "bwd_dbase_g": _mutant(compose_bwd=lambda *a, add_base=False: _bwd(*a, add_base=add_base, dbase_g=True)),
+    "bwd_dlora_no_s": _mutant(compose_bwd=lambda *a, add_base=False: _bwd(*a, add_base=add_base, dlora_s=False)),
+    "bwd_extra_g": _mutant(compose_bwd=lambda *a, add_base=False: _bwd(*a, add_base=add_base, extra_g=True)),
+}
+
+
+def test_mutant_helpers_match_oracle_when_unmutated():
+    # the helpers above reproduce the oracle when no mistake is planted, so a
+    # caught mutant is caught because of its mistake
+    rng = np.random.default_rng(0)
+    W0, A, B = rng.standard_normal((5, 7)), rng.standard_normal((3, 7)), rng.standard_normal((5, 3))
+    np.testing.assert_allclose(_norm_dense(W0, A, B, 1.3), O.weight_norm(W0, A, B, 1.3), rtol=1e-15)
+    base, lora, dy = rng.standard_normal((3, (4))), rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
+    m, n = rng.uniform(1, 2, 4), rng.uniform(1, 2, 4)
+    for ab in (False, True):
+        np.testing.assert_allclose(_fwd(base, lora, m, n, 0.7, ab), O.compose_fwd(base, lora, m, n, 0.7, ab), rtol=1e-15)
+        for x, y in zip(_bwd(dy, base, lora, m, n, 0.7, ab), O.compose_bwd(dy, base, lora, m, n, 0.7, ab)):
+            np.testing.assert_allclose(x, y, rtol=1e-15)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(MUTANTS[name])
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
