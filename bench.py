@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the DoRA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input at the
+8192 x 8192, rank-384 module (T = 8192 tokens, bf16): the factored weight norm,
+the compose forward and the compose backward with the magnitude gradient.  All
+inputs are resident in HBM before timing starts.  Kernels run on torch's current
+stream, so torch.cuda.Event pairs around each call time exactly that call's
+kernels.
+
+Prints one JSON line.  ``value`` is the compose fwd+bwd throughput in GB/s of
+algorithmic bytes (reads of base, lora, dy and writes of y, d_lora, d_base,
+plus the fp32 vectors); the factored norm time is reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from dora_fine_tuning_amd import binding, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+WORKLOAD = "wide_8192_r384"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compose_bwd_wide_8192_r384_traffic.json")
+COMPOSE_SRC = os.path.join(ROOT, "dora_fine_tuning_amd", "csrc", "compose.hip")
+
+
+def compose_bytes(T, out, e=2):
+    """Algorithmic bytes per call: fwd reads base+lora and writes y; bwd reads dy,
+    base, lora and writes d_lora, d_base; plus the fp32 m, n (and d_mag) vectors."""
+    fwd = 3 * e * T * out + 8 * out
+    bwd = 5 * e * T * out + 12 * out
+    return fwd, bwd
+
+
+def norm_work(out, in_, r, e=2):
+    byts = e * (out * in_ + r * in_ + out * r) + 4 * out
+    flops = 2 * out * in_ * r + 2 * r * r * in_ + 2 * out * r * r
+    return byts, flops
+
+
+def kernel_traffic(bwd_launch_bytes):
+    """HBM traffic of the compose backward from committed rocprofv3 counter runs,
+    or None when there are none or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    src = hashlib.sha256(open(COMPOSE_SRC, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != src:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, W0, A, B, base, lora, dy, sample_tokens):
+    """The CPU fp64 oracle timed on a bounded sample of the same workload."""
+    from oracle import dora_oracle as O
+
+    t = time.perf_counter()
+    n = O.weight_norm(W0, A, B, cfg.s)
+    norm_s = time.perf_counter() - t
+    m = synth.magnitude(n, synth.magnitude_eps(cfg))
+    n32 = n.astype(np.float32)
+    bs = base[:sample_tokens].cpu()
+    ls = lora[:sample_tokens].cpu()
+    ds = dy[:sample_tokens].cpu()
+    t = time.perf_counter()
+    O.compose_fwd(bs, ls, m, n32, cfg.s)
+    O.compose_bwd(ds, bs, ls, m, n32, cfg.s)
+    comp_s = time.perf_counter() - t
+    fb, bb = compose_bytes(sample_tokens, cfg.out)
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    return {
+        "value": (fb + bb) / comp_s / 1e9,
+        "unit": "GB/s",
+        # numpy elementwise ufuncs (the whole compose oracle) run on one thread
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"compose fwd+bwd (numpy fp64) on the first {sample_tokens} of {cfg.T} tokens x {cfg.out} "
+                  f"columns: {comp_s:.2f} s; factored-norm oracle (dense fp64, BLAS matmul on "
+                  f"{blas_threads} threads) on all {cfg.out} rows: {norm_s:.2f} s",
+        "norm_us": norm_s * 1e6,
+        "norm_threads": blas_threads,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (reference dispatch for byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[WORKLOAD]
+    T, out, in_, r, s = cfg.T, cfg.out, cfg.in_, cfg.r, cfg.s
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    W0c, Ac, Bc = synth.weights(cfg)
+    xc, dyc = synth.activations(cfg)
+    W0, A, B = W0c.to(dev), Ac.to(dev), Bc.to(dev)
+    base, lora = synth.base_and_lora(xc, W0c, Ac, Bc, device=dev)
+    dy = dyc.to(dev)
+    del xc
+    norm = torch.empty(out, dtype=torch.float32, device=dev)
+    ws_norm = torch.empty(binding.dora_norm_workspace_bytes(out, in_, r), dtype=torch.uint8, device=dev)
+    binding.dora_norm_factored(W0, A, B, s, norm_out=norm, workspace=ws_norm)
+    mag = torch.from_numpy(synth.magnitude(norm.cpu().numpy(), synth.magnitude_eps(cfg))).to(dev)
+    y = torch.empty_like(base)
+    d_lora = torch.empty_like(base)
+    d_base = torch.empty_like(base)
+    d_mag = torch.empty(out, dtype=torch.float32, device=dev)
+    ws_bwd = torch.empty(max(binding.dora_compose_bwd_workspace_bytes(T, out), 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        binding.dora_norm_factored(W0, A, B, s, norm_out=norm, workspace=ws_norm)
+        if ev:
+            ev[1].record()
+        binding.dora_compose_fwd(base, lora, mag, norm, s, y=y)
+        if ev:
+            ev[2].record()
+        binding.dora_compose_bwd(dy, base, lora, mag, norm, s, d_lora=d_lora, d_base=d_base, d_mag=d_mag,
+                                 workspace=ws_bwd)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    norm_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    fwd_b, bwd_b = compose_bytes(T, out)
+    comp_ms = fwd_ms.mean() + bwd_ms.mean()
+    value = (fwd_b + bwd_b) / (comp_ms * 1e-3) / 1e9
+    nb, nf = norm_work(out, in_, r)
+    bwd_gbs = bwd_b / (bwd_ms.mean() * 1e-3) / 1e9
+    traffic = kernel_traffic(bwd_b)
+
+    res = {
+        "metric": "DoRA compose fwd+bwd GB/s (% HBM peak); factored-norm us at 8192^2 r=384",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"DoRA module out=8192 in=8192 r=384 T=8192 tokens, bf16, s=32/sqrt(r)",
+                   "out": out, "in": in_, "r": r, "T": T},
+        "compose_frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "norm_us": round(float(norm_ms.mean()) * 1e3, 2),
+        "norm_tflops": round(nf / (norm_ms.mean() * 1e-3) / 1e12, 1),
+        "norm_frac_mfma_peak": round(nf / (norm_ms.mean() * 1e-3) / 2.5e15, 4),
+        "compose_fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
+        "compose_bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
+        "roofline": {
+            "kernel": "dora_compose_bwd (compose_bwd_vec + dmag_finalize)",
+            "bound": "hbm",
+            "achieved": round(bwd_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bwd_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bwd_b,
+            "avg_launch_us": round(float(bwd_ms.mean()) * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, W0c, Ac, Bc, base, lora, dy, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

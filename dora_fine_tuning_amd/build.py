@@ -1,0 +1,68 @@
+"""Build the HIP library libdora_hip.so in-tree with hipcc for gfx950.
+
+Every source under csrc/ is compiled to an object in parallel and linked into
+one shared library next to this file.  Packed fp32 instructions are disabled
+(-packed-fp32-ops) for all device code.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libdora_hip.so")
+ROOT = os.path.dirname(HERE)
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-fvisibility=hidden",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip and link libdora_hip.so; returns its path."""
+    srcs = sources()
+    tmp = tempfile.mkdtemp(prefix="dora_build_")
+    try:
+        objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
+        with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+            logs = list(ex.map(lambda so: _run([HIPCC, *COMMON, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+        tmp_lib = LIB + ".tmp"
+        logs.append(_run([HIPCC, *COMMON, "-shared", "-o", tmp_lib, *objs]))
+        os.replace(tmp_lib, LIB)
+        if verbose:
+            for l in logs:
+                if l.strip():
+                    print(l)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,185 @@
+// C ABI of the DoRA hot path: argument validation, workspace queries, launch
+// selection (16-byte fast path or general path) and the per-thread error string.
+// Every check runs before the first HIP call, so invalid calls touch no device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/dora.h"
+#include "compose_kernels.hpp"
+#include "norm_kernels.hpp"
+
+#ifndef DORA_VERSION_STRING
+#define DORA_VERSION_STRING "0.1.0"
+#endif
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return DORA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DORA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Two byte ranges [p, p + n) and [q, q + m) that overlap without being the same buffer.
+bool partial_overlap(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  if (a == b && n == m) return false;
+  return a < b + m && b < a + n;
+}
+
+bool any_overlap(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+bool valid_dtype(int dtype) { return dtype == DORA_BF16 || dtype == DORA_F16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dora_last_error(void) { return g_err.c_str(); }
+
+const char* dora_version(void) { return "dora_fine_tuning_amd " DORA_VERSION_STRING " (HIP, gfx950)"; }
+
+size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
+  if (out < 0 || in < 0 || r < 0 || !valid_dtype(dtype)) return 0;
+  return dora::make_norm_plan(out, in, r, dtype).bytes;
+}
+
+int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out, int64_t in, int64_t r, float s,
+                       int dtype, float* norm_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "dora_norm_factored: unknown dtype %d", dtype);
+  if (out < 0 || in < 0 || r < 0)
+    return fail(DORA_INVALID_ARG, "dora_norm_factored: negative size (out=%lld in=%lld r=%lld)", (long long)out,
+                (long long)in, (long long)r);
+  if (out == 0) return ok();
+  if (!norm_out) return fail(DORA_INVALID_ARG, "dora_norm_factored: norm_out is NULL");
+  if (in > 0 && !W0) return fail(DORA_INVALID_ARG, "dora_norm_factored: W0 is NULL");
+  if (r > 0 && in > 0 && !A) return fail(DORA_INVALID_ARG, "dora_norm_factored: A is NULL");
+  if (r > 0 && !B) return fail(DORA_INVALID_ARG, "dora_norm_factored: B is NULL");
+  const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype);
+  if (ws_bytes < plan.bytes)
+    return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace of %zu bytes, %zu needed", ws_bytes, plan.bytes);
+  if (plan.bytes > 0 && !ws) return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace is NULL");
+  const size_t e = 2;
+  const size_t nb = static_cast<size_t>(out) * 4;
+  if (any_overlap(norm_out, nb, ws, plan.bytes) || any_overlap(norm_out, nb, W0, out * in * e) ||
+      any_overlap(norm_out, nb, B, out * r * e) || any_overlap(norm_out, nb, A, r * in * e))
+    return fail(DORA_INVALID_ARG, "dora_norm_factored: norm_out overlaps an input or the workspace");
+  if (any_overlap(ws, plan.bytes, W0, out * in * e) || any_overlap(ws, plan.bytes, A, r * in * e) ||
+      any_overlap(ws, plan.bytes, B, out * r * e))
+    return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace overlaps an input");
+  const bool vec =
+      (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) && aligned16(ws);
+  dora::NormArgs a{W0, A, B, s, norm_out, ws, stream};
+  return hip_status(dora::launch_norm(plan, a, vec), "dora_norm_factored");
+}
+
+int dora_compose_fwd(const void* base, const void* lora, const float* mag, const float* norm, float s, int64_t T,
+                     int64_t out, int dtype, int add_base, void* y, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "dora_compose_fwd: unknown dtype %d", dtype);
+  if (T < 0 || out < 0)
+    return fail(DORA_INVALID_ARG, "dora_compose_fwd: negative size (T=%lld out=%lld)", (long long)T, (long long)out);
+  if (T == 0 || out == 0) return ok();
+  if (!base || !lora || !mag || !norm || !y) return fail(DORA_INVALID_ARG, "dora_compose_fwd: NULL pointer argument");
+  const size_t mb = static_cast<size_t>(T) * out * 2, vb = static_cast<size_t>(out) * 4;
+  if (partial_overlap(y, mb, base, mb) || partial_overlap(y, mb, lora, mb))
+    return fail(DORA_INVALID_ARG, "dora_compose_fwd: y partially overlaps base or lora");
+  if (any_overlap(y, mb, mag, vb) || any_overlap(y, mb, norm, vb))
+    return fail(DORA_INVALID_ARG, "dora_compose_fwd: y overlaps mag or norm");
+  dora::ComposeArgs a{};
+  a.dtype = dtype;
+  a.T = T;
+  a.out = out;
+  a.s = s;
+  a.add_base = add_base ? 1 : 0;
+  a.mag = mag;
+  a.norm = norm;
+  a.base = base;
+  a.lora = lora;
+  a.y = y;
+  a.stream = stream;
+  const bool vec = (out % 8 == 0) && aligned16(base) && aligned16(lora) && aligned16(y) && aligned16(mag) &&
+                   aligned16(norm);
+  return hip_status(dora::launch_compose_fwd(a, vec), "dora_compose_fwd");
+}
+
+size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out) {
+  if (T <= 0 || out <= 0) return 0;
+  return static_cast<size_t>((T + dora::kBwdRows - 1) / dora::kBwdRows) * static_cast<size_t>(out) * 4;
+}
+
+int dora_compose_bwd(const void* dy, const void* base, const void* lora, const float* mag, const float* norm, float s,
+                     int64_t T, int64_t out, int dtype, int add_base, void* d_lora, void* d_base, float* d_mag,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "dora_compose_bwd: unknown dtype %d", dtype);
+  if (T < 0 || out < 0)
+    return fail(DORA_INVALID_ARG, "dora_compose_bwd: negative size (T=%lld out=%lld)", (long long)T, (long long)out);
+  if (out == 0) return ok();
+  if (!norm || !d_mag) return fail(DORA_INVALID_ARG, "dora_compose_bwd: norm or d_mag is NULL");
+  if (T > 0 && (!dy || !base || !lora || !mag || !d_lora))
+    return fail(DORA_INVALID_ARG, "dora_compose_bwd: NULL pointer argument");
+  const size_t need = dora_compose_bwd_workspace_bytes(T, out);
+  if (ws_bytes < need) return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace is NULL");
+  const size_t mb = static_cast<size_t>(T) * out * 2, vb = static_cast<size_t>(out) * 4;
+  if (any_overlap(d_lora, mb, d_base, mb)) return fail(DORA_INVALID_ARG, "dora_compose_bwd: d_lora and d_base overlap");
+  const void* ins[3] = {dy, base, lora};
+  for (const void* p : ins) {
+    if (partial_overlap(d_lora, mb, p, mb) || partial_overlap(d_base, mb, p, mb))
+      return fail(DORA_INVALID_ARG, "dora_compose_bwd: an output partially overlaps an input");
+    if (any_overlap(ws, need, p, mb)) return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace overlaps an input");
+  }
+  if (any_overlap(ws, need, d_lora, mb) || any_overlap(ws, need, d_base, mb) || any_overlap(ws, need, d_mag, vb) ||
+      any_overlap(ws, need, norm, vb) || any_overlap(ws, need, mag, vb))
+    return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace overlaps an argument");
+  if (any_overlap(d_mag, vb, d_lora, mb) || any_overlap(d_mag, vb, d_base, mb) || any_overlap(d_mag, vb, dy, mb) ||
+      any_overlap(d_mag, vb, base, mb) || any_overlap(d_mag, vb, lora, mb) || partial_overlap(d_mag, vb, norm, vb) ||
+      partial_overlap(d_mag, vb, mag, vb))
+    return fail(DORA_INVALID_ARG, "dora_compose_bwd: d_mag overlaps another argument");
+  dora::ComposeArgs a{};
+  a.dtype = dtype;
+  a.T = T;
+  a.out = out;
+  a.s = s;
+  a.add_base = add_base ? 1 : 0;
+  a.mag = mag;
+  a.norm = norm;
+  a.dy = dy;
+  a.base = base;
+  a.lora = lora;
+  a.d_lora = d_lora;
+  a.d_base = d_base;
+  a.d_mag = d_mag;
+  a.partial = static_cast<float*>(ws);
+  a.stream = stream;
+  const bool vec = (out % 8 == 0) && aligned16(dy) && aligned16(base) && aligned16(lora) && aligned16(d_lora) &&
+                   (d_base == nullptr || aligned16(d_base)) && aligned16(mag) && aligned16(norm) && aligned16(ws);
+  return hip_status(dora::launch_compose_bwd(a, vec), "dora_compose_bwd");
+}
+
+}  // extern "C"

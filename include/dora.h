@@ -1,0 +1,151 @@
+/*
+ * dora.h -- C ABI of the DoRA adapter hot path on AMD Instinct MI355X (gfx950).
+ *
+ * DoRA (weight-decomposed low-rank adaptation) scales each output row of the
+ * adapted weight W0 + s*B*A by g = m / n, where m is a trained magnitude and
+ * n = ||W0_i + s*B_i*A||_2 is the weight norm of that row.  This library
+ * provides the three operations that the press summary of arXiv:2603.22276
+ * ("AI training breakthrough: Anthropic team cracks the memory bottleneck of
+ * large-model fine-tuning", techwalker.com/2026/0401/3182870) singles out:
+ *
+ *   dora_norm_factored  the weight norm as base + cross + Gram terms, never
+ *                       forming the out x in matrix B*A (paragraph on the
+ *                       "factored norm");
+ *   dora_compose_fwd    the fused magnitude compose in its stable form
+ *                       (g-1)*base + g*s*lora with fp32 intermediates
+ *                       (paragraphs on the fused kernel and on stability near
+ *                       g = 1; the forward-only inference tier);
+ *   dora_compose_bwd    its fused backward with the magnitude-gradient token
+ *                       reduction (paragraphs on the three-tier dispatch and on
+ *                       the convergence study's dmag reduction).
+ *
+ * Conventions shared by every entry point
+ *  - Matrices are row-major and contiguous.  W0 is [out x in], A is [r x in],
+ *    B is [out x r] (nn.Linear orientation); base, lora, y, dy, d_lora and
+ *    d_base are [T x out] (T tokens).  Vectors mag (m), norm (n) and d_mag are
+ *    fp32 [out].
+ *  - dtype selects the storage type of every matrix argument: DORA_BF16 or
+ *    DORA_F16.  Arithmetic is fp32 throughout; each stored output is rounded
+ *    once, to nearest even.
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises: each call enqueues its kernels on
+ *    `stream` and returns.  Scratch memory is passed in by the caller (size from
+ *    the *_workspace_bytes queries), so no call makes a transient allocation.
+ *  - Return value: DORA_OK, or a status below.  Arguments are validated before
+ *    any launch; on a non-zero status nothing was enqueued (except
+ *    DORA_HIP_ERROR, reported by the launch itself).  dora_last_error() gives
+ *    the message of the calling thread's last failure.
+ *  - Any sizes are accepted.  The fast paths need 16-byte aligned pointers and
+ *    a row length that is a multiple of 8 elements; other cases take a slower
+ *    general path with identical results.
+ *  - Results are deterministic: no floating-point atomics, fixed reduction
+ *    orders, so repeated calls give bitwise identical outputs.
+ */
+#ifndef DORA_H_
+#define DORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifndef DORA_API
+#define DORA_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dora_status {
+  DORA_OK = 0,
+  DORA_INVALID_ARG = 1, /* null pointer, negative size, workspace too small, bad alias */
+  DORA_UNSUPPORTED = 2, /* unknown dtype code */
+  DORA_HIP_ERROR = 3    /* a kernel launch failed (message from the HIP runtime) */
+};
+
+enum dora_dtype { DORA_BF16 = 0, DORA_F16 = 1 };
+
+/*
+ * Bytes of device workspace dora_norm_factored needs for these sizes.
+ * The scratch is O(out*r + r*r): split-K partial sums of G = A*A^T, the
+ * two-term split of (s/2)*G in the storage dtype, and per-split row partials.
+ * For r <= out it never exceeds 4*(out*r + r*r) + 64*out + 256 bytes (the
+ * factored norm's memory bound, paragraph on the factored norm; 256 bytes of
+ * region alignment).  Returns 0 for invalid
+ * sizes (negative) or an unknown dtype.
+ */
+DORA_API size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
+
+/*
+ * norm_out[i] = || W0_i + s * B_i * A ||_2, i in [0, out), in fp32.
+ *
+ * Computed as sqrt(base_i + cross_i + gram_i) with
+ *   base_i  = sum_k W0_ik^2,
+ *   cross_i = 2 s * sum_j B_ij * U_ij,   U = W0 * A^T   [out x r],
+ *   gram_i  = s^2 * B_i * G * B_i^T,     G = A * A^T    [r x r],
+ * (summary page, paragraph on the factored norm).  U and G are dense MFMA
+ * contractions with fp32 accumulation; U never leaves the registers.  A
+ * negative sum from rounding is clamped to 0.  The norm is a plain value: the
+ * backward of the compose treats it as a constant.
+ *
+ * W0, A, B: device, dtype.  A and B may be NULL when r == 0.  norm_out: device
+ * fp32 [out].  ws: device scratch of at least dora_norm_workspace_bytes(...)
+ * bytes, contents undefined on entry and exit; ws may be NULL when that size is
+ * 0.  out == 0 is a no-op; in == 0 gives n = 0.
+ */
+DORA_API int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out, int64_t in,
+                       int64_t r, float s, int dtype, float* norm_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * y = (g - 1) * base + g * s * lora, g_j = mag_j / norm_j broadcast over the T
+ * rows (summary page, paragraph on stability near g = 1).  g - 1 is formed as
+ * (mag - norm) / norm, whose subtraction is exact when mag/norm is in [1/2, 2],
+ * so the base correction is nonzero wherever mag != norm and base != 0.  With
+ * add_base != 0, y = base + that delta (the full layer output) in the same
+ * pass.  One read of base and lora, one write of y.
+ *
+ * base, lora, y: device, dtype, [T x out].  mag, norm: device fp32 [out].
+ * y may be the same buffer as base or lora (in place); no other overlap.
+ * T == 0 or out == 0 is a no-op.  norm_j == 0 follows IEEE division.
+ */
+DORA_API int dora_compose_fwd(const void* base, const void* lora, const float* mag, const float* norm, float s,
+                     int64_t T, int64_t out, int dtype, int add_base, void* y, hipStream_t stream);
+
+/* Bytes of device workspace dora_compose_bwd needs (per-token-block fp32 partial sums). */
+DORA_API size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out);
+
+/*
+ * Backward of dora_compose_fwd for L = sum(dy * y), with norm held constant:
+ *   d_lora = g * s * dy
+ *   d_base = (g - 1) * dy         (add_base == 0)
+ *          = g * dy               (add_base != 0)
+ *   d_mag_j = sum_t dy_tj * (base_tj + s * lora_tj) / norm_j
+ * (summary page: fused backward of the training tier; the magnitude gradient is
+ * a token reduction whose order may differ from an eager implementation).  The
+ * reduction is fixed-order: fp32 partial sums over blocks of tokens, combined
+ * in fp64 in a second kernel, so d_mag is bitwise reproducible.
+ *
+ * dy, base, lora, d_lora, d_base: device, dtype, [T x out]; d_base may be NULL
+ * (not computed).  mag, norm, d_mag: device fp32 [out].  d_lora may be the same
+ * buffer as dy or lora; d_base may be the same buffer as dy or base; d_lora
+ * and d_base must differ.  ws: at least dora_compose_bwd_workspace_bytes(T,
+ * out) bytes.  out == 0 is a no-op; T == 0 writes d_mag = 0 / norm.
+ */
+DORA_API int dora_compose_bwd(const void* dy, const void* base, const void* lora, const float* mag,
+                     const float* norm, float s, int64_t T, int64_t out, int dtype, int add_base,
+                     void* d_lora, void* d_base, float* d_mag, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Message of the calling thread's last non-OK status ("" if none).  Valid until the next call. */
+DORA_API const char* dora_last_error(void);
+
+/* Library build string (version, target architecture). */
+DORA_API const char* dora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DORA_H_ */

@@ -1,0 +1,134 @@
+"""The C-ABI library on the host: it loads, exports every entry point the header
+declares, answers workspace queries inside the factored memory bound, and
+rejects invalid arguments before any launch (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dora_fine_tuning_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = binding.LIB
+OK, INVALID, UNSUPPORTED = binding.DORA_OK, binding.DORA_INVALID_ARG, binding.DORA_UNSUPPORTED
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dora.h")).read()
+    return re.findall(r"DORA_API\s+[\w\s\*]+?\b(dora_\w+)\s*\(", text)
+
+
+def test_header_declarations_are_exported():
+    names = declared_symbols()
+    assert set(names) == set(binding.EXPORTS), names
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version():
+    v = binding.dora_version()
+    assert "gfx950" in v and "dora_fine_tuning_amd" in v
+
+
+def bound(out, r):
+    return 4 * (out * r + r * r) + 64 * out + 256
+
+
+@pytest.mark.parametrize("name", sorted(synth.CONFIGS))
+def test_norm_workspace_within_factored_bound(name):
+    c = synth.CONFIGS[name]
+    for dt in (0, 1):
+        ws = LIB.dora_norm_workspace_bytes(c.out, c.in_, c.r, dt)
+        assert 0 < ws <= bound(c.out, c.r), (name, ws, bound(c.out, c.r))
+    # the 8192 x 8192 rank-384 module: scratch far below one dense fp32 out x in buffer
+    if name == "wide_8192_r384":
+        assert LIB.dora_norm_workspace_bytes(8192, 8192, 384, 0) < 8192 * 8192 * 4 / 15
+
+
+def test_norm_workspace_bound_over_shapes():
+    for out in (1, 7, 128, 129, 1000, 4096, 27648):
+        for in_ in (0, 8, 100, 4096):
+            for r in (0, 1, 8, 16, 64, 130, 384, 768):
+                if r > out:
+                    continue
+                ws = LIB.dora_norm_workspace_bytes(out, in_, r, 0)
+                assert ws <= bound(out, r), (out, in_, r, ws)
+
+
+def test_workspace_queries_invalid():
+    assert LIB.dora_norm_workspace_bytes(-1, 8, 8, 0) == 0
+    assert LIB.dora_norm_workspace_bytes(8, 8, 8, 7) == 0
+    assert LIB.dora_norm_workspace_bytes(0, 8, 8, 0) == 0
+    assert LIB.dora_compose_bwd_workspace_bytes(0, 8) == 0
+    assert LIB.dora_compose_bwd_workspace_bytes(64, 8) == 2 * 8 * 4  # two 32-token blocks
+
+
+P = 1 << 20  # fake, never dereferenced: every call below fails validation first
+
+
+def _status(ret, want, fragment):
+    assert ret == want, (ret, binding.dora_last_error())
+    assert fragment in binding.dora_last_error()
+
+
+def test_norm_validation():
+    ws = LIB.dora_norm_workspace_bytes(64, 64, 8, 0)
+    _status(LIB.dora_norm_factored(P, P, P, 64, 64, 8, 1.0, 5, P * 2, P * 3, ws, None), UNSUPPORTED, "dtype")
+    _status(LIB.dora_norm_factored(P, P, P, -1, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID, "negative")
+    _status(LIB.dora_norm_factored(None, P, P, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID, "W0")
+    _status(LIB.dora_norm_factored(P, None, P, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID, "A")
+    _status(LIB.dora_norm_factored(P, P, None, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID, "B")
+    _status(LIB.dora_norm_factored(P, P, P, 64, 64, 8, 1.0, 0, None, P * 3, ws, None), INVALID, "norm_out")
+    _status(LIB.dora_norm_factored(P, P, P, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws - 1, None), INVALID, "workspace")
+    _status(LIB.dora_norm_factored(P, P, P, 64, 64, 8, 1.0, 0, P * 2, None, ws, None), INVALID, "NULL")
+    _status(LIB.dora_norm_factored(P * 8, P * 9, P * 10, 64, 64, 8, 1.0, 0, P * 8 + 4, P * 3, ws, None),
+            INVALID, "overlaps")
+    # out == 0 is a no-op that succeeds without touching the device
+    assert LIB.dora_norm_factored(None, None, None, 0, 64, 8, 1.0, 0, None, None, 0, None) == OK
+    assert binding.dora_last_error() == ""
+
+
+def test_compose_fwd_validation():
+    _status(LIB.dora_compose_fwd(P, P * 2, P * 3, P * 4, 1.0, 8, 8, 3, 0, P * 5, None), UNSUPPORTED, "dtype")
+    _status(LIB.dora_compose_fwd(P, P * 2, P * 3, P * 4, 1.0, -8, 8, 0, 0, P * 5, None), INVALID, "negative")
+    _status(LIB.dora_compose_fwd(P, None, P * 3, P * 4, 1.0, 8, 8, 0, 0, P * 5, None), INVALID, "NULL")
+    _status(LIB.dora_compose_fwd(P, P * 2, P * 3, P * 4, 1.0, 8, 8, 0, 0, P + 2, None), INVALID, "partially")
+    _status(LIB.dora_compose_fwd(P, P * 2, P * 3, P * 4, 1.0, 8, 8, 0, 0, P * 3, None), INVALID, "mag")
+    assert LIB.dora_compose_fwd(None, None, None, None, 1.0, 0, 8, 0, 0, None, None) == OK
+    assert LIB.dora_compose_fwd(None, None, None, None, 1.0, 8, 0, 0, 0, None, None) == OK
+
+
+def test_compose_bwd_validation():
+    T, out = 64, 16
+    ws = LIB.dora_compose_bwd_workspace_bytes(T, out)
+    args = dict(dy=P, base=P * 2, lora=P * 3, mag=P * 4, norm=P * 5, d_lora=P * 6, d_base=P * 7, d_mag=P * 8,
+                ws=P * 9)
+
+    def call(dtype=0, T=T, ws_bytes=ws, **kw):
+        a = dict(args, **kw)
+        return LIB.dora_compose_bwd(a["dy"], a["base"], a["lora"], a["mag"], a["norm"], 1.0, T, out, dtype, 0,
+                                    a["d_lora"], a["d_base"], a["d_mag"], a["ws"], ws_bytes, None)
+
+    _status(call(dtype=9), UNSUPPORTED, "dtype")
+    _status(call(T=-1), INVALID, "negative")
+    _status(call(d_mag=None), INVALID, "d_mag")
+    _status(call(dy=None), INVALID, "NULL")
+    _status(call(ws_bytes=ws - 4), INVALID, "workspace")
+    _status(call(ws=None), INVALID, "workspace is NULL")
+    _status(call(d_base=P * 6 + 2), INVALID, "d_lora and d_base overlap")
+    _status(call(d_lora=P + 2), INVALID, "partially overlaps")
+    _status(call(ws=P * 2), INVALID, "workspace overlaps")
+    _status(call(d_mag=P * 2 + 8), INVALID, "d_mag overlaps")
+    assert LIB.dora_compose_bwd(None, None, None, None, None, 1.0, 8, 0, 0, 0, None, None, None, None, 0, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    W0 = torch.zeros(8, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        binding.dora_norm_factored(W0, W0, W0, 1.0)
+    with pytest.raises(ValueError, match="dtype"):
+        binding.dora_compose_fwd(W0.float(), W0.float(), None, None, 1.0)

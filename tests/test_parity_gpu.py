@@ -1,0 +1,284 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU fp64 oracle.
+
+Small shapes span several tiles with ragged tails and run both the 16-byte and
+the general path; the adapter configs run at full size, in the same launch
+configuration as the benchmark, with every norm row and sampled compose rows
+and gradient columns compared with the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity_util as PU
+from dora_fine_tuning_amd import synth
+from oracle import dora_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "GPU parity tests need a HIP device"
+    from dora_fine_tuning_amd import binding
+
+    return binding
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------- norm
+
+NORM_SMALL = [
+    (300, 520, 24),   # ragged rows, rank tile and K stage; 16-byte path
+    (257, 1000, 136),  # two rank tiles, ragged everywhere
+    (130, 75, 13),    # in, r not multiples of 8: general path
+    (512, 512, 16),   # the tiny module
+    (64, 64, 0),      # no adapter: plain row norms
+    (5, 0, 8),        # empty input axis
+    (1, 8, 8),
+    (33, 200, 200),   # rank above out
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("shape", NORM_SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_norm_small(lib, shape, dtype):
+    out, in_, r = shape
+    cfg = synth.custom("norm_small", out, in_, r, 1)
+    W0, A, B = synth.weights(cfg, dtype)
+    s = cfg.s
+    n_gpu = lib.dora_norm_factored(W0.to(DEV), A.to(DEV), B.to(DEV), s)
+    ref = O.weight_norm(W0, A, B, s)
+    mass = PU.norm_term_mass(f64(W0), f64(A), f64(B), s)
+    PU.assert_norm(f64(n_gpu), ref, mass, f"norm {shape} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_norm_large_adapter(lib, dtype):
+    """A trained-looking adapter (B 30x larger): the Gram and cross terms carry
+    a large share of n^2, which stresses the split of G."""
+    cfg = synth.custom("norm_big_B", 384, 1024, 64, 1)
+    W0, A, B = synth.weights(cfg, dtype)
+    B = (B.float() * 30).to(B.dtype)
+    n_gpu = lib.dora_norm_factored(W0.to(DEV), A.to(DEV), B.to(DEV), cfg.s)
+    ref = O.weight_norm(W0, A, B, cfg.s)
+    W, Af, Bf = f64(W0), f64(A), f64(B)
+    gram = cfg.s**2 * np.sum((Bf @ (Af @ Af.T)) * Bf, axis=1)
+    assert np.median(gram / ref**2) > 0.5  # the Gram term dominates
+    PU.assert_norm(f64(n_gpu), ref, PU.norm_term_mass(W, Af, Bf, cfg.s), f"norm big B {dtype}")
+
+
+def test_norm_exact_cancellation(lib):
+    """W0 = -s B A with dyadic entries: every product and sum is exact, n = 0."""
+    rng = np.random.default_rng(7)
+    out, in_, r, s = 200, 136, 8, 2.0
+    A = rng.choice([-1.0, -0.5, 0.0, 0.5, 1.0], size=(r, in_))
+    B = rng.choice([-0.25, 0.0, 0.25, 0.5], size=(out, r))
+    W0 = -s * (B @ A)
+    W0[::3] += 0.125  # every third row keeps a known residual: n^2 = in * 2^-6
+    t = lambda a: torch.tensor(a, dtype=torch.bfloat16)
+    assert np.array_equal(t(W0).double().numpy(), W0)
+    n_gpu = f64(lib.dora_norm_factored(t(W0).to(DEV), t(A).to(DEV), t(B).to(DEV), s))
+    ref = O.weight_norm(W0, A, B, s)
+    np.testing.assert_array_equal(ref[1::3], 0.0)
+    PU.assert_norm(n_gpu, ref, PU.norm_term_mass(W0, A, B, s), "cancellation")
+    np.testing.assert_allclose(n_gpu[::3], np.sqrt(in_ * 2.0**-6), rtol=1e-6)
+
+
+def test_norm_b_zero_is_plain_row_norm(lib):
+    cfg = synth.custom("bzero", 300, 1024, 32, 1)
+    W0, A, B = synth.weights(cfg)
+    n_gpu = f64(lib.dora_norm_factored(W0.to(DEV), A.to(DEV), torch.zeros_like(B).to(DEV), cfg.s))
+    np.testing.assert_allclose(n_gpu, np.linalg.norm(f64(W0), axis=1), rtol=1e-6)
+
+
+# -------------------------------------------------------------------------- compose
+
+COMPOSE_SMALL = [(37, 1000), (50, 517), (1, 8), (3, 2056), (70, 4104), (33, 8)]
+
+
+def _compose_case(T, out, dtype, seed, eps=1e-3):
+    rng = np.random.default_rng(seed)
+    base = synth.to_dtype(rng.standard_normal((T, out), dtype=np.float32) * 1.8, dtype)
+    lora = synth.to_dtype(rng.standard_normal((T, out), dtype=np.float32) * 0.08, dtype)
+    dy = synth.to_dtype(rng.standard_normal((T, out), dtype=np.float32), dtype)
+    n = rng.uniform(0.5, 2.0, out).astype(np.float32)
+    m = synth.magnitude(n, rng.standard_normal(out) * eps)
+    return base, lora, dy, m, n
+
+
+def _check_compose(lib, base, lora, dy, m, n, s, dtype, tag, add_base_modes=(False, True)):
+    bd, ld, dyd = base.to(DEV), lora.to(DEV), dy.to(DEV)
+    md, nd = torch.from_numpy(m).to(DEV), torch.from_numpy(n).to(DEV)
+    B_, L_, D_ = f64(base), f64(lora), f64(dy)
+    g = m.astype(np.float64) / n.astype(np.float64)
+    floor_only = 0
+    for add_base in add_base_modes:
+        y = f64(lib.dora_compose_fwd(bd, ld, md, nd, s, add_base=add_base))
+        ref = O.compose_fwd(B_, L_, m, n, s, add_base=add_base)
+        mass = np.abs((g - 1) * B_) + np.abs(g * s * L_) + (np.abs(B_) if add_base else 0)
+        floor_only += PU.assert_compose(y, ref, mass, dtype, f"{tag} fwd add_base={add_base}")
+        dl, db, dm = lib.dora_compose_bwd(dyd, bd, ld, md, nd, s, add_base=add_base)
+        rl, rb, rm = O.compose_bwd(D_, B_, L_, m, n, s, add_base=add_base)
+        PU.assert_compose(f64(dl), rl, np.abs(rl), dtype, f"{tag} d_lora")
+        PU.assert_compose(f64(db), rb, np.abs(rb), dtype, f"{tag} d_base")
+        cond = np.sum(np.abs(D_ * (B_ + s * L_)), axis=0) / n
+        PU.assert_dmag(f64(dm), rm, cond, f"{tag} d_mag")
+    return floor_only
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("shape", COMPOSE_SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_compose_small(lib, shape, dtype):
+    T, out = shape
+    base, lora, dy, m, n = _compose_case(T, out, dtype, seed=T * 7919 + out)
+    _check_compose(lib, base, lora, dy, m, n, 4.0, dtype, f"compose {shape} {dtype}")
+
+
+def test_compose_without_d_base_and_empty_tokens(lib):
+    base, lora, dy, m, n = _compose_case(40, 1024, "bf16", seed=3)
+    bd, ld, dyd = base.to(DEV), lora.to(DEV), dy.to(DEV)
+    md, nd = torch.from_numpy(m).to(DEV), torch.from_numpy(n).to(DEV)
+    dl, db, dm = lib.dora_compose_bwd(dyd, bd, ld, md, nd, 2.0, want_d_base=False)
+    assert db is None
+    dl2, _, dm2 = lib.dora_compose_bwd(dyd, bd, ld, md, nd, 2.0)
+    assert torch.equal(dl, dl2) and torch.equal(dm, dm2)
+    # no tokens: forward is a no-op, the magnitude gradient is an empty sum
+    e = torch.empty((0, 1024), dtype=torch.bfloat16, device=DEV)
+    assert lib.dora_compose_fwd(e, e, md, nd, 2.0).shape == (0, 1024)
+    _, _, dm0 = lib.dora_compose_bwd(e, e, e, md, nd, 2.0)
+    assert torch.all(dm0 == 0)
+
+
+def test_compose_in_place_matches(lib):
+    base, lora, dy, m, n = _compose_case(64, 2048, "bf16", seed=11)
+    bd, ld = base.to(DEV), lora.to(DEV)
+    md, nd = torch.from_numpy(m).to(DEV), torch.from_numpy(n).to(DEV)
+    y = lib.dora_compose_fwd(bd, ld, md, nd, 3.0, add_base=True)
+    bd2 = bd.clone()
+    lib.dora_compose_fwd(bd2, ld, md, nd, 3.0, add_base=True, y=bd2)
+    assert torch.equal(y, bd2)
+    dyd = dy.to(DEV)
+    dl, db, dm = lib.dora_compose_bwd(dyd, bd, ld, md, nd, 3.0)
+    dy2 = dyd.clone()
+    dl2, _, dm2 = lib.dora_compose_bwd(dy2, bd, ld, md, nd, 3.0, d_lora=dy2, want_d_base=False)
+    assert torch.equal(dl, dl2) and torch.equal(dm, dm2)
+
+
+def test_compose_identity_invariants(lib):
+    """g = 1 exactly: the correction is exactly zero; with lora = 0 the full
+    output is base bit for bit and the delta is zero."""
+    base, lora, dy, _, n = _compose_case(48, 1536, "bf16", seed=5)
+    bd = base.to(DEV)
+    nd = torch.from_numpy(n).to(DEV)
+    z = torch.zeros_like(bd)
+    assert torch.equal(lib.dora_compose_fwd(bd, z, nd, nd, 5.0, add_base=True), bd)
+    assert torch.all(lib.dora_compose_fwd(bd, z, nd, nd, 5.0) == 0)
+    # g = 1, lora != 0: the delta is s * lora rounded once
+    ld = lora.to(DEV)
+    y = f64(lib.dora_compose_fwd(bd, ld, nd, nd, 5.0))
+    np.testing.assert_array_equal(y, synth.to_dtype((5.0 * f64(lora)).astype(np.float32), "bf16").double().numpy())
+
+
+# ------------------------------------------------------------ full-size adapter configs
+
+FULL = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("mlp_up_27648x5120", "bf16")]
+FULL += [(f"sweep_r{r}", dt) for r in (16, 64, 128, 384, 512, 768) for dt in ("bf16", "fp16")]
+
+
+@pytest.mark.parametrize("name,dtype", FULL, ids=[f"{a}-{b}" for a, b in FULL])
+def test_full_config(lib, name, dtype):
+    cfg = synth.CONFIGS[name]
+    log(f"[full] {name} {dtype}: generating")
+    W0, A, B = synth.weights(cfg, dtype)
+    W0d, Ad, Bd = W0.to(DEV), A.to(DEV), B.to(DEV)
+    n_gpu = f64(lib.dora_norm_factored(W0d, Ad, Bd, cfg.s))
+    n_ref = O.weight_norm(W0, A, B, cfg.s)
+    W, Af, Bf = f64(W0), f64(A), f64(B)
+    PU.assert_norm(n_gpu, n_ref, PU.norm_term_mass(W, Af, Bf, cfg.s), f"{name} norm")
+    log(f"[full] {name} {dtype}: norm ok (max rel {np.max(np.abs(n_gpu - n_ref) / n_ref):.2e})")
+    del W, Af, Bf
+
+    x, dy = synth.activations(cfg, dtype)
+    base, lora = synth.base_and_lora(x, W0, A, B, device=DEV)
+    del x
+    n32 = n_ref.astype(np.float32)
+    m = synth.magnitude(n_ref, synth.magnitude_eps(cfg))
+    md, nd = torch.from_numpy(m).to(DEV), torch.from_numpy(n32).to(DEV)
+    dyd = dy.to(DEV)
+    rng = np.random.default_rng(cfg.index)
+    rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 62, replace=False)]))
+    cols = np.unique(np.concatenate([[0, cfg.out - 1], rng.choice(cfg.out, 254, replace=False)]))
+    ri, ci = torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)
+    Br, Lr, Dr = f64(base[ri]), f64(lora[ri]), f64(dyd[ri])
+    g = m.astype(np.float64) / n32.astype(np.float64)
+    s = cfg.s
+    for add_base in (False, True):
+        y = lib.dora_compose_fwd(base, lora, md, nd, s, add_base=add_base)
+        ref = O.compose_fwd(Br, Lr, m, n32, s, add_base=add_base)
+        mass = np.abs((g - 1) * Br) + np.abs(g * s * Lr) + (np.abs(Br) if add_base else 0)
+        fo = PU.assert_compose(f64(y[ri]), ref, mass, dtype, f"{name} fwd add_base={add_base}")
+        del y
+        dl, db, dm = lib.dora_compose_bwd(dyd, base, lora, md, nd, s, add_base=add_base)
+        rl, rb, _ = O.compose_bwd(Dr, Br, Lr, m, n32, s, add_base=add_base)
+        PU.assert_compose(f64(dl[ri]), rl, np.abs(rl), dtype, f"{name} d_lora")
+        PU.assert_compose(f64(db[ri]), rb, np.abs(rb), dtype, f"{name} d_base")
+        Bc, Lc, Dc = f64(base[:, ci]), f64(lora[:, ci]), f64(dyd[:, ci])
+        _, _, rm = O.compose_bwd(Dc, Bc, Lc, m[cols], n32[cols], s, add_base=add_base)
+        cond = np.sum(np.abs(Dc * (Bc + s * Lc)), axis=0) / n32[cols]
+        PU.assert_dmag(f64(dm)[cols], rm, cond, f"{name} d_mag")
+        del dl, db, dm, Bc, Lc, Dc
+        log(f"[full] {name} {dtype}: compose add_base={add_base} ok ({fo} floor-only elements)")
+
+    # near-unity region: with lora = 0 the delta is the base correction alone and
+    # must be nonzero wherever the oracle's is (|g - 1| < 2^-8 columns included),
+    # as far as the storage dtype can hold it: fp16 rounds magnitudes at or below
+    # 2^-25 to zero
+    z = torch.zeros_like(lora)
+    y = f64(lib.dora_compose_fwd(base, z, md, nd, s)[ri])
+    ref = O.compose_fwd(Br, np.zeros_like(Br), m, n32, s)
+    near = np.abs(g - 1) < 2.0**-8
+    assert near.any()
+    want = PU.representable_nonzero(ref, dtype)[:, near]
+    assert np.all((y != 0)[:, near] == want)
+    log(f"[full] {name} {dtype}: near-unity correction nonzero in all {int(want.sum())} representable elements "
+        f"({int(((ref != 0)[:, near] & ~want).sum())} below the dtype's range)")
+    PU.assert_compose(y, ref, np.abs((g - 1) * Br), dtype, f"{name} correction only")
+    # the naive low-precision compose (g rounded to the storage dtype first)
+    # loses the correction in every collapsed column
+    g_lo = synth.to_dtype(g.astype(np.float32), dtype).double().numpy()
+    collapsed = (g_lo == 1.0) & (g != 1.0)
+    log(f"[full] {name} {dtype}: {collapsed.mean():.1%} of columns collapse under a naive {dtype} compose, "
+        f"{near.mean():.1%} have |g-1| < 2^-8")
+    if name == "wide_8192_r384":
+        assert collapsed.mean() > 0.5
+        assert np.all(y[:, collapsed][Br[:, collapsed] != 0] != 0)
+
+
+def test_determinism_and_streams(lib):
+    """Bitwise identical norm and gradients across calls and across streams."""
+    cfg = synth.CONFIGS["attn_proj"]
+    W0, A, B = (t.to(DEV) for t in synth.weights(cfg))
+    n1 = lib.dora_norm_factored(W0, A, B, cfg.s)
+    n2 = lib.dora_norm_factored(W0, A, B, cfg.s)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        n3 = lib.dora_norm_factored(W0, A, B, cfg.s)
+    side.synchronize()
+    assert torch.equal(n1, n2) and torch.equal(n1, n3)
+    base, lora, dy, m, n = _compose_case(cfg.T, cfg.out, "bf16", seed=1)
+    args = [t.to(DEV) for t in (dy, base, lora)] + [torch.from_numpy(m).to(DEV), torch.from_numpy(n).to(DEV)]
+    r1 = lib.dora_compose_bwd(*args, cfg.s)
+    r2 = lib.dora_compose_bwd(*args, cfg.s)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
