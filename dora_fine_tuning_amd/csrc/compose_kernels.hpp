@@ -8,7 +8,7 @@ namespace dora {
 
 // Tokens per block of the backward; one fp32 partial of the magnitude gradient
 // per (token block, column) lives in the workspace.
-constexpr int kBwdRows = 32;
+constexpr int kBwdRows = 64;
 
 struct ComposeArgs {
   int dtype;

@@ -67,7 +67,7 @@ const char* dora_version(void) { return "dora_fine_tuning_amd " DORA_VERSION_STR
 
 size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
   if (out < 0 || in < 0 || r < 0 || !valid_dtype(dtype)) return 0;
-  return dora::make_norm_plan(out, in, r, dtype).bytes;
+  return dora::norm_workspace_bytes(out, in, r, dtype);
 }
 
 int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out, int64_t in, int64_t r, float s,
@@ -81,22 +81,25 @@ int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out
   if (in > 0 && !W0) return fail(DORA_INVALID_ARG, "dora_norm_factored: W0 is NULL");
   if (r > 0 && in > 0 && !A) return fail(DORA_INVALID_ARG, "dora_norm_factored: A is NULL");
   if (r > 0 && !B) return fail(DORA_INVALID_ARG, "dora_norm_factored: B is NULL");
-  const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype);
-  if (ws_bytes < plan.bytes)
-    return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace of %zu bytes, %zu needed", ws_bytes, plan.bytes);
-  if (plan.bytes > 0 && !ws) return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace is NULL");
+  const size_t need = dora::norm_workspace_bytes(out, in, r, dtype);
+  if (ws_bytes < need)
+    return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace is NULL");
   const size_t e = 2;
   const size_t nb = static_cast<size_t>(out) * 4;
-  if (any_overlap(norm_out, nb, ws, plan.bytes) || any_overlap(norm_out, nb, W0, out * in * e) ||
+  if (any_overlap(norm_out, nb, ws, need) || any_overlap(norm_out, nb, W0, out * in * e) ||
       any_overlap(norm_out, nb, B, out * r * e) || any_overlap(norm_out, nb, A, r * in * e))
     return fail(DORA_INVALID_ARG, "dora_norm_factored: norm_out overlaps an input or the workspace");
-  if (any_overlap(ws, plan.bytes, W0, out * in * e) || any_overlap(ws, plan.bytes, A, r * in * e) ||
-      any_overlap(ws, plan.bytes, B, out * r * e))
+  if (any_overlap(ws, need, W0, out * in * e) || any_overlap(ws, need, A, r * in * e) ||
+      any_overlap(ws, need, B, out * r * e))
     return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace overlaps an input");
-  const bool vec =
-      (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) && aligned16(ws);
+  // 16-byte path: 16-byte rows and pointers, and 32-bit buffer offsets over a
+  // 128-row panel of W0 and a 512-row panel of G'
+  const bool vec = (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) &&
+                   aligned16(ws) && in <= (int64_t(1) << 22) && r <= (int64_t(1) << 20);
+  const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype, vec);
   dora::NormArgs a{W0, A, B, s, norm_out, ws, stream};
-  return hip_status(dora::launch_norm(plan, a, vec), "dora_norm_factored");
+  return hip_status(dora::launch_norm(plan, a), "dora_norm_factored");
 }
 
 int dora_compose_fwd(const void* base, const void* lora, const float* mag, const float* norm, float s, int64_t T,

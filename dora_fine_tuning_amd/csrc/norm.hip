@@ -7,20 +7,23 @@
 // O(out*r + r*r)).
 //
 // Kernels, in launch order:
-//   gram_kernel    split-K partials of G over upper-triangular 64x64 tiles
-//                  (G is symmetric), MFMA 32x32x16 with fp32 accumulation;
-//   gram_finalize  fixed-order fp64 sum of the partials, G' = (s/2) G split
-//                  into two storage-dtype matrices G'hi + G'lo;
-//   wstream_kernel one pass over W0.  A workgroup owns 128 rows x 128 rank
-//                  columns and a slice of the augmented K axis
-//                    [ W0 | B | B ] . [ A | G'hi | G'lo ]^T
-//                  so its accumulator holds U + B G' = U + (s/2) B G for those
-//                  rows and columns.  The epilogue reduces B_ij * acc_ij over its
-//                  columns (cross + Gram share one dot product:
-//                  2s * sum_j B_ij (U + (s/2) B G)_ij = cross_i + gram_i), and
-//                  the loader squares the W0 chunks it moves to LDS for the base
-//                  term.  U is never written to memory.
-//   norm_finalize  n_i = sqrt(max(sum of partials, 0)) in fp64, rounded to fp32.
+//   gram_partial      split-K partials of G = A A^T on upper-triangular 32x32
+//                     tiles (G is symmetric), MFMA 32x32x16 with fp32
+//                     accumulation;
+//   gram_finalize     fixed-order sum of the partials, then G' = (s/2) G split
+//                     into two storage-dtype matrices G'hi + G'lo (written with
+//                     their mirror images);
+//   wstream_dma       (16-byte path) one pass over W0.  A workgroup owns 128 rows
+//   wstream_general   (general path) x a block of rank columns and a slice of the
+//                     augmented K axis
+//                       [ W0 | B | B ] . [ A | G'hi | G'lo ]^T
+//                     so its accumulator holds U + B G' = U + (s/2) B G for those
+//                     rows and columns.  The epilogue reduces B_ij * acc_ij over
+//                     its columns, since 2s * sum_j B_ij (U + (s/2) B G)_ij =
+//                     cross_i + gram_i, and the W0 elements the waves read for
+//                     the MFMAs are also squared for the base term.  U is never
+//                     written to memory;
+//   norm_finalize     n_i = sqrt(max(sum of partials, 0)) in fp64, rounded to fp32.
 //
 // All reductions are in fixed order, so the result is bitwise reproducible.
 #include <algorithm>
@@ -32,29 +35,112 @@ namespace dora {
 
 namespace {
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15); }
 
-// MFMA tile of a workgroup: BM x BN outputs, K stage BK, WM x WN waves each
-// owning (BM/WM) x (BN/WN) outputs as 32x32 MFMA tiles.  LDS rows are padded
-// by 8 elements (16 bytes) so the 16-byte fragment reads of 16 consecutive
-// rows fall in distinct bank groups.
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
-struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-  static constexpr int NT = WM * WN * 64;
-  static constexpr int TM = BM / (WM * 32), TN = BN / (WN * 32);
-  static constexpr int LDK = BK + 8;
-  static constexpr int CPR = BK / 8;
-  static constexpr int RPP = NT / CPR;
-  static constexpr int XCH = BM / RPP, YCH = BN / RPP;
-  static constexpr int LDS_ELEMS = 2 * (BM + BN) * LDK;
-  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile");
-  static_assert(NT % CPR == 0 && BM % RPP == 0 && BN % RPP == 0, "loader mapping");
-};
+// ---------------------------------------------------------------------------
+// Gram matrix
 
-using TileW = Tile<128, 128, 64, 2, 2>;
-using TileG = Tile<64, 64, 64, 2, 2>;
+constexpr int kGramU = 8;  // K steps per batch of fragment loads
+
+// Split-K partial products of G on its upper-triangular 32x32 tiles (G is
+// symmetric).  Workgroup (tile, split) = 4 waves; each wave accumulates a
+// quarter of the split's K steps with MFMA 32x32x16, its operand fragments
+// loaded straight from global memory (A is small and L2/MALL resident) in
+// batches of kGramU steps; the four wave partials are summed in LDS in a fixed
+// order and stored as the split's 32x32 tile.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A, int64_t in, int64_t r, int nT,
+                                                    int splitG, float* gpart) {
+  using T = typename Dt<DT>::T;
+  using V8 = typename Dt<DT>::V8;
+  __shared__ float red[4][32 * 32];
+  const int nUpper = nT * (nT + 1) / 2;
+  int u = blockIdx.x % nUpper;
+  const int sp = blockIdx.x / nUpper;
+  int ti = 0;
+  while (u >= nT - ti) {
+    u -= nT - ti;
+    ++ti;
+  }
+  const int tj = ti + u;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t xr = static_cast<int64_t>(ti) * 32 + (lane & 31);
+  const int64_t yr = static_cast<int64_t>(tj) * 32 + (lane & 31);
+  const int64_t nk = cdiv(in, 16);
+  const int64_t part = static_cast<int64_t>(sp) * 4 + wave;
+  const int64_t kb0 = nk * part / (4 * splitG), kb1 = nk * (part + 1) / (4 * splitG);
+  const int koff = (lane >> 5) * 8;
+
+  auto frag = [&](int64_t row, int64_t k) -> V8 {
+    if (row >= r || k >= in) return __builtin_bit_cast(V8, zero_chunk());
+    const T* p = A + row * in + k;
+    if (VEC) return *reinterpret_cast<const V8*>(p);
+    V8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (k + j < in) ? p[j] : static_cast<T>(0.0f);
+    return v;
+  };
+
+  f32x16 acc = {};
+  int64_t kb = kb0;
+  for (; kb + kGramU <= kb1; kb += kGramU) {
+    V8 x[kGramU], y[kGramU];
+#pragma unroll
+    for (int q = 0; q < kGramU; ++q) {
+      x[q] = frag(xr, (kb + q) * 16 + koff);
+      y[q] = frag(yr, (kb + q) * 16 + koff);
+    }
+#pragma unroll
+    for (int q = 0; q < kGramU; ++q) acc = Dt<DT>::mfma32(x[q], y[q], acc);
+  }
+  for (; kb < kb1; ++kb) acc = Dt<DT>::mfma32(frag(xr, kb * 16 + koff), frag(yr, kb * 16 + koff), acc);
+
+#pragma unroll
+  for (int q = 0; q < 16; ++q) red[wave][(8 * (q / 4) + 4 * (lane >> 5) + (q % 4)) * 32 + (lane & 31)] = acc[q];
+  __syncthreads();
+  float* dst = gpart + static_cast<int64_t>(sp) * r * r;
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int64_t row = static_cast<int64_t>(ti) * 32 + e / 32, col = static_cast<int64_t>(tj) * 32 + e % 32;
+    if (row < r && col < r) dst[row * r + col] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+  }
+}
+
+// G'[a][b] = (s/2) * (sum over splits of the partials, in split order) for the
+// entries of the upper tiles, split into G'hi = round(G') and G'lo =
+// round(G' - G'hi) in the storage dtype and written at (a, b) and its mirror
+// (b, a).  G'hi + G'lo carries about 16 (bf16) or 22 (fp16) significant bits.
+template <int DT>
+__global__ __launch_bounds__(256) void gram_finalize(const float* gpart, int splitG, int64_t r, float half_s,
+                                                     typename Dt<DT>::T* ghi, typename Dt<DT>::T* glo) {
+  using T = typename Dt<DT>::T;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= r * r) return;
+  const int64_t row = idx / r, col = idx % r;
+  if (row / 32 > col / 32) return;  // written as the mirror of (col, row)
+  const float* src = gpart + idx;
+  const int64_t stride = r * r;
+  float g = 0.0f;
+  int sp = 0;
+  for (; sp + 4 <= splitG; sp += 4) {
+    const float a0 = src[(sp + 0) * stride], a1 = src[(sp + 1) * stride];
+    const float a2 = src[(sp + 2) * stride], a3 = src[(sp + 3) * stride];
+    g += (a0 + a1) + (a2 + a3);
+  }
+  for (; sp < splitG; ++sp) g += src[sp * stride];
+  const float gp = half_s * g;
+  const T hi = Dt<DT>::from_f(gp);
+  const T lo = Dt<DT>::from_f(gp - Dt<DT>::to_f(hi));
+  ghi[row * r + col] = hi;
+  glo[row * r + col] = lo;
+  if (row / 32 != col / 32) {
+    ghi[col * r + row] = hi;
+    glo[col * r + row] = lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the W stream
 
 // A row-major operand panel: rows x klen valid elements, ld elements per row.
 struct Operand {
@@ -62,20 +148,8 @@ struct Operand {
   int64_t ld, rows, klen;
 };
 
-template <int DT, bool VEC>
-__device__ inline Chunk load_chunk(const Operand& op, int64_t row, int64_t k) {
-  using T = typename Dt<DT>::T;
-  if (row >= op.rows || k >= op.klen) return zero_chunk();
-  const T* src = static_cast<const T*>(op.p) + row * op.ld + k;
-  if (VEC) return *reinterpret_cast<const Chunk*>(src);
-  typename Dt<DT>::V8 v;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (k + j < op.klen) ? src[j] : static_cast<T>(0.0f);
-  return __builtin_bit_cast(Chunk, v);
-}
-
 // Stage map of the fused W stream: stage st covers BK columns of one segment of
-// the augmented K axis.
+// the augmented K axis [W0 | B | B] . [A | G'hi | G'lo]^T.
 struct WStages {
   const void *W0, *A, *B, *Ghi, *Glo;
   int64_t out, in, r, S1, S2;
@@ -100,47 +174,464 @@ struct WStages {
   }
 };
 
-struct GStages {
-  const void* A;
-  int64_t in, r;
-  template <int BK>
-  __device__ inline void get(int64_t st, Operand& X, Operand& Y, int64_t& k0, bool& seg_w) const {
-    X = Operand{A, in, r, in};
-    Y = X;
-    k0 = st * BK;
-    seg_w = false;
-  }
+struct WArgs {
+  WStages sm;
+  int64_t nRB, S, total;
+  int nTiles, nSplit;
+  float* base_part;   // [nSplit][out]
+  float* cross_part;  // [nSplit][nTiles][out]
 };
 
-// acc[i][j] += X[m0 + rows, K stages] . Y[n0 + cols, K stages]^T over stages
-// [st0, st1).  Double-buffered LDS; the next stage's global loads are issued
-// before the current stage's MFMAs.  With want_base, the squares of the X
-// chunks of W0 stages are summed into bsum (thread rows lrow + i*RPP).
-template <int DT, bool VEC, class TL, class Stages>
-__device__ inline void mainloop(const Stages& sm, int64_t st0, int64_t st1, int64_t m0, int64_t n0,
-                                typename Dt<DT>::T* smem, f32x16 (&acc)[TL::TM][TL::TN], float (&bsum)[TL::XCH],
-                                bool want_base) {
+// Workgroups are dealt to the 8 XCDs round-robin by index; renumber them so
+// each XCD receives a contiguous range of the logical work list (one K slice of
+// A per XCD's L2, and the rank tiles of a row block together).  gridDim.x is a
+// multiple of 8.
+__device__ inline int64_t xcd_logical_index() {
+  const int64_t b = blockIdx.x;
+  return (b & 7) * (gridDim.x >> 3) + (b >> 3);
+}
+
+// Epilogue shared by both W-stream kernels.  The MFMAs take the rank-side
+// fragment as their first operand, so acc[i][j] is the transposed 32x32 tile:
+// lane l holds W0 row m0 + wm*TM*32 + i*32 + l%32 (the tile column) and, in
+// register q, rank column n0 + wn*TN*32 + j*32 + 8*(q/4) + 4*(l/32) + q%4 of
+// U + B G'.  Each lane therefore needs B[row][4 consecutive columns] per
+// register group (one 8-byte load on the 16-byte path), sums its products in
+// registers, adds the other half-wave's sum, and the waves along the rank axis
+// are combined in LDS in a fixed order.
+template <int DT, int TM, int TN, int WM, int WN, int BM, bool VEC>
+__device__ inline void cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0, int64_t n0,
+                                      const f32x16 (&acc)[TM][TN], float (*red)[BM]) {
+  using T = typename Dt<DT>::T;
+  using T4 = T __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t out = a.sm.out, r = a.sm.r;
+  const T* B = static_cast<const T*>(a.sm.B);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = m0 + wm * TM * 32 + i * 32 + (lane & 31);
+    const bool rv = row < out;
+    // clamped, unconditional loads (no divergent branches around them); the
+    // products of rows or columns outside the matrices are selected away
+    const int64_t rowc = rv ? row : out - 1;
+    float rs = 0.0f;
+    if (r > 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        T4 b4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = n0 + wn * TN * 32 + j * 32 + 8 * g + 4 * h;
+          if (VEC) {
+            // r is a multiple of 8: a 4-column group is wholly inside or outside
+            const int64_t colc = col < r ? col : r - 4;
+            b4[g] = *reinterpret_cast<const T4*>(B + rowc * r + colc);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[g][e] = B[rowc * r + (col + e < r ? col + e : r - 1)];
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = n0 + wn * TN * 32 + j * 32 + 8 * g + 4 * h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = __builtin_fmaf(Dt<DT>::to_f(b4[g][e]), acc[i][j][4 * g + e], rs);
+            rs = (rv && col + e < r) ? t : rs;
+          }
+        }
+      }
+    }
+    rs += __shfl_xor(rs, 32, 64);
+    if (h == 0) red[wn][wm * TM * 32 + i * 32 + (lane & 31)] = rs;
+  }
+  __syncthreads();
+  if (tid < BM && m0 + tid < out) {
+    float c = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WN; ++w) c += red[w][tid];
+    a.cross_part[(static_cast<int64_t>(sp) * a.nTiles + nt) * out + m0 + tid] = c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// W stream, 16-byte path: direct global -> LDS loads through buffer resources.
+//
+// Tile 32*TM rows x 128*TN rank columns, K stage 32, four waves side by side
+// along the rank axis, each owning all 32*TM rows (one wave per SIMD, so the
+// TM*TN*16 accumulators fit in the accumulation registers).  Every workgroup
+// reads the whole rank panel of A once per K stage; the taller the tile, the
+// fewer times that panel is re-read from L2 for the same W0 rows.  A stage is one 64-byte row
+// segment per panel row; one wave instruction moves 16 rows x 64 bytes, lane l
+// writing bytes [16l, 16l+16) of that 1 KiB block.  Lane l fetches the logical
+// 16-byte chunk (l%4) ^ ((row>>2)&3) of its row, so the LDS slot of logical
+// chunk c in row m is c ^ ((m>>2)&3): the fragment reads of 16 consecutive rows
+// then hit 16 distinct bank groups.  Rows past the operand and K chunks past
+// its end get an out-of-range buffer offset, which the hardware turns into
+// zeros in LDS.  NS stages rotate through LDS; a stage is waited for with
+// s_waitcnt vmcnt once the loads of the NS-2 younger stages are in flight.
+template <int TN_, int TM_, int NS_>
+struct DmaTile {
+  static constexpr int TN = TN_, TM = TM_, NS = NS_;
+  static constexpr int BM = 32 * TM, BN = 128 * TN, BK = 32, WN = 4;
+  static constexpr int X_BYTES = BM * BK * 2, Y_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
+  static constexpr int XL = BM / 16 / WN, YL = BN / 16 / WN;  // wave load instructions per stage
+  static constexpr int L = XL + YL;
+  static constexpr int NB = (TM + WN - 1) / WN;  // W0 fragments each wave squares for the base term
+  static_assert(BM % 64 == 0, "X panel splits evenly over the waves");
+  static_assert(NS * STAGE_BYTES + WN * BM * 4 <= 160 * 1024, "LDS");
+  static_assert((NS - 2) * L < 64, "vmcnt range");
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kOob = 0xFFFFFF00u;   // buffer offset past any range: loads read zero
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer resource, gfx9 family
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS fragment reads are issued as inline assembly: the compiler cannot tell
+// them apart from the in-flight DMA writes into other stages and would
+// otherwise wait for every outstanding load before each read.  lds_wait()
+// completes them; tie() keeps the MFMAs that use a fragment after that wait.
+__device__ inline u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Epilogue of the 16-byte path.  The workgroup's B tile (BM rows x BN rank
+// columns) is brought into the free stage buffers by DMA, in passes of as many
+// 32-row blocks as fit; within a pass the 16-byte chunks of each row are
+// rotated by the row index (slot p of row m holds chunk (p + m) mod CPR), so the
+// reads of 16 consecutive rows at one column hit 16 distinct bank groups.  A
+// lane then needs, per rank tile, the 16 consecutive B columns matching its
+// accumulator registers: two 16-byte LDS reads.
+template <int DT, class TL>
+__device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0, int64_t n0,
+                                          const f32x16 (&acc)[TL::TM][TL::TN], float (*red)[TL::BM], char* smem,
+                                          uint32_t lds0) {
+  using V8 = typename Dt<DT>::V8;
+  constexpr int CPR = TL::BN / 8;                                     // 16-byte chunks per B-tile row
+  constexpr int AREA = TL::NS * TL::STAGE_BYTES;
+  constexpr int RPP = std::min(TL::BM, (AREA / (TL::BN * 2)) / 32 * 32);  // rows per pass
+  static_assert(RPP >= 32, "one 32-row block per pass at least");
+  constexpr int NPASS = (TL::BM + RPP - 1) / RPP;
+  constexpr int INSTR = RPP * CPR / 64;                               // 1 KiB DMA instructions per pass
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, frow = lane & 31;
+  const int64_t out = a.sm.out, r = a.sm.r;
+  const int64_t rows_here = std::min<int64_t>(std::max<int64_t>(out - m0, 0), TL::BM);
+  const int64_t cols_here = std::min<int64_t>(std::max<int64_t>(r - n0, 0), TL::BN);
+  // rows of B from m0; columns from n0 (offsets past the tile's valid part read zero)
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.sm.B) + (rows_here > 0 ? m0 * r * 2 : 0)), static_cast<short>(0),
+      static_cast<int>(rows_here * r * 2), kBufferWord3);
+  float rs[TL::TM];
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i) rs[i] = 0.0f;
+
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    const int row_base = pass * RPP;
+    __syncthreads();  // stage buffers (or the previous pass) no longer read
+    if (cols_here > 0) {
+      for (int q = wave; q < INSTR; q += TL::WN) {
+        const int slot = q * 64 + lane;
+        const int rl = slot / CPR, pp = slot % CPR;
+        const int ch = (pp + rl) % CPR;
+        const int64_t row = row_base + rl;
+        const int64_t col = static_cast<int64_t>(ch) * 8;
+        const uint32_t off = (col < cols_here) ? static_cast<uint32_t>((row * r + n0 + col) * 2) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(smem + q * 1024), 16, off, 0, 0, 0);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (cols_here > 0) {
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i) {
+        if (i * 32 < row_base || i * 32 >= row_base + RPP) continue;
+        const int rl = i * 32 - row_base + frow;
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j) {
+          const int c0 = wave * TL::TN * 4 + j * 4 + 2 * h;  // first of the lane's two chunks
+          const int p0 = (c0 - rl % CPR + CPR) % CPR, p1 = (c0 + 1 - rl % CPR + CPR) % CPR;
+          u32x4 w0 = lds_read16(lds0 + static_cast<uint32_t>((rl * CPR + p0) * 16));
+          u32x4 w1 = lds_read16(lds0 + static_cast<uint32_t>((rl * CPR + p1) * 16));
+          lds_wait();
+          tie(w0);
+          tie(w1);
+          const V8 b0 = __builtin_bit_cast(V8, w0), b1 = __builtin_bit_cast(V8, w1);
+          const int64_t colb = n0 + c0 * 8;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float bv = Dt<DT>::to_f(e < 8 ? b0[e] : b1[e - 8]);
+            const float t = __builtin_fmaf(bv, acc[i][j][e], rs[i]);
+            rs[i] = (colb + e < r) ? t : rs[i];
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i) {
+    const float v = rs[i] + __shfl_xor(rs[i], 32, 64);
+    if (h == 0) red[wave][i * 32 + frow] = v;
+  }
+  __syncthreads();
+  if (tid < TL::BM && m0 + tid < out) {
+    float c = 0.0f;
+#pragma unroll
+    for (int w = 0; w < TL::WN; ++w) c += red[w][tid];
+    a.cross_part[(static_cast<int64_t>(sp) * a.nTiles + nt) * out + m0 + tid] = c;
+  }
+}
+
+template <int DT, int TN, int TM, int NS>
+__global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
+  using TL = DmaTile<TN, TM, NS>;
+  using V8 = typename Dt<DT>::V8;
+  __shared__ __attribute__((aligned(1024))) char smem[TL::NS * TL::STAGE_BYTES];
+  __shared__ float red[TL::WN][TL::BM];
+
+  const int64_t v = xcd_logical_index();
+  if (v >= a.total) return;
+  const int nt = static_cast<int>(v % a.nTiles);
+  const int64_t rb = (v / a.nTiles) % a.nRB;
+  const int sp = static_cast<int>(v / (static_cast<int64_t>(a.nTiles) * a.nRB));
+  const int64_t m0 = rb * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
+  const int64_t st0 = a.S * sp / a.nSplit, st1 = a.S * (sp + 1) / a.nSplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool want_base = (nt == 0);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+
+  // per-lane load geometry: row within a 16-row group and swizzled chunk
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);  // equals ((16g + lrow) >> 2) & 3 for any group g
+
+  auto rsrc = [](const void* base, int64_t row0, int64_t rows, int64_t ld, int64_t max_rows) {
+    const int64_t nrows = std::min<int64_t>(std::max<int64_t>(rows - row0, 0), max_rows);
+    const char* p = static_cast<const char*>(base) + (nrows > 0 ? row0 * ld * 2 : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), static_cast<short>(0),
+                                             static_cast<int>(nrows * ld * 2), kBufferWord3);
+  };
+
+  auto issue = [&](int64_t st, int buf) {
+    Operand X, Y;
+    int64_t k0;
+    bool seg_w;
+    a.sm.template get<TL::BK>(st, X, Y, k0, seg_w);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(X.p, m0, X.rows, X.ld, TL::BM);
+    const __amdgpu_buffer_rsrc_t ry = rsrc(Y.p, n0, Y.rows, Y.ld, TL::BN);
+    const int64_t k = k0 + lchunk * 8;
+    // 32-bit byte offsets (a panel spans at most 512 rows of at most 2^22 elements)
+    const uint32_t kbytes = static_cast<uint32_t>(k) * 2u;
+    const uint32_t xmask = (k < X.klen) ? 0xFFFFFFFFu : 0u;
+    const uint32_t ymask = (k < Y.klen) ? 0xFFFFFFFFu : 0u;
+    const uint32_t xld = static_cast<uint32_t>(X.ld) * 2u, yld = static_cast<uint32_t>(Y.ld) * 2u;
+    char* stage = smem + buf * TL::STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < TL::XL; ++q) {
+      const int g = wave * TL::XL + q;  // 16-row group of the X panel
+      const uint32_t row = static_cast<uint32_t>(g * 16 + lrow);
+      const uint32_t off = ((row * xld + kbytes) & xmask) | (kOob & ~xmask);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(stage + g * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < TL::YL; ++q) {
+      const int g = wave * TL::YL + q;
+      const uint32_t row = static_cast<uint32_t>(g * 16 + lrow);
+      const uint32_t off = ((row * yld + kbytes) & ymask) | (kOob & ~ymask);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(stage + TL::X_BYTES + g * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[TL::TM][TL::TN];
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
+  float bsum[TL::NB];
+#pragma unroll
+  for (int k = 0; k < TL::NB; ++k) bsum[k] = 0.0f;
+
+  const int frow = lane & 31, fhalf = lane >> 5;
+  // LDS byte offsets (within a stage) of this lane's fragments for K chunk kc
+  auto xaddr = [&](int i, int kc) {
+    const int m = i * 32 + frow;
+    return static_cast<uint32_t>(m * 64 + ((kc ^ ((m >> 2) & 3)) * 16));
+  };
+  // MFMA row p of rank tile j reads rank row sigma(p) = 16*((p>>2)&1) + 4*(p>>3) + (p&3),
+  // so accumulator register q of a lane in half h holds rank column 16h + q
+  const int srow = 16 * ((frow >> 2) & 1) + 4 * (frow >> 3) + (frow & 3);
+  auto yaddr = [&](int j, int kc) {
+    const int nn = wave * TL::TN * 32 + j * 32 + srow;
+    return static_cast<uint32_t>(TL::X_BYTES + nn * 64 + ((kc ^ ((nn >> 2) & 3)) * 16));
+  };
+
+#pragma unroll
+  for (int i = 0; i < TL::NS - 1; ++i)
+    if (st0 + i < st1) issue(st0 + i, i);
+  for (int64_t st = st0; st < st1; ++st) {
+    if (st + TL::NS - 2 < st1)
+      wait_vmcnt<(TL::NS - 2) * TL::L>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (st + TL::NS - 1 < st1) issue(st + TL::NS - 1, static_cast<int>((st - st0 + TL::NS - 1) % TL::NS));
+    const uint32_t sbase = lds0 + static_cast<uint32_t>(((st - st0) % TL::NS) * TL::STAGE_BYTES);
+    const bool base_here = want_base && st < a.sm.S1;
+
+    u32x4 x[2][TL::TM], y[2][TL::TN];
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i) x[0][i] = lds_read16(sbase + xaddr(i, fhalf));
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) y[0][j] = lds_read16(sbase + yaddr(j, fhalf));
+    lds_wait();
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i) tie(x[0][i]);
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) tie(y[0][j]);
+    // second K step's fragments load while the first step's MFMAs run
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i) x[1][i] = lds_read16(sbase + xaddr(i, 2 + fhalf));
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) y[1][j] = lds_read16(sbase + yaddr(j, 2 + fhalf));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks == 1) {
+        lds_wait();
+#pragma unroll
+        for (int i = 0; i < TL::TM; ++i) tie(x[1][i]);
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j) tie(y[1][j]);
+      }
+      if (base_here) {
+        // wave w squares the W0 fragments x[i], i = w, w + 4, ...: every row once
+#pragma unroll
+        for (int k = 0; k < TL::NB; ++k) {
+          u32x4 xw = x[ks][0];
+#pragma unroll
+          for (int i = 1; i < TL::TM; ++i)
+            if (wave + TL::WN * k == i) xw = x[ks][i];
+          const V8 xv = __builtin_bit_cast(V8, xw);
+          if (wave + TL::WN * k < TL::TM) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float f = Dt<DT>::to_f(xv[e]);
+              bsum[k] = __builtin_fmaf(f, f, bsum[k]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j)
+          acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, y[ks][j]), __builtin_bit_cast(V8, x[ks][i]), acc[i][j]);
+    }
+  }
+  __syncthreads();
+
+  if (want_base) {
+#pragma unroll
+    for (int k = 0; k < TL::NB; ++k) {
+      const float b = bsum[k] + __shfl_xor(bsum[k], 32, 64);
+      const int i = wave + TL::WN * k;
+      const int64_t row = m0 + i * 32 + frow;
+      if (i < TL::TM && fhalf == 0 && row < a.sm.out) a.base_part[static_cast<int64_t>(sp) * a.sm.out + row] = b;
+    }
+  }
+  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, red, smem, lds0);
+}
+
+// ---------------------------------------------------------------------------
+// W stream, general path (row lengths not multiples of 8, or unaligned
+// pointers): register-staged loads with element-wise bounds, LDS rows padded
+// by 8 elements, double buffered.
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int TM = BM / (WM * 32), TN = BN / (WN * 32);
+  static constexpr int LDK = BK + 8;
+  static constexpr int CPR = BK / 8;
+  static constexpr int RPP = NT / CPR;
+  static constexpr int XCH = BM / RPP, YCH = BN / RPP;
+  static constexpr int LDS_ELEMS = 2 * (BM + BN) * LDK;
+  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "wave tile");
+  static_assert(NT % CPR == 0 && BM % RPP == 0 && BN % RPP == 0, "loader mapping");
+};
+
+using TileW = Tile<128, 128, 64, 2, 2>;
+
+template <int DT>
+__device__ inline Chunk load_chunk_any(const Operand& op, int64_t row, int64_t k) {
+  using T = typename Dt<DT>::T;
+  if (row >= op.rows || k >= op.klen) return zero_chunk();
+  const T* src = static_cast<const T*>(op.p) + row * op.ld + k;
+  typename Dt<DT>::V8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (k + j < op.klen) ? src[j] : static_cast<T>(0.0f);
+  return __builtin_bit_cast(Chunk, v);
+}
+
+template <int DT>
+__global__ __launch_bounds__(TileW::NT, 2) void wstream_general(WArgs a) {
+  using TL = TileW;
   using T = typename Dt<DT>::T;
   using V8 = typename Dt<DT>::V8;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) T smem[TL::LDS_ELEMS];
+  __shared__ float red[TL::WN][TL::BM];
+  const int64_t v = xcd_logical_index();
+  if (v >= a.total) return;
+  const int nt = static_cast<int>(v % a.nTiles);
+  const int64_t rb = (v / a.nTiles) % a.nRB;
+  const int sp = static_cast<int>(v / (static_cast<int64_t>(a.nTiles) * a.nRB));
+  const int64_t m0 = rb * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
+  const int64_t st0 = a.S * sp / a.nSplit, st1 = a.S * (sp + 1) / a.nSplit;
+  const bool want_base = (nt == 0);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int lrow = tid / TL::CPR, lkc = tid % TL::CPR;
-  T* Xs[2] = {smem, smem + (TL::BM + TL::BN) * TL::LDK};
-  T* Ys[2] = {Xs[0] + TL::BM * TL::LDK, Xs[1] + TL::BM * TL::LDK};
+  // buffer b: X panel at smem + b*(BM+BN)*LDK, Y panel right after it
+  auto Xs = [&](int b) { return smem + b * (TL::BM + TL::BN) * TL::LDK; };
+  auto Ys = [&](int b) { return smem + b * (TL::BM + TL::BN) * TL::LDK + TL::BM * TL::LDK; };
+
+  f32x16 acc[TL::TM][TL::TN];
+#pragma unroll
+  for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
+  float bsum[TL::XCH] = {};
 
   Chunk xr[TL::XCH], yr[TL::YCH];
   auto gload = [&](int64_t st) -> bool {
     Operand X, Y;
     int64_t k0;
     bool seg_w;
-    sm.template get<TL::BK>(st, X, Y, k0, seg_w);
+    a.sm.template get<TL::BK>(st, X, Y, k0, seg_w);
     const int64_t k = k0 + lkc * 8;
 #pragma unroll
-    for (int i = 0; i < TL::XCH; ++i) xr[i] = load_chunk<DT, VEC>(X, m0 + lrow + i * TL::RPP, k);
+    for (int i = 0; i < TL::XCH; ++i) xr[i] = load_chunk_any<DT>(X, m0 + lrow + i * TL::RPP, k);
 #pragma unroll
-    for (int i = 0; i < TL::YCH; ++i) yr[i] = load_chunk<DT, VEC>(Y, n0 + lrow + i * TL::RPP, k);
+    for (int i = 0; i < TL::YCH; ++i) yr[i] = load_chunk_any<DT>(Y, n0 + lrow + i * TL::RPP, k);
     return seg_w;
   };
   auto lstore = [&](int buf, bool seg_w) {
@@ -155,205 +646,56 @@ __device__ inline void mainloop(const Stages& sm, int64_t st0, int64_t st1, int6
     }
 #pragma unroll
     for (int i = 0; i < TL::XCH; ++i)
-      *reinterpret_cast<Chunk*>(Xs[buf] + (lrow + i * TL::RPP) * TL::LDK + lkc * 8) = xr[i];
+      *reinterpret_cast<Chunk*>(Xs(buf) + (lrow + i * TL::RPP) * TL::LDK + lkc * 8) = xr[i];
 #pragma unroll
     for (int i = 0; i < TL::YCH; ++i)
-      *reinterpret_cast<Chunk*>(Ys[buf] + (lrow + i * TL::RPP) * TL::LDK + lkc * 8) = yr[i];
+      *reinterpret_cast<Chunk*>(Ys(buf) + (lrow + i * TL::RPP) * TL::LDK + lkc * 8) = yr[i];
   };
 
-  if (st0 >= st1) return;
-  lstore(0, gload(st0));
-  __syncthreads();
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  for (int64_t st = st0; st < st1; ++st) {
-    const int buf = static_cast<int>((st - st0) & 1);
-    const bool have_next = st + 1 < st1;
-    bool next_w = false;
-    if (have_next) next_w = gload(st + 1);
-    const T* xs = Xs[buf] + (wm * TL::TM * 32 + frow) * TL::LDK + fk;
-    const T* ys = Ys[buf] + (wn * TL::TN * 32 + frow) * TL::LDK + fk;
-#pragma unroll
-    for (int kk = 0; kk < TL::BK / 16; ++kk) {
-      V8 a[TL::TM], b[TL::TN];
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i) a[i] = *reinterpret_cast<const V8*>(xs + i * 32 * TL::LDK + kk * 16);
-#pragma unroll
-      for (int j = 0; j < TL::TN; ++j) b[j] = *reinterpret_cast<const V8*>(ys + j * 32 * TL::LDK + kk * 16);
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::TN; ++j) acc[i][j] = Dt<DT>::mfma32(a[i], b[j], acc[i][j]);
-    }
-    if (have_next) lstore(buf ^ 1, next_w);
+  if (st0 < st1) {
+    lstore(0, gload(st0));
     __syncthreads();
-  }
-}
-
-// Workgroups are dealt to the 8 XCDs round-robin by index; renumber them so
-// each XCD receives a contiguous range of the logical work list (one K slice of
-// A per XCD's L2, and the rank tiles of a row block together).  gridDim.x is a
-// multiple of 8.
-__device__ inline int64_t xcd_logical_index() {
-  const int64_t b = blockIdx.x;
-  return (b & 7) * (gridDim.x >> 3) + (b >> 3);
-}
-
-struct GramArgs {
-  const void* A;
-  int64_t in, r, Sg;
-  int nTg, nUpper, splitG;
-  float* gpart;
-};
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(TileG::NT) void gram_kernel(GramArgs a) {
-  using TL = TileG;
-  __shared__ __attribute__((aligned(16))) typename Dt<DT>::T smem[TL::LDS_ELEMS];
-  const int64_t v = xcd_logical_index();
-  if (v >= static_cast<int64_t>(a.nUpper) * a.splitG) return;
-  int u = static_cast<int>(v % a.nUpper);
-  const int sp = static_cast<int>(v / a.nUpper);
-  int ti = 0;
-  while (u >= a.nTg - ti) {
-    u -= a.nTg - ti;
-    ++ti;
-  }
-  const int tj = ti + u;
-  const int64_t m0 = static_cast<int64_t>(ti) * TL::BM, n0 = static_cast<int64_t>(tj) * TL::BN;
-  const int64_t st0 = a.Sg * sp / a.splitG, st1 = a.Sg * (sp + 1) / a.splitG;
-
-  f32x16 acc[TL::TM][TL::TN];
+    const int frow = lane & 31;
+    const int fk = (lane >> 5) * 8;
+    for (int64_t st = st0; st < st1; ++st) {
+      const int buf = static_cast<int>((st - st0) & 1);
+      const bool have_next = st + 1 < st1;
+      bool next_w = false;
+      if (have_next) next_w = gload(st + 1);
+      const T* xs = Xs(buf) + (wm * TL::TM * 32 + frow) * TL::LDK + fk;
+      const T* ys = Ys(buf) + (wn * TL::TN * 32 + frow) * TL::LDK + fk;
 #pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
+      for (int kk = 0; kk < TL::BK / 16; ++kk) {
+        V8 x[TL::TM], y[TL::TN];
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
-  float bsum[TL::XCH] = {};
-  mainloop<DT, VEC, TL>(GStages{a.A, a.in, a.r}, st0, st1, m0, n0, smem, acc, bsum, false);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
-  float* dst = a.gpart + static_cast<int64_t>(sp) * a.r * a.r;
+        for (int i = 0; i < TL::TM; ++i) x[i] = *reinterpret_cast<const V8*>(xs + i * 32 * TL::LDK + kk * 16);
 #pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
+        for (int j = 0; j < TL::TN; ++j) y[j] = *reinterpret_cast<const V8*>(ys + j * 32 * TL::LDK + kk * 16);
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) {
-      const int64_t col = n0 + wn * TL::TN * 32 + j * 32 + (lane & 31);
+        for (int i = 0; i < TL::TM; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * TL::TM * 32 + i * 32 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-        if (row < a.r && col < a.r) dst[row * a.r + col] = acc[i][j][q];
+          for (int j = 0; j < TL::TN; ++j) acc[i][j] = Dt<DT>::mfma32(y[j], x[i], acc[i][j]);
       }
+      if (have_next) lstore(buf ^ 1, next_w);
+      __syncthreads();
     }
-}
-
-// G'[a][b] = (s/2) * sum_sp Gpart[sp][a][b] in fp64 (entries below the tiled
-// diagonal are read from their mirror), then G'hi = round(G'), G'lo =
-// round(G' - G'hi).  G'hi + G'lo carries about 16 (bf16) or 22 (fp16)
-// significant bits of G'.
-template <int DT>
-__global__ __launch_bounds__(256) void gram_finalize(const float* gpart, int splitG, int64_t r, float half_s,
-                                                     typename Dt<DT>::T* ghi, typename Dt<DT>::T* glo) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= r * r) return;
-  const int64_t ra = idx / r, rb = idx % r;
-  const int64_t src = (ra / TileG::BM <= rb / TileG::BN) ? idx : rb * r + ra;
-  double sum = 0.0;
-  for (int sp = 0; sp < splitG; ++sp) sum += static_cast<double>(gpart[static_cast<int64_t>(sp) * r * r + src]);
-  const double gp = static_cast<double>(half_s) * sum;
-  const typename Dt<DT>::T hi = Dt<DT>::from_d(gp);
-  const double rem = gp - static_cast<double>(Dt<DT>::to_f(hi));
-  ghi[idx] = hi;
-  glo[idx] = Dt<DT>::from_d(rem);
-}
-
-struct WArgs {
-  WStages sm;
-  int64_t nRB, S, total;
-  int nTiles, nSplit;
-  float* base_part;   // [nSplit][out]
-  float* cross_part;  // [nSplit][nTiles][out]
-};
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(TileW::NT, 2) void wstream_kernel(WArgs a) {
-  using TL = TileW;
-  __shared__ __attribute__((aligned(16))) typename Dt<DT>::T smem[TL::LDS_ELEMS];
-  __shared__ float red[TL::WN][TL::BM];
-  const int64_t v = xcd_logical_index();
-  if (v >= a.total) return;
-  const int nt = static_cast<int>(v % a.nTiles);
-  const int64_t rb = (v / a.nTiles) % a.nRB;
-  const int sp = static_cast<int>(v / (static_cast<int64_t>(a.nTiles) * a.nRB));
-  const int64_t m0 = rb * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
-  const int64_t st0 = a.S * sp / a.nSplit, st1 = a.S * (sp + 1) / a.nSplit;
-  const int64_t out = a.sm.out, r = a.sm.r;
-
-  f32x16 acc[TL::TM][TL::TN];
-#pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
-  float bsum[TL::XCH] = {};
-  const bool want_base = (nt == 0);
-  mainloop<DT, VEC, TL>(a.sm, st0, st1, m0, n0, smem, acc, bsum, want_base);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
-  using T = typename Dt<DT>::T;
-  const T* B = static_cast<const T*>(a.sm.B);
-
-  // rs[i][q] = sum over this lane's columns of B[row][col] * acc[row][col]
-  float rs[TL::TM][16];
-#pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) rs[i][q] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    const int64_t col = n0 + wn * TL::TN * 32 + j * 32 + (lane & 31);
-    const bool cv = col < r;
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * TL::TM * 32 + i * 32 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-        const float bv = (cv && row < out) ? Dt<DT>::to_f(B[row * r + col]) : 0.0f;
-        rs[i][q] = __builtin_fmaf(bv, acc[i][j][q], rs[i][q]);
-      }
   }
-  // reduce over the 32 columns held by each half-wave
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1)
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) rs[i][q] += __shfl_xor(rs[i][q], off, 64);
-  if ((lane & 31) == 0) {
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) red[wn][wm * TL::TM * 32 + i * 32 + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4)] = rs[i][q];
-  }
-  // base term: the 8 loader lanes of a row are consecutive
+
   if (want_base) {
+    const int64_t out = a.sm.out;
 #pragma unroll
     for (int i = 0; i < TL::XCH; ++i) {
       float b = bsum[i];
 #pragma unroll
       for (int off = 1; off < TL::CPR; off <<= 1) b += __shfl_xor(b, off, 64);
-      const int64_t row = m0 + tid / TL::CPR + i * TL::RPP;
-      if ((tid % TL::CPR) == 0 && row < out) a.base_part[static_cast<int64_t>(sp) * out + row] = b;
+      const int64_t row = m0 + lrow + i * TL::RPP;
+      if (lkc == 0 && row < out) a.base_part[static_cast<int64_t>(sp) * out + row] = b;
     }
   }
-  __syncthreads();
-  if (tid < TL::BM && m0 + tid < out) {
-    float c = 0.0f;
-#pragma unroll
-    for (int w = 0; w < TL::WN; ++w) c += red[w][tid];
-    a.cross_part[(static_cast<int64_t>(sp) * a.nTiles + nt) * out + m0 + tid] = c;
-  }
+  cross_epilogue<DT, TL::TM, TL::TN, TL::WM, TL::WN, TL::BM, false>(a, sp, nt, m0, n0, acc, red);
 }
+
+// ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void norm_finalize(const float* base_part, const float* cross_part, int nSplit,
                                                      int nTiles, int64_t out, float s, float* norm_out) {
@@ -366,7 +708,43 @@ __global__ __launch_bounds__(256) void norm_finalize(const float* base_part, con
   norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
 }
 
-constexpr int kSlotsW = 512;  // resident W-stream workgroups: 256 CUs x 2
+// Rank tile width of the 16-byte path: 128*TN columns, TN in 1..4, choosing the
+// least padding of r and then the widest tile (fewest passes over W0).
+int dma_tn(int64_t r) {
+  int best = 1;
+  int64_t best_pad = -1;
+  for (int tn = 1; tn <= 4; ++tn) {
+    const int64_t w = 128 * tn;
+    const int64_t pad = cdiv(std::max<int64_t>(r, 1), w) * w;
+    if (best_pad < 0 || pad <= best_pad) {
+      best = tn;
+      best_pad = pad;
+    }
+  }
+  return best;
+}
+
+// Per rank-tile width: W0 rows per tile (32*TM) and LDS stages.
+template <int TN> struct DmaShape;
+template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6; };
+template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4; };
+template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 4; };
+template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3; };
+
+int dma_rows(int tn) {
+  switch (tn) {
+    case 1: return 32 * DmaShape<1>::TM;
+    case 2: return 32 * DmaShape<2>::TM;
+    case 3: return 32 * DmaShape<3>::TM;
+    default: return 32 * DmaShape<4>::TM;
+  }
+}
+
+template <int DT, int TN>
+void launch_dma(const WArgs& w, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
+  hipLaunchKernelGGL((wstream_dma<DT, TN, DmaShape<TN>::TM, DmaShape<TN>::NS>), grid, dim3(256), 0, stream, w);
+}
 
 template <int DT>
 hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
@@ -375,17 +753,19 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   T* ghi = reinterpret_cast<T*>(ws + p.off_ghi);
   T* glo = reinterpret_cast<T*>(ws + p.off_glo);
   if (p.r > 0) {
-    GramArgs g{a.A, p.in, p.r, p.Sg, p.nTg, p.nUpper, p.splitG, reinterpret_cast<float*>(ws + p.off_gpart)};
-    const int64_t n = static_cast<int64_t>(p.nUpper) * p.splitG;
-    const dim3 grid(static_cast<unsigned>(cdiv(n, 8) * 8));
+    const T* A = static_cast<const T*>(a.A);
+    float* gpart = reinterpret_cast<float*>(ws + p.off_gpart);
+    const int nUpper = p.nTg * (p.nTg + 1) / 2;
     if (vec)
-      hipLaunchKernelGGL((gram_kernel<DT, true>), grid, dim3(TileG::NT), 0, a.stream, g);
+      hipLaunchKernelGGL((gram_partial<DT, true>), dim3(static_cast<unsigned>(nUpper * p.splitG)), dim3(256), 0,
+                         a.stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
     else
-      hipLaunchKernelGGL((gram_kernel<DT, false>), grid, dim3(TileG::NT), 0, a.stream, g);
+      hipLaunchKernelGGL((gram_partial<DT, false>), dim3(static_cast<unsigned>(nUpper * p.splitG)), dim3(256), 0,
+                         a.stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(cdiv(p.r * p.r, 256))), dim3(256), 0, a.stream,
-                       g.gpart, p.splitG, p.r, a.s * 0.5f, ghi, glo);
+                       gpart, p.splitG, p.r, a.s * 0.5f, ghi, glo);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -398,11 +778,17 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   w.total = p.nRB * p.nTiles * p.nSplit;
   w.base_part = reinterpret_cast<float*>(ws + p.off_base);
   w.cross_part = reinterpret_cast<float*>(ws + p.off_cross);
-  const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
-  if (vec)
-    hipLaunchKernelGGL((wstream_kernel<DT, true>), grid, dim3(TileW::NT), 0, a.stream, w);
-  else
-    hipLaunchKernelGGL((wstream_kernel<DT, false>), grid, dim3(TileW::NT), 0, a.stream, w);
+  if (vec) {
+    switch (p.tn) {
+      case 1: launch_dma<DT, 1>(w, a.stream); break;
+      case 2: launch_dma<DT, 2>(w, a.stream); break;
+      case 3: launch_dma<DT, 3>(w, a.stream); break;
+      default: launch_dma<DT, 4>(w, a.stream); break;
+    }
+  } else {
+    const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
+    hipLaunchKernelGGL((wstream_general<DT>), grid, dim3(TileW::NT), 0, a.stream, w);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(norm_finalize, dim3(static_cast<unsigned>(cdiv(p.out, 256))), dim3(256), 0, a.stream,
@@ -416,27 +802,43 @@ size_t norm_scratch_bound(int64_t out, int64_t r) {
   return static_cast<size_t>(4 * (out * r + r * r) + 64 * out + 256);
 }
 
-NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype) {
+NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec) {
   NormPlan p;
   p.out = out;
   p.in = in;
   p.r = r;
   p.dtype = dtype;
+  p.vec = vec;
   if (out <= 0) return p;
   const int64_t e = 2;  // bytes per storage element (bf16, fp16)
-  p.nRB = cdiv(out, TileW::BM);
-  p.nTiles = static_cast<int>(std::max<int64_t>(1, cdiv(r, TileW::BN)));
-  p.S1 = cdiv(in, TileW::BK);
-  p.S2 = cdiv(r, TileW::BK);
+  int64_t bm, bn, bk, slots;
+  if (vec) {
+    p.tn = dma_tn(r);
+    bm = dma_rows(p.tn);
+    bn = 128 * p.tn;
+    bk = 32;
+    slots = 256;
+  } else {
+    p.tn = 0;
+    bm = TileW::BM;
+    bn = TileW::BN;
+    bk = TileW::BK;
+    slots = 512;
+  }
+  p.nRB = cdiv(out, bm);
+  p.nTiles = static_cast<int>(std::max<int64_t>(1, cdiv(r, bn)));
+  p.S1 = cdiv(in, bk);
+  p.S2 = cdiv(r, bk);
   p.S = p.S1 + 2 * p.S2;
-  // K splits: minimise (rounds of resident workgroups) x (stages per workgroup),
-  // keeping at least 4 stages per workgroup; ties go to fewer splits.
+  // K splits: minimise (rounds of resident workgroups) x (stages per workgroup
+  // + a fixed cost of about 8 stages for the pipeline fill and the epilogue),
+  // keeping at least 8 stages per workgroup; ties go to fewer splits.
   {
     const int64_t per = p.nRB * p.nTiles;
-    const int64_t maxs = std::max<int64_t>(1, std::min<int64_t>(64, p.S / 4));
+    const int64_t maxs = std::max<int64_t>(1, std::min<int64_t>(64, p.S / 8));
     int64_t best = -1, bestc = 0;
     for (int64_t k = 1; k <= maxs; ++k) {
-      const int64_t cost = cdiv(per * k, kSlotsW) * cdiv(std::max<int64_t>(p.S, 1), k);
+      const int64_t cost = cdiv(per * k, slots) * (cdiv(std::max<int64_t>(p.S, 1), k) + 8);
       if (best < 0 || cost < bestc) {
         best = k;
         bestc = cost;
@@ -445,10 +847,12 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype) {
     p.nSplit = static_cast<int>(best);
   }
   if (r > 0) {
-    p.nTg = static_cast<int>(cdiv(r, TileG::BM));
-    p.nUpper = p.nTg * (p.nTg + 1) / 2;
-    p.Sg = cdiv(in, TileG::BK);
-    p.splitG = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(cdiv(256, p.nUpper), std::max<int64_t>(1, p.Sg / 4))));
+    // Gram: 32x32 upper tiles x K splits, ~512 workgroups, at least 8 K steps
+    // of 16 per wave
+    p.nTg = static_cast<int>(cdiv(r, 32));
+    const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
+    const int64_t max_split = std::max<int64_t>(1, cdiv(in, 16) / (4 * 8));
+    p.splitG = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({cdiv(512, nUpper), 16, max_split})));
   }
   auto layout = [&]() {
     size_t off = 0;
@@ -465,7 +869,6 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype) {
     p.bytes = off;
   };
   layout();
-  // stay inside the factored memory bound: fewer Gram splits first, then fewer K splits
   const size_t bound = norm_scratch_bound(out, r);
   while (p.bytes > bound && p.splitG > 1) {
     --p.splitG;
@@ -478,9 +881,15 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype) {
   return p;
 }
 
-hipError_t launch_norm(const NormPlan& p, const NormArgs& a, bool vec) {
+size_t norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
+  size_t b = make_norm_plan(out, in, r, dtype, false).bytes;
+  if (in % 8 == 0 && r % 8 == 0) b = std::max(b, make_norm_plan(out, in, r, dtype, true).bytes);
+  return b;
+}
+
+hipError_t launch_norm(const NormPlan& p, const NormArgs& a) {
   if (p.out <= 0) return hipSuccess;
-  return p.dtype == 0 ? launch_norm_t<0>(p, a, vec) : launch_norm_t<1>(p, a, vec);
+  return p.dtype == 0 ? launch_norm_t<0>(p, a, p.vec) : launch_norm_t<1>(p, a, p.vec);
 }
 
 }  // namespace dora

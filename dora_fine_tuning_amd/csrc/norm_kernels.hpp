@@ -8,24 +8,29 @@
 namespace dora {
 
 // Work decomposition and workspace layout of one factored-norm call.  A pure
-// function of (out, in, r, dtype), so the workspace query and the launch agree.
+// function of (out, in, r, dtype, path), so the workspace query and the launch
+// agree.  vec selects the 16-byte path (direct global->LDS loads).
 struct NormPlan {
   int64_t out = 0, in = 0, r = 0;
   int dtype = 0;
+  bool vec = false;
+  int tn = 0;  // 16-byte path: rank tile width 128*tn
   // fused W stream: row blocks x rank tiles x K splits over the augmented K axis
   int64_t nRB = 0;
   int nTiles = 0;
   int64_t S1 = 0, S2 = 0, S = 0;  // K stages: W0.A^T part, each B.G' part, total
   int nSplit = 0;
-  // Gram: upper-triangular tiles x K splits
-  int nTg = 0, nUpper = 0;
-  int64_t Sg = 0;
-  int splitG = 0;
+  // Gram: 32x32 upper-triangular tiles x K splits
+  int nTg = 0, splitG = 0;
   // workspace byte offsets
   size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, bytes = 0;
 };
 
-NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype);
+NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec);
+
+// Workspace bytes covering both paths (the path depends on pointer alignment,
+// known only at the call).
+size_t norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
 
 // The factored memory bound 4*(out*r + r*r) + 64*out bytes, plus 256 bytes of
 // region alignment.
@@ -41,8 +46,6 @@ struct NormArgs {
   hipStream_t stream;
 };
 
-// vec: every row length (in, r) is a multiple of 8 elements and W0, A, B are
-// 16-byte aligned, so operand panels move as 16-byte chunks.
-hipError_t launch_norm(const NormPlan& p, const NormArgs& a, bool vec);
+hipError_t launch_norm(const NormPlan& p, const NormArgs& a);
 
 }  // namespace dora

@@ -62,7 +62,8 @@ def test_workspace_queries_invalid():
     assert LIB.dora_norm_workspace_bytes(8, 8, 8, 7) == 0
     assert LIB.dora_norm_workspace_bytes(0, 8, 8, 0) == 0
     assert LIB.dora_compose_bwd_workspace_bytes(0, 8) == 0
-    assert LIB.dora_compose_bwd_workspace_bytes(64, 8) == 2 * 8 * 4  # two 32-token blocks
+    assert LIB.dora_compose_bwd_workspace_bytes(64, 8) == 8 * 4  # one 64-token block
+    assert LIB.dora_compose_bwd_workspace_bytes(65, 8) == 2 * 8 * 4
 
 
 P = 1 << 20  # fake, never dereferenced: every call below fails validation first

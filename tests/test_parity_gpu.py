@@ -47,6 +47,11 @@ NORM_SMALL = [
     (5, 0, 8),        # empty input axis
     (1, 8, 8),
     (33, 200, 200),   # rank above out
+    (200, 264, 296),  # 384-wide rank tile, ragged
+    (150, 128, 504),  # 512-wide rank tile
+    (260, 392, 1000),  # two 512-wide rank tiles
+    (140, 136, 776),  # seven 128-wide rank tiles
+    (90, 100, 300),   # general path, rank above 128
 ]
 
 
