@@ -38,6 +38,15 @@ namespace {
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15); }
 
+// Workgroups are dealt to the 8 XCDs round-robin by index; renumber them so
+// each XCD receives a contiguous range of the logical work list (one K slice of
+// A per XCD's L2, and the rank tiles of a row block together).  gridDim.x is a
+// multiple of 8.
+__device__ inline int64_t xcd_logical_index() {
+  const int64_t b = blockIdx.x;
+  return (b & 7) * (gridDim.x >> 3) + (b >> 3);
+}
+
 // ---------------------------------------------------------------------------
 // Gram matrix
 
@@ -56,8 +65,12 @@ __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A,
   using V8 = typename Dt<DT>::V8;
   __shared__ float red[4][32 * 32];
   const int nUpper = nT * (nT + 1) / 2;
-  int u = blockIdx.x % nUpper;
-  const int sp = blockIdx.x / nUpper;
+  // XCD-aware: with splitG a multiple of 8 each XCD takes whole K splits, so
+  // its L2 holds one K slice of A
+  const int64_t v = xcd_logical_index();
+  if (v >= static_cast<int64_t>(nUpper) * splitG) return;
+  int u = static_cast<int>(v % nUpper);
+  const int sp = static_cast<int>(v / nUpper);
   int ti = 0;
   while (u >= nT - ti) {
     u -= nT - ti;
@@ -72,13 +85,20 @@ __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A,
   const int64_t kb0 = nk * part / (4 * splitG), kb1 = nk * (part + 1) / (4 * splitG);
   const int koff = (lane >> 5) * 8;
 
-  auto frag = [&](int64_t row, int64_t k) -> V8 {
-    if (row >= r || k >= in) return __builtin_bit_cast(V8, zero_chunk());
-    const T* p = A + row * in + k;
-    if (VEC) return *reinterpret_cast<const V8*>(p);
+  // clamped, unconditional loads; out-of-range rows and K are selected to zero
+  const int64_t xrc = xr < r ? xr : r - 1, yrc = yr < r ? yr : r - 1;
+  auto frag = [&](int64_t row, int64_t rowc, int64_t k) -> V8 {
+    const bool ok = row < r && k < in;
+    if (VEC) {
+      const Chunk c = *reinterpret_cast<const Chunk*>(A + rowc * in + (k < in ? k : in - 8));
+      return __builtin_bit_cast(V8, ok ? c : zero_chunk());
+    }
     V8 v;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (k + j < in) ? p[j] : static_cast<T>(0.0f);
+    for (int j = 0; j < 8; ++j) {
+      const T t = A[rowc * in + (k + j < in ? k + j : in - 1)];
+      v[j] = (ok && k + j < in) ? t : static_cast<T>(0.0f);
+    }
     return v;
   };
 
@@ -88,13 +108,13 @@ __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A,
     V8 x[kGramU], y[kGramU];
 #pragma unroll
     for (int q = 0; q < kGramU; ++q) {
-      x[q] = frag(xr, (kb + q) * 16 + koff);
-      y[q] = frag(yr, (kb + q) * 16 + koff);
+      x[q] = frag(xr, xrc, (kb + q) * 16 + koff);
+      y[q] = frag(yr, yrc, (kb + q) * 16 + koff);
     }
 #pragma unroll
     for (int q = 0; q < kGramU; ++q) acc = Dt<DT>::mfma32(x[q], y[q], acc);
   }
-  for (; kb < kb1; ++kb) acc = Dt<DT>::mfma32(frag(xr, kb * 16 + koff), frag(yr, kb * 16 + koff), acc);
+  for (; kb < kb1; ++kb) acc = Dt<DT>::mfma32(frag(xr, xrc, kb * 16 + koff), frag(yr, yrc, kb * 16 + koff), acc);
 
 #pragma unroll
   for (int q = 0; q < 16; ++q) red[wave][(8 * (q / 4) + 4 * (lane >> 5) + (q % 4)) * 32 + (lane & 31)] = acc[q];
@@ -182,15 +202,6 @@ struct WArgs {
   float* cross_part;  // [nSplit][nTiles][out]
 };
 
-// Workgroups are dealt to the 8 XCDs round-robin by index; renumber them so
-// each XCD receives a contiguous range of the logical work list (one K slice of
-// A per XCD's L2, and the rank tiles of a row block together).  gridDim.x is a
-// multiple of 8.
-__device__ inline int64_t xcd_logical_index() {
-  const int64_t b = blockIdx.x;
-  return (b & 7) * (gridDim.x >> 3) + (b >> 3);
-}
-
 // Epilogue shared by both W-stream kernels.  The MFMAs take the rank-side
 // fragment as their first operand, so acc[i][j] is the transposed 32x32 tile:
 // lane l holds W0 row m0 + wm*TM*32 + i*32 + l%32 (the tile column) and, in
@@ -272,17 +283,27 @@ __device__ inline void cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0
 // its end get an out-of-range buffer offset, which the hardware turns into
 // zeros in LDS.  NS stages rotate through LDS; a stage is waited for with
 // s_waitcnt vmcnt once the loads of the NS-2 younger stages are in flight.
-template <int TN_, int TM_, int NS_>
+template <int TN_, int TM_, int NS_, int WM_>
 struct DmaTile {
-  static constexpr int TN = TN_, TM = TM_, NS = NS_;
-  static constexpr int BM = 32 * TM, BN = 128 * TN, BK = 32, WN = 4;
+  static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_;
+  static constexpr int WN = 4, NW = WM * WN, NT = NW * 64;
+  static constexpr int TMW = TM / WM;  // 32-row W0 tiles per wave
+  static constexpr int BM = 32 * TM, BN = 128 * TN, BK = 32;
   static constexpr int X_BYTES = BM * BK * 2, Y_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
-  static constexpr int XL = BM / 16 / WN, YL = BN / 16 / WN;  // wave load instructions per stage
+  static constexpr int XL = BM / 16 / NW, YL = BN / 16 / NW;  // wave load instructions per stage
   static constexpr int L = XL + YL;
-  static constexpr int NB = (TM + WN - 1) / WN;  // W0 fragments each wave squares for the base term
-  static_assert(BM % 64 == 0, "X panel splits evenly over the waves");
-  static_assert(NS * STAGE_BYTES + WN * BM * 4 <= 160 * 1024, "LDS");
+  static constexpr int NB = (TMW + WN - 1) / WN;  // W0 fragments each wave squares for the base term
+  // epilogue: B tile passes of RPP rows in the stage area, row sums after them
+  static constexpr int AREA = NS * STAGE_BYTES;
+  static constexpr int RED_BYTES = WN * BM * 4;
+  static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
+  static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
+  static constexpr int RED_OFF = AREA - RED_BYTES;
+  static_assert(TM % WM == 0, "row tiles split over the waves");
+  static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "panels split evenly over the waves");
+  static_assert(AREA <= 160 * 1024, "LDS");
+  static_assert(RPP >= 32 && RPP * BN * 2 <= RED_OFF, "epilogue B-tile pass fits beside the row sums");
   static_assert((NS - 2) * L < 64, "vmcnt range");
 };
 
@@ -311,6 +332,12 @@ __device__ inline u32x4 lds_read16(uint32_t addr) {
   return v;
 }
 __device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// wait until at most N LDS reads of this wave are outstanding (they complete in order)
+template <int N>
+__device__ inline void lds_wait_keep() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Epilogue of the 16-byte path.  The workgroup's B tile (BM rows x BN rank
@@ -322,16 +349,15 @@ __device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 // accumulator registers: two 16-byte LDS reads.
 template <int DT, class TL>
 __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0, int64_t n0,
-                                          const f32x16 (&acc)[TL::TM][TL::TN], float (*red)[TL::BM], char* smem,
+                                          const f32x16 (&acc)[TL::TMW][TL::TN], float (*red)[TL::BM], char* smem,
                                           uint32_t lds0) {
   using V8 = typename Dt<DT>::V8;
-  constexpr int CPR = TL::BN / 8;                                     // 16-byte chunks per B-tile row
-  constexpr int AREA = TL::NS * TL::STAGE_BYTES;
-  constexpr int RPP = std::min(TL::BM, (AREA / (TL::BN * 2)) / 32 * 32);  // rows per pass
-  static_assert(RPP >= 32, "one 32-row block per pass at least");
+  constexpr int CPR = TL::BN / 8;  // 16-byte chunks per B-tile row
+  constexpr int RPP = TL::RPP;     // rows per pass
   constexpr int NPASS = (TL::BM + RPP - 1) / RPP;
-  constexpr int INSTR = RPP * CPR / 64;                               // 1 KiB DMA instructions per pass
+  constexpr int INSTR = RPP * CPR / 64;  // 1 KiB DMA instructions per pass
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int h = lane >> 5, frow = lane & 31;
   const int64_t out = a.sm.out, r = a.sm.r;
   const int64_t rows_here = std::min<int64_t>(std::max<int64_t>(out - m0, 0), TL::BM);
@@ -340,16 +366,16 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(static_cast<const char*>(a.sm.B) + (rows_here > 0 ? m0 * r * 2 : 0)), static_cast<short>(0),
       static_cast<int>(rows_here * r * 2), kBufferWord3);
-  float rs[TL::TM];
+  float rs[TL::TMW];
 #pragma unroll
-  for (int i = 0; i < TL::TM; ++i) rs[i] = 0.0f;
+  for (int i = 0; i < TL::TMW; ++i) rs[i] = 0.0f;
 
 #pragma unroll
   for (int pass = 0; pass < NPASS; ++pass) {
     const int row_base = pass * RPP;
     __syncthreads();  // stage buffers (or the previous pass) no longer read
     if (cols_here > 0) {
-      for (int q = wave; q < INSTR; q += TL::WN) {
+      for (int q = wave; q < INSTR; q += TL::NW) {
         const int slot = q * 64 + lane;
         const int rl = slot / CPR, pp = slot % CPR;
         const int ch = (pp + rl) % CPR;
@@ -363,12 +389,13 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     __syncthreads();
     if (cols_here > 0) {
 #pragma unroll
-      for (int i = 0; i < TL::TM; ++i) {
-        if (i * 32 < row_base || i * 32 >= row_base + RPP) continue;
-        const int rl = i * 32 - row_base + frow;
+      for (int i = 0; i < TL::TMW; ++i) {
+        const int r32 = wm * TL::TMW * 32 + i * 32;  // first tile row within the workgroup tile
+        if (r32 < row_base || r32 >= row_base + RPP) continue;
+        const int rl = r32 - row_base + frow;
 #pragma unroll
         for (int j = 0; j < TL::TN; ++j) {
-          const int c0 = wave * TL::TN * 4 + j * 4 + 2 * h;  // first of the lane's two chunks
+          const int c0 = wn * TL::TN * 4 + j * 4 + 2 * h;  // first of the lane's two chunks
           const int p0 = (c0 - rl % CPR + CPR) % CPR, p1 = (c0 + 1 - rl % CPR + CPR) % CPR;
           u32x4 w0 = lds_read16(lds0 + static_cast<uint32_t>((rl * CPR + p0) * 16));
           u32x4 w1 = lds_read16(lds0 + static_cast<uint32_t>((rl * CPR + p1) * 16));
@@ -388,9 +415,9 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     }
   }
 #pragma unroll
-  for (int i = 0; i < TL::TM; ++i) {
+  for (int i = 0; i < TL::TMW; ++i) {
     const float v = rs[i] + __shfl_xor(rs[i], 32, 64);
-    if (h == 0) red[wave][i * 32 + frow] = v;
+    if (h == 0) red[wn][wm * TL::TMW * 32 + i * 32 + frow] = v;
   }
   __syncthreads();
   if (tid < TL::BM && m0 + tid < out) {
@@ -401,12 +428,31 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   }
 }
 
-template <int DT, int TN, int TM, int NS>
-__global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
-  using TL = DmaTile<TN, TM, NS>;
+// MFMAs of one K step (rank fragments as the first operand) and the base-term
+// squares of the W0 fragments this wave owns (local tiles i = wn, wn + 4, ...).
+#define DORA_STEP_MFMAS(X, Y)                                                                           \
+  _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) \
+      acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, Y[j]), __builtin_bit_cast(V8, X[i]), acc[i][j]);
+#define DORA_STEP_SQUARES(X)                                                                      \
+  _Pragma("unroll") for (int k = 0; k < TL::NB; ++k) {                                            \
+    u32x4 xw = X[0];                                                                              \
+    _Pragma("unroll") for (int i = 1; i < TL::TMW; ++i) if (wn + TL::WN * k == i) xw = X[i];      \
+    const V8 xv = __builtin_bit_cast(V8, xw);                                                     \
+    if (wn + TL::WN * k < TL::TMW) {                                                              \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                             \
+        const float f = Dt<DT>::to_f(xv[e]);                                                      \
+        bsum[k] = __builtin_fmaf(f, f, bsum[k]);                                                  \
+      }                                                                                           \
+    }                                                                                             \
+  }
+
+template <int DT, int TN, int TM, int NS, int WM>
+__global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(WArgs a) {
+  using TL = DmaTile<TN, TM, NS, WM>;
   using V8 = typename Dt<DT>::V8;
-  __shared__ __attribute__((aligned(1024))) char smem[TL::NS * TL::STAGE_BYTES];
-  __shared__ float red[TL::WN][TL::BM];
+  __shared__ __attribute__((aligned(1024))) char smem[TL::AREA];
+  // the epilogue's row sums live past the B-tile passes, in the dead stage area
+  float(*red)[TL::BM] = reinterpret_cast<float(*)[TL::BM]>(smem + TL::RED_OFF);
 
   const int64_t v = xcd_logical_index();
   if (v >= a.total) return;
@@ -416,6 +462,7 @@ __global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
   const int64_t m0 = rb * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
   const int64_t st0 = a.S * sp / a.nSplit, st1 = a.S * (sp + 1) / a.nSplit;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
   const bool want_base = (nt == 0);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
@@ -454,15 +501,17 @@ __global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
 #pragma unroll
     for (int q = 0; q < TL::YL; ++q) {
       const int g = wave * TL::YL + q;
-      const uint32_t row = static_cast<uint32_t>(g * 16 + lrow);
+      // LDS row p of each 32-row rank tile holds rank row sigma(p) (see yaddr)
+      const int prow = (g * 16 + lrow) & 31;
+      const uint32_t row = static_cast<uint32_t>(((g * 16 + lrow) & ~31) + 16 * ((prow >> 2) & 1) + 4 * (prow >> 3) + (prow & 3));
       const uint32_t off = ((row * yld + kbytes) & ymask) | (kOob & ~ymask);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(stage + TL::X_BYTES + g * 1024), 16, off, 0, 0, 0);
     }
   };
 
-  f32x16 acc[TL::TM][TL::TN];
+  f32x16 acc[TL::TMW][TL::TN];
 #pragma unroll
-  for (int i = 0; i < TL::TM; ++i)
+  for (int i = 0; i < TL::TMW; ++i)
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
   float bsum[TL::NB];
@@ -472,14 +521,14 @@ __global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
   const int frow = lane & 31, fhalf = lane >> 5;
   // LDS byte offsets (within a stage) of this lane's fragments for K chunk kc
   auto xaddr = [&](int i, int kc) {
-    const int m = i * 32 + frow;
+    const int m = wm * TL::TMW * 32 + i * 32 + frow;
     return static_cast<uint32_t>(m * 64 + ((kc ^ ((m >> 2) & 3)) * 16));
   };
-  // MFMA row p of rank tile j reads rank row sigma(p) = 16*((p>>2)&1) + 4*(p>>3) + (p&3),
-  // so accumulator register q of a lane in half h holds rank column 16h + q
-  const int srow = 16 * ((frow >> 2) & 1) + 4 * (frow >> 3) + (frow & 3);
+  // LDS row p of rank tile j holds rank row sigma(p) = 16*((p>>2)&1) + 4*(p>>3) + (p&3)
+  // (placed so by the DMA), so accumulator register q of a lane in half h holds
+  // rank column 16h + q; the rows themselves are read in order
   auto yaddr = [&](int j, int kc) {
-    const int nn = wave * TL::TN * 32 + j * 32 + srow;
+    const int nn = wn * TL::TN * 32 + j * 32 + frow;
     return static_cast<uint32_t>(TL::X_BYTES + nn * 64 + ((kc ^ ((nn >> 2) & 3)) * 16));
   };
 
@@ -493,56 +542,36 @@ __global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (st + TL::NS - 1 < st1) issue(st + TL::NS - 1, static_cast<int>((st - st0 + TL::NS - 1) % TL::NS));
-    const uint32_t sbase = lds0 + static_cast<uint32_t>(((st - st0) % TL::NS) * TL::STAGE_BYTES);
+    const uint32_t sb = lds0 + static_cast<uint32_t>(((st - st0) % TL::NS) * TL::STAGE_BYTES);
     const bool base_here = want_base && st < a.sm.S1;
 
-    u32x4 x[2][TL::TM], y[2][TL::TN];
+    u32x4 x0[TL::TMW], y0[TL::TN], x1[TL::TMW], y1[TL::TN];
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i) x[0][i] = lds_read16(sbase + xaddr(i, fhalf));
+    for (int i = 0; i < TL::TMW; ++i) x0[i] = lds_read16(sb + xaddr(i, fhalf));
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) y[0][j] = lds_read16(sbase + yaddr(j, fhalf));
+    for (int j = 0; j < TL::TN; ++j) y0[j] = lds_read16(sb + yaddr(j, fhalf));
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) x1[i] = lds_read16(sb + xaddr(i, 2 + fhalf));
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) y1[j] = lds_read16(sb + yaddr(j, 2 + fhalf));
+    // the first step's fragments were read first: wait for those only
+    lds_wait_keep<TL::TMW + TL::TN>();
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) tie(y0[j]);
+    DORA_STEP_MFMAS(x0, y0)
+    if (base_here) {
+      DORA_STEP_SQUARES(x0)
+    }
     lds_wait();
 #pragma unroll
-    for (int i = 0; i < TL::TM; ++i) tie(x[0][i]);
+    for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);
 #pragma unroll
-    for (int j = 0; j < TL::TN; ++j) tie(y[0][j]);
-    // second K step's fragments load while the first step's MFMAs run
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i) x[1][i] = lds_read16(sbase + xaddr(i, 2 + fhalf));
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) y[1][j] = lds_read16(sbase + yaddr(j, 2 + fhalf));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks == 1) {
-        lds_wait();
-#pragma unroll
-        for (int i = 0; i < TL::TM; ++i) tie(x[1][i]);
-#pragma unroll
-        for (int j = 0; j < TL::TN; ++j) tie(y[1][j]);
-      }
-      if (base_here) {
-        // wave w squares the W0 fragments x[i], i = w, w + 4, ...: every row once
-#pragma unroll
-        for (int k = 0; k < TL::NB; ++k) {
-          u32x4 xw = x[ks][0];
-#pragma unroll
-          for (int i = 1; i < TL::TM; ++i)
-            if (wave + TL::WN * k == i) xw = x[ks][i];
-          const V8 xv = __builtin_bit_cast(V8, xw);
-          if (wave + TL::WN * k < TL::TM) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float f = Dt<DT>::to_f(xv[e]);
-              bsum[k] = __builtin_fmaf(f, f, bsum[k]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::TN; ++j)
-          acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, y[ks][j]), __builtin_bit_cast(V8, x[ks][i]), acc[i][j]);
+    for (int j = 0; j < TL::TN; ++j) tie(y1[j]);
+    DORA_STEP_MFMAS(x1, y1)
+    if (base_here) {
+      DORA_STEP_SQUARES(x1)
     }
   }
   __syncthreads();
@@ -551,9 +580,9 @@ __global__ __launch_bounds__(256, 1) void wstream_dma(WArgs a) {
 #pragma unroll
     for (int k = 0; k < TL::NB; ++k) {
       const float b = bsum[k] + __shfl_xor(bsum[k], 32, 64);
-      const int i = wave + TL::WN * k;
-      const int64_t row = m0 + i * 32 + frow;
-      if (i < TL::TM && fhalf == 0 && row < a.sm.out) a.base_part[static_cast<int64_t>(sp) * a.sm.out + row] = b;
+      const int i = wn + TL::WN * k;
+      const int64_t row = m0 + wm * TL::TMW * 32 + i * 32 + frow;
+      if (i < TL::TMW && fhalf == 0 && row < a.sm.out) a.base_part[static_cast<int64_t>(sp) * a.sm.out + row] = b;
     }
   }
   dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, red, smem, lds0);
@@ -726,10 +755,10 @@ int dma_tn(int64_t r) {
 
 // Per rank-tile width: W0 rows per tile (32*TM) and LDS stages.
 template <int TN> struct DmaShape;
-template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6; };
-template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4; };
-template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 4; };
-template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3; };
+template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6, WM = 2; };
+template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4, WM = 2; };
+template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 5, WM = 2; };
+template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3, WM = 2; };
 
 int dma_rows(int tn) {
   switch (tn) {
@@ -742,8 +771,10 @@ int dma_rows(int tn) {
 
 template <int DT, int TN>
 void launch_dma(const WArgs& w, hipStream_t stream) {
+  using S = DmaShape<TN>;
   const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
-  hipLaunchKernelGGL((wstream_dma<DT, TN, DmaShape<TN>::TM, DmaShape<TN>::NS>), grid, dim3(256), 0, stream, w);
+  hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM>), grid, dim3(DmaTile<TN, S::TM, S::NS, S::WM>::NT), 0,
+                     stream, w);
 }
 
 template <int DT>
@@ -756,12 +787,12 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
     const T* A = static_cast<const T*>(a.A);
     float* gpart = reinterpret_cast<float*>(ws + p.off_gpart);
     const int nUpper = p.nTg * (p.nTg + 1) / 2;
+    const dim3 ggrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(nUpper) * p.splitG, 8) * 8));
     if (vec)
-      hipLaunchKernelGGL((gram_partial<DT, true>), dim3(static_cast<unsigned>(nUpper * p.splitG)), dim3(256), 0,
-                         a.stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
+      hipLaunchKernelGGL((gram_partial<DT, true>), ggrid, dim3(256), 0, a.stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
     else
-      hipLaunchKernelGGL((gram_partial<DT, false>), dim3(static_cast<unsigned>(nUpper * p.splitG)), dim3(256), 0,
-                         a.stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
+      hipLaunchKernelGGL((gram_partial<DT, false>), ggrid, dim3(256), 0, a.stream, A, p.in, p.r, p.nTg, p.splitG,
+                         gpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(cdiv(p.r * p.r, 256))), dim3(256), 0, a.stream,
@@ -852,7 +883,9 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
     p.nTg = static_cast<int>(cdiv(r, 32));
     const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
     const int64_t max_split = std::max<int64_t>(1, cdiv(in, 16) / (4 * 8));
-    p.splitG = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({cdiv(512, nUpper), 16, max_split})));
+    int64_t sg = std::max<int64_t>(1, std::min<int64_t>({cdiv(512, nUpper), 16, max_split}));
+    if (sg >= 8) sg = sg / 8 * 8;  // whole K splits per XCD
+    p.splitG = static_cast<int>(sg);
   }
   auto layout = [&]() {
     size_t off = 0;
