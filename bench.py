@@ -35,7 +35,8 @@ from dora_fine_tuning_amd import binding, synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 WORKLOAD = "wide_8192_r384"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compose_bwd_wide_8192_r384_traffic.json")
-COMPOSE_SRC = os.path.join(ROOT, "dora_fine_tuning_amd", "csrc", "compose.hip")
+COMPOSE_SRCS = [os.path.join(ROOT, "dora_fine_tuning_amd", "csrc", f)
+                for f in ("compose.hip", "compose_kernels.hpp", "dora_common.hpp")]
 
 
 def compose_bytes(T, out, e=2):
@@ -58,8 +59,11 @@ def kernel_traffic(bwd_launch_bytes):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    src = hashlib.sha256(open(COMPOSE_SRC, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != src:
+    h = hashlib.sha256()
+    for f in COMPOSE_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256") != h.hexdigest():
         return None
     return rec.get("bytes_per_launch")
 
