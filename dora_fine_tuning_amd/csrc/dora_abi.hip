@@ -96,7 +96,7 @@ int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out
   // 16-byte path: 16-byte rows and pointers, and 32-bit buffer offsets over a
   // 128-row panel of W0 and a 512-row panel of G'
   const bool vec = (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) &&
-                   aligned16(ws) && in <= (int64_t(1) << 22) && r <= (int64_t(1) << 20);
+                   aligned16(ws) && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20);
   const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype, vec);
   dora::NormArgs a{W0, A, B, s, norm_out, ws, stream};
   return hip_status(dora::launch_norm(plan, a), "dora_norm_factored");

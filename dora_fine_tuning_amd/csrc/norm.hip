@@ -293,10 +293,10 @@ struct DmaTile {
   static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
   static constexpr int XL = BM / 16 / NW, YL = BN / 16 / NW;  // wave load instructions per stage
   static constexpr int L = XL + YL;
-  static constexpr int NB = (TMW + WN - 1) / WN;  // W0 fragments each wave squares for the base term
+  static constexpr int NP = (2 * TMW + WN - 1) / WN;  // (tile, K half) pairs each wave squares for the base term
   // epilogue: B tile passes of RPP rows in the stage area, row sums after them
   static constexpr int AREA = NS * STAGE_BYTES;
-  static constexpr int RED_BYTES = WN * BM * 4;
+  static constexpr int RED_BYTES = 2 * WN * BM * 4;  // cross and base row sums per rank-axis wave
   static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
   static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
   static constexpr int RED_OFF = AREA - RED_BYTES;
@@ -304,7 +304,7 @@ struct DmaTile {
   static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "panels split evenly over the waves");
   static_assert(AREA <= 160 * 1024, "LDS");
   static_assert(RPP >= 32 && RPP * BN * 2 <= RED_OFF, "epilogue B-tile pass fits beside the row sums");
-  static_assert((NS - 2) * L < 64, "vmcnt range");
+  static_assert(NS >= 3 && (NS - 2) * L < 64, "ring depth and vmcnt range");
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -339,6 +339,36 @@ __device__ inline void lds_wait_keep() {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+// One 16-byte-per-lane buffer load straight into LDS: lane l writes bytes
+// [16l, 16l + 16) of the 1 KiB block at lds (wave-uniform); offsets at or past
+// the resource's num_records read zero.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, off, 0, 0, 0);
+}
+// ds_read_b128 at a per-lane base plus a compile-time byte offset
+template <int OFF>
+__device__ inline u32x4 lds_read16_at(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
+  return v;
+}
+
+// acc + x0^2 + x1^2 for the two storage-dtype values packed in w (one dot2 instruction)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ inline float sq2(uint32_t w, float acc);
+template <>
+__device__ inline float sq2<0>(uint32_t w, float acc) {
+  const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+template <>
+__device__ inline float sq2<1>(uint32_t w, float acc) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  return __builtin_amdgcn_fdot2(v, v, acc, false);
+}
 
 // Epilogue of the 16-byte path.  The workgroup's B tile (BM rows x BN rank
 // columns) is brought into the free stage buffers by DMA, in passes of as many
@@ -349,8 +379,8 @@ __device__ inline void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 // accumulator registers: two 16-byte LDS reads.
 template <int DT, class TL>
 __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0, int64_t n0,
-                                          const f32x16 (&acc)[TL::TMW][TL::TN], float (*red)[TL::BM], char* smem,
-                                          uint32_t lds0) {
+                                          const f32x16 (&acc)[TL::TMW][TL::TN], const float (&bs)[TL::NP],
+                                          bool want_base, float (*red)[TL::BM], char* smem, uint32_t lds0) {
   using V8 = typename Dt<DT>::V8;
   constexpr int CPR = TL::BN / 8;  // 16-byte chunks per B-tile row
   constexpr int RPP = TL::RPP;     // rows per pass
@@ -419,174 +449,272 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     const float v = rs[i] + __shfl_xor(rs[i], 32, 64);
     if (h == 0) red[wn][wm * TL::TMW * 32 + i * 32 + frow] = v;
   }
+  if (want_base) {
+    // wave wn holds the squares of pairs p = wn + WN*t (tile p/2); at most one
+    // t of a wave falls on a given tile
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) {
+      float b = 0.0f;
+#pragma unroll
+      for (int t = 0; t < TL::NP; ++t)
+        if ((wn + TL::WN * t) >> 1 == i) b = bs[t];
+      b += __shfl_xor(b, 32, 64);
+      if (h == 0) red[TL::WN + wn][wm * TL::TMW * 32 + i * 32 + frow] = b;
+    }
+  }
   __syncthreads();
   if (tid < TL::BM && m0 + tid < out) {
     float c = 0.0f;
 #pragma unroll
     for (int w = 0; w < TL::WN; ++w) c += red[w][tid];
     a.cross_part[(static_cast<int64_t>(sp) * a.nTiles + nt) * out + m0 + tid] = c;
+    if (want_base) {
+      float b = 0.0f;
+#pragma unroll
+      for (int w = 0; w < TL::WN; ++w) b += red[TL::WN + w][tid];
+      a.base_part[static_cast<int64_t>(sp) * out + m0 + tid] = b;
+    }
   }
 }
 
-// MFMAs of one K step (rank fragments as the first operand) and the base-term
-// squares of the W0 fragments this wave owns (local tiles i = wn, wn + 4, ...).
+// MFMAs of one K step, rank fragments as the first operand.
 #define DORA_STEP_MFMAS(X, Y)                                                                           \
   _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) \
       acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, Y[j]), __builtin_bit_cast(V8, X[i]), acc[i][j]);
-#define DORA_STEP_SQUARES(X)                                                                      \
-  _Pragma("unroll") for (int k = 0; k < TL::NB; ++k) {                                            \
-    u32x4 xw = X[0];                                                                              \
-    _Pragma("unroll") for (int i = 1; i < TL::TMW; ++i) if (wn + TL::WN * k == i) xw = X[i];      \
-    const V8 xv = __builtin_bit_cast(V8, xw);                                                     \
-    if (wn + TL::WN * k < TL::TMW) {                                                              \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                             \
-        const float f = Dt<DT>::to_f(xv[e]);                                                      \
-        bsum[k] = __builtin_fmaf(f, f, bsum[k]);                                                  \
-      }                                                                                           \
-    }                                                                                             \
+
+// Base-term squares of one K step.  The 2*TMW (row tile, K half) fragment pairs
+// of a stage are dealt to the WN waves that share them: wave wn squares pair
+// p = wn + WN*t into bs[t] (pair p is tile p/2, step p%2).  wn is wave-uniform,
+// so the selection is a scalar branch.
+#define DORA_STEP_SQUARES(X, C)                                            \
+  _Pragma("unroll") for (int t = 0; t < TL::NP; ++t)                       \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i)                    \
+      if (wn + TL::WN * t == 2 * i + (C)) {                                \
+        bs[t] = sq2<DT>(X[i][0], bs[t]);                                   \
+        bs[t] = sq2<DT>(X[i][1], bs[t]);                                   \
+        bs[t] = sq2<DT>(X[i][2], bs[t]);                                   \
+        bs[t] = sq2<DT>(X[i][3], bs[t]);                                   \
+      }
+
+// N fragment reads from one base register at compile-time offsets SI + 2048*i.
+#define DORA_READS(V, BASE, SI, N)                                              \
+  V[0] = lds_read16_at<(SI)>(BASE);                                             \
+  if constexpr ((N) > 1) V[1] = lds_read16_at<(SI) + 2048>(BASE);               \
+  if constexpr ((N) > 2) V[2] = lds_read16_at<(SI) + 4096>(BASE);               \
+  if constexpr ((N) > 3) V[3] = lds_read16_at<(SI) + 6144>(BASE);
+
+// DMA of one stage of one segment: KST is the stage index within the segment,
+// KLEN its K length.  Whole stages add the stage's byte offset to the per-lane
+// row offsets; the last stage of a segment whose K length is not a multiple of
+// 32 sends the lanes past KLEN out of range (zeros).
+#define DORA_ISSUE_SEG(RX, RY, OX, OY, KST, KLEN, SO)                                                     \
+  {                                                                                                       \
+    const uint32_t kb_ = static_cast<uint32_t>(KST) * 64u;                                                \
+    const int krem_ = (KLEN) - (KST) * 32;                                                                \
+    if (krem_ >= 32) {                                                                                    \
+      _Pragma("unroll") for (int q = 0; q < TL::XL; ++q)                                                  \
+          dma16(RX, smem + (SO) + (wave * TL::XL + q) * 1024, OX[q] + kb_);                               \
+      _Pragma("unroll") for (int q = 0; q < TL::YL; ++q)                                                  \
+          dma16(RY, smem + (SO) + TL::X_BYTES + (wave * TL::YL + q) * 1024, OY[q] + kb_);                 \
+    } else {                                                                                              \
+      const bool ok_ = kc8 < krem_;                                                                       \
+      _Pragma("unroll") for (int q = 0; q < TL::XL; ++q)                                                  \
+          dma16(RX, smem + (SO) + (wave * TL::XL + q) * 1024, ok_ ? OX[q] + kb_ : kOob);                  \
+      _Pragma("unroll") for (int q = 0; q < TL::YL; ++q)                                                  \
+          dma16(RY, smem + (SO) + TL::X_BYTES + (wave * TL::YL + q) * 1024, ok_ ? OY[q] + kb_ : kOob);    \
+    }                                                                                                     \
+  }
+
+// DMA of stage ST (of the whole augmented K axis) into ring slot SLOT.
+#define DORA_ISSUE(ST, SLOT)                                                      \
+  {                                                                               \
+    const int st_ = (ST);                                                         \
+    constexpr int so_ = (SLOT) * TL::STAGE_BYTES;                                 \
+    if (st_ < S1)                                                                 \
+      DORA_ISSUE_SEG(rxW, ryA, oxW, oyA, st_, in, so_)                            \
+    else if (st_ < S12)                                                           \
+      DORA_ISSUE_SEG(rxB, ryH, oxB, oyG, st_ - S1, r, so_)                        \
+    else                                                                          \
+      DORA_ISSUE_SEG(rxB, ryL, oxB, oyG, st_ - S12, r, so_)                       \
+  }
+
+#define DORA_PROLOGUE(U)                                                      \
+  if constexpr ((U) < TL::NS - 1) {                                           \
+    if (st0 + (U) < st1) DORA_ISSUE(st0 + (U), (U))                           \
+  }
+
+// Fragment reads of one stage from ring slot SLOT into register set B.
+#define DORA_READ_STAGE(SLOT, B)                                                   \
+  {                                                                               \
+    constexpr int so_ = (SLOT) * TL::STAGE_BYTES;                                 \
+    constexpr int sw_ = so_ & ~32767, si_ = so_ & 32767;                          \
+    const uint32_t xa0 = xb0 + sw_, xa1 = xb1 + sw_, ya0 = yb0 + sw_, ya1 = yb1 + sw_; \
+    DORA_READS(fx0[B], xa0, si_, TL::TMW)                                         \
+    DORA_READS(fy0[B], ya0, si_, TL::TN)                                          \
+    DORA_READS(fx1[B], xa1, si_, TL::TMW)                                         \
+    DORA_READS(fy1[B], ya1, si_, TL::TN)                                          \
+  }
+
+// Stage st = sb + U, software-pipelined: its fragments were read into
+// register set U % 2 during the previous stage.  Wait for those reads, then
+// (unless st is the last stage) wait for this wave's DMA of stage st + 1 and
+// meet the other waves: after the barrier every wave's stage st + 1 has landed
+// and nobody reads the slot of stage st - 1 any more, so that slot takes the
+// DMA of stage st + NS - 1 and the reads of stage st + 1 go out before this
+// stage's MFMAs, hiding their latency behind them.
+#define DORA_STAGE(U)                                                                               \
+  if constexpr ((U) < 2 * TL::NS) {                                                                 \
+    constexpr int cb = (U) % 2, nb = 1 - (U) % 2;                                                   \
+    const int st = sb + (U);                                                                        \
+    if (st >= st1) break;                                                                           \
+    lds_wait();                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) { tie(fx0[cb][i]); tie(fx1[cb][i]); }      \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) { tie(fy0[cb][j]); tie(fy1[cb][j]); }       \
+    if (st + 1 < st1) {                                                                             \
+      if (st + TL::NS - 2 < st1)                                                                    \
+        wait_vmcnt<(TL::NS - 3) * TL::L>();                                                         \
+      else                                                                                          \
+        wait_vmcnt<0>();                                                                            \
+      __builtin_amdgcn_s_barrier();                                                                 \
+      if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS)           \
+      DORA_READ_STAGE(((U) + 1) % TL::NS, nb)                                                       \
+    }                                                                                               \
+    const bool base_here = want_base && st < S1;                                                    \
+    DORA_STEP_MFMAS(fx0[cb], fy0[cb])                                                               \
+    if (base_here) {                                                                                \
+      DORA_STEP_SQUARES(fx0[cb], 0)                                                                 \
+    }                                                                                               \
+    DORA_STEP_MFMAS(fx1[cb], fy1[cb])                                                               \
+    if (base_here) {                                                                                \
+      DORA_STEP_SQUARES(fx1[cb], 1)                                                                 \
+    }                                                                                               \
   }
 
 template <int DT, int TN, int TM, int NS, int WM>
 __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(WArgs a) {
   using TL = DmaTile<TN, TM, NS, WM>;
   using V8 = typename Dt<DT>::V8;
+  static_assert(TL::NS <= 6, "ring slots expanded below");
   __shared__ __attribute__((aligned(1024))) char smem[TL::AREA];
-  // the epilogue's row sums live past the B-tile passes, in the dead stage area
+  // the epilogue's row sums (cross, then base) live past the B-tile passes, in the dead stage area
   float(*red)[TL::BM] = reinterpret_cast<float(*)[TL::BM]>(smem + TL::RED_OFF);
 
-  const int64_t v = xcd_logical_index();
-  if (v >= a.total) return;
-  const int nt = static_cast<int>(v % a.nTiles);
-  const int64_t rb = (v / a.nTiles) % a.nRB;
-  const int sp = static_cast<int>(v / (static_cast<int64_t>(a.nTiles) * a.nRB));
-  const int64_t m0 = rb * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
-  const int64_t st0 = a.S * sp / a.nSplit, st1 = a.S * (sp + 1) / a.nSplit;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
+  if (v >= static_cast<uint32_t>(a.total)) return;
+  const uint32_t nTiles = static_cast<uint32_t>(a.nTiles), nRB = static_cast<uint32_t>(a.nRB);
+  const int nt = static_cast<int>(v % nTiles);
+  const uint32_t rb = (v / nTiles) % nRB;
+  const int sp = static_cast<int>(v / (nTiles * nRB));
+  const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
+  // stage bookkeeping in 32 bits: the augmented K axis has at most 2^16 + 2^16 stages here
+  const int S1 = static_cast<int>(a.sm.S1), S12 = S1 + static_cast<int>(a.sm.S2);
+  const int st0 = static_cast<int>(a.S * sp / a.nSplit), st1 = static_cast<int>(a.S * (sp + 1) / a.nSplit);
+  const int in = static_cast<int>(a.sm.in), r = static_cast<int>(a.sm.r);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const bool want_base = (nt == 0);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
-  // per-lane load geometry: row within a 16-row group and swizzled chunk
-  const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);  // equals ((16g + lrow) >> 2) & 3 for any group g
-
+  // Buffer resources of the five operand panels, each rebased to the
+  // workgroup's first row; rows past the operand lie beyond num_records and
+  // read zero.  Byte offsets stay below 2^31 (at most 512 rows of under 2^21
+  // elements).
   auto rsrc = [](const void* base, int64_t row0, int64_t rows, int64_t ld, int64_t max_rows) {
     const int64_t nrows = std::min<int64_t>(std::max<int64_t>(rows - row0, 0), max_rows);
     const char* p = static_cast<const char*>(base) + (nrows > 0 ? row0 * ld * 2 : 0);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), static_cast<short>(0),
                                              static_cast<int>(nrows * ld * 2), kBufferWord3);
   };
+  const int64_t out = a.sm.out;
+  const __amdgpu_buffer_rsrc_t rxW = rsrc(a.sm.W0, m0, out, in, TL::BM);
+  const __amdgpu_buffer_rsrc_t ryA = rsrc(a.sm.A, n0, r, in, TL::BN);
+  const __amdgpu_buffer_rsrc_t rxB = rsrc(a.sm.B, m0, out, r, TL::BM);
+  const __amdgpu_buffer_rsrc_t ryH = rsrc(a.sm.Ghi, n0, r, r, TL::BN);
+  const __amdgpu_buffer_rsrc_t ryL = rsrc(a.sm.Glo, n0, r, r, TL::BN);
 
-  auto issue = [&](int64_t st, int buf) {
-    Operand X, Y;
-    int64_t k0;
-    bool seg_w;
-    a.sm.template get<TL::BK>(st, X, Y, k0, seg_w);
-    const __amdgpu_buffer_rsrc_t rx = rsrc(X.p, m0, X.rows, X.ld, TL::BM);
-    const __amdgpu_buffer_rsrc_t ry = rsrc(Y.p, n0, Y.rows, Y.ld, TL::BN);
-    const int64_t k = k0 + lchunk * 8;
-    // 32-bit byte offsets (a panel spans at most 512 rows of at most 2^22 elements)
-    const uint32_t kbytes = static_cast<uint32_t>(k) * 2u;
-    const uint32_t xmask = (k < X.klen) ? 0xFFFFFFFFu : 0u;
-    const uint32_t ymask = (k < Y.klen) ? 0xFFFFFFFFu : 0u;
-    const uint32_t xld = static_cast<uint32_t>(X.ld) * 2u, yld = static_cast<uint32_t>(Y.ld) * 2u;
-    char* stage = smem + buf * TL::STAGE_BYTES;
+  // Per-lane DMA geometry: one wave instruction moves 16 rows x 64 bytes; lane
+  // l takes row l/4 of its group and the logical 16-byte chunk (l%4) ^ ((row/4)%4),
+  // which lands in LDS slot l%4 (the XOR swizzle of the fragment reads).  The
+  // rank-side panel is fetched in the row order sigma (see the fragment reads).
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const int kc8 = lchunk * 8;  // first K element of the lane's chunk within a stage
+  uint32_t oxW[TL::XL], oxB[TL::XL], oyA[TL::YL], oyG[TL::YL];
 #pragma unroll
-    for (int q = 0; q < TL::XL; ++q) {
-      const int g = wave * TL::XL + q;  // 16-row group of the X panel
-      const uint32_t row = static_cast<uint32_t>(g * 16 + lrow);
-      const uint32_t off = ((row * xld + kbytes) & xmask) | (kOob & ~xmask);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(stage + g * 1024), 16, off, 0, 0, 0);
-    }
+  for (int q = 0; q < TL::XL; ++q) {
+    const uint32_t row = static_cast<uint32_t>((wave * TL::XL + q) * 16 + lrow);
+    oxW[q] = row * static_cast<uint32_t>(in) * 2u + kc8 * 2u;
+    oxB[q] = row * static_cast<uint32_t>(r) * 2u + kc8 * 2u;
+  }
 #pragma unroll
-    for (int q = 0; q < TL::YL; ++q) {
-      const int g = wave * TL::YL + q;
-      // LDS row p of each 32-row rank tile holds rank row sigma(p) (see yaddr)
-      const int prow = (g * 16 + lrow) & 31;
-      const uint32_t row = static_cast<uint32_t>(((g * 16 + lrow) & ~31) + 16 * ((prow >> 2) & 1) + 4 * (prow >> 3) + (prow & 3));
-      const uint32_t off = ((row * yld + kbytes) & ymask) | (kOob & ~ymask);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(stage + TL::X_BYTES + g * 1024), 16, off, 0, 0, 0);
-    }
-  };
+  for (int q = 0; q < TL::YL; ++q) {
+    const int p = (wave * TL::YL + q) * 16 + lrow, prow = p & 31;
+    const uint32_t row = static_cast<uint32_t>((p & ~31) + 16 * ((prow >> 2) & 1) + 4 * (prow >> 3) + (prow & 3));
+    oyA[q] = row * static_cast<uint32_t>(in) * 2u + kc8 * 2u;
+    oyG[q] = row * static_cast<uint32_t>(r) * 2u + kc8 * 2u;
+  }
+
+  // Fragment reads.  LDS row m of a stage's W-side panel holds logical chunk c
+  // at slot c ^ ((m/4)%4); a lane reads row 32*i + (l%32) of its wave's tiles,
+  // K chunk 2*step + l/32, so the swizzle depends on l only and tile i is a
+  // fixed 2048-byte step.  Rank-side row p of each 32-row tile holds rank row
+  // sigma(p) = 16*((p/4)%2) + 4*(p/8) + p%4, so accumulator register q of a lane
+  // in half h holds rank column 16h + q.
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow >> 2) & 3;
+  const uint32_t xrow = lds0 + static_cast<uint32_t>((wm * TL::TMW * 32 + frow) * 64);
+  const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * 64);
+  const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), xb1 = xrow + (((2 + fhalf) ^ fsw) * 16);
+  const uint32_t yb0 = yrow + ((fhalf ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
 
   f32x16 acc[TL::TMW][TL::TN];
 #pragma unroll
   for (int i = 0; i < TL::TMW; ++i)
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
-  float bsum[TL::NB];
+  float bs[TL::NP];
 #pragma unroll
-  for (int k = 0; k < TL::NB; ++k) bsum[k] = 0.0f;
+  for (int t = 0; t < TL::NP; ++t) bs[t] = 0.0f;
 
-  const int frow = lane & 31, fhalf = lane >> 5;
-  // LDS byte offsets (within a stage) of this lane's fragments for K chunk kc
-  auto xaddr = [&](int i, int kc) {
-    const int m = wm * TL::TMW * 32 + i * 32 + frow;
-    return static_cast<uint32_t>(m * 64 + ((kc ^ ((m >> 2) & 3)) * 16));
-  };
-  // LDS row p of rank tile j holds rank row sigma(p) = 16*((p>>2)&1) + 4*(p>>3) + (p&3)
-  // (placed so by the DMA), so accumulator register q of a lane in half h holds
-  // rank column 16h + q; the rows themselves are read in order
-  auto yaddr = [&](int j, int kc) {
-    const int nn = wn * TL::TN * 32 + j * 32 + frow;
-    return static_cast<uint32_t>(TL::X_BYTES + nn * 64 + ((kc ^ ((nn >> 2) & 3)) * 16));
-  };
-
-#pragma unroll
-  for (int i = 0; i < TL::NS - 1; ++i)
-    if (st0 + i < st1) issue(st0 + i, i);
-  for (int64_t st = st0; st < st1; ++st) {
-    if (st + TL::NS - 2 < st1)
+  // fragments of the current and the next stage: [register set][tile]
+  u32x4 fx0[2][TL::TMW], fx1[2][TL::TMW], fy0[2][TL::TN], fy1[2][TL::TN];
+  DORA_PROLOGUE(0)
+  DORA_PROLOGUE(1)
+  DORA_PROLOGUE(2)
+  DORA_PROLOGUE(3)
+  DORA_PROLOGUE(4)
+  if (st0 < st1) {
+    if (st0 + TL::NS - 2 < st1)
       wait_vmcnt<(TL::NS - 2) * TL::L>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (st + TL::NS - 1 < st1) issue(st + TL::NS - 1, static_cast<int>((st - st0 + TL::NS - 1) % TL::NS));
-    const uint32_t sb = lds0 + static_cast<uint32_t>(((st - st0) % TL::NS) * TL::STAGE_BYTES);
-    const bool base_here = want_base && st < a.sm.S1;
-
-    u32x4 x0[TL::TMW], y0[TL::TN], x1[TL::TMW], y1[TL::TN];
-#pragma unroll
-    for (int i = 0; i < TL::TMW; ++i) x0[i] = lds_read16(sb + xaddr(i, fhalf));
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) y0[j] = lds_read16(sb + yaddr(j, fhalf));
-#pragma unroll
-    for (int i = 0; i < TL::TMW; ++i) x1[i] = lds_read16(sb + xaddr(i, 2 + fhalf));
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) y1[j] = lds_read16(sb + yaddr(j, 2 + fhalf));
-    // the first step's fragments were read first: wait for those only
-    lds_wait_keep<TL::TMW + TL::TN>();
-#pragma unroll
-    for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) tie(y0[j]);
-    DORA_STEP_MFMAS(x0, y0)
-    if (base_here) {
-      DORA_STEP_SQUARES(x0)
-    }
-    lds_wait();
-#pragma unroll
-    for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) tie(y1[j]);
-    DORA_STEP_MFMAS(x1, y1)
-    if (base_here) {
-      DORA_STEP_SQUARES(x1)
-    }
+    DORA_READ_STAGE(0, 0)
   }
-  __syncthreads();
-
-  if (want_base) {
-#pragma unroll
-    for (int k = 0; k < TL::NB; ++k) {
-      const float b = bsum[k] + __shfl_xor(bsum[k], 32, 64);
-      const int i = wn + TL::WN * k;
-      const int64_t row = m0 + wm * TL::TMW * 32 + i * 32 + frow;
-      if (i < TL::TMW && fhalf == 0 && row < a.sm.out) a.base_part[static_cast<int64_t>(sp) * a.sm.out + row] = b;
-    }
+  for (int sb = st0; sb < st1; sb += 2 * TL::NS) {
+    DORA_STAGE(0)
+    DORA_STAGE(1)
+    DORA_STAGE(2)
+    DORA_STAGE(3)
+    DORA_STAGE(4)
+    DORA_STAGE(5)
+    DORA_STAGE(6)
+    DORA_STAGE(7)
+    DORA_STAGE(8)
+    DORA_STAGE(9)
+    DORA_STAGE(10)
+    DORA_STAGE(11)
   }
-  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, red, smem, lds0);
+
+  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0);
 }
+#undef DORA_STAGE
+#undef DORA_READ_STAGE
+#undef DORA_PROLOGUE
+#undef DORA_ISSUE
+#undef DORA_ISSUE_SEG
+#undef DORA_READS
+#undef DORA_STEP_SQUARES
 
 // ---------------------------------------------------------------------------
 // W stream, general path (row lengths not multiples of 8, or unaligned
