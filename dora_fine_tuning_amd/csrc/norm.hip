@@ -7,9 +7,9 @@
 // O(out*r + r*r)).
 //
 // Kernels, in launch order:
-//   gram_partial      split-K partials of G = A A^T on upper-triangular 32x32
-//                     tiles (G is symmetric), MFMA 32x32x16 with fp32
-//                     accumulation;
+//   gram_dma          (16-byte path) split-K partials of G = A A^T on the
+//   gram_partial      (general path) upper-triangular tiles (G is symmetric),
+//                     MFMA 32x32x16 with fp32 accumulation;
 //   gram_finalize     fixed-order sum of the partials, then G' = (s/2) G split
 //                     into two storage-dtype matrices G'hi + G'lo (written with
 //                     their mirror images);
@@ -58,7 +58,7 @@ constexpr int kGramU = 8;  // K steps per batch of fragment loads
 // loaded straight from global memory (A is small and L2/MALL resident) in
 // batches of kGramU steps; the four wave partials are summed in LDS in a fixed
 // order and stored as the split's 32x32 tile.
-template <int DT, bool VEC>
+template <int DT>
 __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A, int64_t in, int64_t r, int nT,
                                                     int splitG, float* gpart) {
   using T = typename Dt<DT>::T;
@@ -89,10 +89,6 @@ __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A,
   const int64_t xrc = xr < r ? xr : r - 1, yrc = yr < r ? yr : r - 1;
   auto frag = [&](int64_t row, int64_t rowc, int64_t k) -> V8 {
     const bool ok = row < r && k < in;
-    if (VEC) {
-      const Chunk c = *reinterpret_cast<const Chunk*>(A + rowc * in + (k < in ? k : in - 8));
-      return __builtin_bit_cast(V8, ok ? c : zero_chunk());
-    }
     V8 v;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -141,13 +137,25 @@ __global__ __launch_bounds__(256) void gram_finalize(const float* gpart, int spl
   const float* src = gpart + idx;
   const int64_t stride = r * r;
   float g = 0.0f;
-  int sp = 0;
-  for (; sp + 4 <= splitG; sp += 4) {
-    const float a0 = src[(sp + 0) * stride], a1 = src[(sp + 1) * stride];
-    const float a2 = src[(sp + 2) * stride], a3 = src[(sp + 3) * stride];
-    g += (a0 + a1) + (a2 + a3);
+  // groups of up to kFinSplits partials, all loaded before they are summed
+  // pairwise; the groups are added in order
+  constexpr int kFinSplits = 16;
+  for (int s0 = 0; s0 < splitG; s0 += kFinSplits) {
+    float a[kFinSplits];
+#pragma unroll
+    for (int k = 0; k < kFinSplits; ++k) {
+      const int sp = s0 + k < splitG ? s0 + k : splitG - 1;
+      a[k] = src[sp * stride];
+    }
+#pragma unroll
+    for (int k = 0; k < kFinSplits; ++k)
+      if (s0 + k >= splitG) a[k] = 0.0f;
+#pragma unroll
+    for (int w = 1; w < kFinSplits; w *= 2)
+#pragma unroll
+      for (int k = 0; k < kFinSplits; k += 2 * w) a[k] += a[k + w];
+    g += a[0];
   }
-  for (; sp < splitG; ++sp) g += src[sp * stride];
   const float gp = half_s * g;
   const T hi = Dt<DT>::from_f(gp);
   const T lo = Dt<DT>::from_f(gp - Dt<DT>::to_f(hi));
@@ -474,6 +482,135 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
       for (int w = 0; w < TL::WN; ++w) b += red[TL::WN + w][tid];
       a.base_part[static_cast<int64_t>(sp) * out + m0 + tid] = b;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gram matrix, 16-byte path: split-K partials of G = A A^T on the upper 64x64
+// blocks (G is symmetric).  Workgroup (block, split) = 4 waves, one 32x32
+// sub-tile each.  K stages of 64 go global -> LDS by DMA: one wave
+// instruction moves 8 rows x 128 bytes (whole cache lines), lane l taking row
+// l/8 and the logical 16-byte chunk (l%8) ^ ((row/2)%8), which lands in LDS
+// slot l%8; the fragment reads of 16 consecutive rows at one logical chunk then
+// hit 16 distinct bank groups.  Rows past r and K past in read zero.
+constexpr int kGramStage = 2 * 64 * 128;  // X and Y panels, 64 rows x 128 bytes
+constexpr int kGramL = 4;                 // DMA instructions per wave per stage
+
+template <int DT, int kGramNS>
+__global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int in, int r, int nB, int splitG,
+                                                float* gpart) {
+  using V8 = typename Dt<DT>::V8;
+  static_assert(kGramNS >= 3 && kGramNS <= 8 && (kGramNS - 2) * kGramL < 64, "ring slots");
+  __shared__ __attribute__((aligned(1024))) char smem[kGramNS * kGramStage];
+  const int nUpper = nB * (nB + 1) / 2;
+  // XCD-aware: consecutive logical indices share a K split, so each XCD's L2
+  // holds one K slice of A
+  const int v = static_cast<int>(xcd_logical_index());
+  if (v >= nUpper * splitG) return;
+  int u = v % nUpper;
+  const int sp = v / nUpper;
+  int bi = 0;
+  while (u >= nB - bi) {
+    u -= nB - bi;
+    ++bi;
+  }
+  const int bj = bi + u;
+  const int x0 = bi * 64, y0 = bj * 64;
+  const int nk = (in + 63) / 64;
+  const int st0 = static_cast<int>(static_cast<int64_t>(nk) * sp / splitG);
+  const int st1 = static_cast<int>(static_cast<int64_t>(nk) * (sp + 1) / splitG);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+
+  auto rsrc = [&](int row0) {
+    const int nrows = std::min(std::max(r - row0, 0), 64);
+    const char* p = reinterpret_cast<const char*>(A) + (nrows > 0 ? static_cast<int64_t>(row0) * in * 2 : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), static_cast<short>(0), nrows * in * 2,
+                                             kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x0), ry = rsrc(y0);
+  // this wave's DMA instructions: X groups 2*wave, 2*wave + 1; Y likewise
+  uint32_t off[2];
+  int kc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = (2 * wave + q) * 8 + (lane >> 3);
+    kc[q] = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    off[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(in) * 2u + kc[q] * 2u;
+  }
+  auto issue = [&](int st, int slot) {
+    const uint32_t kb = static_cast<uint32_t>(st) * 128u;
+    const int krem = in - st * 64;
+    char* base = smem + slot * kGramStage;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t o = (kc[q] < krem) ? off[q] + kb : kOob;
+      dma16(rx, base + (2 * wave + q) * 1024, o);
+      dma16(ry, base + 8192 + (2 * wave + q) * 1024, o);
+    }
+  };
+
+  // fragment addresses: lane l reads row 32*w + l%32, logical chunk 2*step + l/32
+  const int frow = lane & 31, fh = lane >> 5, fsw = (frow >> 1) & 7;
+  uint32_t xq[4], yq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    xq[q] = lds0 + static_cast<uint32_t>((wm * 32 + frow) * 128 + (((2 * q + fh) ^ fsw) * 16));
+    yq[q] = lds0 + 8192u + static_cast<uint32_t>((wn * 32 + frow) * 128 + (((2 * q + fh) ^ fsw) * 16));
+  }
+
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int i = 0; i < kGramNS - 1; ++i)
+    if (st0 + i < st1) issue(st0 + i, i);
+#define DORA_GSTAGE(U)                                                                    \
+  if constexpr ((U) < kGramNS) {                                                          \
+    const int st = sb + (U);                                                              \
+    if (st >= st1) break;                                                                 \
+    if (st + kGramNS - 2 < st1)                                                           \
+      wait_vmcnt<(kGramNS - 2) * kGramL>();                                               \
+    else                                                                                  \
+      wait_vmcnt<0>();                                                                    \
+    __builtin_amdgcn_s_barrier();                                                         \
+    if (st + kGramNS - 1 < st1) issue(st + kGramNS - 1, ((U) + kGramNS - 1) % kGramNS);   \
+    constexpr int so = (U) * kGramStage;                                                  \
+    constexpr int sw = so & ~32767, si = so & 32767;                                      \
+    u32x4 fx[4], fy[4];                                                                   \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                       \
+      fx[q] = lds_read16_at<si>(xq[q] + sw);                                              \
+      fy[q] = lds_read16_at<si>(yq[q] + sw);                                              \
+    }                                                                                     \
+    lds_wait();                                                                           \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                       \
+      tie(fx[q]);                                                                         \
+      tie(fy[q]);                                                                         \
+    }                                                                                     \
+    acc0 = Dt<DT>::mfma32(__builtin_bit_cast(V8, fx[0]), __builtin_bit_cast(V8, fy[0]), acc0); \
+    acc1 = Dt<DT>::mfma32(__builtin_bit_cast(V8, fx[1]), __builtin_bit_cast(V8, fy[1]), acc1); \
+    acc0 = Dt<DT>::mfma32(__builtin_bit_cast(V8, fx[2]), __builtin_bit_cast(V8, fy[2]), acc0); \
+    acc1 = Dt<DT>::mfma32(__builtin_bit_cast(V8, fx[3]), __builtin_bit_cast(V8, fy[3]), acc1); \
+  }
+  for (int sb = st0; sb < st1; sb += kGramNS) {
+    DORA_GSTAGE(0)
+    DORA_GSTAGE(1)
+    DORA_GSTAGE(2)
+    DORA_GSTAGE(3)
+    DORA_GSTAGE(4)
+    DORA_GSTAGE(5)
+    DORA_GSTAGE(6)
+    DORA_GSTAGE(7)
+  }
+#undef DORA_GSTAGE
+
+  // acc register q of lane l: G[x0 + 32*wm + 8*(q/4) + 4*(l/32) + q%4][y0 + 32*wn + l%32]
+  float* dst = gpart + static_cast<int64_t>(sp) * r * r;
+  const int col = y0 + wn * 32 + frow;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = x0 + wm * 32 + 8 * (q / 4) + 4 * fh + (q % 4);
+    if (row < r && col < r) dst[static_cast<int64_t>(row) * r + col] = acc0[q] + acc1[q];
   }
 }
 
@@ -917,9 +1054,10 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
     const int nUpper = p.nTg * (p.nTg + 1) / 2;
     const dim3 ggrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(nUpper) * p.splitG, 8) * 8));
     if (vec)
-      hipLaunchKernelGGL((gram_partial<DT, true>), ggrid, dim3(256), 0, a.stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
+      hipLaunchKernelGGL((gram_dma<DT, 4>), ggrid, dim3(256), 0, a.stream, A, static_cast<int>(p.in),
+                         static_cast<int>(p.r), p.nTg, p.splitG, gpart);
     else
-      hipLaunchKernelGGL((gram_partial<DT, false>), ggrid, dim3(256), 0, a.stream, A, p.in, p.r, p.nTg, p.splitG,
+      hipLaunchKernelGGL((gram_partial<DT>), ggrid, dim3(256), 0, a.stream, A, p.in, p.r, p.nTg, p.splitG,
                          gpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1006,11 +1144,13 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
     p.nSplit = static_cast<int>(best);
   }
   if (r > 0) {
-    // Gram: 32x32 upper tiles x K splits, ~512 workgroups, at least 8 K steps
-    // of 16 per wave
-    p.nTg = static_cast<int>(cdiv(r, 32));
+    // Gram: upper tiles (64x64 on the 16-byte path, 32x32 otherwise) x K
+    // splits; about 512 workgroups, at least 4 K stages of
+    // 64 (general path: 8 K steps of 16 per wave) per workgroup
+    const int64_t tile = vec ? 64 : 32;
+    p.nTg = static_cast<int>(cdiv(r, tile));
     const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
-    const int64_t max_split = std::max<int64_t>(1, cdiv(in, 16) / (4 * 8));
+    const int64_t max_split = std::max<int64_t>(1, vec ? cdiv(in, 64) / 4 : cdiv(in, 16) / (4 * 8));
     int64_t sg = std::max<int64_t>(1, std::min<int64_t>({cdiv(512, nUpper), 16, max_split}));
     if (sg >= 8) sg = sg / 8 * 8;  // whole K splits per XCD
     p.splitG = static_cast<int>(sg);

@@ -20,7 +20,8 @@ struct NormPlan {
   int nTiles = 0;
   int64_t S1 = 0, S2 = 0, S = 0;  // K stages: W0.A^T part, each B.G' part, total
   int nSplit = 0;
-  // Gram: 32x32 upper-triangular tiles x K splits
+  // Gram: upper-triangular tiles per side (64 rows on the 16-byte path, 32
+  // otherwise) x K splits
   int nTg = 0, splitG = 0;
   // workspace byte offsets
   size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, bytes = 0;
