@@ -112,6 +112,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cold-reps", type=int, default=10, help="compose calls timed after a cache-evicting read")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for byte counters)")
     args = ap.parse_args()
@@ -175,6 +176,28 @@ def main():
     norm_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    # Cold compose: before each call a 1 GiB read-only pass evicts L2 and the
+    # 256 MB last-level cache without leaving dirty lines, so the kernel's
+    # inputs come from HBM.  In the step above the backward partly reads base
+    # and lora that the forward left in the last-level cache.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    cold = {"fwd": [], "bwd": []}
+    for k in range(2 + args.cold_reps if args.cold_reps > 0 else 0):
+        for name, call in (("fwd", lambda: binding.dora_compose_fwd(base, lora, mag, norm, s, y=y)),
+                           ("bwd", lambda: binding.dora_compose_bwd(dy, base, lora, mag, norm, s, d_lora=d_lora,
+                                                                    d_base=d_base, d_mag=d_mag,
+                                                                    workspace=ws_bwd))):
+            flush.view(torch.int64).sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            if k >= 2:
+                cold[name].append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    cold_us = {k: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3 if v else None for k, v in cold.items()}
+
     fwd_b, bwd_b = compose_bytes(T, out)
     comp_ms = fwd_ms.mean() + bwd_ms.mean()
     value = (fwd_b + bwd_b) / (comp_ms * 1e-3) / 1e9
@@ -203,6 +226,9 @@ def main():
         "norm_frac_mfma_peak": round(nf / (norm_ms.mean() * 1e-3) / 2.5e15, 4),
         "compose_fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "compose_bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
+        "compose_cold": ({"fwd_us": round(cold_us["fwd"], 2), "bwd_us": round(cold_us["bwd"], 2),
+                          "gbs": round((fwd_b + bwd_b) / ((cold_us["fwd"] + cold_us["bwd"]) * 1e-6) / 1e9, 1),
+                          "reps": args.cold_reps} if args.cold_reps > 0 else None),
         "roofline": {
             "kernel": "dora_compose_bwd (compose_bwd_vec + dmag_finalize)",
             "bound": "hbm",

@@ -268,7 +268,10 @@ __global__ __launch_bounds__(COLS* GRPS) void dmag_finalize(const float* partial
 // the best pair is nontemporal stores in the forward and nontemporal loads and
 // stores in the backward (~74% of peak HBM bandwidth over both, against ~67%
 // with default policies).
-constexpr int kFwdThreads = 256, kFwdRows = 16, kFwdUnroll = 4;
+// Short token blocks: consecutive workgroups then cover adjacent memory and
+// the resident set sweeps HBM compactly (4-row blocks measured about 15%
+// faster than 16-row blocks on data not in the caches).
+constexpr int kFwdThreads = 256, kFwdRows = 4, kFwdUnroll = 4;
 constexpr bool kFwdNtLoad = false, kFwdNtStore = true;
 constexpr int kBwdThreads = 256, kBwdUnroll = 4;
 constexpr bool kBwdNtLoad = true, kBwdNtStore = true;
