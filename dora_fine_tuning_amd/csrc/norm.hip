@@ -291,28 +291,41 @@ __device__ inline void cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0
 // its end get an out-of-range buffer offset, which the hardware turns into
 // zeros in LDS.  NS stages rotate through LDS; a stage is waited for with
 // s_waitcnt vmcnt once the loads of the NS-2 younger stages are in flight.
-template <int TN_, int TM_, int NS_, int WM_>
+template <int TN_, int TM_, int NS_, int WM_, int BK_>
 struct DmaTile {
-  static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_;
+  static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_, BK = BK_;
   static constexpr int WN = 4, NW = WM * WN, NT = NW * 64;
   static constexpr int TMW = TM / WM;  // 32-row W0 tiles per wave
-  static constexpr int BM = 32 * TM, BN = 128 * TN, BK = 32;
-  static constexpr int X_BYTES = BM * BK * 2, Y_BYTES = BN * BK * 2;
+  static constexpr int BM = 32 * TM, BN = 128 * TN;
+  static constexpr int KS = BK / 16;    // MFMA K steps per stage
+  static constexpr int CPR = BK / 8;    // 16-byte chunks per LDS row
+  static constexpr int ROWB = BK * 2;   // bytes per LDS row
+  static constexpr int RPI = 64 / CPR;  // rows per 1 KiB DMA instruction
+  static constexpr int SWP = 16 / CPR;  // consecutive rows sharing one chunk swizzle
+  static constexpr int X_BYTES = BM * ROWB, Y_BYTES = BN * ROWB;
   static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
-  static constexpr int XL = BM / 16 / NW, YL = BN / 16 / NW;  // wave load instructions per stage
-  static constexpr int L = XL + YL;
-  static constexpr int NP = (2 * TMW + WN - 1) / WN;  // (tile, K half) pairs each wave squares for the base term
+  static constexpr int XI = BM / RPI, YI = BN / RPI;   // DMA instructions per stage and panel
+  static constexpr int XQ = XI / NW, YQ = YI / NW;     // per wave
+  static constexpr int L = XQ + YQ;
+  static constexpr int NPAIR = TMW * KS;               // (tile, K step) fragment pairs per stage
+  static constexpr int NP = (NPAIR + WN - 1) / WN;     // pairs each rank-axis wave squares
+  // read the second K step's fragments only after the first step's MFMAs
+  // (same registers) when accumulators and both steps' fragments would not
+  // fit beside each other
+  static constexpr bool SEQ_READS = TMW * TN * 16 + (TMW + TN) * KS * 4 > 200;
   // epilogue: B tile passes of RPP rows in the stage area, row sums after them
   static constexpr int AREA = NS * STAGE_BYTES;
-  static constexpr int RED_BYTES = 2 * WN * BM * 4;  // cross and base row sums per rank-axis wave
+  static constexpr int LDS_BYTES = AREA;
+  static constexpr int RED_BYTES = 2 * WN * BM * 4;    // cross and base row sums per rank-axis wave
   static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
   static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
   static constexpr int RED_OFF = AREA - RED_BYTES;
+  static_assert(BK == 16 || BK == 32, "K stage");
   static_assert(TM % WM == 0, "row tiles split over the waves");
-  static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "panels split evenly over the waves");
-  static_assert(AREA <= 160 * 1024, "LDS");
+  static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(RPP >= 32 && RPP * BN * 2 <= RED_OFF, "epilogue B-tile pass fits beside the row sums");
-  static_assert(NS >= 3 && (NS - 2) * L < 64, "ring depth and vmcnt range");
+  static_assert(NS >= 3 && NS <= 8 && (NS - 2) * L < 64, "ring depth and vmcnt range");
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -458,14 +471,14 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     if (h == 0) red[wn][wm * TL::TMW * 32 + i * 32 + frow] = v;
   }
   if (want_base) {
-    // wave wn holds the squares of pairs p = wn + WN*t (tile p/2); at most one
+    // wave wn holds the squares of pairs p = wn + WN*t (tile p/KS); at most one
     // t of a wave falls on a given tile
 #pragma unroll
     for (int i = 0; i < TL::TMW; ++i) {
       float b = 0.0f;
 #pragma unroll
       for (int t = 0; t < TL::NP; ++t)
-        if ((wn + TL::WN * t) >> 1 == i) b = bs[t];
+        if ((wn + TL::WN * t) / TL::KS == i) b = bs[t];
       b += __shfl_xor(b, 32, 64);
       if (h == 0) red[TL::WN + wn][wm * TL::TMW * 32 + i * 32 + frow] = b;
     }
@@ -619,47 +632,45 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
   _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) \
       acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, Y[j]), __builtin_bit_cast(V8, X[i]), acc[i][j]);
 
-// Base-term squares of one K step.  The 2*TMW (row tile, K half) fragment pairs
+// Base-term squares of K step C.  The TMW*KS (row tile, K step) fragment pairs
 // of a stage are dealt to the WN waves that share them: wave wn squares pair
-// p = wn + WN*t into bs[t] (pair p is tile p/2, step p%2).  wn is wave-uniform,
-// so the selection is a scalar branch.
+// p = wn + WN*t into bs[t] (pair p is tile p/KS, step p%KS).  wn is
+// wave-uniform, so the selection is a scalar branch.
 #define DORA_STEP_SQUARES(X, C)                                            \
   _Pragma("unroll") for (int t = 0; t < TL::NP; ++t)                       \
     _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i)                    \
-      if (wn + TL::WN * t == 2 * i + (C)) {                                \
+      if (wn + TL::WN * t == TL::KS * i + (C)) {                           \
         bs[t] = sq2<DT>(X[i][0], bs[t]);                                   \
         bs[t] = sq2<DT>(X[i][1], bs[t]);                                   \
         bs[t] = sq2<DT>(X[i][2], bs[t]);                                   \
         bs[t] = sq2<DT>(X[i][3], bs[t]);                                   \
       }
 
-// N fragment reads from one base register at compile-time offsets SI + 2048*i.
-#define DORA_READS(V, BASE, SI, N)                                              \
+// N fragment reads from one base register at compile-time offsets SI + STEP*i.
+#define DORA_READS(V, BASE, SI, STEP, N)                                        \
   V[0] = lds_read16_at<(SI)>(BASE);                                             \
-  if constexpr ((N) > 1) V[1] = lds_read16_at<(SI) + 2048>(BASE);               \
-  if constexpr ((N) > 2) V[2] = lds_read16_at<(SI) + 4096>(BASE);               \
-  if constexpr ((N) > 3) V[3] = lds_read16_at<(SI) + 6144>(BASE);
+  if constexpr ((N) > 1) V[1] = lds_read16_at<(SI) + (STEP)>(BASE);             \
+  if constexpr ((N) > 2) V[2] = lds_read16_at<(SI) + 2 * (STEP)>(BASE);         \
+  if constexpr ((N) > 3) V[3] = lds_read16_at<(SI) + 3 * (STEP)>(BASE);
 
-// DMA of one stage of one segment: KST is the stage index within the segment,
-// KLEN its K length.  Whole stages add the stage's byte offset to the per-lane
-// row offsets; the last stage of a segment whose K length is not a multiple of
-// 32 sends the lanes past KLEN out of range (zeros).
-#define DORA_ISSUE_SEG(RX, RY, OX, OY, KST, KLEN, SO)                                                     \
-  {                                                                                                       \
-    const uint32_t kb_ = static_cast<uint32_t>(KST) * 64u;                                                \
-    const int krem_ = (KLEN) - (KST) * 32;                                                                \
-    if (krem_ >= 32) {                                                                                    \
-      _Pragma("unroll") for (int q = 0; q < TL::XL; ++q)                                                  \
-          dma16(RX, smem + (SO) + (wave * TL::XL + q) * 1024, OX[q] + kb_);                               \
-      _Pragma("unroll") for (int q = 0; q < TL::YL; ++q)                                                  \
-          dma16(RY, smem + (SO) + TL::X_BYTES + (wave * TL::YL + q) * 1024, OY[q] + kb_);                 \
-    } else {                                                                                              \
-      const bool ok_ = kc8 < krem_;                                                                       \
-      _Pragma("unroll") for (int q = 0; q < TL::XL; ++q)                                                  \
-          dma16(RX, smem + (SO) + (wave * TL::XL + q) * 1024, ok_ ? OX[q] + kb_ : kOob);                  \
-      _Pragma("unroll") for (int q = 0; q < TL::YL; ++q)                                                  \
-          dma16(RY, smem + (SO) + TL::X_BYTES + (wave * TL::YL + q) * 1024, ok_ ? OY[q] + kb_ : kOob);    \
-    }                                                                                                     \
+// DMA of one stage of one segment into ring slot offset SO: KST is the stage
+// index within the segment, KLEN the segment's K length.  Whole stages add the
+// stage's byte offset to the per-lane row offsets; the last stage of a segment
+// whose K length is not a multiple of BK sends the lanes past KLEN out of range
+// (zeros).
+#define DORA_ISSUE_SEG(RX, RY, LD, LX, LY, KST, KLEN, SO)                                             \
+  {                                                                                                   \
+    const uint32_t kb_ = static_cast<uint32_t>(KST) * static_cast<uint32_t>(TL::ROWB);                \
+    const int krem_ = (KLEN) - (KST) * TL::BK;                                                        \
+    const bool tail_ = krem_ < TL::BK && kc >= krem_;                                                 \
+    _Pragma("unroll") for (int q = 0; q < TL::XQ; ++q) {                                              \
+      const uint32_t o_ = (LX) + static_cast<uint32_t>(q * TL::NW * TL::RPI) * (LD) + kb_;            \
+      dma16(RX, smem + (SO) + (q * TL::NW + wave) * 1024, tail_ ? kOob : o_);                         \
+    }                                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < TL::YQ; ++q) {                                              \
+      const uint32_t o_ = (LY) + static_cast<uint32_t>(q * TL::NW * TL::RPI) * (LD) + kb_;            \
+      dma16(RY, smem + (SO) + TL::X_BYTES + (q * TL::NW + wave) * 1024, tail_ ? kOob : o_);           \
+    }                                                                                                 \
   }
 
 // DMA of stage ST (of the whole augmented K axis) into ring slot SLOT.
@@ -668,11 +679,11 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
     const int st_ = (ST);                                                         \
     constexpr int so_ = (SLOT) * TL::STAGE_BYTES;                                 \
     if (st_ < S1)                                                                 \
-      DORA_ISSUE_SEG(rxW, ryA, oxW, oyA, st_, in, so_)                            \
+      DORA_ISSUE_SEG(rxW, ryA, ldA, lxA, lyA, st_, in, so_)                       \
     else if (st_ < S12)                                                           \
-      DORA_ISSUE_SEG(rxB, ryH, oxB, oyG, st_ - S1, r, so_)                        \
+      DORA_ISSUE_SEG(rxB, ryH, ldB, lxB, lyB, st_ - S1, r, so_)                   \
     else                                                                          \
-      DORA_ISSUE_SEG(rxB, ryL, oxB, oyG, st_ - S12, r, so_)                       \
+      DORA_ISSUE_SEG(rxB, ryL, ldB, lxB, lyB, st_ - S12, r, so_)                  \
   }
 
 #define DORA_PROLOGUE(U)                                                      \
@@ -680,59 +691,80 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
     if (st0 + (U) < st1) DORA_ISSUE(st0 + (U), (U))                           \
   }
 
-// Fragment reads of one stage from ring slot SLOT into register set B.
-#define DORA_READ_STAGE(SLOT, B)                                                   \
-  {                                                                               \
-    constexpr int so_ = (SLOT) * TL::STAGE_BYTES;                                 \
-    constexpr int sw_ = so_ & ~32767, si_ = so_ & 32767;                          \
-    const uint32_t xa0 = xb0 + sw_, xa1 = xb1 + sw_, ya0 = yb0 + sw_, ya1 = yb1 + sw_; \
-    DORA_READS(fx0[B], xa0, si_, TL::TMW)                                         \
-    DORA_READS(fy0[B], ya0, si_, TL::TN)                                          \
-    DORA_READS(fx1[B], xa1, si_, TL::TMW)                                         \
-    DORA_READS(fy1[B], ya1, si_, TL::TN)                                          \
-  }
-
-// Stage st = sb + U, software-pipelined: its fragments were read into
-// register set U % 2 during the previous stage.  Wait for those reads, then
-// (unless st is the last stage) wait for this wave's DMA of stage st + 1 and
-// meet the other waves: after the barrier every wave's stage st + 1 has landed
-// and nobody reads the slot of stage st - 1 any more, so that slot takes the
-// DMA of stage st + NS - 1 and the reads of stage st + 1 go out before this
-// stage's MFMAs, hiding their latency behind them.
+// One stage in ring slot U: wait for its DMA (this wave's loads; the barrier
+// makes every wave's loads visible and frees the slot read last), hand that
+// slot to the DMA of stage st + NS - 1, then KS K steps of 16 from LDS.
 #define DORA_STAGE(U)                                                                               \
-  if constexpr ((U) < 2 * TL::NS) {                                                                 \
-    constexpr int cb = (U) % 2, nb = 1 - (U) % 2;                                                   \
+  if constexpr ((U) < TL::NS) {                                                                     \
     const int st = sb + (U);                                                                        \
     if (st >= st1) break;                                                                           \
-    lds_wait();                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) { tie(fx0[cb][i]); tie(fx1[cb][i]); }      \
-    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) { tie(fy0[cb][j]); tie(fy1[cb][j]); }       \
-    if (st + 1 < st1) {                                                                             \
-      if (st + TL::NS - 2 < st1)                                                                    \
-        wait_vmcnt<(TL::NS - 3) * TL::L>();                                                         \
-      else                                                                                          \
-        wait_vmcnt<0>();                                                                            \
-      __builtin_amdgcn_s_barrier();                                                                 \
-      if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS)           \
-      DORA_READ_STAGE(((U) + 1) % TL::NS, nb)                                                       \
-    }                                                                                               \
+    if (st + TL::NS - 2 < st1)                                                                      \
+      wait_vmcnt<(TL::NS - 2) * TL::L>();                                                           \
+    else                                                                                            \
+      wait_vmcnt<0>();                                                                              \
+    __builtin_amdgcn_s_barrier();                                                                   \
+    if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS)             \
+    constexpr int so = (U) * TL::STAGE_BYTES;                                                       \
+    constexpr int sw = so & ~32767, si = so & 32767;                                                \
+    constexpr int tstep = 32 * TL::ROWB;                                                            \
     const bool base_here = want_base && st < S1;                                                    \
-    DORA_STEP_MFMAS(fx0[cb], fy0[cb])                                                               \
-    if (base_here) {                                                                                \
-      DORA_STEP_SQUARES(fx0[cb], 0)                                                                 \
-    }                                                                                               \
-    DORA_STEP_MFMAS(fx1[cb], fy1[cb])                                                               \
-    if (base_here) {                                                                                \
-      DORA_STEP_SQUARES(fx1[cb], 1)                                                                 \
+    u32x4 x0[TL::TMW], y0[TL::TN];                                                                  \
+    const uint32_t xa0 = xb0 + sw, ya0 = yb0 + sw;                                                  \
+    DORA_READS(x0, xa0, si, tstep, TL::TMW)                                                         \
+    DORA_READS(y0, ya0, si, tstep, TL::TN)                                                          \
+    if constexpr (TL::KS == 2 && TL::SEQ_READS) {                                                   \
+      lds_wait();                                                                                   \
+      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
+      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
+      DORA_STEP_MFMAS(x0, y0)                                                                       \
+      if (base_here) {                                                                              \
+        DORA_STEP_SQUARES(x0, 0)                                                                    \
+      }                                                                                             \
+      const uint32_t xa1 = xb1 + sw, ya1 = yb1 + sw;                                                \
+      DORA_READS(x0, xa1, si, tstep, TL::TMW)                                                       \
+      DORA_READS(y0, ya1, si, tstep, TL::TN)                                                        \
+      lds_wait();                                                                                   \
+      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
+      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
+      DORA_STEP_MFMAS(x0, y0)                                                                       \
+      if (base_here) {                                                                              \
+        DORA_STEP_SQUARES(x0, 1)                                                                    \
+      }                                                                                             \
+    } else if constexpr (TL::KS == 2) {                                                             \
+      u32x4 x1[TL::TMW], y1[TL::TN];                                                                \
+      const uint32_t xa1 = xb1 + sw, ya1 = yb1 + sw;                                                \
+      DORA_READS(x1, xa1, si, tstep, TL::TMW)                                                       \
+      DORA_READS(y1, ya1, si, tstep, TL::TN)                                                        \
+      lds_wait_keep<TL::TMW + TL::TN>();                                                            \
+      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
+      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
+      DORA_STEP_MFMAS(x0, y0)                                                                       \
+      if (base_here) {                                                                              \
+        DORA_STEP_SQUARES(x0, 0)                                                                    \
+      }                                                                                             \
+      lds_wait();                                                                                   \
+      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);                               \
+      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y1[j]);                                \
+      DORA_STEP_MFMAS(x1, y1)                                                                       \
+      if (base_here) {                                                                              \
+        DORA_STEP_SQUARES(x1, 1)                                                                    \
+      }                                                                                             \
+    } else {                                                                                        \
+      lds_wait();                                                                                   \
+      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
+      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
+      DORA_STEP_MFMAS(x0, y0)                                                                       \
+      if (base_here) {                                                                              \
+        DORA_STEP_SQUARES(x0, 0)                                                                    \
+      }                                                                                             \
     }                                                                                               \
   }
 
-template <int DT, int TN, int TM, int NS, int WM>
-__global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(WArgs a) {
-  using TL = DmaTile<TN, TM, NS, WM>;
+template <int DT, int TN, int TM, int NS, int WM, int BK>
+__global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_dma(WArgs a) {
+  using TL = DmaTile<TN, TM, NS, WM, BK>;
   using V8 = typename Dt<DT>::V8;
-  static_assert(TL::NS <= 6, "ring slots expanded below");
-  __shared__ __attribute__((aligned(1024))) char smem[TL::AREA];
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
   // the epilogue's row sums (cross, then base) live past the B-tile passes, in the dead stage area
   float(*red)[TL::BM] = reinterpret_cast<float(*)[TL::BM]>(smem + TL::RED_OFF);
 
@@ -743,7 +775,7 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(
   const uint32_t rb = (v / nTiles) % nRB;
   const int sp = static_cast<int>(v / (nTiles * nRB));
   const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
-  // stage bookkeeping in 32 bits: the augmented K axis has at most 2^16 + 2^16 stages here
+  // stage bookkeeping in 32 bits (the augmented K axis has well under 2^31 stages)
   const int S1 = static_cast<int>(a.sm.S1), S12 = S1 + static_cast<int>(a.sm.S2);
   const int st0 = static_cast<int>(a.S * sp / a.nSplit), st1 = static_cast<int>(a.S * (sp + 1) / a.nSplit);
   const int in = static_cast<int>(a.sm.in), r = static_cast<int>(a.sm.r);
@@ -770,39 +802,41 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(
   const __amdgpu_buffer_rsrc_t ryH = rsrc(a.sm.Ghi, n0, r, r, TL::BN);
   const __amdgpu_buffer_rsrc_t ryL = rsrc(a.sm.Glo, n0, r, r, TL::BN);
 
-  // Per-lane DMA geometry: one wave instruction moves 16 rows x 64 bytes; lane
-  // l takes row l/4 of its group and the logical 16-byte chunk (l%4) ^ ((row/4)%4),
-  // which lands in LDS slot l%4 (the XOR swizzle of the fragment reads).  The
-  // rank-side panel is fetched in the row order sigma (see the fragment reads).
-  const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
-  const int kc8 = lchunk * 8;  // first K element of the lane's chunk within a stage
-  uint32_t oxW[TL::XL], oxB[TL::XL], oyA[TL::YL], oyG[TL::YL];
-#pragma unroll
-  for (int q = 0; q < TL::XL; ++q) {
-    const uint32_t row = static_cast<uint32_t>((wave * TL::XL + q) * 16 + lrow);
-    oxW[q] = row * static_cast<uint32_t>(in) * 2u + kc8 * 2u;
-    oxB[q] = row * static_cast<uint32_t>(r) * 2u + kc8 * 2u;
-  }
-#pragma unroll
-  for (int q = 0; q < TL::YL; ++q) {
-    const int p = (wave * TL::YL + q) * 16 + lrow, prow = p & 31;
-    const uint32_t row = static_cast<uint32_t>((p & ~31) + 16 * ((prow >> 2) & 1) + 4 * (prow >> 3) + (prow & 3));
-    oyA[q] = row * static_cast<uint32_t>(in) * 2u + kc8 * 2u;
-    oyG[q] = row * static_cast<uint32_t>(r) * 2u + kc8 * 2u;
-  }
+  // Per-lane DMA geometry.  One wave instruction moves RPI rows x ROWB bytes;
+  // lane l takes row l/CPR of its group and the logical 16-byte chunk
+  // (l%CPR) ^ ((row/SWP)%CPR), which lands in LDS slot l%CPR (the XOR swizzle
+  // of the fragment reads; a group starts on a multiple of 4*SWP rows, so the
+  // chunk depends on l only).  Wave instruction q < XQ moves X-panel group
+  // NW*q + wave, the others Y-panel group NW*(q - XQ) + wave.  The Y panel is
+  // fetched in the row order sigma of the fragment reads, which maps rows
+  // 16..31 of a 32-row tile to sigma(row - 16) + 8.  A lane's byte offset is
+  // then a per-lane value plus (q's first row) x row pitch + the stage's K
+  // offset, where q's first row is a compile-time multiple of NW*RPI.
+  const int lrow = lane / TL::CPR, lslot = lane % TL::CPR;
+  const int lc = lslot ^ ((lrow / TL::SWP) % TL::CPR);
+  const int kc = lc * 8;
+  auto sigma = [](int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); };
+  // row of this lane within the panel for q = 0 (X) and q = XQ (Y)
+  const int xr0 = wave * TL::RPI + lrow;
+  const int yp = wave * TL::RPI + lrow;  // LDS row
+  const int yr0 = (yp & ~31) + sigma(yp & 31);
+  const uint32_t ldA = static_cast<uint32_t>(in) * 2u, ldB = static_cast<uint32_t>(r) * 2u;
+  const uint32_t lxA = static_cast<uint32_t>(xr0) * ldA + kc * 2u, lxB = static_cast<uint32_t>(xr0) * ldB + kc * 2u;
+  const uint32_t lyA = static_cast<uint32_t>(yr0) * ldA + kc * 2u, lyB = static_cast<uint32_t>(yr0) * ldB + kc * 2u;
 
-  // Fragment reads.  LDS row m of a stage's W-side panel holds logical chunk c
-  // at slot c ^ ((m/4)%4); a lane reads row 32*i + (l%32) of its wave's tiles,
+  // Fragment reads.  LDS row m of a panel holds logical chunk c at slot
+  // c ^ ((m/SWP)%CPR); a lane reads row 32*i + (l%32) of its wave's tiles,
   // K chunk 2*step + l/32, so the swizzle depends on l only and tile i is a
-  // fixed 2048-byte step.  Rank-side row p of each 32-row tile holds rank row
+  // fixed step of 32 rows.  Rank-side row p of each 32-row tile holds rank row
   // sigma(p) = 16*((p/4)%2) + 4*(p/8) + p%4, so accumulator register q of a lane
   // in half h holds rank column 16h + q.
-  const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow >> 2) & 3;
-  const uint32_t xrow = lds0 + static_cast<uint32_t>((wm * TL::TMW * 32 + frow) * 64);
-  const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * 64);
-  const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), xb1 = xrow + (((2 + fhalf) ^ fsw) * 16);
-  const uint32_t yb0 = yrow + ((fhalf ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow / TL::SWP) % TL::CPR;
+  const uint32_t xrow = lds0 + static_cast<uint32_t>((wm * TL::TMW * 32 + frow) * TL::ROWB);
+  const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * TL::ROWB);
+  const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), yb0 = yrow + ((fhalf ^ fsw) * 16);
+  const uint32_t xb1 = xrow + (((2 + fhalf) ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
+  (void)xb1;
+  (void)yb1;
 
   f32x16 acc[TL::TMW][TL::TN];
 #pragma unroll
@@ -813,22 +847,14 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(
 #pragma unroll
   for (int t = 0; t < TL::NP; ++t) bs[t] = 0.0f;
 
-  // fragments of the current and the next stage: [register set][tile]
-  u32x4 fx0[2][TL::TMW], fx1[2][TL::TMW], fy0[2][TL::TN], fy1[2][TL::TN];
   DORA_PROLOGUE(0)
   DORA_PROLOGUE(1)
   DORA_PROLOGUE(2)
   DORA_PROLOGUE(3)
   DORA_PROLOGUE(4)
-  if (st0 < st1) {
-    if (st0 + TL::NS - 2 < st1)
-      wait_vmcnt<(TL::NS - 2) * TL::L>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    DORA_READ_STAGE(0, 0)
-  }
-  for (int sb = st0; sb < st1; sb += 2 * TL::NS) {
+  DORA_PROLOGUE(5)
+  DORA_PROLOGUE(6)
+  for (int sb = st0; sb < st1; sb += TL::NS) {
     DORA_STAGE(0)
     DORA_STAGE(1)
     DORA_STAGE(2)
@@ -837,16 +863,11 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM>::NT), 1) void wstream_dma(
     DORA_STAGE(5)
     DORA_STAGE(6)
     DORA_STAGE(7)
-    DORA_STAGE(8)
-    DORA_STAGE(9)
-    DORA_STAGE(10)
-    DORA_STAGE(11)
   }
 
   dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0);
 }
 #undef DORA_STAGE
-#undef DORA_READ_STAGE
 #undef DORA_PROLOGUE
 #undef DORA_ISSUE
 #undef DORA_ISSUE_SEG
@@ -1018,19 +1039,34 @@ int dma_tn(int64_t r) {
   return best;
 }
 
-// Per rank-tile width: W0 rows per tile (32*TM) and LDS stages.
+// Per rank-tile width: W0 rows per tile (32*TM), LDS ring slots, waves along
+// the rows and K depth of a stage.  K stages of 32 give 64-byte row segments
+// per DMA lane group: global -> LDS DMA from L2 runs at about 40 B/clk per CU
+// with 64-byte segments and at about half that with 32-byte ones.
 template <int TN> struct DmaShape;
-template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6, WM = 2; };
-template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4, WM = 2; };
-template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 5, WM = 2; };
-template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3, WM = 2; };
+template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6, WM = 2, BK = 32; };
+template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4, WM = 2, BK = 32; };
+template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 5, WM = 2, BK = 32; };
+template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3, WM = 2, BK = 32; };
+
+template <int TN>
+using DmaTileOf = DmaTile<TN, DmaShape<TN>::TM, DmaShape<TN>::NS, DmaShape<TN>::WM, DmaShape<TN>::BK>;
 
 int dma_rows(int tn) {
   switch (tn) {
-    case 1: return 32 * DmaShape<1>::TM;
-    case 2: return 32 * DmaShape<2>::TM;
-    case 3: return 32 * DmaShape<3>::TM;
-    default: return 32 * DmaShape<4>::TM;
+    case 1: return DmaTileOf<1>::BM;
+    case 2: return DmaTileOf<2>::BM;
+    case 3: return DmaTileOf<3>::BM;
+    default: return DmaTileOf<4>::BM;
+  }
+}
+
+int dma_bk(int tn) {
+  switch (tn) {
+    case 1: return DmaTileOf<1>::BK;
+    case 2: return DmaTileOf<2>::BK;
+    case 3: return DmaTileOf<3>::BK;
+    default: return DmaTileOf<4>::BK;
   }
 }
 
@@ -1038,8 +1074,7 @@ template <int DT, int TN>
 void launch_dma(const WArgs& w, hipStream_t stream) {
   using S = DmaShape<TN>;
   const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
-  hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM>), grid, dim3(DmaTile<TN, S::TM, S::NS, S::WM>::NT), 0,
-                     stream, w);
+  hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTileOf<TN>::NT), 0, stream, w);
 }
 
 template <int DT>
@@ -1113,7 +1148,7 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
     p.tn = dma_tn(r);
     bm = dma_rows(p.tn);
     bn = 128 * p.tn;
-    bk = 32;
+    bk = dma_bk(p.tn);
     slots = 256;
   } else {
     p.tn = 0;
@@ -1128,14 +1163,15 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
   p.S2 = cdiv(r, bk);
   p.S = p.S1 + 2 * p.S2;
   // K splits: minimise (rounds of resident workgroups) x (stages per workgroup
-  // + a fixed cost of about 8 stages for the pipeline fill and the epilogue),
-  // keeping at least 8 stages per workgroup; ties go to fewer splits.
+  // + a fixed cost of about 8 stages of 32 for the pipeline fill and the
+  // epilogue), keeping at least 8 stages per workgroup; ties go to fewer splits.
   {
+    const int64_t fixed = 8 * 32 / bk;
     const int64_t per = p.nRB * p.nTiles;
     const int64_t maxs = std::max<int64_t>(1, std::min<int64_t>(64, p.S / 8));
     int64_t best = -1, bestc = 0;
     for (int64_t k = 1; k <= maxs; ++k) {
-      const int64_t cost = cdiv(per * k, slots) * (cdiv(std::max<int64_t>(p.S, 1), k) + 8);
+      const int64_t cost = cdiv(per * k, slots) * (cdiv(std::max<int64_t>(p.S, 1), k) + fixed);
       if (best < 0 || cost < bestc) {
         best = k;
         bestc = cost;
