@@ -309,10 +309,6 @@ struct DmaTile {
   static constexpr int L = XQ + YQ;
   static constexpr int NPAIR = TMW * KS;               // (tile, K step) fragment pairs per stage
   static constexpr int NP = (NPAIR + WN - 1) / WN;     // pairs each rank-axis wave squares
-  // read the second K step's fragments only after the first step's MFMAs
-  // (same registers) when accumulators and both steps' fragments would not
-  // fit beside each other
-  static constexpr bool SEQ_READS = TMW * TN * 16 + (TMW + TN) * KS * 4 > 200;
   // epilogue: B tile passes of RPP rows in the stage area, row sums after them
   static constexpr int AREA = NS * STAGE_BYTES;
   static constexpr int LDS_BYTES = AREA;
@@ -320,7 +316,7 @@ struct DmaTile {
   static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
   static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
   static constexpr int RED_OFF = AREA - RED_BYTES;
-  static_assert(BK == 16 || BK == 32, "K stage");
+  static_assert(BK == 32, "K stages of 32: 64-byte DMA row segments, two MFMA K steps");
   static_assert(TM % WM == 0, "row tiles split over the waves");
   static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -693,71 +689,43 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
 
 // One stage in ring slot U: wait for its DMA (this wave's loads; the barrier
 // makes every wave's loads visible and frees the slot read last), hand that
-// slot to the DMA of stage st + NS - 1, then KS K steps of 16 from LDS.
-#define DORA_STAGE(U)                                                                               \
-  if constexpr ((U) < TL::NS) {                                                                     \
-    const int st = sb + (U);                                                                        \
-    if (st >= st1) break;                                                                           \
-    if (st + TL::NS - 2 < st1)                                                                      \
-      wait_vmcnt<(TL::NS - 2) * TL::L>();                                                           \
-    else                                                                                            \
-      wait_vmcnt<0>();                                                                              \
-    __builtin_amdgcn_s_barrier();                                                                   \
-    if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS)             \
-    constexpr int so = (U) * TL::STAGE_BYTES;                                                       \
-    constexpr int sw = so & ~32767, si = so & 32767;                                                \
-    constexpr int tstep = 32 * TL::ROWB;                                                            \
-    const bool base_here = want_base && st < S1;                                                    \
-    u32x4 x0[TL::TMW], y0[TL::TN];                                                                  \
-    const uint32_t xa0 = xb0 + sw, ya0 = yb0 + sw;                                                  \
-    DORA_READS(x0, xa0, si, tstep, TL::TMW)                                                         \
-    DORA_READS(y0, ya0, si, tstep, TL::TN)                                                          \
-    if constexpr (TL::KS == 2 && TL::SEQ_READS) {                                                   \
-      lds_wait();                                                                                   \
-      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
-      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
-      DORA_STEP_MFMAS(x0, y0)                                                                       \
-      if (base_here) {                                                                              \
-        DORA_STEP_SQUARES(x0, 0)                                                                    \
-      }                                                                                             \
-      const uint32_t xa1 = xb1 + sw, ya1 = yb1 + sw;                                                \
-      DORA_READS(x0, xa1, si, tstep, TL::TMW)                                                       \
-      DORA_READS(y0, ya1, si, tstep, TL::TN)                                                        \
-      lds_wait();                                                                                   \
-      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
-      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
-      DORA_STEP_MFMAS(x0, y0)                                                                       \
-      if (base_here) {                                                                              \
-        DORA_STEP_SQUARES(x0, 1)                                                                    \
-      }                                                                                             \
-    } else if constexpr (TL::KS == 2) {                                                             \
-      u32x4 x1[TL::TMW], y1[TL::TN];                                                                \
-      const uint32_t xa1 = xb1 + sw, ya1 = yb1 + sw;                                                \
-      DORA_READS(x1, xa1, si, tstep, TL::TMW)                                                       \
-      DORA_READS(y1, ya1, si, tstep, TL::TN)                                                        \
-      lds_wait_keep<TL::TMW + TL::TN>();                                                            \
-      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
-      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
-      DORA_STEP_MFMAS(x0, y0)                                                                       \
-      if (base_here) {                                                                              \
-        DORA_STEP_SQUARES(x0, 0)                                                                    \
-      }                                                                                             \
-      lds_wait();                                                                                   \
-      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);                               \
-      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y1[j]);                                \
-      DORA_STEP_MFMAS(x1, y1)                                                                       \
-      if (base_here) {                                                                              \
-        DORA_STEP_SQUARES(x1, 1)                                                                    \
-      }                                                                                             \
-    } else {                                                                                        \
-      lds_wait();                                                                                   \
-      _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                               \
-      _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                                \
-      DORA_STEP_MFMAS(x0, y0)                                                                       \
-      if (base_here) {                                                                              \
-        DORA_STEP_SQUARES(x0, 0)                                                                    \
-      }                                                                                             \
-    }                                                                                               \
+// slot to the DMA of stage st + NS - 1, then two K steps of 16 from LDS (the
+// second step's fragments are read with the first's, and waited for after the
+// first step's MFMAs).
+#define DORA_STAGE(U)                                                                   \
+  if constexpr ((U) < TL::NS) {                                                         \
+    const int st = sb + (U);                                                            \
+    if (st >= st1) break;                                                               \
+    if (st + TL::NS - 2 < st1)                                                          \
+      wait_vmcnt<(TL::NS - 2) * TL::L>();                                               \
+    else                                                                                \
+      wait_vmcnt<0>();                                                                  \
+    __builtin_amdgcn_s_barrier();                                                       \
+    if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS) \
+    constexpr int so = (U) * TL::STAGE_BYTES;                                           \
+    constexpr int sw = so & ~32767, si = so & 32767;                                    \
+    constexpr int tstep = 32 * TL::ROWB;                                                \
+    const bool base_here = want_base && st < S1;                                        \
+    u32x4 x0[TL::TMW], y0[TL::TN], x1[TL::TMW], y1[TL::TN];                             \
+    const uint32_t xa0 = xb0 + sw, ya0 = yb0 + sw, xa1 = xb1 + sw, ya1 = yb1 + sw;      \
+    DORA_READS(x0, xa0, si, tstep, TL::TMW)                                             \
+    DORA_READS(y0, ya0, si, tstep, TL::TN)                                              \
+    DORA_READS(x1, xa1, si, tstep, TL::TMW)                                             \
+    DORA_READS(y1, ya1, si, tstep, TL::TN)                                              \
+    lds_wait_keep<TL::TMW + TL::TN>();                                                  \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                     \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                      \
+    DORA_STEP_MFMAS(x0, y0)                                                             \
+    if (base_here) {                                                                    \
+      DORA_STEP_SQUARES(x0, 0)                                                          \
+    }                                                                                   \
+    lds_wait();                                                                         \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);                     \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y1[j]);                      \
+    DORA_STEP_MFMAS(x1, y1)                                                             \
+    if (base_here) {                                                                    \
+      DORA_STEP_SQUARES(x1, 1)                                                          \
+    }                                                                                   \
   }
 
 template <int DT, int TN, int TM, int NS, int WM, int BK>
@@ -835,8 +803,6 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
   const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * TL::ROWB);
   const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), yb0 = yrow + ((fhalf ^ fsw) * 16);
   const uint32_t xb1 = xrow + (((2 + fhalf) ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
-  (void)xb1;
-  (void)yb1;
 
   f32x16 acc[TL::TMW][TL::TN];
 #pragma unroll
