@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--cold-reps", type=int, default=10, help="compose calls timed after a cache-evicting read")
+    ap.add_argument("--torch-reps", type=int, default=10,
+                    help="compose forward+backward timed through the PyTorch custom operator and autograd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for byte counters)")
     args = ap.parse_args()
@@ -198,6 +200,26 @@ def main():
     del flush
     cold_us = {k: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3 if v else None for k, v in cold.items()}
 
+    # The same compose forward + backward driven through the PyTorch custom
+    # operator and autograd (dora_amd::compose), against the direct calls above.
+    torch_us = None
+    if args.torch_reps > 0:
+        from dora_fine_tuning_amd import torch_ops
+
+        bg, lg, mg = base.detach().requires_grad_(), lora.detach().requires_grad_(), mag.detach().requires_grad_()
+        evt = []
+        for k in range(3 + args.torch_reps):
+            bg.grad = lg.grad = mg.grad = None
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch_ops.compose(bg, lg, mg, norm, s, False).backward(dy)
+            e1.record()
+            if k >= 3:
+                evt.append((e0, e1))
+        torch.cuda.synchronize()
+        torch_us = float(np.median([a.elapsed_time(b) for a, b in evt])) * 1e3
+        del bg, lg, mg
+
     fwd_b, bwd_b = compose_bytes(T, out)
     comp_ms = fwd_ms.mean() + bwd_ms.mean()
     value = (fwd_b + bwd_b) / (comp_ms * 1e-3) / 1e9
@@ -229,6 +251,9 @@ def main():
         "compose_cold": ({"fwd_us": round(cold_us["fwd"], 2), "bwd_us": round(cold_us["bwd"], 2),
                           "gbs": round((fwd_b + bwd_b) / ((cold_us["fwd"] + cold_us["bwd"]) * 1e-6) / 1e9, 1),
                           "reps": args.cold_reps} if args.cold_reps > 0 else None),
+        "torch_compose": ({"fwd_bwd_us": round(torch_us, 2),
+                           "direct_fwd_bwd_us": round(float(fwd_ms.mean() + bwd_ms.mean()) * 1e3, 2),
+                           "reps": args.torch_reps} if torch_us is not None else None),
         "roofline": {
             "kernel": "dora_compose_bwd (compose_bwd_vec + dmag_finalize)",
             "bound": "hbm",

@@ -1,0 +1,157 @@
+"""PyTorch integration of the DoRA hot path: custom operators and a DoRA linear layer.
+
+The press summary of arXiv:2603.22276 describes the fused kernels as a PyTorch
+custom operator, which compiled graphs keep without breaks (paragraph on
+framework compatibility). It also describes a three-tier dispatch (paragraph
+on the dispatch tiers): training runs the fused forward and the fused
+backward, inference runs the forward kernel alone, and whatever the kernels
+cannot take goes to eager PyTorch.
+
+This module registers:
+
+* ``dora_amd::weight_norm`` -- the factored norm ||W0 + s*B*A|| per output row
+  (fp32). It has no autograd formula: the norm is treated as a constant,
+  and callers pass detached A and B.
+* ``dora_amd::compose`` -- the stable compose (g - 1)*base + g*s*lora
+  (+ base), g = m / n. Its autograd formula is the fused backward
+  ``dora_amd::compose_backward``, which gives the gradients of base, lora and
+  the magnitude m.
+* ``DoRALinear`` -- a linear layer with frozen W0 and trainable A, B and m:
+  y = x W0^T + compose(x W0^T, x A^T B^T, m, n, s), with n = ||W0 + s*B*A||
+  detached.
+
+Tiers: autograd records the compose only when a gradient is needed, so
+under ``torch.no_grad()`` or ``torch.inference_mode()`` the forward kernel
+runs alone and saves nothing. There is no eager fallback. Inputs the kernels
+cannot take raise: CPU tensors, dtypes other than bf16/fp16, and a missing
+library.
+
+Every operator is argument marshalling around the C ABI (``binding``); the
+arithmetic runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from . import binding
+
+Tensor = torch.Tensor
+
+
+# --------------------------------------------------------------------------- norm
+
+
+@torch.library.custom_op("dora_amd::weight_norm", mutates_args=(), device_types="cuda")
+def weight_norm(W0: Tensor, A: Tensor, B: Tensor, s: float) -> Tensor:
+    """||W0_i + s * B_i A||_2 per output row i, fp32, via the factored kernels."""
+    return binding.dora_norm_factored(W0.contiguous(), A.contiguous(), B.contiguous(), s)
+
+
+@weight_norm.register_fake
+def _weight_norm_fake(W0, A, B, s):
+    return W0.new_empty((W0.shape[0],), dtype=torch.float32)
+
+
+# ------------------------------------------------------------------------ compose
+
+
+@torch.library.custom_op("dora_amd::compose", mutates_args=(), device_types="cuda")
+def compose(base: Tensor, lora: Tensor, mag: Tensor, norm: Tensor, s: float, add_base: bool) -> Tensor:
+    """(g - 1) * base + g * s * lora, plus base when add_base, with g = mag / norm per column."""
+    return binding.dora_compose_fwd(base.contiguous(), lora.contiguous(), mag.contiguous(), norm.contiguous(), s,
+                                    add_base=add_base)
+
+
+@compose.register_fake
+def _compose_fake(base, lora, mag, norm, s, add_base):
+    return torch.empty_like(base)
+
+
+@torch.library.custom_op("dora_amd::compose_backward", mutates_args=(), device_types="cuda")
+def compose_backward(dy: Tensor, base: Tensor, lora: Tensor, mag: Tensor, norm: Tensor, s: float, add_base: bool,
+                     want_base: bool) -> tuple[Tensor, Tensor, Tensor]:
+    """(d_lora, d_base, d_mag) of the compose.  With want_base false the kernel
+    does not write d_base and an empty tensor stands in for it."""
+    d_lora, d_base, d_mag = binding.dora_compose_bwd(dy.contiguous(), base, lora, mag, norm, s, add_base=add_base,
+                                                     want_d_base=want_base)
+    if d_base is None:
+        d_base = dy.new_empty((0,))
+    return d_lora, d_base, d_mag
+
+
+@compose_backward.register_fake
+def _compose_backward_fake(dy, base, lora, mag, norm, s, add_base, want_base):
+    d_base = torch.empty_like(dy) if want_base else dy.new_empty((0,))
+    return torch.empty_like(dy), d_base, mag.new_empty(mag.shape)
+
+
+def _compose_setup(ctx, inputs, output):
+    base, lora, mag, norm, s, add_base = inputs
+    ctx.save_for_backward(base, lora, mag, norm)
+    ctx.s = s
+    ctx.add_base = add_base
+
+
+def _compose_grad(ctx, dy):
+    base, lora, mag, norm = ctx.saved_tensors
+    want_base = bool(ctx.needs_input_grad[0])
+    d_lora, d_base, d_mag = compose_backward(dy, base, lora, mag, norm, ctx.s, ctx.add_base, want_base)
+    return (d_base if want_base else None,
+            d_lora if ctx.needs_input_grad[1] else None,
+            d_mag if ctx.needs_input_grad[2] else None,
+            None, None, None)
+
+
+compose.register_autograd(_compose_grad, setup_context=_compose_setup)
+
+
+# -------------------------------------------------------------------------- layer
+
+
+class DoRALinear(torch.nn.Module):
+    """DoRA-adapted linear layer: frozen W0 [out x in], trainable A [r x in],
+    B [out x r] and magnitude m [out] (fp32); scale s = alpha / sqrt(r) (rsLoRA).
+
+    Initialisation follows LoRA/DoRA practice: B = 0 and m = ||W0|| per row,
+    so the layer starts out equal to x W0^T.  A is drawn from N(0, 1/in).  On a
+    HIP device m is taken from the factored norm itself, so g = m / n is exactly
+    1 at B = 0 and the first output equals x W0^T bit for bit.
+    """
+
+    def __init__(self, in_features: int, out_features: int, r: int, alpha: float = 32.0,
+                 weight: Tensor | None = None, dtype: torch.dtype = torch.bfloat16, device=None):
+        super().__init__()
+        if dtype not in binding.DTYPE_CODE:
+            raise ValueError(f"unsupported dtype {dtype}; bf16 and fp16 are")
+        self.in_features, self.out_features, self.r = in_features, out_features, r
+        self.s = float(np.float32(alpha / math.sqrt(r)))
+        if weight is None:
+            weight = torch.randn(out_features, in_features, device=device) / math.sqrt(in_features)
+        self.register_buffer("weight", weight.to(device=device, dtype=dtype).contiguous())
+        self.lora_A = torch.nn.Parameter(
+            (torch.randn(r, in_features, device=device) / math.sqrt(in_features)).to(dtype))
+        self.lora_B = torch.nn.Parameter(torch.zeros(out_features, r, device=device, dtype=dtype))
+        self.magnitude = torch.nn.Parameter(self.weight.float().norm(dim=1))
+        if self.weight.is_cuda:
+            self.reset_magnitude()
+
+    @torch.no_grad()
+    def reset_magnitude(self) -> None:
+        """m = ||W0 + s*B*A|| per row (the DoRA initialisation of the magnitude)."""
+        self.magnitude.copy_(self.weight_norm())
+
+    def weight_norm(self) -> Tensor:
+        """n = ||W0 + s*B*A|| per output row, detached."""
+        return weight_norm(self.weight, self.lora_A.detach(), self.lora_B.detach(), self.s)
+
+    def forward(self, x: Tensor) -> Tensor:
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.in_features)
+        base = F.linear(x2, self.weight)
+        lora = F.linear(F.linear(x2, self.lora_A), self.lora_B)
+        y = compose(base, lora, self.magnitude, self.weight_norm(), self.s, True)
+        return y.reshape(*lead, self.out_features)

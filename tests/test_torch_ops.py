@@ -1,0 +1,149 @@
+"""PyTorch integration: custom operators, autograd through the fused compose,
+and the DoRA linear layer.  Gradients are checked against the fp64 oracle
+(compose) and against a float64 CPU evaluation of the dense DoRA formula with
+the norm detached (layer)."""
+import numpy as np
+import pytest
+import torch
+
+from dora_fine_tuning_amd import synth
+from oracle import dora_oracle as O
+from parity_util import assert_compose, assert_dmag
+
+torch_ops = pytest.importorskip("dora_fine_tuning_amd.torch_ops")
+
+gpu = pytest.mark.gpu
+
+
+def test_ops_reject_host_tensors():
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    v = torch.ones(8, dtype=torch.float32)
+    with pytest.raises((NotImplementedError, RuntimeError, ValueError)):
+        torch_ops.compose(x, x, v, v, 1.0, False)
+    with pytest.raises((NotImplementedError, RuntimeError, ValueError)):
+        torch_ops.weight_norm(torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(2, 8, dtype=torch.bfloat16),
+                              torch.zeros(8, 2, dtype=torch.bfloat16), 1.0)
+
+
+def test_layer_rejects_other_dtypes():
+    with pytest.raises(ValueError):
+        torch_ops.DoRALinear(8, 8, 2, dtype=torch.float32)
+
+
+def _compose_inputs(T, out, dtype, seed):
+    cfg = synth.custom("torch_ops", out, 64, 8, T, index=seed)
+    g = np.random.default_rng(seed)
+    base = torch.from_numpy(g.standard_normal((T, out)).astype(np.float32)).to(dtype)
+    lora = torch.from_numpy(g.standard_normal((T, out)).astype(np.float32) * 0.5).to(dtype)
+    dy = torch.from_numpy(g.standard_normal((T, out)).astype(np.float32)).to(dtype)
+    n = np.abs(g.standard_normal(out)).astype(np.float32) + 0.5
+    m = synth.magnitude(n, g.uniform(-2**-8, 2**-8, out))
+    return base, lora, dy, torch.from_numpy(m), torch.from_numpy(n), cfg.s
+
+
+@gpu
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("add_base", [False, True])
+def test_compose_autograd_matches_oracle(dtype, add_base):
+    dev = torch.device("cuda:0")
+    base, lora, dy, m, n, s = _compose_inputs(300, 264, dtype, 7)
+    bg, lg, mg = (t.to(dev).requires_grad_() for t in (base, lora, m))
+    y = torch_ops.compose(bg, lg, mg, n.to(dev), s, add_base)
+    y.backward(dy.to(dev))
+    kind = "bf16" if dtype == torch.bfloat16 else "fp16"
+    b64, l64, dy64 = (O.as_f64(t.float().numpy()) for t in (base, lora, dy))
+    y_ref = O.compose_fwd(b64, l64, O.as_f64(m.numpy()), O.as_f64(n.numpy()), s, add_base)
+    dl_ref, db_ref, dm_ref = O.compose_bwd(dy64, b64, l64, O.as_f64(m.numpy()), O.as_f64(n.numpy()), s, add_base)
+    g = m.double().numpy() / n.double().numpy()
+    mass_y = np.abs((g - 1) * b64) + np.abs(g * s * l64) + (np.abs(b64) if add_base else 0)
+    assert_compose(y.detach().float().cpu().numpy(), y_ref, mass_y, kind, "y")
+    assert_compose(lg.grad.float().cpu().numpy(), dl_ref, np.abs(dl_ref), kind, "d_lora")
+    assert_compose(bg.grad.float().cpu().numpy(), db_ref, np.abs(db_ref), kind, "d_base")
+    cond = np.sum(np.abs(dy64 * (b64 + s * l64)), axis=0) / n.double().numpy()
+    assert_dmag(mg.grad.cpu().numpy(), dm_ref, cond, "d_mag")
+
+
+@gpu
+def test_compose_grad_base_skipped_when_not_needed():
+    dev = torch.device("cuda:0")
+    base, lora, dy, m, n, s = _compose_inputs(64, 64, torch.bfloat16, 3)
+    lg = lora.to(dev).requires_grad_()
+    y = torch_ops.compose(base.to(dev), lg, m.to(dev), n.to(dev), s, False)
+    y.backward(dy.to(dev))
+    assert lg.grad is not None and lg.grad.shape == lora.shape
+
+
+@gpu
+def test_opcheck():
+    dev = torch.device("cuda:0")
+    base, lora, dy, m, n, s = _compose_inputs(64, 64, torch.bfloat16, 5)
+    args = (base.to(dev).requires_grad_(), lora.to(dev).requires_grad_(), m.to(dev).requires_grad_(), n.to(dev), s,
+            False)
+    torch.library.opcheck(torch_ops.compose, args,
+                          test_utils=("test_schema", "test_autograd_registration", "test_faketensor"))
+    W0, A, B = (t.to(dev) for t in synth.weights(synth.CONFIGS["tiny"]))
+    torch.library.opcheck(torch_ops.weight_norm, (W0, A, B, 1.5), test_utils=("test_schema", "test_faketensor"))
+
+
+def _dense_reference(x, W0, A, B, m, s, dy):
+    """float64 CPU: y = x W0^T + (g-1) x W0^T + g s x A^T B^T with n detached; grads of A, B, m, x."""
+    xd, W0d, Ad, Bd, md = (t.detach().double().cpu().requires_grad_() for t in (x, W0, A, B, m))
+    W0d.requires_grad_(False)
+    n = torch.from_numpy(O.weight_norm(*(t.detach().float().cpu().numpy() for t in (W0, A, B)), s))
+    g = md / n
+    base = xd @ W0d.T
+    lora = (xd @ Ad.T) @ Bd.T
+    y = base + (g - 1) * base + g * s * lora
+    y.backward(dy.double().cpu())
+    return y.detach(), xd.grad, Ad.grad, Bd.grad, md.grad, n
+
+
+def _rel(a, b):
+    a, b = a.detach().double().cpu(), b.detach().double().cpu()
+    return float((a - b).norm() / b.norm().clamp_min(1e-300))
+
+
+@gpu
+def test_dora_linear_forward_backward():
+    dev = torch.device("cuda:0")
+    torch.manual_seed(0)
+    layer = torch_ops.DoRALinear(320, 256, 16, alpha=32.0, device=dev)
+    with torch.no_grad():
+        layer.lora_B.normal_(0.0, 0.02)
+        layer.magnitude.mul_(1.0 + 0.01 * torch.randn_like(layer.magnitude))
+    x = torch.randn(3, 70, 320, device=dev, dtype=torch.bfloat16).requires_grad_()
+    y = layer(x)
+    dy = torch.randn_like(y)
+    y.backward(dy)
+    y_ref, dx_ref, dA_ref, dB_ref, dm_ref, n_ref = _dense_reference(
+        x.reshape(-1, 320), layer.weight, layer.lora_A, layer.lora_B, layer.magnitude, layer.s, dy.reshape(-1, 256))
+    # the layer's norm is the factored kernel's, to fp32 rounding
+    np.testing.assert_allclose(layer.weight_norm().double().cpu().numpy(), n_ref.numpy(), rtol=1e-5)
+    # bf16 GEMM outputs and inputs bound the rest
+    assert _rel(y.reshape(-1, 256), y_ref) < 2e-2
+    assert _rel(x.grad.reshape(-1, 320), dx_ref) < 2e-2
+    assert _rel(layer.lora_A.grad, dA_ref) < 3e-2
+    assert _rel(layer.lora_B.grad, dB_ref) < 3e-2
+    assert _rel(layer.magnitude.grad, dm_ref) < 2e-2
+    assert layer.weight.grad is None
+
+
+@gpu
+def test_dora_linear_starts_as_base_layer_and_inference_tier():
+    dev = torch.device("cuda:0")
+    torch.manual_seed(1)
+    layer = torch_ops.DoRALinear(256, 192, 8, device=dev)
+    x = torch.randn(50, 256, device=dev, dtype=torch.bfloat16)
+    base = torch.nn.functional.linear(x, layer.weight)
+    with torch.no_grad():
+        y0 = layer(x)
+    # B = 0 and m = n exactly: g - 1 = 0 and s*lora = 0, so y is base bit for bit
+    assert torch.equal(y0, base)
+    with torch.no_grad():
+        layer.lora_B.normal_(0.0, 0.05)
+    with torch.inference_mode():
+        y_inf = layer(x)
+    assert y_inf.grad_fn is None
+    y_train = layer(x.requires_grad_())
+    assert y_train.grad_fn is not None
+    assert torch.equal(y_inf, y_train.detach())
