@@ -18,6 +18,8 @@
 // each thread writes the fp32 sum over its ROWS tokens for its columns to a
 // [token-blocks x out] partial buffer, and dmag_finalize adds the partials in
 // a fixed order in fp64 and divides by n.  Results are bitwise reproducible.
+#include <algorithm>
+
 #include "compose_kernels.hpp"
 #include "dora_common.hpp"
 
@@ -331,6 +333,13 @@ hipError_t launch_compose_bwd_t(const ComposeArgs& a, bool vec) {
 
 hipError_t launch_compose_fwd(const ComposeArgs& a, bool vec) {
   return a.dtype == 0 ? launch_compose_fwd_t<0>(a, vec) : launch_compose_fwd_t<1>(a, vec);
+}
+
+int64_t compose_max_grid(int64_t T, int64_t out, bool vec) {
+  const int64_t ncb_fwd = vec ? cdiv(out / 8, kFwdThreads) : cdiv(out, kThreads);
+  const int64_t ncb_bwd = vec ? cdiv(out / 8, kBwdThreads) : cdiv(out, kThreads);
+  const int64_t fwd = ncb_fwd * cdiv(T, kFwdRows), bwd = ncb_bwd * cdiv(T, kBwdRows);
+  return std::max({fwd, bwd, cdiv(out, kFinCols)});
 }
 
 hipError_t launch_compose_bwd(const ComposeArgs& a, bool vec) {

@@ -33,4 +33,8 @@ struct ComposeArgs {
 hipError_t launch_compose_fwd(const ComposeArgs& a, bool vec);
 hipError_t launch_compose_bwd(const ComposeArgs& a, bool vec);
 
+// Largest grid (workgroups in one dimension) the launches of these sizes use;
+// the caller rejects sizes whose grid would exceed the launch limit.
+int64_t compose_max_grid(int64_t T, int64_t out, bool vec);
+
 }  // namespace dora

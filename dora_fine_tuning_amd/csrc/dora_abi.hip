@@ -93,8 +93,8 @@ int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out
   if (any_overlap(ws, need, W0, out * in * e) || any_overlap(ws, need, A, r * in * e) ||
       any_overlap(ws, need, B, out * r * e))
     return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace overlaps an input");
-  // 16-byte path: 16-byte rows and pointers, and 32-bit buffer offsets over a
-  // 128-row panel of W0 and a 512-row panel of G'
+  // 16-byte path: 16-byte rows and pointers, and buffer byte offsets below
+  // 2^31 within a panel of at most 512 rows of in (< 2^21) or r elements
   const bool vec = (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) &&
                    aligned16(ws) && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20);
   const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype, vec);
@@ -128,6 +128,9 @@ int dora_compose_fwd(const void* base, const void* lora, const float* mag, const
   a.stream = stream;
   const bool vec = (out % 8 == 0) && aligned16(base) && aligned16(lora) && aligned16(y) && aligned16(mag) &&
                    aligned16(norm);
+  if (dora::compose_max_grid(T, out, vec) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "dora_compose_fwd: T=%lld x out=%lld needs more workgroups than one launch holds",
+                (long long)T, (long long)out);
   return hip_status(dora::launch_compose_fwd(a, vec), "dora_compose_fwd");
 }
 
@@ -182,6 +185,9 @@ int dora_compose_bwd(const void* dy, const void* base, const void* lora, const f
   a.stream = stream;
   const bool vec = (out % 8 == 0) && aligned16(dy) && aligned16(base) && aligned16(lora) && aligned16(d_lora) &&
                    (d_base == nullptr || aligned16(d_base)) && aligned16(mag) && aligned16(norm) && aligned16(ws);
+  if (dora::compose_max_grid(T, out, vec) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "dora_compose_bwd: T=%lld x out=%lld needs more workgroups than one launch holds",
+                (long long)T, (long long)out);
   return hip_status(dora::launch_compose_bwd(a, vec), "dora_compose_bwd");
 }
 

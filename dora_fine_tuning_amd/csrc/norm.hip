@@ -278,19 +278,21 @@ __device__ inline void cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0
 // ---------------------------------------------------------------------------
 // W stream, 16-byte path: direct global -> LDS loads through buffer resources.
 //
-// Tile 32*TM rows x 128*TN rank columns, K stage 32, four waves side by side
-// along the rank axis, each owning all 32*TM rows (one wave per SIMD, so the
-// TM*TN*16 accumulators fit in the accumulation registers).  Every workgroup
-// reads the whole rank panel of A once per K stage; the taller the tile, the
-// fewer times that panel is re-read from L2 for the same W0 rows.  A stage is one 64-byte row
-// segment per panel row; one wave instruction moves 16 rows x 64 bytes, lane l
-// writing bytes [16l, 16l+16) of that 1 KiB block.  Lane l fetches the logical
+// Workgroup tile: 32*TM W0 rows x 128*TN rank columns, K stages of 32.  The
+// NW = WM*4 waves form a WM x 4 grid (WM along the rows, 4 along the rank
+// axis); a wave owns TMW = TM/WM row tiles x TN rank tiles of 32 and keeps
+// their accumulators in registers.  Every workgroup reads the whole rank panel
+// once per K stage; the taller the tile, the fewer times that panel is re-read
+// from L2 for the same W0 rows.  A stage holds one 64-byte segment of each
+// panel row; one wave instruction moves 16 rows x 64 bytes, lane l writing
+// bytes [16l, 16l + 16) of that 1 KiB block.  Lane l fetches the logical
 // 16-byte chunk (l%4) ^ ((row>>2)&3) of its row, so the LDS slot of logical
-// chunk c in row m is c ^ ((m>>2)&3): the fragment reads of 16 consecutive rows
-// then hit 16 distinct bank groups.  Rows past the operand and K chunks past
-// its end get an out-of-range buffer offset, which the hardware turns into
-// zeros in LDS.  NS stages rotate through LDS; a stage is waited for with
-// s_waitcnt vmcnt once the loads of the NS-2 younger stages are in flight.
+// chunk c in row m is c ^ ((m>>2)&3): the fragment reads of 16 consecutive
+// rows then hit 16 distinct bank groups.  Rows past the operand lie beyond the
+// buffer resource's range and K chunks past its end get an out-of-range
+// offset; the hardware writes zeros to LDS for both.  NS stages rotate through
+// LDS; a stage is waited for with s_waitcnt vmcnt once the loads of the NS-2
+// younger stages are in flight.
 template <int TN_, int TM_, int NS_, int WM_, int BK_>
 struct DmaTile {
   static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_, BK = BK_;

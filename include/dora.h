@@ -36,8 +36,10 @@
  *    DORA_HIP_ERROR, reported by the launch itself).  dora_last_error() gives
  *    the message of the calling thread's last failure.
  *  - Any sizes are accepted.  The fast paths need 16-byte aligned pointers and
- *    a row length that is a multiple of 8 elements; other cases take a slower
- *    general path with identical results.
+ *    row lengths that are multiples of 8 elements (for the norm also
+ *    in < 2^21); other cases take a slower general path with the same
+ *    accuracy (its summation order differs, so results are not bitwise equal
+ *    to the fast path's).
  *  - Results are deterministic: no floating-point atomics, fixed reduction
  *    orders, so repeated calls give bitwise identical outputs.
  */

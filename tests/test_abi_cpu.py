@@ -125,6 +125,17 @@ def test_compose_bwd_validation():
     assert LIB.dora_compose_bwd(None, None, None, None, None, 1.0, 8, 0, 0, 0, None, None, None, None, 0, None) == OK
 
 
+def test_compose_rejects_grids_beyond_one_launch():
+    # 2^36 tokens of 8 columns: the forward would need 2^34 workgroups.  Far-apart
+    # fake pointers keep the overlap checks quiet; nothing is launched.
+    T, out, far = 1 << 36, 8, 1 << 46
+    p = [far * k for k in range(1, 10)]
+    _status(LIB.dora_compose_fwd(p[0], p[1], p[2], p[3], 1.0, T, out, 0, 0, p[4], None), UNSUPPORTED, "workgroups")
+    ws = LIB.dora_compose_bwd_workspace_bytes(T, out)
+    _status(LIB.dora_compose_bwd(p[0], p[1], p[2], p[3], p[4], 1.0, T, out, 0, 0, p[5], p[6], p[7], p[8], ws, None),
+            UNSUPPORTED, "workgroups")
+
+
 def test_binding_rejects_host_tensors():
     import torch
 
