@@ -98,6 +98,9 @@ int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out
   const bool vec = (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) &&
                    aligned16(ws) && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20);
   const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype, vec);
+  if (dora::norm_max_grid(plan) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "dora_norm_factored: out=%lld r=%lld needs more workgroups than one launch holds",
+                (long long)out, (long long)r);
   dora::NormArgs a{W0, A, B, s, norm_out, ws, stream};
   return hip_status(dora::launch_norm(plan, a), "dora_norm_factored");
 }

@@ -1102,6 +1102,13 @@ size_t norm_scratch_bound(int64_t out, int64_t r) {
   return static_cast<size_t>(4 * (out * r + r * r) + 64 * out + 256);
 }
 
+int64_t norm_max_grid(const NormPlan& p) {
+  const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
+  const int64_t gram = p.r > 0 ? std::max(cdiv(nUpper * p.splitG, 8) * 8, cdiv(p.r * p.r, 256)) : 0;
+  const int64_t stream = cdiv(p.nRB * p.nTiles * p.nSplit, 8) * 8;
+  return std::max({gram, stream, cdiv(p.out, 256)});
+}
+
 NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec) {
   NormPlan p;
   p.out = out;

@@ -29,6 +29,9 @@ struct NormPlan {
 
 NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec);
 
+// Largest grid (workgroups in one dimension) the launches of this plan use.
+int64_t norm_max_grid(const NormPlan& p);
+
 // Workspace bytes covering both paths (the path depends on pointer alignment,
 // known only at the call).
 size_t norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
