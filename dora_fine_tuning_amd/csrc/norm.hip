@@ -389,35 +389,58 @@ __device__ inline float sq2<1>(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2(v, v, acc, false);
 }
 
-// Epilogue of the 16-byte path.  The workgroup's B tile (BM rows x BN rank
-// columns) is brought into the free stage buffers by DMA, in passes of as many
-// 32-row blocks as fit; within a pass the 16-byte chunks of each row are
-// rotated by the row index (slot p of row m holds chunk (p + m) mod CPR), so the
-// reads of 16 consecutive rows at one column hit 16 distinct bank groups.  A
-// lane then needs, per rank tile, the 16 consecutive B columns matching its
-// accumulator registers: two 16-byte LDS reads.
+// Wait for a stage's DMA while the n younger stages already issued (at most
+// NS-2, each L loads per wave) stay in flight; n is wave-uniform.
+template <class TL, int N = TL::NS - 2>
+__device__ inline void wait_younger(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N)
+      wait_vmcnt<N * TL::L>();
+    else
+      wait_younger<TL, N - 1>(n);
+  }
+}
+
+// Epilogue of the 16-byte path: the cross term's row sums
+// sum_c B[m][c] * (W0 A^T + B G')[m][c] over the workgroup's rank columns.
+// The B tile (BM rows x BN rank columns) is brought into the free stage area
+// by DMA, in passes of as many 32-row blocks as fit.  Row m of a pass sits at
+// m * BN * 2 bytes, its logical 16-byte chunk c in slot (c & ~15) | ((c ^ m) & 15),
+// so the reads of 16 consecutive rows at one chunk hit 16 distinct bank
+// groups.  A lane needs, per rank tile, the 16 consecutive B columns matching
+// its accumulator registers: two 16-byte LDS reads, whose slots depend on the
+// lane only (tile rows start on multiples of 32).  Rank columns past r hold
+// zero in both operands; a chunk there is still left out of the sum.
 template <int DT, class TL>
 __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0, int64_t n0,
                                           const f32x16 (&acc)[TL::TMW][TL::TN], const float (&bs)[TL::NP],
-                                          bool want_base, float (*red)[TL::BM], char* smem, uint32_t lds0) {
-  using V8 = typename Dt<DT>::V8;
+                                          bool want_base, float (*red)[TL::BM], char* smem, uint32_t lds0,
+                                          __amdgpu_buffer_rsrc_t rb) {
   constexpr int CPR = TL::BN / 8;  // 16-byte chunks per B-tile row
   constexpr int RPP = TL::RPP;     // rows per pass
   constexpr int NPASS = (TL::BM + RPP - 1) / RPP;
   constexpr int INSTR = RPP * CPR / 64;  // 1 KiB DMA instructions per pass
+  static_assert(CPR % 16 == 0 && RPP % 32 == 0, "swizzle groups of 16 chunks, passes of whole row tiles");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int h = lane >> 5, frow = lane & 31;
   const int64_t out = a.sm.out, r = a.sm.r;
-  const int64_t rows_here = std::min<int64_t>(std::max<int64_t>(out - m0, 0), TL::BM);
-  const int64_t cols_here = std::min<int64_t>(std::max<int64_t>(r - n0, 0), TL::BN);
-  // rows of B from m0; columns from n0 (offsets past the tile's valid part read zero)
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(a.sm.B) + (rows_here > 0 ? m0 * r * 2 : 0)), static_cast<short>(0),
-      static_cast<int>(rows_here * r * 2), kBufferWord3);
-  float rs[TL::TMW];
+  const int cols_here = static_cast<int>(std::min<int64_t>(std::max<int64_t>(r - n0, 0), TL::BN));
+  // byte offsets within a row of the lane's chunks (tile j, chunk k of two)
+  uint32_t cofs[TL::TN][2];
 #pragma unroll
-  for (int i = 0; i < TL::TMW; ++i) rs[i] = 0.0f;
+  for (int j = 0; j < TL::TN; ++j)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = wn * TL::TN * 4 + j * 4 + 2 * h + k;
+      cofs[j][k] = static_cast<uint32_t>((c & ~15) | ((c ^ frow) & 15)) * 16u;
+    }
+  const uint32_t lrow = lds0 + static_cast<uint32_t>(frow * CPR * 16);
+  float rs[TL::TMW][2];
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i) rs[i][0] = rs[i][1] = 0.0f;
 
 #pragma unroll
   for (int pass = 0; pass < NPASS; ++pass) {
@@ -425,13 +448,13 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     __syncthreads();  // stage buffers (or the previous pass) no longer read
     if (cols_here > 0) {
       for (int q = wave; q < INSTR; q += TL::NW) {
-        const int slot = q * 64 + lane;
-        const int rl = slot / CPR, pp = slot % CPR;
-        const int ch = (pp + rl) % CPR;
-        const int64_t row = row_base + rl;
-        const int64_t col = static_cast<int64_t>(ch) * 8;
-        const uint32_t off = (col < cols_here) ? static_cast<uint32_t>((row * r + n0 + col) * 2) : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(smem + q * 1024), 16, off, 0, 0, 0);
+        const int sl = q * 64 + lane;
+        const int rl = sl / CPR, p = sl % CPR;
+        const int c = (p & ~15) | ((p ^ rl) & 15);  // logical chunk held by slot p
+        const int col = c * 8;
+        const uint32_t off =
+            col < cols_here ? static_cast<uint32_t>(((row_base + rl) * r + n0 + col) * 2) : kOob;
+        dma16(rb, smem + q * 1024, off);
       }
     }
     wait_vmcnt<0>();
@@ -441,23 +464,27 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
       for (int i = 0; i < TL::TMW; ++i) {
         const int r32 = wm * TL::TMW * 32 + i * 32;  // first tile row within the workgroup tile
         if (r32 < row_base || r32 >= row_base + RPP) continue;
-        const int rl = r32 - row_base + frow;
+        const uint32_t rbase = lrow + static_cast<uint32_t>((r32 - row_base) * CPR * 16);
 #pragma unroll
         for (int j = 0; j < TL::TN; ++j) {
-          const int c0 = wn * TL::TN * 4 + j * 4 + 2 * h;  // first of the lane's two chunks
-          const int p0 = (c0 - rl % CPR + CPR) % CPR, p1 = (c0 + 1 - rl % CPR + CPR) % CPR;
-          u32x4 w0 = lds_read16(lds0 + static_cast<uint32_t>((rl * CPR + p0) * 16));
-          u32x4 w1 = lds_read16(lds0 + static_cast<uint32_t>((rl * CPR + p1) * 16));
+          u32x4 w[2];
+          w[0] = lds_read16(rbase + cofs[j][0]);
+          w[1] = lds_read16(rbase + cofs[j][1]);
           lds_wait();
-          tie(w0);
-          tie(w1);
-          const V8 b0 = __builtin_bit_cast(V8, w0), b1 = __builtin_bit_cast(V8, w1);
-          const int64_t colb = n0 + c0 * 8;
+          tie(w[0]);
+          tie(w[1]);
+          const int c0 = wn * TL::TN * 4 + j * 4 + 2 * h;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float bv = Dt<DT>::to_f(e < 8 ? b0[e] : b1[e - 8]);
-            const float t = __builtin_fmaf(bv, acc[i][j][e], rs[i]);
-            rs[i] = (colb + e < r) ? t : rs[i];
+          for (int k = 0; k < 2; ++k) {
+            const typename Dt<DT>::V8 b = __builtin_bit_cast(typename Dt<DT>::V8, w[k]);
+            float u0 = Dt<DT>::to_f(b[0]) * acc[i][j][8 * k];
+            float u1 = Dt<DT>::to_f(b[1]) * acc[i][j][8 * k + 1];
+#pragma unroll
+            for (int e = 2; e < 8; e += 2) {
+              u0 = __builtin_fmaf(Dt<DT>::to_f(b[e]), acc[i][j][8 * k + e], u0);
+              u1 = __builtin_fmaf(Dt<DT>::to_f(b[e + 1]), acc[i][j][8 * k + e + 1], u1);
+            }
+            rs[i][k] += (c0 + k) * 8 < cols_here ? u0 + u1 : 0.0f;
           }
         }
       }
@@ -465,7 +492,8 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   }
 #pragma unroll
   for (int i = 0; i < TL::TMW; ++i) {
-    const float v = rs[i] + __shfl_xor(rs[i], 32, 64);
+    float v = rs[i][0] + rs[i][1];
+    v += __shfl_xor(v, 32, 64);
     if (h == 0) red[wn][wm * TL::TMW * 32 + i * 32 + frow] = v;
   }
   if (want_base) {
@@ -698,10 +726,7 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
   if constexpr ((U) < TL::NS) {                                                         \
     const int st = sb + (U);                                                            \
     if (st >= st1) break;                                                               \
-    if (st + TL::NS - 2 < st1)                                                          \
-      wait_vmcnt<(TL::NS - 2) * TL::L>();                                               \
-    else                                                                                \
-      wait_vmcnt<0>();                                                                  \
+    wait_younger<TL>(st1 - 1 - st);                                                     \
     __builtin_amdgcn_s_barrier();                                                       \
     if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS) \
     constexpr int so = (U) * TL::STAGE_BYTES;                                           \
@@ -833,7 +858,7 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
     DORA_STAGE(7)
   }
 
-  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0);
+  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0, rxB);
 }
 #undef DORA_STAGE
 #undef DORA_PROLOGUE
