@@ -20,6 +20,12 @@ with numbers; it names the operations:
 * the backward of that compose, including the magnitude gradient, which is a
   reduction over tokens (paragraph on the convergence study: the dmag reduction
   order).  The norm n is treated as a constant in the backward.
+* the cached base term the page lists as future work (paragraph on
+  limitations): W0 is frozen, so ||W0_i||^2 can be computed once and reused.
+  ``row_sqnorm`` is that per-row square norm; ``weight_norm_cached`` is the
+  weight norm with its base term taken from a given cache c instead of W0,
+  n_i^2 = c_i + (||W0_i + s*(BA)_i||^2 - ||W0_i||^2), the difference written
+  out densely as 2s<W0_i, (BA)_i> + s^2 ||(BA)_i||^2.
 
 Everything is computed in fp64 from the exact values of the inputs: bf16/fp16
 tensors and fp32 vectors convert to fp64 without rounding, and ``s`` is the fp32
@@ -55,6 +61,32 @@ def weight_norm(W0, A, B, s) -> np.ndarray:
     s = float(s)
     V = W0 + s * (B @ A)  # the out x in matrix the GPU path never forms
     return np.sqrt(np.sum(V * V, axis=1))
+
+
+def row_sqnorm(W0) -> np.ndarray:
+    """c_i = ||W0_i||^2 = sum_k W0_ik^2 per output row: the base term of the
+    norm, a function of the frozen W0 alone (summary page, paragraph on
+    limitations and future work: cache it).  Returns fp64 [out]."""
+    W0 = as_f64(W0)
+    return np.sum(W0 * W0, axis=1)
+
+
+def weight_norm_cached(base_sq, W0, A, B, s) -> np.ndarray:
+    """The weight norm with a cached base term c (= base_sq):
+
+        n_i = sqrt(max(c_i + 2 s <W0_i, (BA)_i> + s^2 ||(BA)_i||^2, 0))
+
+    With c_i = ||W0_i||^2 this is ||W0_i + s (BA)_i||_2; any other c shifts
+    n_i^2 by c_i - ||W0_i||^2.  BA is formed densely in fp64; a negative n^2
+    is clamped to 0.  base_sq: [out] (fp32 as the kernels receive it, or
+    fp64); returns fp64 [out].
+    """
+    c = as_f64(base_sq)
+    W0, A, B = as_f64(W0), as_f64(A), as_f64(B)
+    s = float(s)
+    V = B @ A
+    n2 = c + 2.0 * s * np.sum(W0 * V, axis=1) + s * s * np.sum(V * V, axis=1)
+    return np.sqrt(np.maximum(n2, 0.0))
 
 
 def scale_factor(m, n) -> np.ndarray:

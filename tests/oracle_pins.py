@@ -1,7 +1,8 @@
 """Pins of the CPU oracle to facts other than itself.
 
-Each ``pin_*`` takes an object with the oracle's three functions
-(``weight_norm``, ``compose_fwd``, ``compose_bwd``) and raises AssertionError
+Each ``pin_*`` takes an object with the oracle's functions (``weight_norm``,
+``row_sqnorm``, ``weight_norm_cached``, ``compose_fwd``, ``compose_bwd``) and
+raises AssertionError
 when the oracle disagrees with:
 
 * exact rational arithmetic on tiny inputs (brute force, using the factored
@@ -157,6 +158,57 @@ def pin_norm_invariances(o, seed=2):
 # ----------------------------------------------------------------------- compose
 
 
+def pin_row_sqnorm(o, seed=6):
+    """||W0_i||^2: exact rational sums on tiny inputs, numpy.linalg.norm squared
+    on larger ones, and zero rows / an empty input axis."""
+    rng = np.random.default_rng(seed)
+    for t in range(4):
+        out, inn = int(rng.integers(1, 6)), int(rng.integers(1, 13))
+        W0 = _bf16_exact(rng, (out, inn), 0.7)
+        got = np.asarray(o.row_sqnorm(W0), dtype=np.float64)
+        assert got.shape == (out,), got.shape
+        for i in range(out):
+            want = float(sum(Fraction(float(v)) ** 2 for v in W0[i]))
+            assert abs(got[i] - want) <= 1e-14 * want + 1e-300, (t, i, got[i], want)
+    W0 = rng.standard_normal((37, 300))
+    np.testing.assert_allclose(o.row_sqnorm(W0), np.linalg.norm(W0, axis=1) ** 2, rtol=1e-13)
+    W0[3] = 0.0
+    assert o.row_sqnorm(W0)[3] == 0.0
+    assert np.all(np.asarray(o.row_sqnorm(np.zeros((4, 0)))) == 0.0)
+
+
+def pin_norm_cached(o, seed=7):
+    """The cached-base norm against exact rational arithmetic with the factored
+    expansion and an arbitrary cache value, against the plain norm when the
+    cache holds ||W0_i||^2, and at the clamp."""
+    rng = np.random.default_rng(seed)
+    for t in range(5):
+        out, inn, r = int(rng.integers(1, 6)), int(rng.integers(1, 10)), int(rng.integers(1, 5))
+        W0 = _bf16_exact(rng, (out, inn), 0.5)
+        A = _bf16_exact(rng, (r, inn), 1.0)
+        B = _bf16_exact(rng, (out, r), 0.5)
+        s = float(np.float32(rng.uniform(0.3, 3.0)))
+        c = (rng.uniform(0.5, 4.0, out) * (1.0 + np.sum(W0 * W0, axis=1))).astype(np.float32)
+        full = _norm_sq_fraction_factored(W0, A, B, s)
+        got = np.asarray(o.weight_norm_cached(c, W0, A, B, s), dtype=np.float64)
+        assert got.shape == (out,), got.shape
+        for i in range(out):
+            base = sum(Fraction(float(v)) ** 2 for v in W0[i])
+            n2 = full[i] - base + Fraction(float(c[i]))
+            want = math.sqrt(max(float(n2), 0.0))
+            assert abs(got[i] - want) <= 1e-12 * max(want, 1e-300) + 1e-300, (t, i, got[i], want)
+    # a cache holding the true base term gives the plain norm
+    W0, A, B = rng.standard_normal((9, 23)), rng.standard_normal((4, 23)), rng.standard_normal((9, 4))
+    c = np.sum(W0 * W0, axis=1)
+    np.testing.assert_allclose(o.weight_norm_cached(c, W0, A, B, 0.9),
+                               np.linalg.norm(W0 + 0.9 * (B @ A), axis=1), rtol=1e-12)
+    # B = 0 leaves sqrt(c); a cache far below the true base term clamps at 0
+    np.testing.assert_allclose(o.weight_norm_cached(c, W0, A, np.zeros_like(B), 0.9), np.sqrt(c), rtol=1e-15)
+    # c = 0, W0 = (1,1,1), BA = -(1,1,1), s = 1: n^2 = 0 - 6 + 3 = -3, clamped to 0
+    r1 = np.ones((1, 3))
+    assert o.weight_norm_cached(np.zeros(1), r1, -r1, np.ones((1, 1)), 1.0)[0] == 0.0
+
+
 def pin_compose_golden(o):
     for ex in _golden("worked_examples.json")["compose"]:
         args = [np.array(ex[k], float) for k in ("base", "lora", "m", "n")]
@@ -260,6 +312,8 @@ ALL_PINS = [
     pin_norm_special_cases,
     pin_norm_golden,
     pin_norm_invariances,
+    pin_row_sqnorm,
+    pin_norm_cached,
     pin_compose_golden,
     pin_compose_closed_forms,
     pin_compose_bwd_finite_differences,

@@ -15,7 +15,9 @@ def test_oracle_pin(pin):
 
 
 def _mutant(**overrides):
-    ns = types.SimpleNamespace(weight_norm=O.weight_norm, compose_fwd=O.compose_fwd, compose_bwd=O.compose_bwd)
+    ns = types.SimpleNamespace(weight_norm=O.weight_norm, row_sqnorm=O.row_sqnorm,
+                               weight_norm_cached=O.weight_norm_cached, compose_fwd=O.compose_fwd,
+                               compose_bwd=O.compose_bwd)
     for k, v in overrides.items():
         setattr(ns, k, v)
     return ns
@@ -30,6 +32,16 @@ def _norm_dense(W0, A, B, s, *, sign=1.0, s_pow=1, axis=1, root=True):
     V = W0 + sign * (float(s) ** s_pow) * (B @ A)
     sq = np.sum(V * V, axis=axis)
     return np.sqrt(sq) if root else sq
+
+
+def _cached(c, W0, A, B, s, *, use_cache=True, cross=True, double_base=False, s_pow=2, clamp=True):
+    c, W0, A, B = _f(c), _f(W0), _f(A), _f(B)
+    s = float(s)
+    V = B @ A
+    base = np.sum(W0 * W0, axis=1)
+    n2 = (c if use_cache else base) + (base if double_base else 0.0)
+    n2 = n2 + (2.0 * s * np.sum(W0 * V, axis=1) if cross else 0.0) + s ** s_pow * np.sum(V * V, axis=1)
+    return np.sqrt(np.maximum(n2, 0.0) if clamp else np.abs(n2))
 
 
 def _fwd(base, lora, m, n, s, add_base=False, *, corr_one=True, s_on_lora=True, invert=False, honour_add=True):
@@ -70,6 +82,13 @@ MUTANTS = {
     "norm_transposed_gram": _mutant(weight_norm=lambda W0, A, B, s: np.sqrt(np.maximum(
         np.sum(_f(W0) ** 2, axis=1) + 2 * float(s) * np.sum(_f(B) * (_f(W0) @ _f(A).T), axis=1)
         + float(s) ** 2 * np.sum((_f(B) @ (_f(A) @ _f(A).T)[::-1, ::-1]) * _f(B), axis=1), 0))),
+    "sqnorm_not_squared": _mutant(row_sqnorm=lambda W0: np.linalg.norm(_f(W0), axis=1)),
+    "sqnorm_column_axis": _mutant(row_sqnorm=lambda W0: np.sum(_f(W0) ** 2, axis=0)),
+    "cached_ignores_cache": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, use_cache=False)),
+    "cached_double_base": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, double_base=True)),
+    "cached_drops_cross": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, cross=False)),
+    "cached_gram_s_linear": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, s_pow=1)),
+    "cached_abs_not_clamp": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, clamp=False)),
     "fwd_no_minus_one": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, corr_one=False)),
     "fwd_drops_s": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, s_on_lora=False)),
     "fwd_inverted_g": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, invert=True)),
@@ -88,6 +107,8 @@ def test_mutant_helpers_match_oracle_when_unmutated():
     rng = np.random.default_rng(0)
     W0, A, B = rng.standard_normal((5, 7)), rng.standard_normal((3, 7)), rng.standard_normal((5, 3))
     np.testing.assert_allclose(_norm_dense(W0, A, B, 1.3), O.weight_norm(W0, A, B, 1.3), rtol=1e-15)
+    c = rng.uniform(1, 3, 5)
+    np.testing.assert_allclose(_cached(c, W0, A, B, 1.3), O.weight_norm_cached(c, W0, A, B, 1.3), rtol=1e-15)
     base, lora, dy = rng.standard_normal((3, (4))), rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
     m, n = rng.uniform(1, 2, 4), rng.uniform(1, 2, 4)
     for ab in (False, True):
