@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--cold-reps", type=int, default=10, help="compose calls timed after a cache-evicting read")
+    ap.add_argument("--cached-reps", type=int, default=10,
+                    help="steps timing the norm with a cached base term (W0 frozen); 0 skips")
     ap.add_argument("--torch-reps", type=int, default=10,
                     help="compose forward+backward timed through the PyTorch custom operator and autograd")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -200,6 +202,42 @@ def main():
     del flush
     cold_us = {k: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3 if v else None for k, v in cold.items()}
 
+    # The norm with its base term cached (W0 is frozen): the row square norms
+    # once, then the factored norm that takes them, timed in the step's place
+    # (before the compose forward and backward) so the caches hold what they do
+    # in the step.
+    cached = None
+    if args.cached_reps > 0:
+        sq = torch.empty(out, dtype=torch.float32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sq_ms = []
+        for k in range(3 + args.cached_reps):
+            e0.record()
+            binding.dora_row_sqnorm(W0, sq_out=sq)
+            e1.record()
+            torch.cuda.synchronize()
+            if k >= 3:
+                sq_ms.append(e0.elapsed_time(e1))
+        n_c = torch.empty_like(norm)
+        evc = []
+        for k in range(3 + args.cached_reps):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            binding.dora_norm_factored_cached(W0, A, B, sq, s, norm_out=n_c, workspace=ws_norm)
+            a1.record()
+            binding.dora_compose_fwd(base, lora, mag, norm, s, y=y)
+            binding.dora_compose_bwd(dy, base, lora, mag, norm, s, d_lora=d_lora, d_base=d_base, d_mag=d_mag,
+                                     workspace=ws_bwd)
+            if k >= 3:
+                evc.append((a0, a1))
+        torch.cuda.synchronize()
+        nc_ms = np.array([a.elapsed_time(b) for a, b in evc])
+        cached = {"norm_us": round(float(nc_ms.mean()) * 1e3, 2),
+                  "row_sqnorm_us": round(float(np.median(sq_ms)) * 1e3, 2),
+                  "max_rel_vs_norm": float(((n_c - norm).abs() / norm).max().item()),
+                  "reps": args.cached_reps}
+        del sq, n_c
+
     # The same compose forward + backward driven through the PyTorch custom
     # operator and autograd (dora_amd::compose), against the direct calls above.
     torch_us = None
@@ -246,6 +284,7 @@ def main():
         "norm_us": round(float(norm_ms.mean()) * 1e3, 2),
         "norm_tflops": round(nf / (norm_ms.mean() * 1e-3) / 1e12, 1),
         "norm_frac_mfma_peak": round(nf / (norm_ms.mean() * 1e-3) / 2.5e15, 4),
+        "norm_cached_base": cached,
         "compose_fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "compose_bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
         "compose_cold": ({"fwd_us": round(cold_us["fwd"], 2), "bwd_us": round(cold_us["bwd"], 2),

@@ -23,6 +23,8 @@ DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
 EXPORTS = (
     "dora_norm_workspace_bytes",
     "dora_norm_factored",
+    "dora_norm_factored_cached",
+    "dora_row_sqnorm",
     "dora_compose_fwd",
     "dora_compose_bwd_workspace_bytes",
     "dora_compose_bwd",
@@ -46,6 +48,10 @@ def _load() -> ctypes.CDLL:
     lib.dora_norm_workspace_bytes.restype = sz
     lib.dora_norm_factored.argtypes = [vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, sz, vp]
     lib.dora_norm_factored.restype = i32
+    lib.dora_norm_factored_cached.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, sz, vp]
+    lib.dora_norm_factored_cached.restype = i32
+    lib.dora_row_sqnorm.argtypes = [vp, i64, i64, i32, vp, vp]
+    lib.dora_row_sqnorm.restype = i32
     lib.dora_compose_fwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp]
     lib.dora_compose_fwd.restype = i32
     lib.dora_compose_bwd_workspace_bytes.argtypes = [i64, i64]
@@ -132,6 +138,41 @@ def dora_norm_factored(W0, A, B, s: float, norm_out=None, workspace=None):
     _check(LIB.dora_norm_factored(_ptr(W0), _ptr(A), _ptr(B), out, in_, r, float(s), code, _ptr(norm_out),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return norm_out
+
+
+def dora_norm_factored_cached(W0, A, B, base_sq, s: float, norm_out=None, workspace=None):
+    """dora_norm_factored with the base term ||W0_i||^2 taken from base_sq (fp32 [out])."""
+    code = _code(W0)
+    out, in_ = W0.shape
+    r = A.shape[0]
+    dev = W0.device
+    _matrix(W0, "W0", (out, in_), W0.dtype, dev)
+    _matrix(A, "A", (r, in_), W0.dtype, dev)
+    _matrix(B, "B", (out, r), W0.dtype, dev)
+    _matrix(base_sq, "base_sq", (out,), torch.float32, dev)
+    if norm_out is None:
+        norm_out = torch.empty(out, dtype=torch.float32, device=dev)
+    _matrix(norm_out, "norm_out", (out,), torch.float32, dev)
+    need = dora_norm_workspace_bytes(out, in_, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(LIB.dora_norm_factored_cached(_ptr(W0), _ptr(A), _ptr(B), _ptr(base_sq), out, in_, r, float(s), code,
+                                         _ptr(norm_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(dev)))
+    return norm_out
+
+
+def dora_row_sqnorm(W0, sq_out=None):
+    """sq_out[i] = ||W0_i||^2 (fp32)."""
+    code = _code(W0)
+    out, in_ = W0.shape
+    dev = W0.device
+    _matrix(W0, "W0", (out, in_), W0.dtype, dev)
+    if sq_out is None:
+        sq_out = torch.empty(out, dtype=torch.float32, device=dev)
+    _matrix(sq_out, "sq_out", (out,), torch.float32, dev)
+    _check(LIB.dora_row_sqnorm(_ptr(W0), out, in_, code, _ptr(sq_out), _stream(dev)))
+    return sq_out
 
 
 def dora_compose_fwd(base, lora, mag, norm, s: float, add_base: bool = False, y=None):

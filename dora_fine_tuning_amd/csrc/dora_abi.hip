@@ -57,6 +57,45 @@ bool any_overlap(const void* p, size_t n, const void* q, size_t m) {
 
 bool valid_dtype(int dtype) { return dtype == DORA_BF16 || dtype == DORA_F16; }
 
+// Validation and launch shared by the two norm entry points (base_sq: the
+// cached base term, or NULL to compute it).
+int norm_call(const char* fn, const void* W0, const void* A, const void* B, const float* base_sq, int64_t out,
+              int64_t in, int64_t r, float s, int dtype, float* norm_out, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (out < 0 || in < 0 || r < 0)
+    return fail(DORA_INVALID_ARG, "%s: negative size (out=%lld in=%lld r=%lld)", fn, (long long)out, (long long)in,
+                (long long)r);
+  if (out == 0) return ok();
+  if (!norm_out) return fail(DORA_INVALID_ARG, "%s: norm_out is NULL", fn);
+  if (in > 0 && !W0) return fail(DORA_INVALID_ARG, "%s: W0 is NULL", fn);
+  if (r > 0 && in > 0 && !A) return fail(DORA_INVALID_ARG, "%s: A is NULL", fn);
+  if (r > 0 && !B) return fail(DORA_INVALID_ARG, "%s: B is NULL", fn);
+  const size_t need = dora::norm_workspace_bytes(out, in, r, dtype);
+  if (ws_bytes < need) return fail(DORA_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "%s: workspace is NULL", fn);
+  const size_t e = 2;
+  const size_t nb = static_cast<size_t>(out) * 4;
+  if (any_overlap(norm_out, nb, ws, need) || any_overlap(norm_out, nb, W0, out * in * e) ||
+      any_overlap(norm_out, nb, B, out * r * e) || any_overlap(norm_out, nb, A, r * in * e))
+    return fail(DORA_INVALID_ARG, "%s: norm_out overlaps an input or the workspace", fn);
+  if (any_overlap(ws, need, W0, out * in * e) || any_overlap(ws, need, A, r * in * e) ||
+      any_overlap(ws, need, B, out * r * e))
+    return fail(DORA_INVALID_ARG, "%s: workspace overlaps an input", fn);
+  if (base_sq && (any_overlap(base_sq, nb, norm_out, nb) || any_overlap(base_sq, nb, ws, need)))
+    return fail(DORA_INVALID_ARG, "%s: base_sq overlaps norm_out or the workspace", fn);
+  // 16-byte path: 16-byte rows and pointers, and buffer byte offsets below
+  // 2^31 within a panel of at most 512 rows of in (< 2^21) or r elements
+  const bool vec = (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) &&
+                   aligned16(ws) && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20);
+  const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype, vec);
+  if (dora::norm_max_grid(plan) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "%s: out=%lld r=%lld needs more workgroups than one launch holds", fn,
+                (long long)out, (long long)r);
+  dora::NormArgs a{W0, A, B, s, norm_out, ws, stream, base_sq};
+  return hip_status(dora::launch_norm(plan, a), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,37 +111,31 @@ size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) 
 
 int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out, int64_t in, int64_t r, float s,
                        int dtype, float* norm_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "dora_norm_factored: unknown dtype %d", dtype);
-  if (out < 0 || in < 0 || r < 0)
-    return fail(DORA_INVALID_ARG, "dora_norm_factored: negative size (out=%lld in=%lld r=%lld)", (long long)out,
-                (long long)in, (long long)r);
+  return norm_call("dora_norm_factored", W0, A, B, nullptr, out, in, r, s, dtype, norm_out, ws, ws_bytes, stream);
+}
+
+int dora_norm_factored_cached(const void* W0, const void* A, const void* B, const float* base_sq, int64_t out,
+                              int64_t in, int64_t r, float s, int dtype, float* norm_out, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (out > 0 && !base_sq) return fail(DORA_INVALID_ARG, "dora_norm_factored_cached: base_sq is NULL");
+  return norm_call("dora_norm_factored_cached", W0, A, B, base_sq, out, in, r, s, dtype, norm_out, ws, ws_bytes,
+                   stream);
+}
+
+int dora_row_sqnorm(const void* W0, int64_t out, int64_t in, int dtype, float* sq_out, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "dora_row_sqnorm: unknown dtype %d", dtype);
+  if (out < 0 || in < 0)
+    return fail(DORA_INVALID_ARG, "dora_row_sqnorm: negative size (out=%lld in=%lld)", (long long)out, (long long)in);
   if (out == 0) return ok();
-  if (!norm_out) return fail(DORA_INVALID_ARG, "dora_norm_factored: norm_out is NULL");
-  if (in > 0 && !W0) return fail(DORA_INVALID_ARG, "dora_norm_factored: W0 is NULL");
-  if (r > 0 && in > 0 && !A) return fail(DORA_INVALID_ARG, "dora_norm_factored: A is NULL");
-  if (r > 0 && !B) return fail(DORA_INVALID_ARG, "dora_norm_factored: B is NULL");
-  const size_t need = dora::norm_workspace_bytes(out, in, r, dtype);
-  if (ws_bytes < need)
-    return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace of %zu bytes, %zu needed", ws_bytes, need);
-  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace is NULL");
-  const size_t e = 2;
-  const size_t nb = static_cast<size_t>(out) * 4;
-  if (any_overlap(norm_out, nb, ws, need) || any_overlap(norm_out, nb, W0, out * in * e) ||
-      any_overlap(norm_out, nb, B, out * r * e) || any_overlap(norm_out, nb, A, r * in * e))
-    return fail(DORA_INVALID_ARG, "dora_norm_factored: norm_out overlaps an input or the workspace");
-  if (any_overlap(ws, need, W0, out * in * e) || any_overlap(ws, need, A, r * in * e) ||
-      any_overlap(ws, need, B, out * r * e))
-    return fail(DORA_INVALID_ARG, "dora_norm_factored: workspace overlaps an input");
-  // 16-byte path: 16-byte rows and pointers, and buffer byte offsets below
-  // 2^31 within a panel of at most 512 rows of in (< 2^21) or r elements
-  const bool vec = (in % 8 == 0) && (r % 8 == 0) && aligned16(W0) && aligned16(A) && aligned16(B) &&
-                   aligned16(ws) && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20);
-  const dora::NormPlan plan = dora::make_norm_plan(out, in, r, dtype, vec);
-  if (dora::norm_max_grid(plan) > INT32_MAX)
-    return fail(DORA_UNSUPPORTED, "dora_norm_factored: out=%lld r=%lld needs more workgroups than one launch holds",
-                (long long)out, (long long)r);
-  dora::NormArgs a{W0, A, B, s, norm_out, ws, stream};
-  return hip_status(dora::launch_norm(plan, a), "dora_norm_factored");
+  if (!sq_out) return fail(DORA_INVALID_ARG, "dora_row_sqnorm: sq_out is NULL");
+  if (in > 0 && !W0) return fail(DORA_INVALID_ARG, "dora_row_sqnorm: W0 is NULL");
+  if (any_overlap(sq_out, static_cast<size_t>(out) * 4, W0, static_cast<size_t>(out) * in * 2))
+    return fail(DORA_INVALID_ARG, "dora_row_sqnorm: sq_out overlaps W0");
+  if ((out + 3) / 4 > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "dora_row_sqnorm: out=%lld needs more workgroups than one launch holds",
+                (long long)out);
+  const bool vec = (in % 8 == 0) && aligned16(W0);
+  return hip_status(dora::launch_row_sqnorm(W0, out, in, dtype, vec, sq_out, stream), "dora_row_sqnorm");
 }
 
 int dora_compose_fwd(const void* base, const void* lora, const float* mag, const float* norm, float s, int64_t T,

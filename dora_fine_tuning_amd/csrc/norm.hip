@@ -208,6 +208,7 @@ struct WArgs {
   int nTiles, nSplit;
   float* base_part;   // [nSplit][out]
   float* cross_part;  // [nSplit][nTiles][out]
+  int skip_base;      // the base term comes from a cache: no squares, no base partials
 };
 
 // Epilogue shared by both W-stream kernels.  The MFMAs take the rank-side
@@ -777,7 +778,7 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const bool want_base = (nt == 0);
+  const bool want_base = (nt == 0) && !a.skip_base;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
   // Buffer resources of the five operand panels, each rebased to the
@@ -913,7 +914,7 @@ __global__ __launch_bounds__(TileW::NT, 2) void wstream_general(WArgs a) {
   const int sp = static_cast<int>(v / (static_cast<int64_t>(a.nTiles) * a.nRB));
   const int64_t m0 = rb * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
   const int64_t st0 = a.S * sp / a.nSplit, st1 = a.S * (sp + 1) / a.nSplit;
-  const bool want_base = (nt == 0);
+  const bool want_base = (nt == 0) && !a.skip_base;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
@@ -1005,12 +1006,65 @@ __global__ __launch_bounds__(TileW::NT, 2) void wstream_general(WArgs a) {
 
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void norm_finalize(const float* base_part, const float* cross_part, int nSplit,
-                                                     int nTiles, int64_t out, float s, float* norm_out) {
+// Row square norms c_i = sum_k W0_ik^2: the base term alone, for a cache of
+// the frozen W0.  One wave per row.  On the 16-byte path lane l reads chunks
+// l, l + 64, .. of 8 elements (four in flight) and squares the four packed
+// pairs of a chunk into four fp32 sums, two squares per dot2 instruction; the
+// general path deals elements l, l + 64, .. to the four sums in turn.  A sum
+// holds at most ceil(in / 256) + 1 squares; the 256 sums of a wave are
+// combined in fp64 and rounded to fp32 once.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void row_sqnorm(const typename Dt<DT>::T* W0, int64_t out, int64_t in, float* sq) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= out) return;
+  const typename Dt<DT>::T* w = W0 + row * in;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (VEC) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(w);
+    const int64_t nc = in / 8;
+    int64_t c = lane;
+    for (; c + 192 < nc; c += 256) {
+      const u32x4 v0 = p[c], v1 = p[c + 64], v2 = p[c + 128], v3 = p[c + 192];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = sq2<DT>(v0[q], acc[q]);
+        acc[q] = sq2<DT>(v1[q], acc[q]);
+        acc[q] = sq2<DT>(v2[q], acc[q]);
+        acc[q] = sq2<DT>(v3[q], acc[q]);
+      }
+    }
+    for (; c < nc; c += 64) {
+      const u32x4 v = p[c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = sq2<DT>(v[q], acc[q]);
+    }
+  } else {
+    int q = 0;
+    for (int64_t k = lane; k < in; k += 64) {
+      const float x = Dt<DT>::to_f(w[k]);
+      acc[q] = __builtin_fmaf(x, x, acc[q]);
+      q = (q + 1) & 3;
+    }
+  }
+  double d = (static_cast<double>(acc[0]) + static_cast<double>(acc[1])) +
+             (static_cast<double>(acc[2]) + static_cast<double>(acc[3]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+  if (lane == 0) sq[row] = static_cast<float>(d);
+}
+
+// n_i from the partials; the base term from base_sq[i] when a cache is given.
+__global__ __launch_bounds__(256) void norm_finalize(const float* base_part, const float* cross_part,
+                                                     const float* base_sq, int nSplit, int nTiles, int64_t out,
+                                                     float s, float* norm_out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= out) return;
   double b = 0.0, c = 0.0;
-  for (int sp = 0; sp < nSplit; ++sp) b += static_cast<double>(base_part[static_cast<int64_t>(sp) * out + i]);
+  if (base_sq)
+    b = static_cast<double>(base_sq[i]);
+  else
+    for (int sp = 0; sp < nSplit; ++sp) b += static_cast<double>(base_part[static_cast<int64_t>(sp) * out + i]);
   for (int q = 0; q < nSplit * nTiles; ++q) c += static_cast<double>(cross_part[static_cast<int64_t>(q) * out + i]);
   const double n2 = b + 2.0 * static_cast<double>(s) * c;
   norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
@@ -1103,6 +1157,7 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   w.total = p.nRB * p.nTiles * p.nSplit;
   w.base_part = reinterpret_cast<float*>(ws + p.off_base);
   w.cross_part = reinterpret_cast<float*>(ws + p.off_cross);
+  w.skip_base = a.base_sq != nullptr;
   if (vec) {
     switch (p.tn) {
       case 1: launch_dma<DT, 1>(w, a.stream); break;
@@ -1117,7 +1172,7 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(norm_finalize, dim3(static_cast<unsigned>(cdiv(p.out, 256))), dim3(256), 0, a.stream,
-                     w.base_part, w.cross_part, p.nSplit, p.nTiles, p.out, a.s, a.norm_out);
+                     w.base_part, w.cross_part, a.base_sq, p.nSplit, p.nTiles, p.out, a.s, a.norm_out);
   return hipGetLastError();
 }
 
@@ -1222,6 +1277,25 @@ size_t norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
   size_t b = make_norm_plan(out, in, r, dtype, false).bytes;
   if (in % 8 == 0 && r % 8 == 0) b = std::max(b, make_norm_plan(out, in, r, dtype, true).bytes);
   return b;
+}
+
+hipError_t launch_row_sqnorm(const void* W0, int64_t out, int64_t in, int dtype, bool vec, float* sq,
+                             hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(cdiv(out, 4))), block(256);
+  if (dtype == 0) {
+    const auto* w = static_cast<const Dt<0>::T*>(W0);
+    if (vec)
+      hipLaunchKernelGGL((row_sqnorm<0, true>), grid, block, 0, stream, w, out, in, sq);
+    else
+      hipLaunchKernelGGL((row_sqnorm<0, false>), grid, block, 0, stream, w, out, in, sq);
+  } else {
+    const auto* w = static_cast<const Dt<1>::T*>(W0);
+    if (vec)
+      hipLaunchKernelGGL((row_sqnorm<1, true>), grid, block, 0, stream, w, out, in, sq);
+    else
+      hipLaunchKernelGGL((row_sqnorm<1, false>), grid, block, 0, stream, w, out, in, sq);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_norm(const NormPlan& p, const NormArgs& a) {

@@ -48,8 +48,13 @@ struct NormArgs {
   float* norm_out;
   void* ws;
   hipStream_t stream;
+  const float* base_sq = nullptr;  // cached ||W0_i||^2 [out]; the W stream then skips the base term
 };
 
 hipError_t launch_norm(const NormPlan& p, const NormArgs& a);
+
+// sq[i] = ||W0_i||^2 in fp32 (vec: in % 8 == 0 and W0 16-byte aligned); grid cdiv(out, 4).
+hipError_t launch_row_sqnorm(const void* W0, int64_t out, int64_t in, int dtype, bool vec, float* sq,
+                             hipStream_t stream);
 
 }  // namespace dora

@@ -12,6 +12,9 @@ This module registers:
 * ``dora_amd::weight_norm`` -- the factored norm ||W0 + s*B*A|| per output row
   (fp32). It has no autograd formula: the norm is treated as a constant,
   and callers pass detached A and B.
+* ``dora_amd::row_sqnorm`` and ``dora_amd::weight_norm_cached`` -- the cached
+  base term the page proposes as future work (W0 is frozen): ||W0_i||^2 once,
+  then the norm that takes it instead of re-deriving it from W0.
 * ``dora_amd::compose`` -- the stable compose (g - 1)*base + g*s*lora
   (+ base), g = m / n. Its autograd formula is the fused backward
   ``dora_amd::compose_backward``, which gives the gradients of base, lora and
@@ -53,6 +56,29 @@ def weight_norm(W0: Tensor, A: Tensor, B: Tensor, s: float) -> Tensor:
 
 @weight_norm.register_fake
 def _weight_norm_fake(W0, A, B, s):
+    return W0.new_empty((W0.shape[0],), dtype=torch.float32)
+
+
+@torch.library.custom_op("dora_amd::row_sqnorm", mutates_args=(), device_types="cuda")
+def row_sqnorm(W0: Tensor) -> Tensor:
+    """||W0_i||^2 per output row, fp32."""
+    return binding.dora_row_sqnorm(W0.contiguous())
+
+
+@row_sqnorm.register_fake
+def _row_sqnorm_fake(W0):
+    return W0.new_empty((W0.shape[0],), dtype=torch.float32)
+
+
+@torch.library.custom_op("dora_amd::weight_norm_cached", mutates_args=(), device_types="cuda")
+def weight_norm_cached(W0: Tensor, A: Tensor, B: Tensor, base_sq: Tensor, s: float) -> Tensor:
+    """The weight norm with the base term ||W0_i||^2 taken from base_sq."""
+    return binding.dora_norm_factored_cached(W0.contiguous(), A.contiguous(), B.contiguous(), base_sq.contiguous(),
+                                             s)
+
+
+@weight_norm_cached.register_fake
+def _weight_norm_cached_fake(W0, A, B, base_sq, s):
     return W0.new_empty((W0.shape[0],), dtype=torch.float32)
 
 
@@ -120,6 +146,11 @@ class DoRALinear(torch.nn.Module):
     so the layer starts out equal to x W0^T.  A is drawn from N(0, 1/in).  On a
     HIP device m is taken from the factored norm itself, so g = m / n is exactly
     1 at B = 0 and the first output equals x W0^T bit for bit.
+
+    W0 is frozen, so its row square norms are computed once (on the first norm
+    on a HIP device) and kept in the buffer ``weight_sqnorm``; the norm then
+    takes its base term from there.  After changing ``weight``, call
+    ``refresh_weight_cache()``.
     """
 
     def __init__(self, in_features: int, out_features: int, r: int, alpha: float = 32.0,
@@ -136,8 +167,14 @@ class DoRALinear(torch.nn.Module):
             (torch.randn(r, in_features, device=device) / math.sqrt(in_features)).to(dtype))
         self.lora_B = torch.nn.Parameter(torch.zeros(out_features, r, device=device, dtype=dtype))
         self.magnitude = torch.nn.Parameter(self.weight.float().norm(dim=1))
+        self.register_buffer("weight_sqnorm", None)
         if self.weight.is_cuda:
             self.reset_magnitude()
+
+    @torch.no_grad()
+    def refresh_weight_cache(self) -> None:
+        """Recompute ||W0_i||^2 (after ``weight`` changed)."""
+        self.weight_sqnorm = row_sqnorm(self.weight)
 
     @torch.no_grad()
     def reset_magnitude(self) -> None:
@@ -145,8 +182,10 @@ class DoRALinear(torch.nn.Module):
         self.magnitude.copy_(self.weight_norm())
 
     def weight_norm(self) -> Tensor:
-        """n = ||W0 + s*B*A|| per output row, detached."""
-        return weight_norm(self.weight, self.lora_A.detach(), self.lora_B.detach(), self.s)
+        """n = ||W0 + s*B*A|| per output row, detached (base term from the cache)."""
+        if self.weight_sqnorm is None or self.weight_sqnorm.device != self.weight.device:
+            self.refresh_weight_cache()
+        return weight_norm_cached(self.weight, self.lora_A.detach(), self.lora_B.detach(), self.weight_sqnorm, self.s)
 
     def forward(self, x: Tensor) -> Tensor:
         lead = x.shape[:-1]

@@ -19,6 +19,11 @@
  *                       reduction (paragraphs on the three-tier dispatch and on
  *                       the convergence study's dmag reduction).
  *
+ * and, for the cached base norm the page lists as future work (W0 is frozen):
+ *
+ *   dora_row_sqnorm            ||W0_i||^2 per row, computed once;
+ *   dora_norm_factored_cached  the weight norm with that cache as its base term.
+ *
  * Conventions shared by every entry point
  *  - Matrices are row-major and contiguous.  W0 is [out x in], A is [r x in],
  *    B is [out x r] (nn.Linear orientation); base, lora, y, dy, d_lora and
@@ -99,6 +104,35 @@ DORA_API size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, in
 DORA_API int dora_norm_factored(const void* W0, const void* A, const void* B, int64_t out, int64_t in,
                        int64_t r, float s, int dtype, float* norm_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/*
+ * sq_out[i] = ||W0_i||^2 = sum_k W0_ik^2, i in [0, out), in fp32: the base term
+ * of the weight norm on its own.  W0 is frozen during fine-tuning, so this is
+ * the cache the summary page proposes as future work (paragraph on
+ * limitations: cache the base norm); compute it once and pass it to
+ * dora_norm_factored_cached.  One read of W0; squares accumulate in fp32
+ * partial sums of at most ceil(in/256) + 1 terms, combined in fp64 and rounded
+ * once.
+ *
+ * W0: device, dtype, [out x in].  sq_out: device fp32 [out], not overlapping
+ * W0.  out == 0 is a no-op; in == 0 gives 0.
+ */
+DORA_API int dora_row_sqnorm(const void* W0, int64_t out, int64_t in, int dtype, float* sq_out,
+                             hipStream_t stream);
+
+/*
+ * dora_norm_factored with the base term taken from a cache:
+ *   norm_out[i] = sqrt(max(base_sq[i] + cross_i + gram_i, 0)),
+ * cross_i and gram_i as in dora_norm_factored (summary page, paragraph on
+ * limitations: the cached base norm).  With base_sq from dora_row_sqnorm on the
+ * same W0 this is ||W0_i + s * B_i * A||_2; the pass over W0 for the cross term
+ * then skips the squares.  Same arguments, workspace and errors as
+ * dora_norm_factored, plus base_sq: device fp32 [out], not overlapping
+ * norm_out or ws (NULL is INVALID_ARG unless out == 0).
+ */
+DORA_API int dora_norm_factored_cached(const void* W0, const void* A, const void* B, const float* base_sq,
+                                       int64_t out, int64_t in, int64_t r, float s, int dtype, float* norm_out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * y = (g - 1) * base + g * s * lora, g_j = mag_j / norm_j broadcast over the T

@@ -91,6 +91,32 @@ def test_norm_validation():
     assert binding.dora_last_error() == ""
 
 
+def test_norm_cached_validation():
+    ws = LIB.dora_norm_workspace_bytes(64, 64, 8, 0)
+    _status(LIB.dora_norm_factored_cached(P, P, P, P * 4, 64, 64, 8, 1.0, 5, P * 2, P * 3, ws, None), UNSUPPORTED,
+            "dtype")
+    _status(LIB.dora_norm_factored_cached(P, P, P, None, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID,
+            "base_sq")
+    _status(LIB.dora_norm_factored_cached(P, P, P, P * 2 + 4, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID,
+            "base_sq overlaps")
+    _status(LIB.dora_norm_factored_cached(P, P, P, P * 3 + 8, 64, 64, 8, 1.0, 0, P * 2, P * 3, ws, None), INVALID,
+            "base_sq overlaps")
+    _status(LIB.dora_norm_factored_cached(P, P, P, P * 4, 64, 64, 8, 1.0, 0, None, P * 3, ws, None), INVALID,
+            "norm_out")
+    assert LIB.dora_norm_factored_cached(None, None, None, None, 0, 64, 8, 1.0, 0, None, None, 0, None) == OK
+
+
+def test_row_sqnorm_validation():
+    _status(LIB.dora_row_sqnorm(P, 64, 64, 7, P * 2, None), UNSUPPORTED, "dtype")
+    _status(LIB.dora_row_sqnorm(P, -1, 64, 0, P * 2, None), INVALID, "negative")
+    _status(LIB.dora_row_sqnorm(None, 64, 64, 0, P * 2, None), INVALID, "W0")
+    _status(LIB.dora_row_sqnorm(P, 64, 64, 0, None, None), INVALID, "sq_out")
+    _status(LIB.dora_row_sqnorm(P, 64, 64, 0, P + 64, None), INVALID, "overlaps")
+    far = 1 << 46
+    _status(LIB.dora_row_sqnorm(far, 1 << 34, 1, 0, 2 * far, None), UNSUPPORTED, "workgroups")
+    assert LIB.dora_row_sqnorm(None, 0, 64, 0, None, None) == OK
+
+
 def test_compose_fwd_validation():
     _status(LIB.dora_compose_fwd(P, P * 2, P * 3, P * 4, 1.0, 8, 8, 3, 0, P * 5, None), UNSUPPORTED, "dtype")
     _status(LIB.dora_compose_fwd(P, P * 2, P * 3, P * 4, 1.0, -8, 8, 0, 0, P * 5, None), INVALID, "negative")

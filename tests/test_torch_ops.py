@@ -83,6 +83,34 @@ def test_opcheck():
                           test_utils=("test_schema", "test_autograd_registration", "test_faketensor"))
     W0, A, B = (t.to(dev) for t in synth.weights(synth.CONFIGS["tiny"]))
     torch.library.opcheck(torch_ops.weight_norm, (W0, A, B, 1.5), test_utils=("test_schema", "test_faketensor"))
+    torch.library.opcheck(torch_ops.row_sqnorm, (W0,), test_utils=("test_schema", "test_faketensor"))
+    sq = torch_ops.row_sqnorm(W0)
+    torch.library.opcheck(torch_ops.weight_norm_cached, (W0, A, B, sq, 1.5),
+                          test_utils=("test_schema", "test_faketensor"))
+
+
+@gpu
+def test_layer_caches_the_base_term():
+    """DoRALinear keeps ||W0_i||^2 and takes its norm with that base term; the
+    result is the plain factored norm within the norm's tolerance, and a
+    refresh after changing W0 follows the new weight."""
+    dev = torch.device("cuda:0")
+    torch.manual_seed(2)
+    layer = torch_ops.DoRALinear(512, 384, 16, device=dev)
+    with torch.no_grad():
+        layer.lora_B.normal_(0.0, 0.02)
+    n = layer.weight_norm()
+    assert layer.weight_sqnorm is not None and layer.weight_sqnorm.dtype == torch.float32
+    W, A, B = (t.detach().float().cpu().numpy() for t in (layer.weight, layer.lora_A, layer.lora_B))
+    np.testing.assert_allclose(layer.weight_sqnorm.double().cpu().numpy(), O.row_sqnorm(W), rtol=1e-6)
+    np.testing.assert_allclose(n.double().cpu().numpy(), O.weight_norm(W, A, B, layer.s), rtol=1e-5)
+    plain = torch_ops.weight_norm(layer.weight, layer.lora_A.detach(), layer.lora_B.detach(), layer.s)
+    np.testing.assert_allclose(n.double().cpu().numpy(), plain.double().cpu().numpy(), rtol=2e-5)
+    with torch.no_grad():
+        layer.weight.mul_(2.0)
+    layer.refresh_weight_cache()
+    W2 = layer.weight.float().cpu().numpy()
+    np.testing.assert_allclose(layer.weight_norm().double().cpu().numpy(), O.weight_norm(W2, A, B, layer.s), rtol=1e-5)
 
 
 def _dense_reference(x, W0, A, B, m, s, dy):
