@@ -255,6 +255,41 @@ def pin_compose_closed_forms(o, seed=3):
     np.testing.assert_allclose(o.compose_fwd(base, lora, 2 * m, n, s, add_base=True), 2 * full, rtol=1e-13)
 
 
+def pin_lora_compose_exact(o, seed=8):
+    """The fused compose against exact rational arithmetic on tiny inputs
+    (square and non-square B, so a transposed operand shows), the unfused
+    compose with B = identity, and h = 0."""
+    rng = np.random.default_rng(seed)
+    for t in range(6):
+        T, out, r = int(rng.integers(1, 5)), int(rng.integers(1, 6)), int(rng.integers(1, 5))
+        if t % 2 == 0:
+            r = out
+        base = _bf16_exact(rng, (T, out), 1.0)
+        h = _bf16_exact(rng, (T, r), 1.0)
+        B = _bf16_exact(rng, (out, r), 0.5)
+        n = rng.uniform(0.5, 2.0, out).astype(np.float32)
+        m = (n * (1 + rng.uniform(-0.01, 0.01, out))).astype(np.float32)
+        s = float(np.float32(rng.uniform(0.5, 3.0)))
+        for add_base in (False, True):
+            got = np.asarray(o.lora_compose_fwd(base, h, B, m, n, s, add_base=add_base), dtype=np.float64)
+            assert got.shape == (T, out), got.shape
+            for i in range(T):
+                for j in range(out):
+                    g = Fraction(float(m[j])) / Fraction(float(n[j]))
+                    lora = sum(Fraction(float(h[i, k])) * Fraction(float(B[j, k])) for k in range(r))
+                    bb = Fraction(float(base[i, j]))
+                    want = (g - 1) * bb + g * Fraction(s) * lora + (bb if add_base else 0)
+                    tol = 1e-13 * (abs(float((g - 1) * bb)) + abs(float(g * Fraction(s) * lora)) + abs(float(bb)))
+                    assert abs(got[i, j] - float(want)) <= tol + 1e-300, (t, i, j, got[i, j], float(want))
+    base, lora, m, n = _compose_inputs(seed, T=6, out=5)
+    eye = np.eye(5)
+    np.testing.assert_array_equal(o.lora_compose_fwd(base, lora, eye, m, n, 1.25),
+                                  o.compose_fwd(base, lora, m, n, 1.25))
+    y0 = o.lora_compose_fwd(base, np.zeros((6, 3)), np.ones((5, 3)), m, n, 1.25)
+    g = m.astype(np.float64) / n.astype(np.float64)
+    np.testing.assert_allclose(y0, (g - 1.0) * base, rtol=1e-15, atol=0)
+
+
 def pin_compose_bwd_finite_differences(o, seed=4):
     """Central differences of L = sum(dy * y); y is affine in m, base and lora, so
     the differences are exact up to rounding."""
@@ -316,6 +351,7 @@ ALL_PINS = [
     pin_norm_cached,
     pin_compose_golden,
     pin_compose_closed_forms,
+    pin_lora_compose_exact,
     pin_compose_bwd_finite_differences,
     pin_compose_bwd_autograd,
 ]

@@ -17,7 +17,7 @@ def test_oracle_pin(pin):
 def _mutant(**overrides):
     ns = types.SimpleNamespace(weight_norm=O.weight_norm, row_sqnorm=O.row_sqnorm,
                                weight_norm_cached=O.weight_norm_cached, compose_fwd=O.compose_fwd,
-                               compose_bwd=O.compose_bwd)
+                               lora_compose_fwd=O.lora_compose_fwd, compose_bwd=O.compose_bwd)
     for k, v in overrides.items():
         setattr(ns, k, v)
     return ns
@@ -89,6 +89,14 @@ MUTANTS = {
     "cached_drops_cross": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, cross=False)),
     "cached_gram_s_linear": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, s_pow=1)),
     "cached_abs_not_clamp": _mutant(weight_norm_cached=lambda c, W0, A, B, s: _cached(c, W0, A, B, s, clamp=False)),
+    "lora_transposed_B": _mutant(lora_compose_fwd=lambda base, h, B, m, n, s, add_base=False: O.compose_fwd(
+        base, _f(h) @ _f(B), m, n, s, add_base)),
+    "lora_drops_s": _mutant(lora_compose_fwd=lambda base, h, B, m, n, s, add_base=False: O.compose_fwd(
+        base, _f(h) @ _f(B).T, m, n, 1.0, add_base)),
+    "lora_ignores_add_base": _mutant(lora_compose_fwd=lambda base, h, B, m, n, s, add_base=False: O.compose_fwd(
+        base, _f(h) @ _f(B).T, m, n, s, False)),
+    "lora_first_column_only": _mutant(lora_compose_fwd=lambda base, h, B, m, n, s, add_base=False: O.compose_fwd(
+        base, np.outer(_f(h)[:, 0], _f(B)[:, 0]), m, n, s, add_base)),
     "fwd_no_minus_one": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, corr_one=False)),
     "fwd_drops_s": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, s_on_lora=False)),
     "fwd_inverted_g": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, invert=True)),
