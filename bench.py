@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=10, help="compose calls timed after a cache-evicting read")
     ap.add_argument("--cached-reps", type=int, default=10,
                     help="steps timing the norm with a cached base term (W0 frozen); 0 skips")
+    ap.add_argument("--fused-reps", type=int, default=20,
+                    help="calls timing the compose with lora = h B^T fused in, against GEMM + compose; 0 skips")
     ap.add_argument("--torch-reps", type=int, default=10,
                     help="compose forward+backward timed through the PyTorch custom operator and autograd")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -140,6 +142,7 @@ def main():
     xc, dyc = synth.activations(cfg)
     W0, A, B = W0c.to(dev), Ac.to(dev), Bc.to(dev)
     base, lora = synth.base_and_lora(xc, W0c, Ac, Bc, device=dev)
+    h = torch.nn.functional.linear(xc.to(dev), A) if args.fused_reps > 0 else None  # x A^T, the adapter's first projection
     dy = dyc.to(dev)
     del xc
     norm = torch.empty(out, dtype=torch.float32, device=dev)
@@ -238,6 +241,39 @@ def main():
                   "reps": args.cached_reps}
         del sq, n_c
 
+    # The compose forward with lora = h B^T formed inside the kernel, against the
+    # unfused pair it replaces (torch's lora GEMM h B^T, then the compose
+    # forward), each timed over the same number of calls.
+    fused = None
+    if args.fused_reps > 0:
+        y2 = torch.empty_like(base)
+        lora2 = torch.empty_like(base)
+
+        def timed(call):
+            evl = []
+            for k in range(3 + args.fused_reps):
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record()
+                call()
+                a1.record()
+                if k >= 3:
+                    evl.append((a0, a1))
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in evl])) * 1e3
+
+        f_us = timed(lambda: binding.dora_lora_compose_fwd(base, h, B, mag, norm, s, y=y2))
+        g_us = timed(lambda: torch.mm(h, B.t(), out=lora2))
+        u_us = timed(lambda: (torch.mm(h, B.t(), out=lora2), binding.dora_compose_fwd(base, lora2, mag, norm, s, y=y2)))
+        fb = 2 * 2 * T * out + 2 * (T * r + out * r) + 8 * out
+        ff = 2.0 * T * out * r
+        fused = {"fused_us": round(f_us, 2), "unfused_us": round(u_us, 2), "lora_gemm_us": round(g_us, 2),
+                 "algorithmic_bytes": fb, "flops": ff,
+                 "fused_gbs": round(fb / (f_us * 1e-6) / 1e9, 1),
+                 "fused_frac_hbm_peak": round(fb / (f_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 "fused_tflops": round(ff / (f_us * 1e-6) / 1e12, 1),
+                 "reps": args.fused_reps}
+        del y2, lora2
+
     # The same compose forward + backward driven through the PyTorch custom
     # operator and autograd (dora_amd::compose), against the direct calls above.
     torch_us = None
@@ -285,6 +321,7 @@ def main():
         "norm_tflops": round(nf / (norm_ms.mean() * 1e-3) / 1e12, 1),
         "norm_frac_mfma_peak": round(nf / (norm_ms.mean() * 1e-3) / 2.5e15, 4),
         "norm_cached_base": cached,
+        "lora_fused_fwd": fused,
         "compose_fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "compose_bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
         "compose_cold": ({"fwd_us": round(cold_us["fwd"], 2), "bwd_us": round(cold_us["bwd"], 2),

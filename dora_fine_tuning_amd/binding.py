@@ -26,6 +26,7 @@ EXPORTS = (
     "dora_norm_factored_cached",
     "dora_row_sqnorm",
     "dora_compose_fwd",
+    "dora_lora_compose_fwd",
     "dora_compose_bwd_workspace_bytes",
     "dora_compose_bwd",
     "dora_last_error",
@@ -54,6 +55,8 @@ def _load() -> ctypes.CDLL:
     lib.dora_row_sqnorm.restype = i32
     lib.dora_compose_fwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp]
     lib.dora_compose_fwd.restype = i32
+    lib.dora_lora_compose_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, vp]
+    lib.dora_lora_compose_fwd.restype = i32
     lib.dora_compose_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.dora_compose_bwd_workspace_bytes.restype = sz
     lib.dora_compose_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -188,6 +191,24 @@ def dora_compose_fwd(base, lora, mag, norm, s: float, add_base: bool = False, y=
     _matrix(y, "y", (T, out), base.dtype, dev)
     _check(LIB.dora_compose_fwd(_ptr(base), _ptr(lora), _ptr(mag), _ptr(norm), float(s), T, out, code,
                                 int(bool(add_base)), _ptr(y), _stream(dev)))
+    return y
+
+
+def dora_lora_compose_fwd(base, h, B, mag, norm, s: float, add_base: bool = False, y=None):
+    """y = (g-1)*base + g*s*(h B^T) (+ base), g = mag/norm per column; lora never stored."""
+    code = _code(base)
+    T, out = base.shape
+    r = h.shape[1]
+    dev = base.device
+    _matrix(h, "h", (T, r), base.dtype, dev)
+    _matrix(B, "B", (out, r), base.dtype, dev)
+    _matrix(mag, "mag", (out,), torch.float32, dev)
+    _matrix(norm, "norm", (out,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(base)
+    _matrix(y, "y", (T, out), base.dtype, dev)
+    _check(LIB.dora_lora_compose_fwd(_ptr(base), _ptr(h), _ptr(B), _ptr(mag), _ptr(norm), float(s), T, out, r, code,
+                                     int(bool(add_base)), _ptr(y), _stream(dev)))
     return y
 
 

@@ -9,6 +9,7 @@
 
 #include "../../include/dora.h"
 #include "compose_kernels.hpp"
+#include "lora_compose_kernels.hpp"
 #include "norm_kernels.hpp"
 
 #ifndef DORA_VERSION_STRING
@@ -168,6 +169,31 @@ int dora_compose_fwd(const void* base, const void* lora, const float* mag, const
     return fail(DORA_UNSUPPORTED, "dora_compose_fwd: T=%lld x out=%lld needs more workgroups than one launch holds",
                 (long long)T, (long long)out);
   return hip_status(dora::launch_compose_fwd(a, vec), "dora_compose_fwd");
+}
+
+int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const float* mag, const float* norm, float s,
+                          int64_t T, int64_t out, int64_t r, int dtype, int add_base, void* y, hipStream_t stream) {
+  const char* fn = "dora_lora_compose_fwd";
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (T < 0 || out < 0 || r < 0)
+    return fail(DORA_INVALID_ARG, "%s: negative size (T=%lld out=%lld r=%lld)", fn, (long long)T, (long long)out,
+                (long long)r);
+  if (T == 0 || out == 0) return ok();
+  if (!base || !mag || !norm || !y) return fail(DORA_INVALID_ARG, "%s: NULL pointer argument", fn);
+  if (r > 0 && (!h || !B)) return fail(DORA_INVALID_ARG, "%s: h or B is NULL", fn);
+  const size_t mb = static_cast<size_t>(T) * out * 2, vb = static_cast<size_t>(out) * 4;
+  const size_t hb = static_cast<size_t>(T) * r * 2, bb = static_cast<size_t>(out) * r * 2;
+  if (partial_overlap(y, mb, base, mb)) return fail(DORA_INVALID_ARG, "%s: y partially overlaps base", fn);
+  if (any_overlap(y, mb, h, hb) || any_overlap(y, mb, B, bb) || any_overlap(y, mb, mag, vb) ||
+      any_overlap(y, mb, norm, vb))
+    return fail(DORA_INVALID_ARG, "%s: y overlaps h, B, mag or norm", fn);
+  const bool vec = (out % 8 == 0) && (r % 8 == 0) && r <= (int64_t(1) << 20) && aligned16(base) &&
+                   (r == 0 || (aligned16(h) && aligned16(B))) && aligned16(mag) && aligned16(norm) && aligned16(y);
+  if (dora::lora_fwd_max_grid(T, out, vec) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "%s: T=%lld x out=%lld needs more workgroups than one launch holds", fn,
+                (long long)T, (long long)out);
+  dora::LoraFwdArgs a{dtype, T, out, r, s, add_base ? 1 : 0, base, h, B, mag, norm, y, stream};
+  return hip_status(dora::launch_lora_fwd(a, vec), fn);
 }
 
 size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out) {

@@ -1,0 +1,349 @@
+// Compose forward with the adapter's second projection fused in, for gfx950:
+//
+//   y = (g - 1) * base + g * s * (h B^T)   (+ base),   g_j = m_j / n_j,
+//
+// with h = x A^T [T x r] and B [out x r] (press summary of arXiv:2603.22276:
+// the fused kernel's gains come from fewer memory accesses).  lora = h B^T
+// lives only in the MFMA accumulators: the kernel reads base once, writes y
+// once, and reads h and B (small, L2 / last-level-cache resident) per tile.
+//
+// Kernels:
+//   lora_fwd_dma      (16-byte path) a workgroup owns 32*TM tokens x 128*TN
+//                     output columns and the whole K = r axis.  K stages of 32
+//                     go global -> LDS by DMA into an NS-slot ring (h rows as
+//                     the X panel, B rows as the Y panel in the fragment row
+//                     order), MFMA 32x32x16 with fp32 accumulation, then an
+//                     epilogue straight from the accumulators: a lane holds one
+//                     token row and 16 consecutive output columns per 32x32
+//                     tile, so it reads base and writes y as two 16-byte chunks
+//                     per tile;
+//   lora_fwd_general  (general path) one thread per output element, the r-term
+//                     dot product in order in fp32.
+#include <algorithm>
+
+#include "dma_common.hpp"
+#include "dora_common.hpp"
+#include "lora_compose_kernels.hpp"
+
+namespace dora {
+
+namespace {
+
+inline int64_t lcdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile geometry: NW = WM*4 waves in a WM x 4 grid (WM along the tokens, 4 along
+// the output columns); a wave owns TMW = TM/WM token tiles x TN column tiles of
+// 32 and keeps their accumulators in registers.  A K stage holds one 64-byte
+// segment (32 elements) of each panel row; one wave DMA instruction moves 16
+// rows x 64 bytes, lane l taking row l/4 and the logical 16-byte chunk
+// (l%4) ^ ((row/4)%4), which lands in LDS slot l%4; the fragment reads of 16
+// consecutive rows at one logical chunk then hit 16 distinct bank groups.
+template <int TN_, int TM_, int NS_, int WM_>
+struct LoraTile {
+  static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_;
+  static constexpr int WN = 4, NW = WM * WN, NT = NW * 64;
+  static constexpr int TMW = TM / WM;
+  static constexpr int BM = 32 * TM, BN = 32 * WN * TN;
+  static constexpr int BK = 32, ROWB = 64, CPR = 4, RPI = 16, SWP = 4;
+  static constexpr int X_BYTES = BM * ROWB, Y_BYTES = BN * ROWB, STAGE_BYTES = X_BYTES + Y_BYTES;
+  static constexpr int XQ = BM / RPI / NW, YQ = BN / RPI / NW;
+  static constexpr int L = XQ + YQ;  // DMA instructions per wave and stage
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  static_assert(TM % WM == 0, "token tiles split over the waves");
+  static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "panels split into whole DMA groups per wave");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NS >= 3 && NS <= 8 && (NS - 2) * L < 64, "ring depth and vmcnt range");
+};
+
+// 256 tokens x 256 columns, 8 waves, four ring slots of 32 KB (one workgroup
+// per CU).  Measured against 128 x 256 with 4 waves and two workgroups per CU:
+// 120 against 141 us at T = out = 8192, r = 384; the two workgroups of a CU
+// run their K loops and epilogues in step, so the second brings no overlap.
+using LoraTileMain = LoraTile<2, 8, 4, 2>;
+
+struct LoraArgs {
+  const void *base, *h, *B;
+  const float *mag, *norm;
+  void* y;
+  float s;
+  int add_base;
+  int64_t T, out, r;
+  int nRB, nTiles, S;
+};
+
+// Wait for the current stage's DMA while the n younger stages already issued
+// (at most NS-2) stay in flight; n is wave-uniform.
+template <class TL, int N = TL::NS - 2>
+__device__ inline void lora_wait_younger(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N)
+      wait_vmcnt<N * TL::L>();
+    else
+      lora_wait_younger<TL, N - 1>(n);
+  }
+}
+
+template <int DT, class TL>
+__global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
+  using V8 = typename Dt<DT>::V8;
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
+
+  const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
+  const uint32_t total = static_cast<uint32_t>(a.nRB) * static_cast<uint32_t>(a.nTiles);
+  if (v >= total) return;
+  const int nt = static_cast<int>(v % static_cast<uint32_t>(a.nTiles));
+  const int rb = static_cast<int>(v / static_cast<uint32_t>(a.nTiles));
+  const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
+  const int64_t T = a.T, out = a.out;
+  const int r = static_cast<int>(a.r), S = a.S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+
+  // Buffer resources of the two panels, rebased to the tile's first row; rows
+  // past the operand lie beyond num_records and read zero.  Offsets stay below
+  // 2^31 (at most 256 rows of r <= 2^20 elements).
+  auto rsrc = [](const void* base, int64_t row0, int64_t rows, int64_t ld, int64_t max_rows) {
+    const int64_t nrows = std::min<int64_t>(std::max<int64_t>(rows - row0, 0), max_rows);
+    const char* p = static_cast<const char*>(base) + (nrows > 0 ? row0 * ld * 2 : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), static_cast<short>(0),
+                                             static_cast<int>(nrows * ld * 2), kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.h, m0, T, r, TL::BM);
+  const __amdgpu_buffer_rsrc_t ry = rsrc(a.B, n0, out, r, TL::BN);
+
+  // Per-lane DMA geometry (as in the W stream of the factored norm): the Y
+  // panel is fetched in the row order sigma of the fragment reads, so that
+  // accumulator register q of a lane in half h holds column 16h + q of its tile.
+  const int lrow = lane / TL::CPR, lslot = lane % TL::CPR;
+  const int lc = lslot ^ ((lrow / TL::SWP) % TL::CPR);
+  const int kc = lc * 8;
+  auto sigma = [](int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); };
+  const int xr0 = wave * TL::RPI + lrow;
+  const int yp = wave * TL::RPI + lrow;
+  const int yr0 = (yp & ~31) + sigma(yp & 31);
+  const uint32_t ld = static_cast<uint32_t>(r) * 2u;
+  const uint32_t lx = static_cast<uint32_t>(xr0) * ld + kc * 2u, ly = static_cast<uint32_t>(yr0) * ld + kc * 2u;
+
+  const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow / TL::SWP) % TL::CPR;
+  const uint32_t xrow = lds0 + static_cast<uint32_t>((wm * TL::TMW * 32 + frow) * TL::ROWB);
+  const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * TL::ROWB);
+  const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), yb0 = yrow + ((fhalf ^ fsw) * 16);
+  const uint32_t xb1 = xrow + (((2 + fhalf) ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
+
+  f32x16 acc[TL::TMW][TL::TN];
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
+
+  // DMA of K stage ST into ring slot SLOT; lanes past r in the last stage get
+  // an out-of-range offset (zeros).
+  auto issue = [&](int st, int slot) {
+    const uint32_t kb = static_cast<uint32_t>(st) * TL::ROWB;
+    const int krem = r - st * TL::BK;
+    const bool tail = krem < TL::BK && kc >= krem;
+    char* so = smem + slot * TL::STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < TL::XQ; ++q)
+      dma16(rx, so + (q * TL::NW + wave) * 1024, tail ? kOob : lx + static_cast<uint32_t>(q * TL::NW * TL::RPI) * ld + kb);
+#pragma unroll
+    for (int q = 0; q < TL::YQ; ++q)
+      dma16(ry, so + TL::X_BYTES + (q * TL::NW + wave) * 1024,
+            tail ? kOob : ly + static_cast<uint32_t>(q * TL::NW * TL::RPI) * ld + kb);
+  };
+
+#pragma unroll
+  for (int u = 0; u < TL::NS - 1; ++u)
+    if (u < S) issue(u, u);
+
+  constexpr int tstep = 32 * TL::ROWB;
+  for (int sb = 0; sb < S; sb += TL::NS) {
+#pragma unroll
+    for (int u = 0; u < TL::NS; ++u) {
+      const int st = sb + u;
+      if (st >= S) break;
+      lora_wait_younger<TL>(S - 1 - st);
+      __builtin_amdgcn_s_barrier();
+      if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, (u + TL::NS - 1) % TL::NS);
+      const uint32_t so = static_cast<uint32_t>(u * TL::STAGE_BYTES);
+      u32x4 x0[TL::TMW], y0[TL::TN], x1[TL::TMW], y1[TL::TN];
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i) x0[i] = lds_read16(xb0 + so + i * tstep);
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) y0[j] = lds_read16(yb0 + so + j * tstep);
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i) x1[i] = lds_read16(xb1 + so + i * tstep);
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) y1[j] = lds_read16(yb1 + so + j * tstep);
+      lds_wait_keep<TL::TMW + TL::TN>();
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) tie(y0[j]);
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j)
+          acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, y0[j]), __builtin_bit_cast(V8, x0[i]), acc[i][j]);
+      lds_wait();
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) tie(y1[j]);
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j)
+          acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, y1[j]), __builtin_bit_cast(V8, x1[i]), acc[i][j]);
+    }
+  }
+
+  // Epilogue.  The column scales (g - 1, g*s) of the tile's BN columns are
+  // formed once, by the first BN threads, into LDS (the ring is free after the
+  // barrier).  Per column tile j a lane needs its 16 columns c0 .. c0 + 15
+  // (whole 8-column chunks, out % 8 == 0) for each of its TMW token rows: the
+  // 2*TMW base chunks of a j are loaded together, before any store of that j
+  // (y may be base, so the compiler keeps loads after earlier stores), and the
+  // loads of j + 1 are issued before the stores of j.
+  using T16 = typename Dt<DT>::T;
+  const T16* base = static_cast<const T16*>(a.base);
+  T16* y = static_cast<T16*>(a.y);
+  float* sc = reinterpret_cast<float*>(smem);  // [2][BN]: g - 1, then g*s
+  Chunk cb[2][TL::TMW][2];
+  auto load_base = [&](int j, Chunk (&c)[TL::TMW][2]) {
+    const int64_t c0 = n0 + wn * TL::TN * 32 + j * 32 + 16 * fhalf;
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) {
+      const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
+      const bool ok0 = t < T && c0 < out, ok1 = t < T && c0 + 8 < out;
+      const int64_t idx = ok0 ? t * out + c0 : 0;
+      c[i][0] = ok0 ? *reinterpret_cast<const Chunk*>(base + idx) : zero_chunk();
+      c[i][1] = ok1 ? *reinterpret_cast<const Chunk*>(base + idx + 8) : zero_chunk();
+    }
+  };
+  load_base(0, cb[0]);
+  __syncthreads();  // every wave is past its last fragment read
+  if (tid < TL::BN) {
+    const int64_t c = n0 + tid;
+    float gm1 = 0.0f, gs = 0.0f;
+    if (c < out) {
+      const float m = a.mag[c], n = a.norm[c];
+      gm1 = (m - n) / n;
+      gs = (m / n) * a.s;
+    }
+    sc[tid] = gm1;
+    sc[TL::BN + tid] = gs;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < TL::TN; ++j) {
+    if (j + 1 < TL::TN) load_base(j + 1, cb[(j + 1) & 1]);
+    const int cl = wn * TL::TN * 32 + j * 32 + 16 * fhalf;  // first column within the tile
+    const int64_t c0 = n0 + cl;
+    if (c0 >= out) continue;
+    const bool hi_ok = c0 + 8 < out;
+    float gm1[16], gs[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(sc + cl + 4 * k);
+      const f32x4 g2 = *reinterpret_cast<const f32x4*>(sc + TL::BN + cl + 4 * k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gm1[4 * k + e] = g1[e];
+        gs[4 * k + e] = g2[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) {
+      const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
+      if (t >= T) continue;
+      const int64_t idx = t * out + c0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float b[8], o[8];
+        chunk_to_f32<DT>(cb[j & 1][i][k], b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = __builtin_fmaf(gs[8 * k + e], acc[i][j][8 * k + e], gm1[8 * k + e] * b[e]);
+          o[e] = a.add_base ? b[e] + d : d;
+        }
+        // plain stores: a 128-byte line of y arrives in 16-byte pieces from
+        // four store instructions, which the L2 merges; nontemporal stores of
+        // such pieces took 107 instead of 62 us for the epilogue alone
+        if (k == 0 || hi_ok) *reinterpret_cast<u32x4*>(y + idx + 8 * k) = __builtin_bit_cast(u32x4, f32_to_chunk<DT>(o));
+      }
+    }
+  }
+}
+
+// General path: one thread per output element, lora_tj = sum_k h_tk B_jk in
+// order in fp32, then the compose.
+template <int DT>
+__global__ __launch_bounds__(256) void lora_fwd_general(LoraArgs a) {
+  using T16 = typename Dt<DT>::T;
+  const T16* h = static_cast<const T16*>(a.h);
+  const T16* B = static_cast<const T16*>(a.B);
+  const T16* base = static_cast<const T16*>(a.base);
+  T16* y = static_cast<T16*>(a.y);
+  const int64_t n = a.T * a.out;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = e / a.out, j = e % a.out;
+    float l = 0.0f;
+    for (int64_t k = 0; k < a.r; ++k) l = __builtin_fmaf(Dt<DT>::to_f(h[t * a.r + k]), Dt<DT>::to_f(B[j * a.r + k]), l);
+    const float m = a.mag[j], nn = a.norm[j];
+    const float gm1 = (m - nn) / nn, gs = (m / nn) * a.s;
+    const float b = Dt<DT>::to_f(base[e]);
+    const float d = __builtin_fmaf(gs, l, gm1 * b);
+    y[e] = Dt<DT>::from_f(a.add_base ? b + d : d);
+  }
+}
+
+constexpr int kGenBlocks = 4096;
+
+}  // namespace
+
+int64_t lora_fwd_max_grid(int64_t T, int64_t out, bool vec) {
+  if (!vec) return kGenBlocks;
+  using TL = LoraTileMain;
+  return lcdiv(lcdiv(T, TL::BM) * lcdiv(out, TL::BN), 8) * 8;
+}
+
+hipError_t launch_lora_fwd(const LoraFwdArgs& p, bool vec) {
+  using TL = LoraTileMain;
+  LoraArgs a{};
+  a.base = p.base;
+  a.h = p.h;
+  a.B = p.B;
+  a.mag = p.mag;
+  a.norm = p.norm;
+  a.y = p.y;
+  a.s = p.s;
+  a.add_base = p.add_base;
+  a.T = p.T;
+  a.out = p.out;
+  a.r = p.r;
+  if (vec) {
+    a.nRB = static_cast<int>(lcdiv(p.T, TL::BM));
+    a.nTiles = static_cast<int>(lcdiv(p.out, TL::BN));
+    a.S = static_cast<int>(lcdiv(p.r, TL::BK));
+    const dim3 grid(static_cast<unsigned>(lora_fwd_max_grid(p.T, p.out, true)));
+    if (p.dtype == 0)
+      hipLaunchKernelGGL((lora_fwd_dma<0, TL>), grid, dim3(TL::NT), 0, p.stream, a);
+    else
+      hipLaunchKernelGGL((lora_fwd_dma<1, TL>), grid, dim3(TL::NT), 0, p.stream, a);
+  } else {
+    const int64_t blocks = std::min<int64_t>(lcdiv(p.T * p.out, 256), kGenBlocks);
+    if (p.dtype == 0)
+      hipLaunchKernelGGL((lora_fwd_general<0>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream, a);
+    else
+      hipLaunchKernelGGL((lora_fwd_general<1>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dora

@@ -6,8 +6,9 @@ adapter-module shapes; it holds none of the method's arithmetic (no norm, no
 compose, no gradient).  The two things it does compute are input-recipe steps
 that sit outside the method:
 
-* ``base = x @ W0^T`` and ``lora = (x @ A^T) @ B^T`` -- the caller's own GEMMs that
-  feed the compose (the pages' compose takes these two products as given);
+* ``base = x @ W0^T``, ``h = x @ A^T`` and ``lora = h @ B^T`` -- the caller's own
+  GEMMs that feed the compose (the pages' compose takes these products as
+  given);
 * ``m = n * (1 + eps)`` -- the magnitude vector of a module whose scale factor
   g = m / n sits at a chosen distance from 1.  ``n`` is passed in by the caller.
 
@@ -127,6 +128,18 @@ def magnitude(n, eps: np.ndarray) -> np.ndarray:
     """m = n * (1 + eps) rounded to fp32; ``n`` is any per-row norm the caller holds."""
     n = np.asarray(n, dtype=np.float64)
     return (n * (1.0 + eps)).astype(np.float32)
+
+
+def base_and_h(x, W0, A, device="cpu"):
+    """base = x W0^T and the adapter's first projection h = x A^T, in x's dtype
+    (the inputs of the compose with the second projection fused in); the same
+    GEMMs as base_and_lora."""
+    dt = x.dtype
+    if str(device) == "cpu":
+        xf = x.float()
+        return (xf @ W0.float().t()).to(dt), (xf @ A.float().t()).to(dt)
+    xd, Wd, Ad = (t.to(device) for t in (x, W0, A))
+    return torch.nn.functional.linear(xd, Wd), torch.nn.functional.linear(xd, Ad)
 
 
 def base_and_lora(x, W0, A, B, device="cpu"):

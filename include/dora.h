@@ -19,6 +19,12 @@
  *                       reduction (paragraphs on the three-tier dispatch and on
  *                       the convergence study's dmag reduction).
  *
+ * and the compose with the adapter's second projection fused in, so that lora
+ * is never stored (the page's account of where the fused kernel's gains come
+ * from: fewer memory accesses):
+ *
+ *   dora_lora_compose_fwd      y = (g-1)*base + g*s*(h*B^T), h = x*A^T;
+ *
  * and, for the cached base norm the page lists as future work (W0 is frozen):
  *
  *   dora_row_sqnorm            ||W0_i||^2 per row, computed once;
@@ -148,6 +154,26 @@ DORA_API int dora_norm_factored_cached(const void* W0, const void* A, const void
  */
 DORA_API int dora_compose_fwd(const void* base, const void* lora, const float* mag, const float* norm, float s,
                      int64_t T, int64_t out, int dtype, int add_base, void* y, hipStream_t stream);
+
+/*
+ * dora_compose_fwd with the adapter's second projection fused in:
+ *   y = (g - 1) * base + g * s * (h * B^T)   (+ base when add_base != 0),
+ * where h = x * A^T is the adapter's first projection [T x r] and B is
+ * [out x r] (summary page: the fused kernel's gains come from fewer memory
+ * accesses).  lora = h * B^T is accumulated in fp32 by MFMA and never stored:
+ * one read of base, one write of y, and h and B read per tile (they are small).
+ * g - 1 is formed as in dora_compose_fwd; one rounding per output.
+ *
+ * base, y: device, dtype, [T x out]; h: [T x r]; B: [out x r]; mag, norm:
+ * device fp32 [out].  y may be the same buffer as base; no other overlap with
+ * an input.  h and B may be NULL when r == 0 (then y is the compose of
+ * lora = 0).  T == 0 or out == 0 is a no-op.  The fast path needs out and r
+ * multiples of 8, r <= 2^20 and 16-byte aligned pointers; other cases take a
+ * slow path (one thread per output element).
+ */
+DORA_API int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const float* mag,
+                                   const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype,
+                                   int add_base, void* y, hipStream_t stream);
 
 /* Bytes of device workspace dora_compose_bwd needs (per-token-block fp32 partial sums). */
 DORA_API size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out);

@@ -151,6 +151,26 @@ def test_compose_bwd_validation():
     assert LIB.dora_compose_bwd(None, None, None, None, None, 1.0, 8, 0, 0, 0, None, None, None, None, 0, None) == OK
 
 
+def test_lora_compose_fwd_validation():
+    def call(base=P, h=P * 2, B=P * 3, mag=P * 4, norm=P * 5, y=P * 6, T=64, out=16, r=8, dtype=0):
+        return LIB.dora_lora_compose_fwd(base, h, B, mag, norm, 1.0, T, out, r, dtype, 0, y, None)
+
+    _status(call(dtype=4), UNSUPPORTED, "dtype")
+    _status(call(r=-1), INVALID, "negative")
+    _status(call(base=None), INVALID, "NULL")
+    _status(call(h=None), INVALID, "h or B")
+    _status(call(y=P + 2), INVALID, "partially")
+    _status(call(y=P * 2 + 8), INVALID, "y overlaps")
+    _status(call(y=P * 4), INVALID, "y overlaps")
+    # r == 0 needs no h or B; empty sizes are no-ops
+    # 2^40 tokens x 256 columns need 2^32 workgroups; far-apart fake pointers
+    # keep the overlap checks quiet (nothing is launched)
+    _status(LIB.dora_lora_compose_fwd(1 << 49, None, None, 1 << 50, (1 << 50) + (1 << 20), 1.0, 1 << 40, 1 << 8, 0,
+                                      0, 0, 1 << 51, None), UNSUPPORTED, "workgroups")
+    assert LIB.dora_lora_compose_fwd(None, None, None, None, None, 1.0, 0, 16, 8, 0, 0, None, None) == OK
+    assert LIB.dora_lora_compose_fwd(None, None, None, None, None, 1.0, 16, 0, 8, 0, 0, None, None) == OK
+
+
 def test_compose_rejects_grids_beyond_one_launch():
     # 2^36 tokens of 8 columns: the forward would need 2^34 workgroups.  Far-apart
     # fake pointers keep the overlap checks quiet; nothing is launched.
