@@ -12,6 +12,10 @@ This module registers:
 * ``dora_amd::weight_norm`` -- the factored norm ||W0 + s*B*A|| per output row
   (fp32). It has no autograd formula: the norm is treated as a constant,
   and callers pass detached A and B.
+* ``dora_amd::lora_compose`` -- the compose with the adapter's second
+  projection fused in: from h = x A^T and B it forms lora = h B^T inside the
+  kernel and never stores it.  No autograd formula: ``DoRALinear`` uses it on
+  the inference tier, where nothing is saved for a backward.
 * ``dora_amd::row_sqnorm`` and ``dora_amd::weight_norm_cached`` -- the cached
   base term the page proposes as future work (W0 is frozen): ||W0_i||^2 once,
   then the norm that takes it instead of re-deriving it from W0.
@@ -23,9 +27,10 @@ This module registers:
   y = x W0^T + compose(x W0^T, x A^T B^T, m, n, s), with n = ||W0 + s*B*A||
   detached.
 
-Tiers: autograd records the compose only when a gradient is needed, so
-under ``torch.no_grad()`` or ``torch.inference_mode()`` the forward kernel
-runs alone and saves nothing. There is no eager fallback. Inputs the kernels
+Tiers: autograd records the compose only when a gradient is needed.  Under
+``torch.no_grad()`` or ``torch.inference_mode()`` (or when no input needs a
+gradient) ``DoRALinear`` runs the compose with the second projection fused in:
+lora = x A^T B^T is never stored. There is no eager fallback. Inputs the kernels
 cannot take raise: CPU tensors, dtypes other than bf16/fp16, and a missing
 library.
 
@@ -115,6 +120,18 @@ def _compose_backward_fake(dy, base, lora, mag, norm, s, add_base, want_base):
     return torch.empty_like(dy), d_base, mag.new_empty(mag.shape)
 
 
+@torch.library.custom_op("dora_amd::lora_compose", mutates_args=(), device_types="cuda")
+def lora_compose(base: Tensor, h: Tensor, B: Tensor, mag: Tensor, norm: Tensor, s: float, add_base: bool) -> Tensor:
+    """(g - 1) * base + g * s * (h B^T), plus base when add_base; lora never stored."""
+    return binding.dora_lora_compose_fwd(base.contiguous(), h.contiguous(), B.contiguous(), mag.contiguous(),
+                                         norm.contiguous(), s, add_base=add_base)
+
+
+@lora_compose.register_fake
+def _lora_compose_fake(base, h, B, mag, norm, s, add_base):
+    return torch.empty_like(base)
+
+
 def _compose_setup(ctx, inputs, output):
     base, lora, mag, norm, s, add_base = inputs
     ctx.save_for_backward(base, lora, mag, norm)
@@ -191,6 +208,11 @@ class DoRALinear(torch.nn.Module):
         lead = x.shape[:-1]
         x2 = x.reshape(-1, self.in_features)
         base = F.linear(x2, self.weight)
-        lora = F.linear(F.linear(x2, self.lora_A), self.lora_B)
-        y = compose(base, lora, self.magnitude, self.weight_norm(), self.s, True)
+        h = F.linear(x2, self.lora_A)
+        if torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in self.parameters())):
+            lora = F.linear(h, self.lora_B)
+            y = compose(base, lora, self.magnitude, self.weight_norm(), self.s, True)
+        else:
+            # inference tier: lora = h B^T is formed inside the compose kernel
+            y = lora_compose(base, h, self.lora_B, self.magnitude, self.weight_norm(), self.s, True)
         return y.reshape(*lead, self.out_features)
