@@ -61,6 +61,8 @@ struct LoraTile {
 // run their K loops and epilogues in step, so the second brings no overlap.
 using LoraTileMain = LoraTile<2, 8, 4, 2>;
 
+constexpr uint32_t kGroupCols = 4;  // column tiles per group of the tile order
+
 struct LoraArgs {
   const void *base, *h, *B;
   const float *mag, *norm;
@@ -93,8 +95,16 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
   const uint32_t total = static_cast<uint32_t>(a.nRB) * static_cast<uint32_t>(a.nTiles);
   if (v >= total) return;
-  const int nt = static_cast<int>(v % static_cast<uint32_t>(a.nTiles));
-  const int rb = static_cast<int>(v / static_cast<uint32_t>(a.nTiles));
+  // Tile order: groups of kGroupCols column tiles, token blocks within a group.
+  // With the XCD-contiguous numbering an XCD then works on one group's B slice
+  // (kGroupCols x 256 rows of B stay in its L2) while it sweeps the token
+  // blocks, instead of streaming all of B once per token block.
+  const uint32_t nRB = static_cast<uint32_t>(a.nRB), nTl = static_cast<uint32_t>(a.nTiles);
+  const uint32_t grp = v / (kGroupCols * nRB);
+  const uint32_t gn = std::min<uint32_t>(kGroupCols, nTl - grp * kGroupCols);
+  const uint32_t loc = v - grp * kGroupCols * nRB;
+  const int rb = static_cast<int>(loc / gn);
+  const int nt = static_cast<int>(grp * kGroupCols + loc % gn);
   const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
   const int64_t T = a.T, out = a.out;
   const int r = static_cast<int>(a.r), S = a.S;
