@@ -214,28 +214,31 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
 
   // Epilogue.  The column scales (g - 1, g*s) of the tile's BN columns are
   // formed once, by the first BN threads, into LDS (the ring is free after the
-  // barrier).  Per column tile j a lane needs its 16 columns c0 .. c0 + 15
-  // (whole 8-column chunks, out % 8 == 0) for each of its TMW token rows: the
-  // 2*TMW base chunks of a j are loaded together, before any store of that j
-  // (y may be base, so the compiler keeps loads after earlier stores), and the
-  // loads of j + 1 are issued before the stores of j.
+  // barrier).  A lane then walks its TMW token rows; for each it needs 2*TN
+  // chunks of 8 columns (16 consecutive columns c0 .. c0 + 15 per column tile j,
+  // whole chunks since out % 8 == 0).  The chunks of row i + 1 are loaded
+  // before the stores of row i (y may be base, so the compiler keeps loads
+  // after earlier stores), and the four stores that complete a row's 128-byte
+  // line of y follow each other, so the L2 merges them before any write-back.
+  // Plain stores: nontemporal stores of these 16-byte pieces took 107 instead
+  // of 62 us for the epilogue alone at T = out = 8192.
   using T16 = typename Dt<DT>::T;
   const T16* base = static_cast<const T16*>(a.base);
   T16* y = static_cast<T16*>(a.y);
   float* sc = reinterpret_cast<float*>(smem);  // [2][BN]: g - 1, then g*s
-  Chunk cb[2][TL::TMW][2];
-  auto load_base = [&](int j, Chunk (&c)[TL::TMW][2]) {
-    const int64_t c0 = n0 + wn * TL::TN * 32 + j * 32 + 16 * fhalf;
+  Chunk cb[2][TL::TN][2];
+  auto load_row = [&](int i, Chunk (&c)[TL::TN][2]) {
+    const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
 #pragma unroll
-    for (int i = 0; i < TL::TMW; ++i) {
-      const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
+    for (int j = 0; j < TL::TN; ++j) {
+      const int64_t c0 = n0 + wn * TL::TN * 32 + j * 32 + 16 * fhalf;
       const bool ok0 = t < T && c0 < out, ok1 = t < T && c0 + 8 < out;
       const int64_t idx = ok0 ? t * out + c0 : 0;
-      c[i][0] = ok0 ? *reinterpret_cast<const Chunk*>(base + idx) : zero_chunk();
-      c[i][1] = ok1 ? *reinterpret_cast<const Chunk*>(base + idx + 8) : zero_chunk();
+      c[j][0] = ok0 ? *reinterpret_cast<const Chunk*>(base + idx) : zero_chunk();
+      c[j][1] = ok1 ? *reinterpret_cast<const Chunk*>(base + idx + 8) : zero_chunk();
     }
   };
-  load_base(0, cb[0]);
+  load_row(0, cb[0]);
   __syncthreads();  // every wave is past its last fragment read
   if (tid < TL::BN) {
     const int64_t c = n0 + tid;
@@ -250,41 +253,33 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < TL::TN; ++j) {
-    if (j + 1 < TL::TN) load_base(j + 1, cb[(j + 1) & 1]);
-    const int cl = wn * TL::TN * 32 + j * 32 + 16 * fhalf;  // first column within the tile
-    const int64_t c0 = n0 + cl;
-    if (c0 >= out) continue;
-    const bool hi_ok = c0 + 8 < out;
-    float gm1[16], gs[16];
+  for (int i = 0; i < TL::TMW; ++i) {
+    if (i + 1 < TL::TMW) load_row(i + 1, cb[(i + 1) & 1]);
+    const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
+    if (t >= T) continue;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(sc + cl + 4 * k);
-      const f32x4 g2 = *reinterpret_cast<const f32x4*>(sc + TL::BN + cl + 4 * k);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gm1[4 * k + e] = g1[e];
-        gs[4 * k + e] = g2[e];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TL::TMW; ++i) {
-      const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
-      if (t >= T) continue;
+    for (int j = 0; j < TL::TN; ++j) {
+      const int cl = wn * TL::TN * 32 + j * 32 + 16 * fhalf;  // first column within the tile
+      const int64_t c0 = n0 + cl;
+      if (c0 >= out) continue;
       const int64_t idx = t * out + c0;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
+        if (k == 1 && c0 + 8 >= out) continue;
+        // the chunk's 8 column scales, read from LDS where they are used
+        const f32x4 g1a = *reinterpret_cast<const f32x4*>(sc + cl + 8 * k);
+        const f32x4 g1b = *reinterpret_cast<const f32x4*>(sc + cl + 8 * k + 4);
+        const f32x4 g2a = *reinterpret_cast<const f32x4*>(sc + TL::BN + cl + 8 * k);
+        const f32x4 g2b = *reinterpret_cast<const f32x4*>(sc + TL::BN + cl + 8 * k + 4);
         float b[8], o[8];
-        chunk_to_f32<DT>(cb[j & 1][i][k], b);
+        chunk_to_f32<DT>(cb[i & 1][j][k], b);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float d = __builtin_fmaf(gs[8 * k + e], acc[i][j][8 * k + e], gm1[8 * k + e] * b[e]);
+          const float gm1 = e < 4 ? g1a[e] : g1b[e - 4], gs = e < 4 ? g2a[e] : g2b[e - 4];
+          const float d = __builtin_fmaf(gs, acc[i][j][8 * k + e], gm1 * b[e]);
           o[e] = a.add_base ? b[e] + d : d;
         }
-        // plain stores: a 128-byte line of y arrives in 16-byte pieces from
-        // four store instructions, which the L2 merges; nontemporal stores of
-        // such pieces took 107 instead of 62 us for the epilogue alone
-        if (k == 0 || hi_ok) *reinterpret_cast<u32x4*>(y + idx + 8 * k) = __builtin_bit_cast(u32x4, f32_to_chunk<DT>(o));
+        *reinterpret_cast<u32x4*>(y + idx + 8 * k) = __builtin_bit_cast(u32x4, f32_to_chunk<DT>(o));
       }
     }
   }
