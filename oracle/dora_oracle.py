@@ -23,7 +23,9 @@ with numbers; it names the operations:
 * the compose with the adapter's second projection fused in (the page's
   paragraph on where the speedup comes from: fewer memory accesses): given
   h = x A^T [T x r] and B [out x r], lora = h B^T is formed inside the compose
-  and never stored; ``lora_compose_fwd`` is the compose forward of that product.
+  and never stored; ``lora_compose_fwd`` is the compose forward of that product,
+  and ``lora_compose_bwd`` its backward with respect to base, B and m, which
+  never needs lora or d_lora stored.
 * the cached base term the page lists as future work (paragraph on
   limitations): W0 is frozen, so ||W0_i||^2 can be computed once and reused.
   ``row_sqnorm`` is that per-row square norm; ``weight_norm_cached`` is the
@@ -124,6 +126,29 @@ def lora_compose_fwd(base, h, B, m, n, s, add_base: bool = False) -> np.ndarray:
     """
     lora = as_f64(h) @ as_f64(B).T
     return compose_fwd(base, lora, m, n, s, add_base)
+
+
+def lora_compose_bwd(dy, base, h, B, m, n, s, add_base: bool = False):
+    """Backward of lora_compose_fwd for L = sum(dy * y), n held fixed:
+
+        d_base = (g - 1) * dy, or g * dy with add_base
+        d_B    = (g * s * dy)^T h                          [out x r]
+        d_mag  = sum_t dy_tj * (base_tj + s * (h B^T)_tj) / n_j
+
+    d_B is the gradient of the adapter's second projection through
+    lora = h B^T (d_lora = g * s * dy, then d_lora^T h).  Returns fp64
+    (d_base [T x out], d_B [out x r], d_mag [out]).
+    """
+    dy, base, h, B = as_f64(dy), as_f64(base), as_f64(h), as_f64(B)
+    n = as_f64(n)
+    g = scale_factor(m, n)
+    s = float(s)
+    lora = h @ B.T
+    d_lora = g * s * dy
+    d_base = (g if add_base else (g - 1.0)) * dy
+    d_B = d_lora.T @ h
+    d_mag = np.sum(dy * (base + s * lora), axis=0) / n
+    return d_base, d_B, d_mag
 
 
 def compose_bwd(dy, base, lora, m, n, s, add_base: bool = False):

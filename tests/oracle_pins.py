@@ -290,6 +290,52 @@ def pin_lora_compose_exact(o, seed=8):
     np.testing.assert_allclose(y0, (g - 1.0) * base, rtol=1e-15, atol=0)
 
 
+def pin_lora_compose_bwd(o, seed=9):
+    """The fused backward against central finite differences of the fp64 loss
+    L = sum(dy * y) through lora_compose_fwd (with respect to base, B and m),
+    torch.autograd in fp64 through the dense formula, and the identity
+    sum_t dy lora = sum_k B (dy^T h) on the magnitude gradient."""
+    rng = np.random.default_rng(seed)
+    T, out, r = 7, 5, 3
+    base = rng.standard_normal((T, out))
+    h = rng.standard_normal((T, r))
+    B = rng.standard_normal((out, r)) * 0.5
+    n = rng.uniform(0.5, 2.0, out)
+    m = n * (1 + rng.uniform(-0.05, 0.05, out))
+    dy = rng.standard_normal((T, out))
+    s = 1.375
+    for add_base in (False, True):
+        db, dB, dm = (np.asarray(a, np.float64) for a in o.lora_compose_bwd(dy, base, h, B, m, n, s, add_base=add_base))
+        assert db.shape == (T, out) and dB.shape == (out, r) and dm.shape == (out,)
+        L = lambda b_, B_, m_: float(np.sum(dy * o.lora_compose_fwd(b_, h, B_, m_, n, s, add_base=add_base)))
+        eps = 1e-6
+        for (i, j) in [(0, 0), (3, 2), (6, 4)]:
+            e = np.zeros_like(base); e[i, j] = eps
+            fd = (L(base + e, B, m) - L(base - e, B, m)) / (2 * eps)
+            assert abs(db[i, j] - fd) <= 1e-6 * max(1.0, abs(fd)), (add_base, i, j, db[i, j], fd)
+        for (j, k) in [(0, 0), (2, 1), (4, 2)]:
+            e = np.zeros_like(B); e[j, k] = eps
+            fd = (L(base, B + e, m) - L(base, B - e, m)) / (2 * eps)
+            assert abs(dB[j, k] - fd) <= 1e-6 * max(1.0, abs(fd)), (add_base, j, k, dB[j, k], fd)
+        for j in range(out):
+            e = np.zeros_like(m); e[j] = eps
+            fd = (L(base, B, m + e) - L(base, B, m - e)) / (2 * eps)
+            assert abs(dm[j] - fd) <= 1e-6 * max(1.0, abs(fd)), (add_base, j, dm[j], fd)
+        tb = torch.tensor(base, requires_grad=True)
+        tB = torch.tensor(B, requires_grad=True)
+        tm = torch.tensor(m, requires_grad=True)
+        y = (tm / torch.tensor(n)) * (tb + s * (torch.tensor(h) @ tB.T))
+        if not add_base:
+            y = y - tb
+        (y * torch.tensor(dy)).sum().backward()
+        np.testing.assert_allclose(db, tb.grad.numpy(), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dm, tm.grad.numpy(), rtol=1e-12, atol=1e-13)
+    E = dy.T @ h
+    alt = (np.sum(dy * base, axis=0) + s * np.sum(B * E, axis=1)) / n
+    np.testing.assert_allclose(o.lora_compose_bwd(dy, base, h, B, m, n, s)[2], alt, rtol=1e-12)
+
+
 def pin_compose_bwd_finite_differences(o, seed=4):
     """Central differences of L = sum(dy * y); y is affine in m, base and lora, so
     the differences are exact up to rounding."""
@@ -352,6 +398,7 @@ ALL_PINS = [
     pin_compose_golden,
     pin_compose_closed_forms,
     pin_lora_compose_exact,
+    pin_lora_compose_bwd,
     pin_compose_bwd_finite_differences,
     pin_compose_bwd_autograd,
 ]

@@ -17,7 +17,8 @@ def test_oracle_pin(pin):
 def _mutant(**overrides):
     ns = types.SimpleNamespace(weight_norm=O.weight_norm, row_sqnorm=O.row_sqnorm,
                                weight_norm_cached=O.weight_norm_cached, compose_fwd=O.compose_fwd,
-                               lora_compose_fwd=O.lora_compose_fwd, compose_bwd=O.compose_bwd)
+                               lora_compose_fwd=O.lora_compose_fwd, lora_compose_bwd=O.lora_compose_bwd,
+                               compose_bwd=O.compose_bwd)
     for k, v in overrides.items():
         setattr(ns, k, v)
     return ns
@@ -97,6 +98,18 @@ MUTANTS = {
         base, _f(h) @ _f(B).T, m, n, s, False)),
     "lora_first_column_only": _mutant(lora_compose_fwd=lambda base, h, B, m, n, s, add_base=False: O.compose_fwd(
         base, np.outer(_f(h)[:, 0], _f(B)[:, 0]), m, n, s, add_base)),
+    "lora_bwd_dB_no_g": _mutant(lora_compose_bwd=lambda dy, base, h, B, m, n, s, add_base=False: (
+        O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[0],
+        float(s) * _f(dy).T @ _f(h), O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[2])),
+    "lora_bwd_dB_transposed_h": _mutant(lora_compose_bwd=lambda dy, base, h, B, m, n, s, add_base=False: (
+        O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[0],
+        (O.scale_factor(m, n) * float(s) * _f(dy)).T @ _f(h)[::-1], O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[2])),
+    "lora_bwd_dmag_drops_lora": _mutant(lora_compose_bwd=lambda dy, base, h, B, m, n, s, add_base=False: (
+        O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[0], O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[1],
+        np.sum(_f(dy) * _f(base), axis=0) / _f(n))),
+    "lora_bwd_dbase_g": _mutant(lora_compose_bwd=lambda dy, base, h, B, m, n, s, add_base=False: (
+        O.scale_factor(m, n) * _f(dy), O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[1],
+        O.lora_compose_bwd(dy, base, h, B, m, n, s, add_base)[2])),
     "fwd_no_minus_one": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, corr_one=False)),
     "fwd_drops_s": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, s_on_lora=False)),
     "fwd_inverted_g": _mutant(compose_fwd=lambda *a, add_base=False: _fwd(*a, add_base=add_base, invert=True)),
