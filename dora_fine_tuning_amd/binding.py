@@ -27,6 +27,8 @@ EXPORTS = (
     "dora_row_sqnorm",
     "dora_compose_fwd",
     "dora_lora_compose_fwd",
+    "dora_lora_compose_bwd_workspace_bytes",
+    "dora_lora_compose_bwd",
     "dora_compose_bwd_workspace_bytes",
     "dora_compose_bwd",
     "dora_last_error",
@@ -57,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.dora_compose_fwd.restype = i32
     lib.dora_lora_compose_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, vp]
     lib.dora_lora_compose_fwd.restype = i32
+    lib.dora_lora_compose_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dora_lora_compose_bwd_workspace_bytes.restype = sz
+    lib.dora_lora_compose_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, i64, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.dora_lora_compose_bwd.restype = i32
     lib.dora_compose_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.dora_compose_bwd_workspace_bytes.restype = sz
     lib.dora_compose_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -210,6 +216,41 @@ def dora_lora_compose_fwd(base, h, B, mag, norm, s: float, add_base: bool = Fals
     _check(LIB.dora_lora_compose_fwd(_ptr(base), _ptr(h), _ptr(B), _ptr(mag), _ptr(norm), float(s), T, out, r, code,
                                      int(bool(add_base)), _ptr(y), _stream(dev)))
     return y
+
+
+def dora_lora_compose_bwd_workspace_bytes(T: int, out: int, r: int) -> int:
+    return int(LIB.dora_lora_compose_bwd_workspace_bytes(T, out, r))
+
+
+def dora_lora_compose_bwd(dy, base, h, B, mag, norm, s: float, add_base: bool = False, d_base=None, d_B=None,
+                          d_mag=None, workspace=None, want_d_base: bool = True):
+    """(d_base, d_B, d_mag) of the fused compose; d_base is None if not wanted."""
+    code = _code(dy)
+    T, out = dy.shape
+    r = h.shape[1]
+    dev = dy.device
+    _matrix(base, "base", (T, out), dy.dtype, dev)
+    _matrix(h, "h", (T, r), dy.dtype, dev)
+    _matrix(B, "B", (out, r), dy.dtype, dev)
+    _matrix(mag, "mag", (out,), torch.float32, dev)
+    _matrix(norm, "norm", (out,), torch.float32, dev)
+    if d_base is None and want_d_base:
+        d_base = torch.empty_like(dy)
+    if d_B is None:
+        d_B = torch.empty_like(B)
+    if d_mag is None:
+        d_mag = torch.empty(out, dtype=torch.float32, device=dev)
+    if d_base is not None:
+        _matrix(d_base, "d_base", (T, out), dy.dtype, dev)
+    _matrix(d_B, "d_B", (out, r), dy.dtype, dev)
+    _matrix(d_mag, "d_mag", (out,), torch.float32, dev)
+    need = dora_lora_compose_bwd_workspace_bytes(T, out, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(LIB.dora_lora_compose_bwd(_ptr(dy), _ptr(base), _ptr(h), _ptr(B), _ptr(mag), _ptr(norm), float(s), T, out,
+                                     r, code, int(bool(add_base)), _ptr(d_base), _ptr(d_B), _ptr(d_mag),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return d_base, d_B, d_mag
 
 
 def dora_compose_bwd(dy, base, lora, mag, norm, s: float, add_base: bool = False, d_lora=None, d_base=None,

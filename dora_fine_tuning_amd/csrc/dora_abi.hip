@@ -196,6 +196,59 @@ int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const 
   return hip_status(dora::launch_lora_fwd(a, vec), fn);
 }
 
+size_t dora_lora_compose_bwd_workspace_bytes(int64_t T, int64_t out, int64_t r) {
+  if (T <= 0 || out <= 0 || r < 0) return 0;
+  return dora::lora_bwd_workspace_bytes(T, out, r);
+}
+
+int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const void* B, const float* mag,
+                          const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype, int add_base,
+                          void* d_base, void* d_B, float* d_mag, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "dora_lora_compose_bwd";
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (T < 0 || out < 0 || r < 0)
+    return fail(DORA_INVALID_ARG, "%s: negative size (T=%lld out=%lld r=%lld)", fn, (long long)T, (long long)out,
+                (long long)r);
+  if (out == 0) return ok();
+  if (!mag || !norm || !d_mag) return fail(DORA_INVALID_ARG, "%s: mag, norm or d_mag is NULL", fn);
+  if (T > 0 && (!dy || !base)) return fail(DORA_INVALID_ARG, "%s: dy or base is NULL", fn);
+  if (r > 0 && (!B || !d_B)) return fail(DORA_INVALID_ARG, "%s: B or d_B is NULL", fn);
+  if (T > 0 && r > 0 && !h) return fail(DORA_INVALID_ARG, "%s: h is NULL", fn);
+  const size_t mb = static_cast<size_t>(T) * out * 2, vb = static_cast<size_t>(out) * 4;
+  const size_t hb = static_cast<size_t>(T) * r * 2, bb = static_cast<size_t>(out) * r * 2;
+  const void* ins[6] = {dy, base, h, B, mag, norm};
+  const size_t insz[6] = {mb, mb, hb, bb, vb, vb};
+  const void* outs[3] = {d_base, d_B, d_mag};
+  const size_t outsz[3] = {mb, bb, vb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (any_overlap(outs[o], outsz[o], ins[i], insz[i]))
+        return fail(DORA_INVALID_ARG, "%s: an output overlaps an input", fn);
+    for (int q = o + 1; q < 3; ++q)
+      if (any_overlap(outs[o], outsz[o], outs[q], outsz[q])) return fail(DORA_INVALID_ARG, "%s: outputs overlap", fn);
+  }
+  const bool vec = T >= 1 && (out % 8 == 0) && (r % 8 == 0) && r >= 8 && r <= (int64_t(1) << 20) && aligned16(dy) &&
+                   aligned16(base) && aligned16(h) && aligned16(B) && (d_base == nullptr || aligned16(d_base)) &&
+                   aligned16(mag) && aligned16(norm) && aligned16(ws);
+  if (vec) {
+    const size_t need = dora::lora_bwd_workspace_bytes(T, out, r);
+    if (ws_bytes < need) return fail(DORA_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+    if (!ws) return fail(DORA_INVALID_ARG, "%s: workspace is NULL", fn);
+    for (int i = 0; i < 6; ++i)
+      if (any_overlap(ws, need, ins[i], insz[i])) return fail(DORA_INVALID_ARG, "%s: workspace overlaps an input", fn);
+    for (int o = 0; o < 3; ++o)
+      if (any_overlap(ws, need, outs[o], outsz[o]))
+        return fail(DORA_INVALID_ARG, "%s: workspace overlaps an output", fn);
+    if (dora::lora_bwd_max_slice_bytes(T, out, r) >= (int64_t(1) << 31))
+      return fail(DORA_UNSUPPORTED, "%s: T=%lld out=%lld r=%lld: a token slice spans 2 GiB or more", fn,
+                  (long long)T, (long long)out, (long long)r);
+  }
+  if (dora::lora_bwd_max_grid(T, out, r, vec) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "%s: out=%lld needs more workgroups than one launch holds", fn, (long long)out);
+  dora::LoraBwdArgs a{dtype, T, out, r, s, add_base ? 1 : 0, dy, base, h, B, mag, norm, d_base, d_B, d_mag, ws, stream};
+  return hip_status(dora::launch_lora_bwd(a, vec), fn);
+}
+
 size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out) {
   if (T <= 0 || out <= 0) return 0;
   return static_cast<size_t>((T + dora::kBwdRows - 1) / dora::kBwdRows) * static_cast<size_t>(out) * 4;

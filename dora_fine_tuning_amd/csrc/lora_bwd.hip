@@ -1,0 +1,530 @@
+// Backward of the compose with the adapter's second projection fused in, for
+// gfx950 (press summary of arXiv:2603.22276: the training tier runs a fused
+// backward; its gains come from fewer memory accesses).  With lora = h B^T
+// never stored, and L = sum(dy * y):
+//
+//   d_base = (g - 1) * dy  (g * dy with add_base)
+//   d_B    = (g * s * dy)^T h = g * s * E,            E = dy^T h   [out x r]
+//   d_mag  = (sum_t dy * base + s * sum_k B * E) / n      (sum_t dy lora = sum_k B E)
+//
+// so neither lora nor d_lora = g * s * dy is ever formed.
+//
+// Kernels:
+//   lora_bwd_dma      one pass over dy and base.  A workgroup owns 128 output
+//                     columns x a block of rank columns x a slice of the tokens.
+//                     K stages of 32 tokens: the dy rows (X panel) and h rows
+//                     (Y panel) go global -> LDS by DMA, and MFMA 32x32x16
+//                     contracts over the tokens, its fragments read with the
+//                     transposing LDS read (ds_read_b64_tr_b16, two per
+//                     fragment).  The same stage's dy rows also give d_base and
+//                     the column sums of dy * base (base loaded one stage
+//                     ahead).  The epilogue forms sum_k B E over its rank block
+//                     and writes its E slice and its column partials;
+//   lora_bwd_finalize_mag   d_mag from the partials, fp64, fixed order;
+//   lora_bwd_finalize_b     d_B = g * s * (sum of the E slices), fixed order;
+//   lora_bwd_general  (general path) one thread per output column, all sums in
+//                     order in fp32, lora per element by its r-term dot product.
+#include <algorithm>
+
+#include "dma_common.hpp"
+#include "dora_common.hpp"
+#include "lora_compose_kernels.hpp"
+
+namespace dora {
+
+namespace {
+
+__host__ __device__ inline int64_t bcdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Transposing LDS read: in each group of 16 lanes, source lane L gives an
+// 8-byte address (4 consecutive 16-bit elements of one row); result lane i
+// receives element i%4 of the source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+// With source lane L addressing row R0 + L/4 at column F(L%4), lane i gets the
+// 4 elements of column F(i/4) + i%4 in rows R0 .. R0 + 3.
+__device__ inline u32x2 lds_read_tr(uint32_t addr) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(static_cast<uintptr_t>(addr)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Tile: 128 output columns (X, 32*TM with TM = 4, WM = 2 waves along them) x
+// 128*TN rank columns (Y, WN = 4 waves along them); a wave owns TMW = 2 x TN
+// tiles of 32x32.  A K stage is 32 tokens: the X panel holds 32 dy rows of 128
+// columns (256 bytes), the Y panel 32 h rows of 128*TN rank columns.  Within
+// each 16-chunk (256-byte) group of a row, logical 16-byte chunk c of row t sits
+// in slot c ^ (4 * (t % 4)): the transposing reads touch 4 consecutive rows and
+// 2 chunks per row, and the 8 (row, chunk) pairs then fall in 8 distinct bank
+// groups.
+template <int TN_, int NS_>
+struct BwdTile {
+  static constexpr int TN = TN_, NS = NS_;
+  static constexpr int WM = 2, WN = 4, NW = 8, NT = 512, TM = 4, TMW = 2;
+  static constexpr int BM = 128, BN = 128 * TN, BK = 32;
+  static constexpr int XROWB = BM * 2, YROWB = BN * 2;  // bytes per token row
+  static constexpr int X_BYTES = BK * XROWB, Y_BYTES = BK * YROWB, STAGE_BYTES = X_BYTES + Y_BYTES;
+  static constexpr int XI = X_BYTES / 1024, YI = Y_BYTES / 1024;  // 1 KiB DMA blocks per stage
+  static constexpr int XQ = XI / NW, YQ = YI / NW, L = XQ + YQ;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NS >= 3 && (NS - 2) * L + 1 < 64, "ring depth and vmcnt range");
+};
+
+// slot of logical 16-byte chunk c in token row t (see BwdTile)
+__device__ inline int bwd_slot(int c, int t) { return (c & ~15) | ((c ^ (4 * (t & 3))) & 15); }
+
+struct BwdArgs {
+  const void *dy, *base, *h, *B;
+  const float *mag, *norm;
+  void* d_base;
+  float s;
+  int add_base;
+  int64_t T, out, r;
+  int nCB, nTiles, nSplit;
+  float* e_part;    // [nSplit][out][r]: the E slices
+  float* col_part;  // [nSplit][nTiles][out]: sum_t dy * base (tile 0 only) + s * sum_k B E
+};
+
+// Wait for the current stage's DMA while the younger loads already issued stay
+// in flight: n younger stages (at most NS-2) of L loads each, plus the one base
+// chunk issued after them.  Younger stores only make the wait longer.
+template <class TL, int N = TL::NS - 2>
+__device__ inline void bwd_wait(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<1>();
+  } else {
+    if (n >= N)
+      wait_vmcnt<N * TL::L + 1>();
+    else
+      bwd_wait<TL, N - 1>(n);
+  }
+}
+
+template <int DT, class TL>
+__global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
+  using V8 = typename Dt<DT>::V8;
+  using T16 = typename Dt<DT>::T;
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
+
+  const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
+  const uint32_t nCB = static_cast<uint32_t>(a.nCB), nTl = static_cast<uint32_t>(a.nTiles);
+  if (v >= nCB * nTl * static_cast<uint32_t>(a.nSplit)) return;
+  // consecutive workgroups share a token slice (one slice of h per XCD's L2)
+  const int nt = static_cast<int>(v % nTl);
+  const int cb = static_cast<int>((v / nTl) % nCB);
+  const int sp = static_cast<int>(v / (nTl * nCB));
+  const int64_t T = a.T, out = a.out, r = a.r;
+  const int64_t j0 = static_cast<int64_t>(cb) * TL::BM, k0 = static_cast<int64_t>(nt) * TL::BN;
+  const int64_t ts = T * sp / a.nSplit, te = T * (sp + 1) / a.nSplit;
+  const int S = static_cast<int>(bcdiv(te - ts, TL::BK));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const bool want_base = nt == 0;  // the elementwise part is done by the first rank block
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+
+  // buffer resources over the token slice; rows past it read zero
+  const int64_t rows = te - ts;
+  const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.dy) + ts * out * 2), static_cast<short>(0),
+      static_cast<int>(rows * out * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rbase = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.base) + ts * out * 2), static_cast<short>(0),
+      static_cast<int>(rows * out * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.h) + ts * r * 2), static_cast<short>(0),
+      static_cast<int>(rows * r * 2), kBufferWord3);
+
+  // Per-lane DMA offsets (stage 0).  Wave instruction q moves 1 KiB block
+  // b = q*NW + wave of its panel, lane l writing bytes 16l .. 16l + 15.  X: a
+  // block is 4 dy rows of 256 bytes, so lane l fills slot l%16 of row 4b + l/16
+  // and fetches the logical chunk that slot holds (bwd_slot is its own inverse
+  // within a 16-chunk group).  Y: linear 16-byte slot b*64 + l of the 32 x BN
+  // panel, row (b*64 + l) / (BN/8).
+  uint32_t xo[TL::XQ], yo[TL::YQ];
+  bool xok[TL::XQ], yok[TL::YQ];
+#pragma unroll
+  for (int q = 0; q < TL::XQ; ++q) {
+    const int b = q * TL::NW + wave;
+    const int t = 4 * b + (lane >> 4), sl = lane & 15;
+    const int c = bwd_slot(sl, t);  // the slot map is its own inverse within a group
+    const int64_t col = j0 + 8 * c;
+    xok[q] = col < out;
+    xo[q] = static_cast<uint32_t>((t * out + col) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < TL::YQ; ++q) {
+    const int b = q * TL::NW + wave;
+    const int lin = b * 64 + lane;
+    const int t = lin / (TL::BN / 8), sl = lin % (TL::BN / 8);
+    const int c = bwd_slot(sl, t);
+    const int64_t col = k0 + 8 * c;
+    yok[q] = col < r;
+    yo[q] = static_cast<uint32_t>((t * r + col) * 2);
+  }
+  const uint32_t xstep = static_cast<uint32_t>(TL::BK * out * 2), ystep = static_cast<uint32_t>(TL::BK * r * 2);
+  auto issue = [&](int st, int slot) {
+    char* so = smem + slot * TL::STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < TL::XQ; ++q)
+      dma16(rdy, so + (q * TL::NW + wave) * 1024, xok[q] ? xo[q] + static_cast<uint32_t>(st) * xstep : kOob);
+#pragma unroll
+    for (int q = 0; q < TL::YQ; ++q)
+      dma16(rh, so + TL::X_BYTES + (q * TL::NW + wave) * 1024, yok[q] ? yo[q] + static_cast<uint32_t>(st) * ystep : kOob);
+  };
+
+  // Fragment read addresses (within a stage slot; add the slot's offset).  In a
+  // 16-lane group g = l/16 (i = l%16), a read covers tokens R0 .. R0 + 3 with
+  // R0 = 16*step + 8*(g/2) (+ 4 for the second read of a fragment).  Y side
+  // (MFMA operand A, rank columns): result lane i must get rank column
+  // 32*kt + sigma(16*(g%2) + i), sigma(p) = 16*((p/4)%2) + 4*(p/8) + p%4, so that
+  // accumulator register q of lane l holds rank column 16*(l/32) + q; source
+  // lane L therefore addresses column 32*kt + 16*((L%4)%2) + 8*(g%2) + 4*((L%4)/2).
+  // X side (operand B, output columns): lane i gets column 32*jt + 16*(g%2) + i,
+  // so source lane L addresses column 32*jt + 16*(g%2) + 4*(L%4).
+  const int g = lane >> 4, L = lane & 15;
+  const int rsrc_row = 8 * (g >> 1) + (L >> 2);  // token row within a K step, first read
+  auto tr_addr = [&](uint32_t panel, int rowb, int row, int col) {
+    const int c = col >> 3;
+    return panel + static_cast<uint32_t>(row * rowb + bwd_slot(c, row) * 16 + (col & 7) * 2);
+  };
+  // per (step, read) the row differs; the column part is per tile
+  int ycol[TL::TN], xcol[TL::TMW];
+#pragma unroll
+  for (int j = 0; j < TL::TN; ++j)
+    ycol[j] = 32 * (wn * TL::TN + j) + 16 * ((L & 3) & 1) + 8 * (g & 1) + 4 * ((L & 3) >> 1);
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i) xcol[i] = 32 * (wm * TL::TMW + i) + 16 * (g & 1) + 4 * (L & 3);
+
+  f32x16 acc[TL::TMW][TL::TN];
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
+
+  // Elementwise part: thread tid takes token row tid/16 of each stage and the
+  // 8 output columns of chunk tid%16.
+  const int et = tid >> 4, ec = tid & 15;
+  const int64_t ecol = j0 + 8 * ec;
+  const bool eok = want_base && ecol < out;
+  float gb[8], colsum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    colsum[e] = 0.0f;
+    gb[e] = 0.0f;
+    if (eok) {
+      const float m = a.mag[ecol + e], n = a.norm[ecol + e];
+      gb[e] = a.add_base ? m / n : (m - n) / n;
+    }
+  }
+  T16* dbase = static_cast<T16*>(a.d_base);
+  // One buffer load per wave and stage, always issued (lanes with nothing to
+  // load use an out-of-range offset and read zero), so the vmcnt bookkeeping of
+  // the stage waits holds in every workgroup.
+  auto load_base = [&](int st) {
+    const int64_t t = static_cast<int64_t>(st) * TL::BK + et;  // within the slice
+    const uint32_t off = (eok && t < rows) ? static_cast<uint32_t>((t * out + ecol) * 2) : kOob;
+    return __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b128(rbase, off, 0, 0));
+  };
+
+  for (int u = 0; u < TL::NS - 1; ++u)
+    if (u < S) issue(u, u);
+  Chunk bnext = load_base(0);
+
+  int slot = 0;
+  for (int st = 0; st < S; ++st) {
+    bwd_wait<TL>(S - 1 - st);
+    __builtin_amdgcn_s_barrier();
+    if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, slot == 0 ? TL::NS - 1 : slot - 1);
+    const Chunk bcur = bnext;
+    if (st + 1 < S) bnext = load_base(st + 1);
+    const uint32_t xp = lds0 + static_cast<uint32_t>(slot * TL::STAGE_BYTES);
+    const uint32_t yp = xp + TL::X_BYTES;
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      const int row = 16 * step + rsrc_row;
+      u32x4 fx[TL::TMW], fy[TL::TN];
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i) {
+        const u32x2 lo = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
+        const u32x2 hi = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
+        fx[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) {
+        const u32x2 lo = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
+        const u32x2 hi = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
+        fy[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j)
+          acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
+    }
+    if (eok) {
+      const int64_t t = ts + static_cast<int64_t>(st) * TL::BK + et;
+      if (t < te) {
+        const u32x4 w = lds_read16(xp + static_cast<uint32_t>(et * TL::XROWB + bwd_slot(ec, et) * 16));
+        lds_wait();
+        u32x4 wt = w;
+        tie(wt);
+        float dyv[8], bv[8], o[8];
+        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wt), dyv);
+        chunk_to_f32<DT>(bcur, bv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[e] = gb[e] * dyv[e];
+          colsum[e] = __builtin_fmaf(dyv[e], bv[e], colsum[e]);
+        }
+        if (dbase) *reinterpret_cast<u32x4*>(dbase + t * out + ecol) = __builtin_bit_cast(u32x4, f32_to_chunk<DT>(o));
+      }
+    }
+    slot = slot == TL::NS - 1 ? 0 : slot + 1;
+  }
+
+  // Epilogue.  The ring is free once every wave is past its last read.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [32][128] column sums, then [WN][128] rank-block sums
+  // (1) s * sum_k B_jk E_jk over this rank block, per output column: lane l holds
+  // output column 32*(wm*TMW + i) + l%32 and rank columns 32*(wn*TN + j) + 16*(l/32) + q
+  const T16* Bp = static_cast<const T16*>(a.B);
+  const int frow = lane & 31, fh = lane >> 5;
+  float* ep = a.e_part + static_cast<int64_t>(sp) * out * r;
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i) {
+    const int jl = 32 * (wm * TL::TMW + i) + frow;
+    const int64_t j = j0 + jl;
+    float bsum = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < TL::TN; ++jj) {
+      const int64_t k = k0 + 32 * (wn * TL::TN + jj) + 16 * fh;
+      if (j < out && k < r) {
+        // k + 16 <= r: r % 8 == 0 and k % 16 == 0 give whole 8-column chunks;
+        // the second chunk is checked on its own
+        const bool hi = k + 8 < r;
+        const Chunk b0 = *reinterpret_cast<const Chunk*>(Bp + j * r + k);
+        const Chunk b1 = hi ? *reinterpret_cast<const Chunk*>(Bp + j * r + k + 8) : zero_chunk();
+        float bf[16];
+        chunk_to_f32<DT>(b0, *reinterpret_cast<float(*)[8]>(bf));
+        chunk_to_f32<DT>(b1, *reinterpret_cast<float(*)[8]>(bf + 8));
+        float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+          u0 = __builtin_fmaf(bf[q], acc[i][jj][q], u0);
+          u1 = __builtin_fmaf(bf[q + 1], acc[i][jj][q + 1], u1);
+        }
+        bsum += u0 + u1;
+        // this slice of E for d_B
+        float* dst = ep + j * r + k;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[i][jj][4], acc[i][jj][5], acc[i][jj][6], acc[i][jj][7]};
+        if (hi) {
+          *reinterpret_cast<f32x4*>(dst + 8) = f32x4{acc[i][jj][8], acc[i][jj][9], acc[i][jj][10], acc[i][jj][11]};
+          *reinterpret_cast<f32x4*>(dst + 12) =
+              f32x4{acc[i][jj][12], acc[i][jj][13], acc[i][jj][14], acc[i][jj][15]};
+        }
+      }
+    }
+    bsum += __shfl_xor(bsum, 32, 64);
+    if (fh == 0) red[32 * 128 + wn * 128 + jl] = bsum;
+  }
+  // (2) the column sums of dy * base over the slice: thread tid holds row tid/16
+  // of each stage and 8 columns
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[et * 128 + 8 * ec + e] = colsum[e];
+  __syncthreads();
+  if (tid < TL::BM && j0 + tid < out) {
+    float bs = 0.0f, cs = 0.0f;
+#pragma unroll
+    for (int w = 0; w < TL::WN; ++w) bs += red[32 * 128 + w * 128 + tid];
+    if (want_base)
+      for (int t = 0; t < 32; ++t) cs += red[t * 128 + tid];
+    a.col_part[(static_cast<int64_t>(sp) * nTl + nt) * out + j0 + tid] = cs + a.s * bs;
+  }
+}
+
+// d_mag_j = (sum of the column partials) / n_j in fp64.
+__global__ __launch_bounds__(256) void lora_bwd_finalize_mag(const float* col_part, int parts, int64_t out,
+                                                             const float* norm, float* d_mag) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= out) return;
+  double sum = 0.0;
+  for (int p = 0; p < parts; ++p) sum += static_cast<double>(col_part[static_cast<int64_t>(p) * out + j]);
+  d_mag[j] = static_cast<float>(sum / static_cast<double>(norm[j]));
+}
+
+// d_B[j][k] = (g_j * s) * sum of the E slices, the slices added in order in fp32.
+template <int DT>
+__global__ __launch_bounds__(256) void lora_bwd_finalize_b(const float* e_part, int nSplit, int64_t out, int64_t r,
+                                                           const float* mag, const float* norm, float s, void* d_B) {
+  using T16 = typename Dt<DT>::T;
+  const int64_t n = out * r;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t j = e / r;
+    float sum = 0.0f;
+    for (int p = 0; p < nSplit; ++p) sum += e_part[static_cast<int64_t>(p) * n + e];
+    const float gs = (mag[j] / norm[j]) * s;
+    static_cast<T16*>(d_B)[e] = Dt<DT>::from_f(gs * sum);
+  }
+}
+
+// General path: thread j owns output column j; everything in order in fp32.
+template <int DT>
+__global__ __launch_bounds__(256) void lora_bwd_general(BwdArgs a, void* d_B, float* d_mag) {
+  using T16 = typename Dt<DT>::T;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= a.out) return;
+  const T16* dy = static_cast<const T16*>(a.dy);
+  const T16* base = static_cast<const T16*>(a.base);
+  const T16* h = static_cast<const T16*>(a.h);
+  const T16* B = static_cast<const T16*>(a.B);
+  T16* db = static_cast<T16*>(a.d_base);
+  const float m = a.mag[j], n = a.norm[j];
+  const float gb = a.add_base ? m / n : (m - n) / n, gs = (m / n) * a.s;
+  float dm = 0.0f;
+  for (int64_t t = 0; t < a.T; ++t) {
+    const float d = Dt<DT>::to_f(dy[t * a.out + j]);
+    float l = 0.0f;
+    for (int64_t k = 0; k < a.r; ++k) l = __builtin_fmaf(Dt<DT>::to_f(h[t * a.r + k]), Dt<DT>::to_f(B[j * a.r + k]), l);
+    dm = __builtin_fmaf(d, Dt<DT>::to_f(base[t * a.out + j]) + a.s * l, dm);
+    if (db) db[t * a.out + j] = Dt<DT>::from_f(gb * d);
+  }
+  d_mag[j] = dm / n;
+  for (int64_t k = 0; k < a.r; ++k) {
+    float e = 0.0f;
+    for (int64_t t = 0; t < a.T; ++t) e = __builtin_fmaf(Dt<DT>::to_f(dy[t * a.out + j]), Dt<DT>::to_f(h[t * a.r + k]), e);
+    static_cast<T16*>(d_B)[j * a.r + k] = Dt<DT>::from_f(gs * e);
+  }
+}
+
+// Rank block width 128*TN (TN 1..3, least padding of r, then widest) and K splits.
+int bwd_tn(int64_t r) {
+  int best = 1;
+  int64_t best_pad = -1;
+  for (int tn = 1; tn <= 3; ++tn) {
+    const int64_t w = 128 * tn;
+    const int64_t pad = bcdiv(std::max<int64_t>(r, 1), w) * w;
+    if (best_pad < 0 || pad <= best_pad) {
+      best = tn;
+      best_pad = pad;
+    }
+  }
+  return best;
+}
+
+struct BwdPlan {
+  int tn = 1, nCB = 0, nTiles = 0, nSplit = 1;
+  size_t off_col = 0, bytes = 0;
+};
+
+BwdPlan bwd_plan(int64_t T, int64_t out, int64_t r, bool vec) {
+  BwdPlan p;
+  if (!vec) return p;
+  p.tn = bwd_tn(r);
+  p.nCB = static_cast<int>(bcdiv(out, 128));
+  p.nTiles = static_cast<int>(bcdiv(std::max<int64_t>(r, 1), 128 * p.tn));
+  const int64_t blocks = static_cast<int64_t>(p.nCB) * p.nTiles;
+  // about two workgroups' worth per CU of the 256, at least 8 stages of 32 tokens each
+  int64_t split = bcdiv(512, std::max<int64_t>(blocks, 1));
+  split = std::min<int64_t>(split, std::max<int64_t>(1, T / 256));
+  split = std::max<int64_t>(1, std::min<int64_t>(split, 64));
+  p.nSplit = static_cast<int>(split);
+  const size_t e_bytes = static_cast<size_t>(p.nSplit) * out * r * 4;
+  p.off_col = (e_bytes + 255) & ~static_cast<size_t>(255);
+  p.bytes = p.off_col + static_cast<size_t>(p.nSplit) * p.nTiles * out * 4;
+  return p;
+}
+
+template <int DT, int TN>
+void launch_bwd_dma(const BwdArgs& a, hipStream_t stream) {
+  using TL = BwdTile<TN, TN == 3 ? 4 : 5>;
+  const int64_t total = static_cast<int64_t>(a.nCB) * a.nTiles * a.nSplit;
+  hipLaunchKernelGGL((lora_bwd_dma<DT, TL>), dim3(static_cast<unsigned>(bcdiv(total, 8) * 8)), dim3(TL::NT), 0,
+                     stream, a);
+}
+
+}  // namespace
+
+size_t lora_bwd_workspace_bytes(int64_t T, int64_t out, int64_t r) {
+  if (T <= 0 || out <= 0) return 0;
+  return bwd_plan(T, out, r, true).bytes;
+}
+
+int64_t lora_bwd_max_grid(int64_t T, int64_t out, int64_t r, bool vec) {
+  if (!vec) return bcdiv(out, 256);
+  const BwdPlan p = bwd_plan(T, out, r, true);
+  return std::max<int64_t>(bcdiv(static_cast<int64_t>(p.nCB) * p.nTiles * p.nSplit, 8) * 8, bcdiv(out, 256));
+}
+
+int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r) {
+  const BwdPlan p = bwd_plan(T, out, r, true);
+  const int64_t rows = bcdiv(T, p.nSplit);
+  return rows * std::max<int64_t>(out, r) * 2;
+}
+
+hipError_t launch_lora_bwd(const LoraBwdArgs& p, bool vec) {
+  BwdArgs a{};
+  a.dy = p.dy;
+  a.base = p.base;
+  a.h = p.h;
+  a.B = p.B;
+  a.mag = p.mag;
+  a.norm = p.norm;
+  a.d_base = p.d_base;
+  a.s = p.s;
+  a.add_base = p.add_base;
+  a.T = p.T;
+  a.out = p.out;
+  a.r = p.r;
+  if (!vec) {
+    const dim3 grid(static_cast<unsigned>(bcdiv(p.out, 256)));
+    if (p.dtype == 0)
+      hipLaunchKernelGGL((lora_bwd_general<0>), grid, dim3(256), 0, p.stream, a, p.d_B, p.d_mag);
+    else
+      hipLaunchKernelGGL((lora_bwd_general<1>), grid, dim3(256), 0, p.stream, a, p.d_B, p.d_mag);
+    return hipGetLastError();
+  }
+  const BwdPlan plan = bwd_plan(p.T, p.out, p.r, true);
+  char* ws = static_cast<char*>(p.ws);
+  a.nCB = plan.nCB;
+  a.nTiles = plan.nTiles;
+  a.nSplit = plan.nSplit;
+  a.e_part = reinterpret_cast<float*>(ws);
+  a.col_part = reinterpret_cast<float*>(ws + plan.off_col);
+  if (p.dtype == 0) {
+    switch (plan.tn) {
+      case 1: launch_bwd_dma<0, 1>(a, p.stream); break;
+      case 2: launch_bwd_dma<0, 2>(a, p.stream); break;
+      default: launch_bwd_dma<0, 3>(a, p.stream); break;
+    }
+  } else {
+    switch (plan.tn) {
+      case 1: launch_bwd_dma<1, 1>(a, p.stream); break;
+      case 2: launch_bwd_dma<1, 2>(a, p.stream); break;
+      default: launch_bwd_dma<1, 3>(a, p.stream); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lora_bwd_finalize_mag, dim3(static_cast<unsigned>(bcdiv(p.out, 256))), dim3(256), 0, p.stream,
+                     a.col_part, plan.nSplit * plan.nTiles, p.out, p.norm, p.d_mag);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.r > 0) {
+    const int64_t blocks = std::min<int64_t>(bcdiv(p.out * p.r, 256), 4096);
+    if (p.dtype == 0)
+      hipLaunchKernelGGL((lora_bwd_finalize_b<0>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream,
+                         a.e_part, plan.nSplit, p.out, p.r, p.mag, p.norm, p.s, p.d_B);
+    else
+      hipLaunchKernelGGL((lora_bwd_finalize_b<1>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream,
+                         a.e_part, plan.nSplit, p.out, p.r, p.mag, p.norm, p.s, p.d_B);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dora

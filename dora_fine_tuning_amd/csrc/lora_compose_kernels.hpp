@@ -23,4 +23,27 @@ int64_t lora_fwd_max_grid(int64_t T, int64_t out, bool vec);
 // vec: out % 8 == 0, r % 8 == 0, r <= 2^20 and every pointer 16-byte aligned.
 hipError_t launch_lora_fwd(const LoraFwdArgs& a, bool vec);
 
+struct LoraBwdArgs {
+  int dtype;
+  int64_t T, out, r;
+  float s;
+  int add_base;
+  const void *dy, *base, *h, *B;
+  const float *mag, *norm;
+  void* d_base;  // may be null
+  void* d_B;
+  float* d_mag;
+  void* ws;
+  hipStream_t stream;
+};
+
+// Workspace of the 16-byte path (the E slices and the column partials).
+size_t lora_bwd_workspace_bytes(int64_t T, int64_t out, int64_t r);
+int64_t lora_bwd_max_grid(int64_t T, int64_t out, int64_t r, bool vec);
+// Largest byte range one token slice's buffer resource spans (must stay below 2^31).
+int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r);
+
+// vec: out % 8 == 0, r % 8 == 0, 1 <= r <= 2^20, T >= 1, every pointer 16-byte aligned.
+hipError_t launch_lora_bwd(const LoraBwdArgs& a, bool vec);
+
 }  // namespace dora

@@ -24,6 +24,8 @@
  * from: fewer memory accesses):
  *
  *   dora_lora_compose_fwd      y = (g-1)*base + g*s*(h*B^T), h = x*A^T;
+ *   dora_lora_compose_bwd      its backward: d_base, d_B and d_mag from dy,
+ *                              base and h, without lora or d_lora;
  *
  * and, for the cached base norm the page lists as future work (W0 is frozen):
  *
@@ -174,6 +176,35 @@ DORA_API int dora_compose_fwd(const void* base, const void* lora, const float* m
 DORA_API int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const float* mag,
                                    const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype,
                                    int add_base, void* y, hipStream_t stream);
+
+/* Bytes of device workspace dora_lora_compose_bwd needs (fp32 slices of dy^T h and column partials). */
+DORA_API size_t dora_lora_compose_bwd_workspace_bytes(int64_t T, int64_t out, int64_t r);
+
+/*
+ * Backward of dora_lora_compose_fwd for L = sum(dy * y), with norm held
+ * constant, never forming lora or d_lora = g * s * dy:
+ *   d_base = (g - 1) * dy         (add_base == 0)
+ *          = g * dy               (add_base != 0)
+ *   d_B    = (g * s * dy)^T h = g * s * (dy^T h)       [out x r]
+ *   d_mag_j = (sum_t dy_tj * base_tj + s * sum_k B_jk (dy^T h)_jk) / norm_j,
+ * which equals sum_t dy_tj * (base_tj + s * (h B^T)_tj) / norm_j (summary page:
+ * the training tier's fused backward; gains from fewer memory accesses).
+ * dy^T h is an MFMA contraction over the tokens with fp32 accumulation, its
+ * token slices added in a fixed order; d_mag sums its partials in fp64.  The
+ * gradient of h, d_lora * B = dy * (g * s * B), is the caller's GEMM.
+ *
+ * dy, base, d_base: device, dtype, [T x out]; d_base may be NULL (not
+ * computed).  h: [T x r]; B, d_B: [out x r].  mag, norm, d_mag: device fp32
+ * [out].  No output may overlap an input or another output.  ws: at least
+ * dora_lora_compose_bwd_workspace_bytes(T, out, r) bytes on the fast path
+ * (out and r multiples of 8, 8 <= r <= 2^20, T >= 1, 16-byte aligned
+ * pointers); other cases take a slow path (one thread per output column) and
+ * need no workspace.  out == 0 is a no-op; T == 0 gives d_B = 0 and d_mag = 0.
+ */
+DORA_API int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const void* B, const float* mag,
+                                   const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype,
+                                   int add_base, void* d_base, void* d_B, float* d_mag, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* Bytes of device workspace dora_compose_bwd needs (per-token-block fp32 partial sums). */
 DORA_API size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out);

@@ -171,6 +171,32 @@ def test_lora_compose_fwd_validation():
     assert LIB.dora_lora_compose_fwd(None, None, None, None, None, 1.0, 16, 0, 8, 0, 0, None, None) == OK
 
 
+def test_lora_compose_bwd_validation():
+    T, out, r = 64, 16, 8
+    ws = LIB.dora_lora_compose_bwd_workspace_bytes(T, out, r)
+    assert ws > 0
+
+    def call(dy=P, base=P * 2, h=P * 3, B=P * 4, mag=P * 5, norm=P * 6, d_base=P * 7, d_B=P * 8, d_mag=P * 9,
+             w=P * 10, ws_bytes=ws, dtype=0, T=T):
+        return LIB.dora_lora_compose_bwd(dy, base, h, B, mag, norm, 1.0, T, out, r, dtype, 0, d_base, d_B, d_mag, w,
+                                         ws_bytes, None)
+
+    _status(call(dtype=3), UNSUPPORTED, "dtype")
+    _status(call(T=-1), INVALID, "negative")
+    _status(call(d_mag=None), INVALID, "d_mag")
+    _status(call(base=None), INVALID, "dy or base")
+    _status(call(B=None), INVALID, "B or d_B")
+    _status(call(h=None), INVALID, "h is NULL")
+    _status(call(d_base=P + 2), INVALID, "overlaps an input")
+    _status(call(d_B=P * 7 + 4), INVALID, "outputs overlap")
+    _status(call(ws_bytes=ws - 16), INVALID, "workspace of")
+    _status(call(w=None), INVALID, "workspace is NULL")
+    _status(call(w=P * 2), INVALID, "workspace overlaps")
+    assert LIB.dora_lora_compose_bwd(None, None, None, None, None, None, 1.0, 8, 0, 8, 0, 0, None, None, None, None, 0,
+                                     None) == OK
+    assert LIB.dora_lora_compose_bwd_workspace_bytes(0, 8, 8) == 0
+
+
 def test_compose_rejects_grids_beyond_one_launch():
     # 2^36 tokens of 8 columns: the forward would need 2^34 workgroups.  Far-apart
     # fake pointers keep the overlap checks quiet; nothing is launched.
