@@ -272,7 +272,25 @@ def main():
                  "fused_frac_hbm_peak": round(fb / (f_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                  "fused_tflops": round(ff / (f_us * 1e-6) / 1e12, 1),
                  "reps": args.fused_reps}
-        del y2, lora2
+        # Its backward: d_base, d_B = g s (dy^T h) and d_mag in one pass over dy
+        # and base, against the unfused backward (the compose backward reading a
+        # stored lora and writing d_lora, then torch's GEMM d_B = d_lora^T h).
+        db2, dB2, dm2 = torch.empty_like(base), torch.empty_like(B), torch.empty_like(mag)
+        dl2 = torch.empty_like(base)
+        ws_lb = torch.empty(max(binding.dora_lora_compose_bwd_workspace_bytes(T, out, r), 1), dtype=torch.uint8,
+                            device=dev)
+        torch.mm(h, B.t(), out=lora2)
+        fbw_us = timed(lambda: binding.dora_lora_compose_bwd(dy, base, h, B, mag, norm, s, d_base=db2, d_B=dB2,
+                                                             d_mag=dm2, workspace=ws_lb))
+        ubw_us = timed(lambda: (binding.dora_compose_bwd(dy, base, lora2, mag, norm, s, d_lora=dl2, d_base=db2,
+                                                         d_mag=dm2, workspace=ws_bwd),
+                                torch.mm(dl2.t(), h, out=dB2)))
+        bb = 3 * 2 * T * out + 2 * (T * r + 2 * out * r) + 12 * out
+        fused["bwd"] = {"fused_us": round(fbw_us, 2), "unfused_us": round(ubw_us, 2), "algorithmic_bytes": bb,
+                        "flops": ff, "fused_gbs": round(bb / (fbw_us * 1e-6) / 1e9, 1),
+                        "fused_frac_hbm_peak": round(bb / (fbw_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "fused_tflops": round(ff / (fbw_us * 1e-6) / 1e12, 1)}
+        del y2, lora2, db2, dB2, dm2, dl2, ws_lb
 
     # The same compose forward + backward driven through the PyTorch custom
     # operator and autograd (dora_amd::compose), against the direct calls above.
