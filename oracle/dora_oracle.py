@@ -32,6 +32,13 @@ with numbers; it names the operations:
   weight norm with its base term taken from a given cache c instead of W0,
   n_i^2 = c_i + (||W0_i + s*(BA)_i||^2 - ||W0_i||^2), the difference written
   out densely as 2s<W0_i, (BA)_i> + s^2 ||(BA)_i||^2.
+* the backward of the weight norm itself, for a caller that does not detach
+  n (the page is silent on whether the norm is differentiated; the detached
+  reading is the main one, this is the alternative).  ``weight_norm_bwd``
+  gives the gradients of L = sum_i dn_i * n_i with respect to A and B (W0 is
+  frozen), written from the dense definition: with V = W0 + s*B*A and
+  n_i = ||V_i||, dn_i/dV_i = V_i / n_i, so dV = (dn/n) * V row-wise,
+  d_B = s * dV A^T and d_A = s * B^T dV.
 
 Everything is computed in fp64 from the exact values of the inputs: bf16/fp16
 tensors and fp32 vectors convert to fp64 without rounding, and ``s`` is the fp32
@@ -93,6 +100,28 @@ def weight_norm_cached(base_sq, W0, A, B, s) -> np.ndarray:
     V = B @ A
     n2 = c + 2.0 * s * np.sum(W0 * V, axis=1) + s * s * np.sum(V * V, axis=1)
     return np.sqrt(np.maximum(n2, 0.0))
+
+
+def weight_norm_bwd(d_norm, norm, W0, A, B, s):
+    """Gradients of L = sum_i d_norm_i * n_i with respect to A and B, where
+    n_i = || W0_i + s * (B A)_i ||_2 and W0 is frozen.
+
+    Chain rule through the dense definition: V = W0 + s * B A, dn_i/dV_i =
+    V_i / n_i, so dV = (d_norm / norm)[:, None] * V; then d_B = s * dV A^T
+    [out x r] and d_A = s * B^T dV [r x in].  ``norm`` is the n the caller
+    holds (the forward's fp32 result, or any positive values): it is used as
+    given, not recomputed.  Rows with n_i = 0 give no gradient (the zero
+    subgradient, which is what a library norm's backward takes at 0).
+    d_norm, norm: [out].  Returns fp64 (d_A [r x in], d_B [out x r]).
+    """
+    W0, A, B = as_f64(W0), as_f64(A), as_f64(B)
+    d, n = as_f64(d_norm), as_f64(norm)
+    s = float(s)
+    c = np.zeros_like(n)
+    nz = n != 0.0
+    c[nz] = d[nz] / n[nz]
+    dV = c[:, None] * (W0 + s * (B @ A))  # the out x in matrix the GPU path never forms
+    return s * (B.T @ dV), s * (dV @ A.T)
 
 
 def scale_factor(m, n) -> np.ndarray:

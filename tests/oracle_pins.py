@@ -1,7 +1,8 @@
 """Pins of the CPU oracle to facts other than itself.
 
 Each ``pin_*`` takes an object with the oracle's functions (``weight_norm``,
-``row_sqnorm``, ``weight_norm_cached``, ``compose_fwd``, ``compose_bwd``) and
+``row_sqnorm``, ``weight_norm_cached``, ``compose_fwd``, ``compose_bwd``,
+``lora_compose_fwd``, ``lora_compose_bwd``, ``weight_norm_bwd``) and
 raises AssertionError
 when the oracle disagrees with:
 
@@ -388,6 +389,104 @@ def pin_compose_bwd_autograd(o, seed=5):
     assert dl.shape == (0, 6) and np.all(dm == 0)
 
 
+# ------------------------------------------------------------------ norm backward
+
+
+def _norm_bwd_fraction_factored(d, n, W0, A, B, s):
+    """The factored gradients, exactly: c_i = d_i / n_i,
+    d_B_i = s c_i (U_i + s B_i G) with U = W0 A^T, G = A A^T, and
+    d_A = s (c B)^T W0 + s^2 (B^T diag(c) B) A."""
+    out, inn = W0.shape
+    r = A.shape[0]
+    F = lambda M: [[Fraction(float(v)) for v in row] for row in M]
+    W, Af, Bf = F(W0), F(A), F(B)
+    c = [Fraction(float(di)) / Fraction(float(ni)) for di, ni in zip(d, n)]
+    sf = Fraction(float(s))
+    G = [[sum(Af[j][k] * Af[l][k] for k in range(inn)) for l in range(r)] for j in range(r)]
+    U = [[sum(W[i][k] * Af[j][k] for k in range(inn)) for j in range(r)] for i in range(out)]
+    dB = [[sf * c[i] * (U[i][j] + sf * sum(Bf[i][l] * G[l][j] for l in range(r))) for j in range(r)]
+          for i in range(out)]
+    M = [[sum(Bf[i][j] * c[i] * Bf[i][l] for i in range(out)) for l in range(r)] for j in range(r)]
+    dA = [[sf * sum(c[i] * Bf[i][j] * W[i][k] for i in range(out))
+           + sf * sf * sum(M[j][l] * Af[l][k] for l in range(r)) for k in range(inn)] for j in range(r)]
+    return dA, dB
+
+
+def pin_norm_bwd(o, seed=10):
+    """weight_norm_bwd against: exact rational arithmetic of the factored
+    formulas (a different formula from the oracle's dense chain rule); central
+    finite differences of weight_norm (itself pinned above); torch.autograd in
+    fp64 through torch's own vector norm; the bilinearity identity
+    <A, d_A> = <B, d_B> (V depends on A and B only through B A, so scaling
+    either by t moves V alike); and B = 0 and r = 1 closed forms."""
+    rng = np.random.default_rng(seed)
+    # exact rational check on bf16-exact inputs with an arbitrary positive n
+    for out, inn, r in [(3, 5, 2), (4, 3, 3)]:
+        W0 = _bf16_exact(rng, (out, inn), 0.5)
+        A = _bf16_exact(rng, (r, inn), 0.5)
+        B = _bf16_exact(rng, (out, r), 0.5)
+        d = _bf16_exact(rng, (out,), 1.0)
+        n = np.abs(_bf16_exact(rng, (out,), 1.0)) + 0.25
+        s = 1.5
+        dA, dB = (np.asarray(x, np.float64) for x in o.weight_norm_bwd(d, n, W0, A, B, s))
+        assert dA.shape == (r, inn) and dB.shape == (out, r)
+        eA, eB = _norm_bwd_fraction_factored(d, n, W0, A, B, s)
+        for got, exact in ((dA, eA), (dB, eB)):
+            ex = np.array([[float(v) for v in row] for row in exact])
+            np.testing.assert_allclose(got, ex, rtol=1e-12, atol=1e-14)
+    # finite differences of the (pinned) forward norm, with the true n
+    out, inn, r = 5, 6, 3
+    W0 = rng.standard_normal((out, inn))
+    A = rng.standard_normal((r, inn)) * 0.7
+    B = rng.standard_normal((out, r)) * 0.7
+    d = rng.standard_normal(out)
+    s = 0.8
+    n = o.weight_norm(W0, A, B, s)
+    dA, dB = o.weight_norm_bwd(d, n, W0, A, B, s)
+    L = lambda A_, B_: float(np.sum(d * o.weight_norm(W0, A_, B_, s)))
+    eps = 1e-6
+    for (j, k) in [(0, 0), (1, 4), (2, 5)]:
+        e = np.zeros_like(A); e[j, k] = eps
+        fd = (L(A + e, B) - L(A - e, B)) / (2 * eps)
+        assert abs(dA[j, k] - fd) <= 1e-7 * max(1.0, abs(fd)), (j, k, dA[j, k], fd)
+    for (i, j) in [(0, 0), (2, 1), (4, 2)]:
+        e = np.zeros_like(B); e[i, j] = eps
+        fd = (L(A, B + e) - L(A, B - e)) / (2 * eps)
+        assert abs(dB[i, j] - fd) <= 1e-7 * max(1.0, abs(fd)), (i, j, dB[i, j], fd)
+    # torch autograd through torch's vector norm
+    tA = torch.tensor(A, requires_grad=True)
+    tB = torch.tensor(B, requires_grad=True)
+    tn = torch.linalg.vector_norm(torch.tensor(W0) + s * (tB @ tA), dim=1)
+    (tn * torch.tensor(d)).sum().backward()
+    np.testing.assert_allclose(dA, tA.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-13)
+    # bilinearity: <A, d_A> = <B, d_B>
+    a, b = float(np.sum(A * dA)), float(np.sum(B * dB))
+    assert abs(a - b) <= 1e-12 * (abs(a) + abs(b) + 1e-300), (a, b)
+    # B = 0: d_A = 0 and d_B_i = s (d_i / n_i) W0_i A^T; n = ||W0_i|| (library norm)
+    Bz = np.zeros_like(B)
+    nz = np.linalg.norm(W0, axis=1)
+    dA0, dB0 = o.weight_norm_bwd(d, nz, W0, A, Bz, s)
+    assert np.all(np.asarray(dA0) == 0.0)
+    np.testing.assert_allclose(dB0, s * (d / nz)[:, None] * (W0 @ A.T), rtol=1e-13, atol=1e-15)
+    # r = 1: d_B_i = s c_i (w_i . a + s b_i |a|^2), d_A = s sum_i c_i b_i (w_i + s b_i a)
+    a1 = rng.standard_normal((1, inn))
+    b1 = rng.standard_normal((out, 1))
+    n1 = o.weight_norm(W0, a1, b1, s)
+    c = d / n1
+    dA1, dB1 = o.weight_norm_bwd(d, n1, W0, a1, b1, s)
+    ref_B = s * c * (W0 @ a1[0] + s * b1[:, 0] * np.dot(a1[0], a1[0]))
+    ref_A = s * np.sum((c * b1[:, 0])[:, None] * (W0 + s * b1[:, 0][:, None] * a1[0][None, :]), axis=0)
+    np.testing.assert_allclose(np.asarray(dB1)[:, 0], ref_B, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.asarray(dA1)[0], ref_A, rtol=1e-12, atol=1e-14)
+    # a zero norm row contributes nothing
+    n0 = n.copy(); n0[1] = 0.0
+    dA2, dB2 = o.weight_norm_bwd(d, n0, W0, A, B, s)
+    assert np.all(np.asarray(dB2)[1] == 0.0) and np.all(np.isfinite(dA2))
+    d_one = d.copy(); d_one[1] = 0.0
+    np.testing.assert_allclose(dA2, o.weight_norm_bwd(d_one, n, W0, A, B, s)[0], rtol=1e-13, atol=1e-15)
+
+
 ALL_PINS = [
     pin_norm_exact_bruteforce,
     pin_norm_special_cases,
@@ -401,4 +500,5 @@ ALL_PINS = [
     pin_lora_compose_bwd,
     pin_compose_bwd_finite_differences,
     pin_compose_bwd_autograd,
+    pin_norm_bwd,
 ]

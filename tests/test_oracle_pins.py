@@ -18,7 +18,7 @@ def _mutant(**overrides):
     ns = types.SimpleNamespace(weight_norm=O.weight_norm, row_sqnorm=O.row_sqnorm,
                                weight_norm_cached=O.weight_norm_cached, compose_fwd=O.compose_fwd,
                                lora_compose_fwd=O.lora_compose_fwd, lora_compose_bwd=O.lora_compose_bwd,
-                               compose_bwd=O.compose_bwd)
+                               compose_bwd=O.compose_bwd, weight_norm_bwd=O.weight_norm_bwd)
     for k, v in overrides.items():
         setattr(ns, k, v)
     return ns
@@ -69,7 +69,25 @@ def _bwd(dy, base, lora, m, n, s, add_base=False, *, div_n=True, lora_sign=1.0, 
     return d_lora, d_base, d_mag
 
 
+def _nbwd(d, n, W0, A, B, s, *, s_on_dB=True, use_adapter=True, n_pow=1, sign=1.0, dA_rows_reversed=False,
+          dA_gram=True):
+    d, n, W0, A, B = _f(d), _f(n), _f(W0), _f(A), _f(B)
+    s = float(s)
+    c = d / n ** n_pow
+    dV = c[:, None] * (W0 + (sign * s * (B @ A) if use_adapter else 0.0))
+    dVa = c[:, None] * (W0 + (s * (B @ A) if dA_gram else 0.0))
+    dA = s * (B.T @ (dVa[::-1] if dA_rows_reversed else dVa))
+    dB = (s if s_on_dB else 1.0) * (dV @ A.T)
+    return dA, dB
+
+
 MUTANTS = {
+    "nbwd_dB_drops_s": _mutant(weight_norm_bwd=lambda *a: _nbwd(*a, s_on_dB=False)),
+    "nbwd_W0_for_V": _mutant(weight_norm_bwd=lambda *a: _nbwd(*a, use_adapter=False)),
+    "nbwd_divides_by_n_squared": _mutant(weight_norm_bwd=lambda *a: _nbwd(*a, n_pow=2)),
+    "nbwd_minus_adapter": _mutant(weight_norm_bwd=lambda *a: _nbwd(*a, sign=-1.0)),
+    "nbwd_dA_rows_misaligned": _mutant(weight_norm_bwd=lambda *a: _nbwd(*a, dA_rows_reversed=True)),
+    "nbwd_dA_drops_gram": _mutant(weight_norm_bwd=lambda *a: _nbwd(*a, dA_gram=False)),
     "norm_drops_s": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, 1.0)),
     "norm_minus_adapter": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, s, sign=-1.0)),
     "norm_s_squared": _mutant(weight_norm=lambda W0, A, B, s: _norm_dense(W0, A, B, s, s_pow=2)),
@@ -130,6 +148,9 @@ def test_mutant_helpers_match_oracle_when_unmutated():
     np.testing.assert_allclose(_norm_dense(W0, A, B, 1.3), O.weight_norm(W0, A, B, 1.3), rtol=1e-15)
     c = rng.uniform(1, 3, 5)
     np.testing.assert_allclose(_cached(c, W0, A, B, 1.3), O.weight_norm_cached(c, W0, A, B, 1.3), rtol=1e-15)
+    d, n5 = rng.standard_normal(5), rng.uniform(1, 2, 5)
+    for x, y in zip(_nbwd(d, n5, W0, A, B, 1.3), O.weight_norm_bwd(d, n5, W0, A, B, 1.3)):
+        np.testing.assert_allclose(x, y, rtol=1e-14)
     base, lora, dy = rng.standard_normal((3, (4))), rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
     m, n = rng.uniform(1, 2, 4), rng.uniform(1, 2, 4)
     for ab in (False, True):
