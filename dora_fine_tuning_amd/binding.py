@@ -31,6 +31,8 @@ EXPORTS = (
     "dora_lora_compose_bwd",
     "dora_compose_bwd_workspace_bytes",
     "dora_compose_bwd",
+    "dora_norm_bwd_workspace_bytes",
+    "dora_norm_bwd",
     "dora_last_error",
     "dora_version",
 )
@@ -67,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.dora_compose_bwd_workspace_bytes.restype = sz
     lib.dora_compose_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.dora_compose_bwd.restype = i32
+    lib.dora_norm_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.dora_norm_bwd_workspace_bytes.restype = sz
+    lib.dora_norm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, vp, sz, vp]
+    lib.dora_norm_bwd.restype = i32
     lib.dora_last_error.argtypes = []
     lib.dora_last_error.restype = ctypes.c_char_p
     lib.dora_version.argtypes = []
@@ -280,3 +286,33 @@ def dora_compose_bwd(dy, base, lora, mag, norm, s: float, add_base: bool = False
                                 int(bool(add_base)), _ptr(d_lora), _ptr(d_base), _ptr(d_mag), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
     return d_lora, d_base, d_mag
+
+
+def dora_norm_bwd_workspace_bytes(out: int, in_: int, r: int, dtype=torch.bfloat16) -> int:
+    return int(LIB.dora_norm_bwd_workspace_bytes(out, in_, r, DTYPE_CODE.get(dtype, -1)))
+
+
+def dora_norm_bwd(W0, A, B, norm, d_norm, s: float, d_A=None, d_B=None, workspace=None):
+    """(d_A, d_B): the gradients of sum(d_norm * n) with respect to A and B,
+    n = the weight norm of W0 + s B A (norm: the forward's n)."""
+    code = _code(W0)
+    out, in_ = W0.shape
+    r = A.shape[0]
+    dev = W0.device
+    _matrix(A, "A", (r, in_), W0.dtype, dev)
+    _matrix(B, "B", (out, r), W0.dtype, dev)
+    _matrix(norm, "norm", (out,), torch.float32, dev)
+    _matrix(d_norm, "d_norm", (out,), torch.float32, dev)
+    if d_A is None:
+        d_A = torch.empty_like(A)
+    if d_B is None:
+        d_B = torch.empty_like(B)
+    _matrix(d_A, "d_A", (r, in_), W0.dtype, dev)
+    _matrix(d_B, "d_B", (out, r), W0.dtype, dev)
+    need = dora_norm_bwd_workspace_bytes(out, in_, r, W0.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(LIB.dora_norm_bwd(_ptr(W0), _ptr(A), _ptr(B), _ptr(norm), _ptr(d_norm), out, in_, r, float(s), code,
+                             _ptr(d_A), _ptr(d_B), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(dev)))
+    return d_A, d_B

@@ -10,6 +10,7 @@
 #include "../../include/dora.h"
 #include "compose_kernels.hpp"
 #include "lora_compose_kernels.hpp"
+#include "norm_bwd_kernels.hpp"
 #include "norm_kernels.hpp"
 
 #ifndef DORA_VERSION_STRING
@@ -247,6 +248,55 @@ int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const
     return fail(DORA_UNSUPPORTED, "%s: out=%lld needs more workgroups than one launch holds", fn, (long long)out);
   dora::LoraBwdArgs a{dtype, T, out, r, s, add_base ? 1 : 0, dy, base, h, B, mag, norm, d_base, d_B, d_mag, ws, stream};
   return hip_status(dora::launch_lora_bwd(a, vec), fn);
+}
+
+size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
+  if (out < 0 || in < 0 || r < 0 || !valid_dtype(dtype)) return 0;
+  return dora::make_norm_bwd_plan(out, in, r, dtype).bytes;
+}
+
+int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* norm, const float* d_norm, int64_t out,
+                  int64_t in, int64_t r, float s, int dtype, void* d_A, void* d_B, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  const char* fn = "dora_norm_bwd";
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (out < 0 || in < 0 || r < 0)
+    return fail(DORA_INVALID_ARG, "%s: negative size (out=%lld in=%lld r=%lld)", fn, (long long)out, (long long)in,
+                (long long)r);
+  if (r == 0) return ok();
+  if (in > 0 && (!A || !d_A)) return fail(DORA_INVALID_ARG, "%s: A or d_A is NULL", fn);
+  if (out > 0 && (!B || !d_B || !norm || !d_norm)) return fail(DORA_INVALID_ARG, "%s: B, d_B, norm or d_norm is NULL", fn);
+  if (out > 0 && in > 0 && !W0) return fail(DORA_INVALID_ARG, "%s: W0 is NULL", fn);
+  if (in % 8 != 0 || r % 8 != 0 || in >= (int64_t(1) << 21) || r > (int64_t(1) << 20))
+    return fail(DORA_UNSUPPORTED, "%s: needs in and r multiples of 8, in < 2^21, r <= 2^20 (in=%lld r=%lld)", fn,
+                (long long)in, (long long)r);
+  if (!aligned16(W0) || !aligned16(A) || !aligned16(B) || !aligned16(d_A) || !aligned16(d_B) || !aligned16(ws))
+    return fail(DORA_UNSUPPORTED, "%s: matrix and workspace pointers must be 16-byte aligned", fn);
+  const dora::NormBwdPlan plan = dora::make_norm_bwd_plan(out, in, r, dtype);
+  const size_t need = plan.bytes;
+  if (ws_bytes < need) return fail(DORA_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "%s: workspace is NULL", fn);
+  const size_t e = 2, vb = static_cast<size_t>(out) * 4;
+  const void* ins[5] = {W0, A, B, norm, d_norm};
+  const size_t insz[5] = {out * in * e, r * in * e, out * r * e, vb, vb};
+  const void* outs[3] = {d_A, d_B, ws};
+  const size_t outsz[3] = {r * in * e, out * r * e, need};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (any_overlap(outs[o], outsz[o], ins[i], insz[i]))
+        return fail(DORA_INVALID_ARG, "%s: an output or the workspace overlaps an input", fn);
+    for (int q = o + 1; q < 3; ++q)
+      if (any_overlap(outs[o], outsz[o], outs[q], outsz[q]))
+        return fail(DORA_INVALID_ARG, "%s: outputs or the workspace overlap", fn);
+  }
+  if (plan.max_grid > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "%s: out=%lld in=%lld r=%lld needs more workgroups than one launch holds", fn,
+                (long long)out, (long long)in, (long long)r);
+  if (plan.max_slice_bytes >= (int64_t(1) << 31))
+    return fail(DORA_UNSUPPORTED, "%s: out=%lld in=%lld r=%lld: a row slice spans 2 GiB or more", fn, (long long)out,
+                (long long)in, (long long)r);
+  dora::NormBwdArgs a{dtype, W0, A, B, norm, d_norm, s, d_A, d_B, ws, stream};
+  return hip_status(dora::launch_norm_bwd(plan, a), fn);
 }
 
 size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out) {

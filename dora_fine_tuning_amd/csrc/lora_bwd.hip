@@ -86,6 +86,7 @@ struct BwdArgs {
   int nCB, nTiles, nSplit;
   float* e_part;    // [nSplit][out][r]: the E slices
   float* col_part;  // [nSplit][nTiles][out]: sum_t dy * base (tile 0 only) + s * sum_k B E
+  int pure;         // plain contraction E = dy^T h: no d_base, no column sums, no B or col_part
 };
 
 // Wait for the current stage's DMA while the younger loads already issued stay
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const bool want_base = nt == 0;  // the elementwise part is done by the first rank block
+  const bool want_base = nt == 0 && !a.pure;  // the elementwise part is done by the first rank block
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
   // buffer resources over the token slice; rows past it read zero
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
         // k + 16 <= r: r % 8 == 0 and k % 16 == 0 give whole 8-column chunks;
         // the second chunk is checked on its own
         const bool hi = k + 8 < r;
+        if (!a.pure) {
         const Chunk b0 = *reinterpret_cast<const Chunk*>(Bp + j * r + k);
         const Chunk b1 = hi ? *reinterpret_cast<const Chunk*>(Bp + j * r + k + 8) : zero_chunk();
         float bf[16];
@@ -318,6 +320,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
           u1 = __builtin_fmaf(bf[q + 1], acc[i][jj][q + 1], u1);
         }
         bsum += u0 + u1;
+        }
         // this slice of E for d_B
         float* dst = ep + j * r + k;
         *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
@@ -332,6 +335,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
     bsum += __shfl_xor(bsum, 32, 64);
     if (fh == 0) red[32 * 128 + wn * 128 + jl] = bsum;
   }
+  if (a.pure) return;  // uniform: the whole workgroup leaves together
   // (2) the column sums of dy * base over the slice: thread tid holds row tid/16
   // of each stage and 8 columns
 #pragma unroll
@@ -465,6 +469,49 @@ int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r) {
   const BwdPlan p = bwd_plan(T, out, r, true);
   const int64_t rows = bcdiv(T, p.nSplit);
   return rows * std::max<int64_t>(out, r) * 2;
+}
+
+RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny) {
+  RowContractPlan q;
+  if (T <= 0 || nx <= 0 || ny <= 0) return q;
+  const BwdPlan p = bwd_plan(T, nx, ny, true);
+  q.nSplit = p.nSplit;
+  q.bytes = static_cast<size_t>(p.nSplit) * nx * ny * 4;
+  q.grid = bcdiv(static_cast<int64_t>(p.nCB) * p.nTiles * p.nSplit, 8) * 8;
+  q.slice_bytes = bcdiv(T, p.nSplit) * std::max(nx, ny) * 2;
+  return q;
+}
+
+hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int dtype,
+                               float* e_part, hipStream_t stream) {
+  if (T <= 0 || nx <= 0 || ny <= 0) return hipSuccess;
+  const BwdPlan plan = bwd_plan(T, nx, ny, true);
+  BwdArgs a{};
+  a.dy = X;
+  a.base = X;  // never read: in a plain contraction every base load is out of range
+  a.h = Y;
+  a.T = T;
+  a.out = nx;
+  a.r = ny;
+  a.nCB = plan.nCB;
+  a.nTiles = plan.nTiles;
+  a.nSplit = plan.nSplit;
+  a.e_part = e_part;
+  a.pure = 1;
+  if (dtype == 0) {
+    switch (plan.tn) {
+      case 1: launch_bwd_dma<0, 1>(a, stream); break;
+      case 2: launch_bwd_dma<0, 2>(a, stream); break;
+      default: launch_bwd_dma<0, 3>(a, stream); break;
+    }
+  } else {
+    switch (plan.tn) {
+      case 1: launch_bwd_dma<1, 1>(a, stream); break;
+      case 2: launch_bwd_dma<1, 2>(a, stream); break;
+      default: launch_bwd_dma<1, 3>(a, stream); break;
+    }
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_lora_bwd(const LoraBwdArgs& p, bool vec) {

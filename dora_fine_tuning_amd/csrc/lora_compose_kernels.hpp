@@ -46,4 +46,19 @@ int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r);
 // vec: out % 8 == 0, r % 8 == 0, 1 <= r <= 2^20, T >= 1, every pointer 16-byte aligned.
 hipError_t launch_lora_bwd(const LoraBwdArgs& a, bool vec);
 
+// Plain contraction over the row (token) axis of two row-major matrices of the
+// storage dtype, X [T x nx] and Y [T x ny]: E = X^T Y, computed in nSplit row
+// slices whose fp32 partials are written to e_part[nSplit][nx][ny] (the caller
+// adds them).  Needs nx, ny multiples of 8, 16-byte aligned X, Y and e_part,
+// and slice_bytes < 2^31.
+struct RowContractPlan {
+  int nSplit = 0;
+  size_t bytes = 0;          // of e_part
+  int64_t grid = 0;          // workgroups of the launch
+  int64_t slice_bytes = 0;   // largest byte range one slice's buffer resource spans
+};
+RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny);
+hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int dtype,
+                               float* e_part, hipStream_t stream);
+
 }  // namespace dora

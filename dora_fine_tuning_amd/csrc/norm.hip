@@ -205,6 +205,7 @@ struct WArgs {
   float* base_part;   // [nSplit][out]
   float* cross_part;  // [nSplit][nTiles][out]
   int skip_base;      // the base term comes from a cache: no squares, no base partials
+  float* acc_part = nullptr;  // [nSplit][out][r]: store the accumulators U + B G' instead of reducing them
 };
 
 // Epilogue shared by both W-stream kernels.  The MFMAs take the rank-side
@@ -335,6 +336,40 @@ __device__ inline void wait_younger(int n) {
       wait_vmcnt<N * TL::L>();
     else
       wait_younger<TL, N - 1>(n);
+  }
+}
+
+// Epilogue of the 16-byte path for the norm backward: the workgroup's split-K
+// partial of U + B G' itself, written to acc_part[sp][row][col] in fp32.  Lane
+// l of wave (wm, wn) holds, for tile (i, j), row m0 + 32*(wm*TMW + i) + l%32
+// and in register q rank column n0 + 32*(wn*TN + j) + 16*(l/32) + q (the
+// rank-side panel is fetched in the fragment row order), so each lane writes
+// 16 consecutive floats per tile; r % 8 == 0 makes each half of them wholly
+// inside or outside the matrix.
+template <class TL>
+__device__ inline void dma_store_acc(const WArgs& a, int sp, int64_t m0, int64_t n0,
+                                     const f32x16 (&acc)[TL::TMW][TL::TN]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int h = lane >> 5, frow = lane & 31;
+  const int64_t out = a.sm.out, r = a.sm.r;
+  float* part = a.acc_part + static_cast<int64_t>(sp) * out * r;
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i) {
+    const int64_t row = m0 + 32 * (wm * TL::TMW + i) + frow;
+    if (row >= out) continue;
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) {
+      const int64_t col = n0 + 32 * (wn * TL::TN + j) + 16 * h;
+      if (col >= r) continue;
+      float* dst = part + row * r + col;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[i][j][4], acc[i][j][5], acc[i][j][6], acc[i][j][7]};
+      if (col + 8 < r) {
+        *reinterpret_cast<f32x4*>(dst + 8) = f32x4{acc[i][j][8], acc[i][j][9], acc[i][j][10], acc[i][j][11]};
+        *reinterpret_cast<f32x4*>(dst + 12) = f32x4{acc[i][j][12], acc[i][j][13], acc[i][j][14], acc[i][j][15]};
+      }
+    }
   }
 }
 
@@ -793,6 +828,10 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
     DORA_STAGE(7)
   }
 
+  if (a.acc_part) {  // norm backward: keep U + B G' (every DMA of the ring has been waited for)
+    dma_store_acc<TL>(a, sp, m0, n0, acc);
+    return;
+  }
   dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0, rxB);
 }
 #undef DORA_STAGE
@@ -1058,28 +1097,37 @@ void launch_dma(const WArgs& w, hipStream_t stream) {
   hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTileOf<TN>::NT), 0, stream, w);
 }
 
+// G' = scale * A A^T as the pair G'hi + G'lo in the plan's workspace regions.
+template <int DT>
+hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* ws, bool vec, hipStream_t stream) {
+  using T = typename Dt<DT>::T;
+  if (p.r <= 0) return hipSuccess;
+  T* ghi = reinterpret_cast<T*>(ws + p.off_ghi);
+  T* glo = reinterpret_cast<T*>(ws + p.off_glo);
+  const T* A = static_cast<const T*>(Av);
+  float* gpart = reinterpret_cast<float*>(ws + p.off_gpart);
+  const int nUpper = p.nTg * (p.nTg + 1) / 2;
+  const dim3 ggrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(nUpper) * p.splitG, 8) * 8));
+  if (vec)
+    hipLaunchKernelGGL((gram_dma<DT, 4>), ggrid, dim3(256), 0, stream, A, static_cast<int>(p.in),
+                       static_cast<int>(p.r), p.nTg, p.splitG, gpart);
+  else
+    hipLaunchKernelGGL((gram_partial<DT>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(cdiv(p.r * p.r, 256))), dim3(256), 0, stream,
+                     gpart, p.splitG, p.r, scale, ghi, glo);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   char* ws = static_cast<char*>(a.ws);
   using T = typename Dt<DT>::T;
   T* ghi = reinterpret_cast<T*>(ws + p.off_ghi);
   T* glo = reinterpret_cast<T*>(ws + p.off_glo);
-  if (p.r > 0) {
-    const T* A = static_cast<const T*>(a.A);
-    float* gpart = reinterpret_cast<float*>(ws + p.off_gpart);
-    const int nUpper = p.nTg * (p.nTg + 1) / 2;
-    const dim3 ggrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(nUpper) * p.splitG, 8) * 8));
-    if (vec)
-      hipLaunchKernelGGL((gram_dma<DT, 4>), ggrid, dim3(256), 0, a.stream, A, static_cast<int>(p.in),
-                         static_cast<int>(p.r), p.nTg, p.splitG, gpart);
-    else
-      hipLaunchKernelGGL((gram_partial<DT>), ggrid, dim3(256), 0, a.stream, A, p.in, p.r, p.nTg, p.splitG,
-                         gpart);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(cdiv(p.r * p.r, 256))), dim3(256), 0, a.stream,
-                       gpart, p.splitG, p.r, a.s * 0.5f, ghi, glo);
-    e = hipGetLastError();
+  {
+    const hipError_t e = launch_gram_t<DT>(p, a.A, a.s * 0.5f, ws, vec, a.stream);
     if (e != hipSuccess) return e;
   }
   WArgs w;
@@ -1110,7 +1158,64 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   return hipGetLastError();
 }
 
+// Norm backward, d_B: d_B[i][j] = s * c_i * (sum of the split partials of
+// U + s B G, added in split order in fp32), rounded once to the storage dtype.
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_finalize_b(const float* part, int nSplit, int64_t out, int64_t r,
+                                                       const float* c, float s, void* dB) {
+  using T = typename Dt<DT>::T;
+  const int64_t n = out * r;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    float sum = 0.0f;
+    for (int p = 0; p < nSplit; ++p) sum += part[static_cast<int64_t>(p) * n + e];
+    static_cast<T*>(dB)[e] = Dt<DT>::from_f((s * c[e / r]) * sum);
+  }
+}
+
+template <int DT>
+hipError_t launch_norm_bwd_db_t(const NormPlan& p, const void* W0, const void* A, const void* B, float s,
+                                const float* c, void* dB, void* wsv, float* acc_part, hipStream_t stream) {
+  char* ws = static_cast<char*>(wsv);
+  using T = typename Dt<DT>::T;
+  hipError_t e = launch_gram_t<DT>(p, A, s, ws, true, stream);  // G' = s G
+  if (e != hipSuccess) return e;
+  WArgs w;
+  w.sm = WStages{W0, A, B, reinterpret_cast<T*>(ws + p.off_ghi), reinterpret_cast<T*>(ws + p.off_glo), p.out, p.in,
+                 p.r, p.S1, p.S2};
+  w.nRB = p.nRB;
+  w.S = p.S;
+  w.nTiles = p.nTiles;
+  w.nSplit = p.nSplit;
+  w.total = p.nRB * p.nTiles * p.nSplit;
+  w.base_part = nullptr;
+  w.cross_part = nullptr;
+  w.skip_base = 1;
+  w.acc_part = acc_part;
+  switch (p.tn) {
+    case 1: launch_dma<DT, 1>(w, stream); break;
+    case 2: launch_dma<DT, 2>(w, stream); break;
+    case 3: launch_dma<DT, 3>(w, stream); break;
+    default: launch_dma<DT, 4>(w, stream); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t blocks = std::min<int64_t>(cdiv(p.out * p.r, 256), 4096);
+  hipLaunchKernelGGL((nbwd_finalize_b<DT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, acc_part,
+                     p.nSplit, p.out, p.r, c, s, dB);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t norm_bwd_acc_bytes(const NormPlan& p) { return static_cast<size_t>(p.nSplit) * p.out * p.r * 4; }
+
+hipError_t launch_norm_bwd_db(const NormPlan& p, const void* W0, const void* A, const void* B, float s,
+                              const float* c, void* dB, void* ws, float* acc_part, hipStream_t stream) {
+  if (p.out <= 0 || p.r <= 0) return hipSuccess;
+  return p.dtype == 0 ? launch_norm_bwd_db_t<0>(p, W0, A, B, s, c, dB, ws, acc_part, stream)
+                      : launch_norm_bwd_db_t<1>(p, W0, A, B, s, c, dB, ws, acc_part, stream);
+}
 
 size_t norm_scratch_bound(int64_t out, int64_t r) {
   return static_cast<size_t>(4 * (out * r + r * r) + 64 * out + 256);

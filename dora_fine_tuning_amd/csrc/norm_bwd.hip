@@ -1,0 +1,203 @@
+// Backward of the factored weight norm, for a caller that does not detach n
+// (the press summary of arXiv:2603.22276 describes the norm as base, cross and
+// Gram parts of ||W0 + s B A||; it is silent on whether n is differentiated, so
+// this is the alternative to the detached reading).  With c_i = dn_i / n_i and
+// L = sum_i dn_i n_i, by the chain rule through the same three parts:
+//
+//   d_B_i = s c_i (U_i + s B_i G),                 U = W0 A^T, G = A A^T
+//   d_A   = s (c*B)^T W0 + s^2 (B^T diag(c) B) A
+//
+// and the out x in matrix B A is never formed.  Steps, in launch order:
+//   nbwd_prep          c_i (0 where n_i = 0) and Y = s c*B [out x r] as the
+//                      storage-dtype pair Yhi | Ylo [out x 2r];
+//   d_B                the norm's W stream with G' = s G, its accumulators
+//                      U + s B G stored and then scaled by s c_i (norm.hip);
+//   M                  the token-axis contraction kernel (lora_bwd.hip) over
+//                      the rows of B: B^T [Yhi | Ylo] = s B^T diag(c) B, in
+//                      row slices;
+//   nbwd_finalize_m    Z = s (that r x r matrix), transposed, as Zhi | Zlo;
+//   d_A                the same contraction kernel over the rows of W0 with
+//                      [Yhi | Ylo] and over the rows of A with [Zhi | Zlo]:
+//                      the contraction axis [out rows of W0 ; r rows of A]
+//                      gives d_A^T in row slices;
+//   nbwd_finalize_a    sum of the slices and of the hi/lo halves, transposed
+//                      through LDS into d_A [r x in].
+// The hi/lo pairs carry about 16 (bf16) or 22 (fp16) significant bits of the
+// computed operands Y and Z into the bf16/fp16 MFMAs; W0, A and B enter exactly.
+#include <algorithm>
+
+#include "dora_common.hpp"
+#include "lora_compose_kernels.hpp"
+#include "norm_bwd_kernels.hpp"
+#include "norm_kernels.hpp"
+
+namespace dora {
+
+namespace {
+
+__host__ __device__ inline int64_t ndiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// c_i = dn_i / n_i (0 where n_i == 0); Y_ij = s c_i B_ij split into
+// hi = round(Y), lo = round(Y - hi), stored at [i][j] and [i][r + j].
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* norm, const float* d_norm, int64_t out,
+                                                 int64_t r, float s, float* c, void* Yv) {
+  using T = typename Dt<DT>::T;
+  const T* B = static_cast<const T*>(Bv);
+  T* Y = static_cast<T*>(Yv);
+  const int64_t n = out * r;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t i = e / r, j = e - i * r;
+    const float ni = norm[i];
+    const float ci = ni != 0.0f ? d_norm[i] / ni : 0.0f;
+    if (j == 0) c[i] = ci;
+    const float y = (s * ci) * Dt<DT>::to_f(B[e]);
+    const T hi = Dt<DT>::from_f(y);
+    Y[i * 2 * r + j] = hi;
+    Y[i * 2 * r + r + j] = Dt<DT>::from_f(y - Dt<DT>::to_f(hi));
+  }
+}
+
+// Z[l][j] = s * M'[j][l], M'[j][l] = sum over slices of E[j][l] + E[j][r + l]
+// (E = B^T [Yhi | Ylo], [nSplit][r][2r]), split into hi/lo at [l][j], [l][r + j].
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSplit, int64_t r, float s, void* Zv) {
+  using T = typename Dt<DT>::T;
+  T* Z = static_cast<T*>(Zv);
+  const int64_t n = r * r, slice = r * 2 * r;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t j = e / r, l = e - j * r;  // l fastest: the reads of E[j][.] are coalesced
+    float m = 0.0f;
+    for (int p = 0; p < nSplit; ++p) {
+      const float* Ep = E + p * slice + j * 2 * r;
+      m += Ep[l] + Ep[r + l];
+    }
+    const float z = s * m;
+    const T hi = Dt<DT>::from_f(z);
+    Z[l * 2 * r + j] = hi;
+    Z[l * 2 * r + r + j] = Dt<DT>::from_f(z - Dt<DT>::to_f(hi));
+  }
+}
+
+// d_A[j][k] = sum over the slices of E[k][j] + E[k][r + j] (E [nParts][in][2r],
+// the slices added in order, each slice's hi and lo halves first), rounded once.
+// A 32 x 32 tile of (k, j) per workgroup: coalesced reads along j, a transpose
+// through LDS, coalesced writes along k.
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nParts, int64_t in, int64_t r, void* dAv) {
+  using T = typename Dt<DT>::T;
+  __shared__ float tile[32][33];
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 32, j0 = static_cast<int64_t>(blockIdx.y) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t slice = in * 2 * r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kk = ty + 8 * q;
+    const int64_t k = k0 + kk, j = j0 + tx;
+    float v = 0.0f;
+    if (k < in && j < r) {
+      const float* Ep = E + k * 2 * r + j;
+      for (int p = 0; p < nParts; ++p) v += Ep[p * slice] + Ep[p * slice + r];
+    }
+    tile[kk][tx] = v;
+  }
+  __syncthreads();
+  T* dA = static_cast<T*>(dAv);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int jj = ty + 8 * q;
+    const int64_t j = j0 + jj, k = k0 + tx;
+    if (j < r && k < in) dA[j * in + k] = Dt<DT>::from_f(tile[tx][jj]);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_zero(void* pv, int64_t n) {
+  using T = typename Dt<DT>::T;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256)
+    static_cast<T*>(pv)[e] = Dt<DT>::from_f(0.0f);
+}
+
+inline dim3 stride_grid(int64_t n) { return dim3(static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(ndiv(n, 256), 4096)))); }
+
+template <int DT>
+hipError_t zero_t(void* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((nbwd_zero<DT>), stride_grid(n), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
+  const int64_t out = p.out, in = p.in, r = p.r;
+  if (r == 0) return hipSuccess;
+  if (out == 0) return zero_t<DT>(a.d_A, r * in, a.stream);
+  if (in == 0) return zero_t<DT>(a.d_B, out * r, a.stream);
+  char* ws = static_cast<char*>(a.ws);
+  float* c = reinterpret_cast<float*>(ws + p.off_c);
+  void* Y = ws + p.off_y;
+  void* Z = ws + p.off_z;
+  float* big = reinterpret_cast<float*>(ws + p.off_big);
+  hipLaunchKernelGGL((nbwd_prep<DT>), stride_grid(out * r), dim3(256), 0, a.stream, a.B, a.norm, a.d_norm, out, r,
+                     a.s, c, Y);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // d_B (the W stream's partials live in the big region until its finalize)
+  e = launch_norm_bwd_db(p.np, a.W0, a.A, a.B, a.s, c, a.d_B, ws + p.off_np, big, a.stream);
+  if (e != hipSuccess) return e;
+  // M = B^T [Yhi | Ylo] -> Z
+  e = launch_row_contract(a.B, Y, out, r, 2 * r, p.np.dtype, big, a.stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((nbwd_finalize_m<DT>), stride_grid(r * r), dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, Z);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // d_A^T slices: rows of W0 with Y, then rows of A with Z
+  e = launch_row_contract(a.W0, Y, out, in, 2 * r, p.np.dtype, big, a.stream);
+  if (e != hipSuccess) return e;
+  e = launch_row_contract(a.A, Z, r, in, 2 * r, p.np.dtype, big + static_cast<int64_t>(p.rW.nSplit) * in * 2 * r,
+                          a.stream);
+  if (e != hipSuccess) return e;
+  const dim3 fgrid(static_cast<unsigned>(ndiv(in, 32)), static_cast<unsigned>(ndiv(r, 32)));
+  hipLaunchKernelGGL((nbwd_finalize_a<DT>), fgrid, dim3(256), 0, a.stream, big, p.rW.nSplit + p.rA.nSplit, in, r,
+                     a.d_A);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype) {
+  NormBwdPlan p;
+  p.out = out;
+  p.in = in;
+  p.r = r;
+  if (out <= 0 || in <= 0 || r <= 0) return p;
+  p.np = make_norm_plan(out, in, r, dtype, true);
+  p.rM = row_contract_plan(out, r, 2 * r);
+  p.rW = row_contract_plan(out, in, 2 * r);
+  p.rA = row_contract_plan(r, in, 2 * r);
+  size_t off = 0;
+  p.off_np = off;
+  off += al256(p.np.bytes);
+  p.off_c = off;
+  off += al256(static_cast<size_t>(out) * 4);
+  p.off_y = off;
+  off += al256(static_cast<size_t>(out) * 2 * r * 2);
+  p.off_z = off;
+  off += al256(static_cast<size_t>(r) * 2 * r * 2);
+  p.off_big = off;
+  off += al256(std::max({norm_bwd_acc_bytes(p.np), p.rM.bytes, p.rW.bytes + p.rA.bytes}));
+  p.bytes = off;
+  p.max_grid = std::max({norm_max_grid(p.np), p.rM.grid, p.rW.grid, p.rA.grid, ndiv(in, 32), ndiv(out * r, 256)});
+  p.max_slice_bytes = std::max({p.rM.slice_bytes, p.rW.slice_bytes, p.rA.slice_bytes});
+  return p;
+}
+
+hipError_t launch_norm_bwd(const NormBwdPlan& p, const NormBwdArgs& a) {
+  return a.dtype == 0 ? launch_norm_bwd_t<0>(p, a) : launch_norm_bwd_t<1>(p, a);
+}
+
+}  // namespace dora

@@ -57,4 +57,13 @@ hipError_t launch_norm(const NormPlan& p, const NormArgs& a);
 hipError_t launch_row_sqnorm(const void* W0, int64_t out, int64_t in, int dtype, bool vec, float* sq,
                              hipStream_t stream);
 
+// Norm backward, the d_B half (16-byte path plans only):
+//   d_B_i = s * c_i * (U_i + s * B_i G),  U = W0 A^T, G = A A^T,
+// by the W stream over [W0 | B | B] . [A | G'hi | G'lo]^T with G' = s G, whose
+// split-K accumulators go to acc_part (norm_bwd_acc_bytes(p) bytes) and are
+// then added and scaled.  ws: the plan's workspace (its Gram regions are used).
+size_t norm_bwd_acc_bytes(const NormPlan& p);
+hipError_t launch_norm_bwd_db(const NormPlan& p, const void* W0, const void* A, const void* B, float s,
+                              const float* c, void* dB, void* ws, float* acc_part, hipStream_t stream);
+
 }  // namespace dora

@@ -27,6 +27,11 @@
  *   dora_lora_compose_bwd      its backward: d_base, d_B and d_mag from dy,
  *                              base and h, without lora or d_lora;
  *
+ * for a caller that does not treat the norm as a constant:
+ *
+ *   dora_norm_bwd              d_A and d_B of the weight norm, from dL/dn,
+ *                              without forming B*A;
+ *
  * and, for the cached base norm the page lists as future work (W0 is frozen):
  *
  *   dora_row_sqnorm            ||W0_i||^2 per row, computed once;
@@ -176,6 +181,44 @@ DORA_API int dora_compose_fwd(const void* base, const void* lora, const float* m
 DORA_API int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const float* mag,
                                    const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype,
                                    int add_base, void* y, hipStream_t stream);
+
+/*
+ * Bytes of device workspace dora_norm_bwd needs for these sizes: the Gram
+ * scratch of the norm, c [out] fp32, the hi/lo pair of s*c*B [out x 2r] and of
+ * an r x r product [r x 2r] in the storage dtype, and one fp32 region of
+ * row-slice partials of size O(out*r + in*r) reused by the steps in turn.
+ * Returns 0 for negative sizes or an unknown dtype.
+ */
+DORA_API size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
+
+/*
+ * Backward of the weight norm n_i = ||W0_i + s * B_i * A||_2 for a caller
+ * that does not treat n as a constant (the summary page's paragraph on the
+ * factored norm gives its base, cross and Gram parts; the page does not say
+ * whether n is differentiated, and dora_compose_bwd takes it as constant).
+ * Given dL/dn = d_norm, with c_i = d_norm_i / norm_i (0 where norm_i == 0):
+ *   d_B_i = s * c_i * (U_i + s * B_i * G),          U = W0 * A^T, G = A * A^T
+ *   d_A   = s * (c .* B)^T * W0 + s^2 * (B^T * diag(c) * B) * A
+ * which is s * B^T * dV and s * dV * A^T for dV = c .* (W0 + s * B * A), with
+ * the out x in matrix B * A never formed.  W0 is frozen: it gets no gradient.
+ * For the DoRA layer, L depends on n only through g = m / n, so
+ * d_norm_j = -(m_j / n_j) * d_mag_j with d_mag from dora_compose_bwd.
+ * U, G and the two contractions over the out rows run on MFMA with fp32
+ * accumulation; the computed operands s*c*B and the r x r product enter them as
+ * hi/lo pairs of the storage dtype.  Each output is rounded once.
+ *
+ * W0: device, dtype, [out x in]; A, d_A: [r x in]; B, d_B: [out x r]; norm
+ * (the forward's n) and d_norm: device fp32 [out].  No output overlaps an
+ * input, the other output or ws.  ws: at least dora_norm_bwd_workspace_bytes
+ * bytes.  r == 0 is a no-op; out == 0 gives d_A = 0; in == 0 gives d_B = 0.
+ * Needs in and r multiples of 8, in < 2^21, r <= 2^20 and 16-byte aligned
+ * matrix and workspace pointers, else DORA_UNSUPPORTED (no general path).
+ * In fp16 the lo halves lose bits where |s*c*B| falls below about 2^-3
+ * (their values reach fp16's subnormal range).
+ */
+DORA_API int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* norm, const float* d_norm,
+                           int64_t out, int64_t in, int64_t r, float s, int dtype, void* d_A, void* d_B, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace dora_lora_compose_bwd needs (fp32 slices of dy^T h and column partials). */
 DORA_API size_t dora_lora_compose_bwd_workspace_bytes(int64_t T, int64_t out, int64_t r);

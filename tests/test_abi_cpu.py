@@ -216,3 +216,28 @@ def test_binding_rejects_host_tensors():
         binding.dora_norm_factored(W0, W0, W0, 1.0)
     with pytest.raises(ValueError, match="dtype"):
         binding.dora_compose_fwd(W0.float(), W0.float(), None, None, 1.0)
+
+
+def test_norm_bwd_validation():
+    ws = LIB.dora_norm_bwd_workspace_bytes(64, 64, 8, 0)
+    assert ws > 0 and LIB.dora_norm_bwd_workspace_bytes(64, 64, 8, 7) == 0
+    assert LIB.dora_norm_bwd_workspace_bytes(-1, 64, 8, 0) == 0
+    # W0 P, A 2P, B 3P, norm 4P, d_norm 5P, d_A 6P, d_B 7P, ws 8P
+    args = lambda **k: [k.get(n, d) for n, d in (("W0", P), ("A", P * 2), ("B", P * 3), ("norm", P * 4),
+                                                 ("d_norm", P * 5), ("out", 64), ("in_", 64), ("r", 8), ("s", 1.0),
+                                                 ("dt", 0), ("d_A", P * 6), ("d_B", P * 7), ("ws", P * 8),
+                                                 ("wsb", ws), ("stream", None))]
+    _status(LIB.dora_norm_bwd(*args(dt=3)), UNSUPPORTED, "dtype")
+    _status(LIB.dora_norm_bwd(*args(out=-1)), INVALID, "negative")
+    _status(LIB.dora_norm_bwd(*args(A=None)), INVALID, "A or d_A")
+    _status(LIB.dora_norm_bwd(*args(d_norm=None)), INVALID, "d_norm")
+    _status(LIB.dora_norm_bwd(*args(W0=None)), INVALID, "W0")
+    _status(LIB.dora_norm_bwd(*args(in_=60)), UNSUPPORTED, "multiples of 8")
+    _status(LIB.dora_norm_bwd(*args(r=12)), UNSUPPORTED, "multiples of 8")
+    _status(LIB.dora_norm_bwd(*args(B=P * 3 + 8)), UNSUPPORTED, "aligned")
+    _status(LIB.dora_norm_bwd(*args(wsb=ws - 1)), INVALID, "workspace")
+    _status(LIB.dora_norm_bwd(*args(ws=None)), INVALID, "workspace is NULL")
+    _status(LIB.dora_norm_bwd(*args(d_B=P * 3 + 64)), INVALID, "overlaps")
+    _status(LIB.dora_norm_bwd(*args(d_A=P * 7 + 16)), INVALID, "overlap")
+    _status(LIB.dora_norm_bwd(*args(ws=P + 1024)), INVALID, "overlaps")
+    assert LIB.dora_norm_bwd(*args(r=0, W0=None, A=None, B=None)) == OK

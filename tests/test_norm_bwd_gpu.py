@@ -1,0 +1,173 @@
+"""Parity of dora_norm_bwd (the weight-norm backward for a non-detached norm)
+with the CPU fp64 oracle, through the C ABI.
+
+The norm n and the upstream gradient d_norm are inputs: both sides take the
+same fp32 arrays (n need not be the exact norm for the definition to hold; the
+tests use the oracle's norm on small shapes and the base row norms at full
+size).
+
+Tolerances, from the arithmetic (stored outputs, bf16 or fp16):
+* the value: 2 bf16 ulps (bf16) or 1e-3 relative (fp16), or
+* the cancellation floor, for elements whose terms cancel:
+  d_B_i = s c_i (U_i + s B_i G) accumulates in fp32 over in + 2r exact MFMA
+  products (steps of 16) plus the split-K partials, so it errs by at most
+  (in/16 + 100) 2^-24 of s |c_i| (|W0| |A|^T + s |B| |G|); the Gram operand
+  enters as a hi/lo pair (16 significant bits in bf16), which adds 2^-16 of
+  the Gram part.  d_A = s (cB)^T W0 + s^2 (B^T diag(c) B) A sums out + r
+  products of a hi/lo pair (2^-17 of each term) with an exact operand, in fp32,
+  over row slices; its floor is 3 (out/16 + 100) 2^-24 + 2^-16 of the term
+  mass s |cB|^T |W0| + s^2 (|B|^T diag|c| |B|) |A|.  The factor 3 covers the
+  final rounding where the floor decides.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity_util as PU
+from dora_fine_tuning_amd import synth
+from oracle import dora_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "GPU parity tests need a HIP device"
+    from dora_fine_tuning_amd import binding
+
+    return binding
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def case(out, in_, r, dtype, seed):
+    rng = np.random.default_rng(3000 + seed)
+    to = lambda a: synth.to_dtype(a.astype(np.float32), dtype)
+    W0 = to(rng.normal(0, 0.02, (out, in_)))
+    A = to(rng.normal(0, 1 / np.sqrt(max(in_, 1)), (r, in_)))
+    B = to(rng.normal(0, 0.01, (out, r)))
+    s = float(np.float32(32.0 / np.sqrt(r)))
+    d_norm = (rng.standard_normal(out) * 30).astype(np.float32)
+    return W0, A, B, s, d_norm
+
+
+def floors(W0, A, B, c, s):
+    """Cancellation floors of d_A [r x in] and d_B [out x r] (see the module docstring)."""
+    out, in_ = W0.shape
+    r = A.shape[0]
+    aW, aA, aB, ac = np.abs(W0), np.abs(A), np.abs(B), np.abs(c)
+    G = A @ A.T
+    gram_B = s * s * ac[:, None] * (aB @ np.abs(G))
+    mass_B = s * ac[:, None] * (aW @ aA.T) + gram_B
+    floor_B = 3.0 * (in_ / 16 + 100) * 2.0**-24 * mass_B + 2.0**-16 * gram_B
+    Ymass = s * ac[:, None] * aB
+    mass_A = Ymass.T @ aW + (s * s * (aB.T @ (ac[:, None] * aB))) @ aA
+    floor_A = (3.0 * ((out + r) / 16 + 100) * 2.0**-24 + 2.0**-16) * mass_A
+    return floor_A, floor_B
+
+
+def check(lib, W0, A, B, s, d_norm, norm, dtype, what, rows=None, cols=None):
+    out, in_ = W0.shape
+    r = A.shape[0]
+    Wd, Ad, Bd = W0.to(DEV), A.to(DEV), B.to(DEV)
+    nd, dd = torch.from_numpy(norm).to(DEV), torch.from_numpy(d_norm).to(DEV)
+    d_A, d_B = lib.dora_norm_bwd(Wd, Ad, Bd, nd, dd, s)
+    torch.cuda.synchronize()
+    Wf, Af, Bf = f64(W0), f64(A), f64(B)
+    c = np.where(norm != 0, d_norm.astype(np.float64) / np.where(norm != 0, norm, 1), 0.0)
+    rows = np.arange(out) if rows is None else rows
+    cols = np.arange(in_) if cols is None else cols
+    # d_B on the sampled rows: the rows of the definition are independent
+    _, rB = O.weight_norm_bwd(d_norm[rows], norm[rows], Wf[rows], Af, Bf[rows], s)
+    # d_A on the sampled input columns: the columns of V = W0 + s B A are independent
+    rA, _ = O.weight_norm_bwd(d_norm, norm, Wf[:, cols], Af[:, cols], Bf, s)
+    fA, _ = floors(Wf[:, cols], Af[:, cols], Bf, c, s)
+    _, fB = floors(Wf[rows], Af, Bf[rows], c[rows], s)
+    nA = PU.assert_compose(f64(d_A)[:, cols], rA, fA, dtype, f"{what} d_A", 1.0)
+    nB = PU.assert_compose(f64(d_B)[rows], rB, fB, dtype, f"{what} d_B", 1.0)
+    log(f"{what}: d_A {rA.size} and d_B {rB.size} elements within tolerance ({nA} and {nB} on the floor only)")
+    return d_A, d_B
+
+
+SMALL = [
+    (200, 136, 24),    # ragged rows; one rank tile, several K stages
+    (72, 64, 8),       # smallest rank
+    (300, 520, 40),    # ragged in every direction the tiles have
+    (1100, 1032, 136), # several row blocks and column blocks, two rank blocks of the 2r axis
+    (513, 264, 384),   # the wide workload's rank
+    (96, 2056, 512),   # wide input axis, the largest rank tile
+    (40, 8, 16),       # in = 8: one K chunk
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_norm_bwd_small(lib, shape, dtype):
+    out, in_, r = shape
+    log(f"norm_bwd small {shape} {dtype}")
+    W0, A, B, s, d_norm = case(out, in_, r, dtype, sum(shape))
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    check(lib, W0, A, B, s, d_norm, norm, dtype, f"{shape} {dtype}")
+
+
+def test_norm_bwd_zero_norm_rows_and_determinism(lib):
+    log("norm_bwd zero-norm rows, determinism")
+    W0, A, B, s, d_norm = case(256, 512, 64, "bf16", 7)
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    norm[[3, 100]] = 0.0  # rows with n = 0 give no gradient
+    d_A, d_B = check(lib, W0, A, B, s, d_norm, norm, "bf16", "zero-norm rows")
+    assert torch.all(d_B[[3, 100]] == 0)
+    Wd, Ad, Bd = W0.to(DEV), A.to(DEV), B.to(DEV)
+    nd, dd = torch.from_numpy(norm).to(DEV), torch.from_numpy(d_norm).to(DEV)
+    d_A2, d_B2 = lib.dora_norm_bwd(Wd, Ad, Bd, nd, dd, s)
+    assert torch.equal(d_A, d_A2) and torch.equal(d_B, d_B2), "repeated calls differ"
+
+
+def test_norm_bwd_b_zero(lib):
+    # B = 0 (DoRA's initialisation): d_A = 0 exactly, d_B = s c W0 A^T
+    log("norm_bwd B = 0")
+    W0, A, B, s, d_norm = case(264, 256, 32, "bf16", 9)
+    B = torch.zeros_like(B)
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    d_A, _ = check(lib, W0, A, B, s, d_norm, norm, "bf16", "B = 0")
+    assert torch.all(d_A == 0)
+
+
+def test_norm_bwd_degenerate_sizes(lib):
+    log("norm_bwd degenerate sizes")
+    W0, A, B, s, d_norm = case(64, 64, 16, "bf16", 11)
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    nd, dd = torch.from_numpy(norm).to(DEV), torch.from_numpy(d_norm).to(DEV)
+    # out = 0: d_A is an empty sum
+    d_A = torch.full((16, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    lib.dora_norm_bwd(W0[:0].to(DEV), A.to(DEV), B[:0].to(DEV), nd[:0], dd[:0], s, d_A=d_A)
+    torch.cuda.synchronize()
+    assert torch.all(d_A == 0)
+    # in = 0: V = 0, so d_B = 0
+    d_B = torch.full((64, 16), 7.0, dtype=torch.bfloat16, device=DEV)
+    lib.dora_norm_bwd(W0[:, :0].contiguous().to(DEV), A[:, :0].contiguous().to(DEV), B.to(DEV), nd, dd, s, d_B=d_B)
+    torch.cuda.synchronize()
+    assert torch.all(d_B == 0)
+
+
+@pytest.mark.parametrize("name", ["attn_proj", "wide_8192_r384"])
+def test_norm_bwd_full_size_sampled(lib, name):
+    cfg = synth.CONFIGS[name]
+    log(f"norm_bwd full size {name}: out={cfg.out} in={cfg.in_} r={cfg.r}")
+    W0, A, B = synth.weights(cfg)
+    rng = np.random.default_rng(4000 + cfg.out + cfg.r)
+    d_norm = (rng.standard_normal(cfg.out) * 30).astype(np.float32)
+    norm = np.linalg.norm(f64(W0), axis=1).astype(np.float32)
+    rows = np.sort(rng.choice(cfg.out, 64, replace=False))
+    cols = np.sort(rng.choice(cfg.in_, 64, replace=False))
+    check(lib, W0, A, B, cfg.s, d_norm, norm, "bf16", f"{name} sampled", rows=rows, cols=cols)
