@@ -117,6 +117,8 @@ def main():
                     help="steps timing the norm with a cached base term (W0 frozen); 0 skips")
     ap.add_argument("--fused-reps", type=int, default=20,
                     help="calls timing the compose with lora = h B^T fused in, against GEMM + compose; 0 skips")
+    ap.add_argument("--norm-bwd-reps", type=int, default=10,
+                    help="calls timing the weight-norm backward (non-detached norm), against the dense torch form; 0 skips")
     ap.add_argument("--torch-reps", type=int, default=10,
                     help="compose forward+backward timed through the PyTorch custom operator and autograd")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -292,6 +294,47 @@ def main():
                         "fused_tflops": round(ff / (fbw_us * 1e-6) / 1e12, 1)}
         del y2, lora2, db2, dB2, dm2, dl2, ws_lb
 
+    # The weight-norm backward for a non-detached norm (d_A, d_B from dL/dn),
+    # against the dense form in torch bf16 that forms V = W0 + s B A:
+    # dV = (dn / n) V, d_B = s dV A^T, d_A = s B^T dV.
+    norm_bwd = None
+    if args.norm_bwd_reps > 0:
+        d_norm = (-(mag / norm) * d_mag).contiguous()  # dL/dn of the DoRA layer: -g d_mag
+        dA_o, dB_o = torch.empty_like(A), torch.empty_like(B)
+        ws_nb = torch.empty(max(binding.dora_norm_bwd_workspace_bytes(out, in_, r), 1), dtype=torch.uint8,
+                            device=dev)
+
+        def timed_n(call, reps):
+            evl = []
+            for k in range(3 + reps):
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record()
+                call()
+                a1.record()
+                if k >= 3:
+                    evl.append((a0, a1))
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in evl])) * 1e3
+
+        nb_us = timed_n(lambda: binding.dora_norm_bwd(W0, A, B, norm, d_norm, s, d_A=dA_o, d_B=dB_o,
+                                                      workspace=ws_nb), args.norm_bwd_reps)
+        cB = (d_norm / norm).to(torch.bfloat16)
+
+        def dense():
+            V = torch.addmm(W0, B, A, alpha=s)
+            dV = V * cB[:, None]
+            return torch.mm(dV, A.t()) * s, torch.mm(B.t().contiguous(), dV) * s
+
+        dn_us = timed_n(dense, args.norm_bwd_reps)
+        nbf = 4.0 * out * in_ * r + 4.0 * r * r * in_ + 4.0 * out * r * r
+        nbb = 2 * (out * in_ + 2 * r * in_ + 2 * out * r) + 8 * out
+        norm_bwd = {"us": round(nb_us, 2), "dense_torch_us": round(dn_us, 2), "algorithmic_flops": nbf,
+                    "algorithmic_bytes": nbb, "tflops": round(nbf / (nb_us * 1e-6) / 1e12, 1),
+                    "frac_mfma_peak": round(nbf / (nb_us * 1e-6) / 2.5e15, 4),
+                    "workspace_bytes": int(ws_nb.numel()), "dense_transient_bytes": 2 * 2 * out * in_,
+                    "reps": args.norm_bwd_reps}
+        del dA_o, dB_o, ws_nb
+
     # The same compose forward + backward driven through the PyTorch custom
     # operator and autograd (dora_amd::compose), against the direct calls above.
     torch_us = None
@@ -340,6 +383,7 @@ def main():
         "norm_frac_mfma_peak": round(nf / (norm_ms.mean() * 1e-3) / 2.5e15, 4),
         "norm_cached_base": cached,
         "lora_fused_fwd": fused,
+        "norm_bwd": norm_bwd,
         "compose_fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "compose_bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
         "compose_cold": ({"fwd_us": round(cold_us["fwd"], 2), "bwd_us": round(cold_us["bwd"], 2),
