@@ -433,8 +433,11 @@ BwdPlan bwd_plan(int64_t T, int64_t out, int64_t r, bool vec) {
   p.nCB = static_cast<int>(bcdiv(out, 128));
   p.nTiles = static_cast<int>(bcdiv(std::max<int64_t>(r, 1), 128 * p.tn));
   const int64_t blocks = static_cast<int64_t>(p.nCB) * p.nTiles;
-  // about two workgroups' worth per CU of the 256, at least 8 stages of 32 tokens each
-  int64_t split = bcdiv(512, std::max<int64_t>(blocks, 1));
+  // about one workgroup per CU of the 256 (a workgroup holds a whole CU's
+  // LDS), at least 8 stages of 32 tokens each.  Measured at T = out = 8192:
+  // r = 384 (64 blocks) takes 158 us with 4 slices against 208 us with 8 and
+  // 243 us with 2; 2r = 768 over 8192 rows (128 blocks) is fastest with 2.
+  int64_t split = bcdiv(256, std::max<int64_t>(blocks, 1));
   split = std::min<int64_t>(split, std::max<int64_t>(1, T / 256));
   split = std::max<int64_t>(1, std::min<int64_t>(split, 64));
   p.nSplit = static_cast<int>(split);

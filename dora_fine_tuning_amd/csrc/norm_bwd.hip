@@ -39,24 +39,31 @@ __host__ __device__ inline int64_t ndiv(int64_t a, int64_t b) { return (a + b - 
 inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // c_i = dn_i / n_i (0 where n_i == 0); Y_ij = s c_i B_ij split into
-// hi = round(Y), lo = round(Y - hi), stored at [i][j] and [i][r + j].
+// hi = round(Y), lo = round(Y - hi), stored at [i][j] and [i][r + j].  One
+// 16-byte chunk (8 elements of one row, r % 8 == 0) per thread and step.
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* norm, const float* d_norm, int64_t out,
                                                  int64_t r, float s, float* c, void* Yv) {
   using T = typename Dt<DT>::T;
-  const T* B = static_cast<const T*>(Bv);
+  const Chunk* B = static_cast<const Chunk*>(Bv);
   T* Y = static_cast<T*>(Yv);
-  const int64_t n = out * r;
+  const int64_t n = out * r / 8;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t i = e / r, j = e - i * r;
+    const int64_t i = (e * 8) / r, j = e * 8 - i * r;
     const float ni = norm[i];
     const float ci = ni != 0.0f ? d_norm[i] / ni : 0.0f;
     if (j == 0) c[i] = ci;
-    const float y = (s * ci) * Dt<DT>::to_f(B[e]);
-    const T hi = Dt<DT>::from_f(y);
-    Y[i * 2 * r + j] = hi;
-    Y[i * 2 * r + r + j] = Dt<DT>::from_f(y - Dt<DT>::to_f(hi));
+    float f[8], hi[8], lo[8];
+    chunk_to_f32<DT>(B[e], f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float y = (s * ci) * f[q];
+      hi[q] = Dt<DT>::to_f(Dt<DT>::from_f(y));
+      lo[q] = y - hi[q];
+    }
+    *reinterpret_cast<Chunk*>(Y + i * 2 * r + j) = f32_to_chunk<DT>(hi);
+    *reinterpret_cast<Chunk*>(Y + i * 2 * r + r + j) = f32_to_chunk<DT>(lo);
   }
 }
 
@@ -142,7 +149,7 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   void* Y = ws + p.off_y;
   void* Z = ws + p.off_z;
   float* big = reinterpret_cast<float*>(ws + p.off_big);
-  hipLaunchKernelGGL((nbwd_prep<DT>), stride_grid(out * r), dim3(256), 0, a.stream, a.B, a.norm, a.d_norm, out, r,
+  hipLaunchKernelGGL((nbwd_prep<DT>), stride_grid(out * r / 8), dim3(256), 0, a.stream, a.B, a.norm, a.d_norm, out, r,
                      a.s, c, Y);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
