@@ -87,6 +87,11 @@ struct BwdArgs {
   float* e_part;    // [nSplit][out][r]: the E slices
   float* col_part;  // [nSplit][nTiles][out]: sum_t dy * base (tile 0 only) + s * sum_k B E
   int pure;         // plain contraction E = dy^T h: no d_base, no column sums, no B or col_part
+  // plain contraction only: the contraction axis continues over the rows of
+  // other matrices, dy2 [T2 x out] and h2 [T2 x r]; slice sp takes rows
+  // [T2 sp / nSplit, T2 (sp + 1) / nSplit) of them after its own rows of dy, h
+  const void *dy2, *h2;
+  int64_t T2;
 };
 
 // Wait for the current stage's DMA while the younger loads already issued stay
@@ -120,7 +125,10 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   const int64_t T = a.T, out = a.out, r = a.r;
   const int64_t j0 = static_cast<int64_t>(cb) * TL::BM, k0 = static_cast<int64_t>(nt) * TL::BN;
   const int64_t ts = T * sp / a.nSplit, te = T * (sp + 1) / a.nSplit;
-  const int S = static_cast<int>(bcdiv(te - ts, TL::BK));
+  // second row segment (plain contraction only; empty when T2 == 0)
+  const int64_t ts2 = a.T2 * sp / a.nSplit, te2 = a.T2 * (sp + 1) / a.nSplit;
+  const int S1 = static_cast<int>(bcdiv(te - ts, TL::BK));
+  const int S = S1 + static_cast<int>(bcdiv(te2 - ts2, TL::BK));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
@@ -138,6 +146,13 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(static_cast<const char*>(a.h) + ts * r * 2), static_cast<short>(0),
       static_cast<int>(rows * r * 2), kBufferWord3);
+  const int64_t rows2 = te2 - ts2;
+  const __amdgpu_buffer_rsrc_t rdy2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.dy2) + ts2 * out * 2 : nullptr), static_cast<short>(0),
+      static_cast<int>(rows2 * out * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rh2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.h2) + ts2 * r * 2 : nullptr), static_cast<short>(0),
+      static_cast<int>(rows2 * r * 2), kBufferWord3);
 
   // Per-lane DMA offsets (stage 0).  Wave instruction q moves 1 KiB block
   // b = q*NW + wave of its panel, lane l writing bytes 16l .. 16l + 15.  X: a
@@ -167,14 +182,20 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
     yo[q] = static_cast<uint32_t>((t * r + col) * 2);
   }
   const uint32_t xstep = static_cast<uint32_t>(TL::BK * out * 2), ystep = static_cast<uint32_t>(TL::BK * r * 2);
+  // stages [0, S1) read the slice's rows of dy and h, stages [S1, S) those of
+  // dy2 and h2 (same row pitches, so the same per-lane offsets); a segment's
+  // last stage reads zeros past its rows
   auto issue = [&](int st, int slot) {
     char* so = smem + slot * TL::STAGE_BYTES;
+    const bool seg2 = st >= S1;
+    const __amdgpu_buffer_rsrc_t rx = seg2 ? rdy2 : rdy, ry = seg2 ? rh2 : rh;
+    const uint32_t ss = static_cast<uint32_t>(seg2 ? st - S1 : st);
 #pragma unroll
     for (int q = 0; q < TL::XQ; ++q)
-      dma16(rdy, so + (q * TL::NW + wave) * 1024, xok[q] ? xo[q] + static_cast<uint32_t>(st) * xstep : kOob);
+      dma16(rx, so + (q * TL::NW + wave) * 1024, xok[q] ? xo[q] + ss * xstep : kOob);
 #pragma unroll
     for (int q = 0; q < TL::YQ; ++q)
-      dma16(rh, so + TL::X_BYTES + (q * TL::NW + wave) * 1024, yok[q] ? yo[q] + static_cast<uint32_t>(st) * ystep : kOob);
+      dma16(ry, so + TL::X_BYTES + (q * TL::NW + wave) * 1024, yok[q] ? yo[q] + ss * ystep : kOob);
   };
 
   // Fragment read addresses (within a stage slot; add the slot's offset).  In a
@@ -474,19 +495,19 @@ int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r) {
   return rows * std::max<int64_t>(out, r) * 2;
 }
 
-RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny) {
+RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny, int64_t T2) {
   RowContractPlan q;
   if (T <= 0 || nx <= 0 || ny <= 0) return q;
   const BwdPlan p = bwd_plan(T, nx, ny, true);
   q.nSplit = p.nSplit;
-  q.bytes = static_cast<size_t>(p.nSplit) * nx * ny * 4;
-  q.grid = bcdiv(static_cast<int64_t>(p.nCB) * p.nTiles * p.nSplit, 8) * 8;
-  q.slice_bytes = bcdiv(T, p.nSplit) * std::max(nx, ny) * 2;
+  q.bytes = static_cast<size_t>(q.nSplit) * nx * ny * 4;
+  q.grid = bcdiv(static_cast<int64_t>(p.nCB) * p.nTiles * q.nSplit, 8) * 8;
+  q.slice_bytes = bcdiv(std::max(T, T2), p.nSplit) * std::max(nx, ny) * 2;
   return q;
 }
 
 hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int dtype,
-                               float* e_part, hipStream_t stream) {
+                               float* e_part, hipStream_t stream, const void* X2, const void* Y2, int64_t T2) {
   if (T <= 0 || nx <= 0 || ny <= 0) return hipSuccess;
   const BwdPlan plan = bwd_plan(T, nx, ny, true);
   BwdArgs a{};
@@ -501,6 +522,11 @@ hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t 
   a.nSplit = plan.nSplit;
   a.e_part = e_part;
   a.pure = 1;
+  if (T2 > 0) {
+    a.dy2 = X2;
+    a.h2 = Y2;
+    a.T2 = T2;
+  }
   if (dtype == 0) {
     switch (plan.tn) {
       case 1: launch_bwd_dma<0, 1>(a, stream); break;

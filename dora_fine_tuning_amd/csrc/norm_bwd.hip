@@ -16,10 +16,11 @@
 //                      the rows of B: B^T [Yhi | Ylo] = s B^T diag(c) B, in
 //                      row slices;
 //   nbwd_finalize_m    Z = s (that r x r matrix), transposed, as Zhi | Zlo;
-//   d_A                the same contraction kernel over the rows of W0 with
-//                      [Yhi | Ylo] and over the rows of A with [Zhi | Zlo]:
-//                      the contraction axis [out rows of W0 ; r rows of A]
-//                      gives d_A^T in row slices;
+//   d_A                the same contraction kernel, in one launch, over the
+//                      rows of W0 with [Yhi | Ylo] and then over the rows of A
+//                      with [Zhi | Zlo] (each row slice takes its share of
+//                      both): the contraction axis [out rows of W0 ; r rows of
+//                      A] gives d_A^T in row slices;
 //   nbwd_finalize_a    sum of the slices and of the hi/lo halves, transposed
 //                      through LDS into d_A [r x in].
 // The hi/lo pairs carry about 16 (bf16) or 22 (fp16) significant bits of the
@@ -162,15 +163,11 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   hipLaunchKernelGGL((nbwd_finalize_m<DT>), stride_grid(r * r), dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, Z);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // d_A^T slices: rows of W0 with Y, then rows of A with Z
-  e = launch_row_contract(a.W0, Y, out, in, 2 * r, p.np.dtype, big, a.stream);
-  if (e != hipSuccess) return e;
-  e = launch_row_contract(a.A, Z, r, in, 2 * r, p.np.dtype, big + static_cast<int64_t>(p.rW.nSplit) * in * 2 * r,
-                          a.stream);
+  // d_A^T slices: the rows of W0 with Y, then (spread over the same slices) the rows of A with Z
+  e = launch_row_contract(a.W0, Y, out, in, 2 * r, p.np.dtype, big, a.stream, a.A, Z, r);
   if (e != hipSuccess) return e;
   const dim3 fgrid(static_cast<unsigned>(ndiv(in, 32)), static_cast<unsigned>(ndiv(r, 32)));
-  hipLaunchKernelGGL((nbwd_finalize_a<DT>), fgrid, dim3(256), 0, a.stream, big, p.rW.nSplit + p.rA.nSplit, in, r,
-                     a.d_A);
+  hipLaunchKernelGGL((nbwd_finalize_a<DT>), fgrid, dim3(256), 0, a.stream, big, p.rW.nSplit, in, r, a.d_A);
   return hipGetLastError();
 }
 
@@ -184,8 +181,7 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype) {
   if (out <= 0 || in <= 0 || r <= 0) return p;
   p.np = make_norm_plan(out, in, r, dtype, true);
   p.rM = row_contract_plan(out, r, 2 * r);
-  p.rW = row_contract_plan(out, in, 2 * r);
-  p.rA = row_contract_plan(r, in, 2 * r);
+  p.rW = row_contract_plan(out, in, 2 * r, r);
   size_t off = 0;
   p.off_np = off;
   off += al256(p.np.bytes);
@@ -196,10 +192,10 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype) {
   p.off_z = off;
   off += al256(static_cast<size_t>(r) * 2 * r * 2);
   p.off_big = off;
-  off += al256(std::max({norm_bwd_acc_bytes(p.np), p.rM.bytes, p.rW.bytes + p.rA.bytes}));
+  off += al256(std::max({norm_bwd_acc_bytes(p.np), p.rM.bytes, p.rW.bytes}));
   p.bytes = off;
-  p.max_grid = std::max({norm_max_grid(p.np), p.rM.grid, p.rW.grid, p.rA.grid, ndiv(in, 32), ndiv(out * r, 256)});
-  p.max_slice_bytes = std::max({p.rM.slice_bytes, p.rW.slice_bytes, p.rA.slice_bytes});
+  p.max_grid = std::max({norm_max_grid(p.np), p.rM.grid, p.rW.grid, ndiv(in, 32), ndiv(out * r, 256)});
+  p.max_slice_bytes = std::max(p.rM.slice_bytes, p.rW.slice_bytes);
   return p;
 }
 

@@ -17,7 +17,7 @@ namespace dora {
 struct NormBwdPlan {
   int64_t out = 0, in = 0, r = 0;
   NormPlan np;
-  RowContractPlan rM, rW, rA;
+  RowContractPlan rM, rW;  // B^T Y; [W0 ; A]^T [Y ; Z]
   size_t off_np = 0, off_c = 0, off_y = 0, off_z = 0, off_big = 0, bytes = 0;
   int64_t max_grid = 0, max_slice_bytes = 0;
 };
