@@ -10,8 +10,10 @@ cannot take goes to eager PyTorch.
 This module registers:
 
 * ``dora_amd::weight_norm`` -- the factored norm ||W0 + s*B*A|| per output row
-  (fp32). It has no autograd formula: the norm is treated as a constant,
-  and callers pass detached A and B.
+  (fp32).  Callers that treat the norm as a constant (the usual DoRA reading)
+  pass detached A and B.  Otherwise its autograd formula is
+  ``dora_amd::weight_norm_backward``, the factored backward into A and B (W0
+  is frozen and gets no gradient); ``weight_norm_cached`` has the same formula.
 * ``dora_amd::lora_compose`` -- the compose with the adapter's second
   projection fused in: from h = x A^T and B it forms lora = h B^T inside the
   kernel and never stores it.  No autograd formula: ``DoRALinear`` uses it on
@@ -25,7 +27,10 @@ This module registers:
   the magnitude m.
 * ``DoRALinear`` -- a linear layer with frozen W0 and trainable A, B and m:
   y = x W0^T + compose(x W0^T, x A^T B^T, m, n, s), with n = ||W0 + s*B*A||
-  detached.
+  detached by default.  With ``detach_norm=False`` the gradient also flows
+  through n: the compose's formula gives dL/dn = -(m / n) * d_mag (L depends on
+  n only through g = m / n; this [out]-sized product is the one step of the
+  chain done by torch), and the norm's formula turns it into d_A and d_B.
 
 Tiers: autograd records the compose only when a gradient is needed.  Under
 ``torch.no_grad()`` or ``torch.inference_mode()`` (or when no input needs a
@@ -87,6 +92,41 @@ def _weight_norm_cached_fake(W0, A, B, base_sq, s):
     return W0.new_empty((W0.shape[0],), dtype=torch.float32)
 
 
+@torch.library.custom_op("dora_amd::weight_norm_backward", mutates_args=(), device_types="cuda")
+def weight_norm_backward(W0: Tensor, A: Tensor, B: Tensor, norm: Tensor, d_norm: Tensor,
+                         s: float) -> tuple[Tensor, Tensor]:
+    """(d_A, d_B) of sum(d_norm * n) for n = ||W0 + s*B*A|| (norm: the forward's n)."""
+    return binding.dora_norm_bwd(W0.contiguous(), A.contiguous(), B.contiguous(), norm.contiguous(),
+                                 d_norm.contiguous().float(), s)
+
+
+@weight_norm_backward.register_fake
+def _weight_norm_backward_fake(W0, A, B, norm, d_norm, s):
+    return torch.empty_like(A), torch.empty_like(B)
+
+
+def _norm_setup(ctx, inputs, output):
+    W0, A, B = inputs[0], inputs[1], inputs[2]
+    ctx.save_for_backward(W0, A, B, output)
+    ctx.s = inputs[-1]
+    ctx.n_inputs = len(inputs)
+
+
+def _norm_grad(ctx, d_norm):
+    W0, A, B, n = ctx.saved_tensors
+    need_a, need_b = ctx.needs_input_grad[1], ctx.needs_input_grad[2]
+    if ctx.needs_input_grad[0]:
+        raise RuntimeError("dora_amd: W0 is frozen; the weight-norm backward gives gradients of A and B only")
+    d_A = d_B = None
+    if need_a or need_b:
+        d_A, d_B = weight_norm_backward(W0, A, B, n, d_norm, ctx.s)
+    return (None, d_A if need_a else None, d_B if need_b else None) + (None,) * (ctx.n_inputs - 3)
+
+
+weight_norm.register_autograd(_norm_grad, setup_context=_norm_setup)
+weight_norm_cached.register_autograd(_norm_grad, setup_context=_norm_setup)
+
+
 # ------------------------------------------------------------------------ compose
 
 
@@ -143,10 +183,13 @@ def _compose_grad(ctx, dy):
     base, lora, mag, norm = ctx.saved_tensors
     want_base = bool(ctx.needs_input_grad[0])
     d_lora, d_base, d_mag = compose_backward(dy, base, lora, mag, norm, ctx.s, ctx.add_base, want_base)
+    # a norm that is not detached: L depends on n only through g = m / n, so
+    # dL/dn = -(m / n) * d_mag, with d_mag = sum_t dy (base + s lora) / n
+    d_norm = -(mag / norm) * d_mag if ctx.needs_input_grad[3] else None
     return (d_base if want_base else None,
             d_lora if ctx.needs_input_grad[1] else None,
             d_mag if ctx.needs_input_grad[2] else None,
-            None, None, None)
+            d_norm, None, None)
 
 
 compose.register_autograd(_compose_grad, setup_context=_compose_setup)
@@ -168,11 +211,17 @@ class DoRALinear(torch.nn.Module):
     on a HIP device) and kept in the buffer ``weight_sqnorm``; the norm then
     takes its base term from there.  After changing ``weight``, call
     ``refresh_weight_cache()``.
+
+    ``detach_norm`` (default True) treats n as a constant in the backward; with
+    False the gradients of A and B also carry the path through n, by the
+    factored norm backward.
     """
 
     def __init__(self, in_features: int, out_features: int, r: int, alpha: float = 32.0,
-                 weight: Tensor | None = None, dtype: torch.dtype = torch.bfloat16, device=None):
+                 weight: Tensor | None = None, dtype: torch.dtype = torch.bfloat16, device=None,
+                 detach_norm: bool = True):
         super().__init__()
+        self.detach_norm = detach_norm
         if dtype not in binding.DTYPE_CODE:
             raise ValueError(f"unsupported dtype {dtype}; bf16 and fp16 are")
         self.in_features, self.out_features, self.r = in_features, out_features, r
@@ -199,10 +248,12 @@ class DoRALinear(torch.nn.Module):
         self.magnitude.copy_(self.weight_norm())
 
     def weight_norm(self) -> Tensor:
-        """n = ||W0 + s*B*A|| per output row, detached (base term from the cache)."""
+        """n = ||W0 + s*B*A|| per output row (base term from the cache); detached
+        unless the layer was built with ``detach_norm=False``."""
         if self.weight_sqnorm is None or self.weight_sqnorm.device != self.weight.device:
             self.refresh_weight_cache()
-        return weight_norm_cached(self.weight, self.lora_A.detach(), self.lora_B.detach(), self.weight_sqnorm, self.s)
+        A, B = (self.lora_A.detach(), self.lora_B.detach()) if self.detach_norm else (self.lora_A, self.lora_B)
+        return weight_norm_cached(self.weight, A, B, self.weight_sqnorm, self.s)
 
     def forward(self, x: Tensor) -> Tensor:
         lead = x.shape[:-1]

@@ -91,6 +91,13 @@ def test_opcheck():
     sq = torch_ops.row_sqnorm(W0)
     torch.library.opcheck(torch_ops.weight_norm_cached, (W0, A, B, sq, 1.5),
                           test_utils=("test_schema", "test_faketensor"))
+    Ag, Bg = A.clone().requires_grad_(), B.clone().requires_grad_()
+    torch.library.opcheck(torch_ops.weight_norm, (W0, Ag, Bg, 1.5),
+                          test_utils=("test_schema", "test_autograd_registration", "test_faketensor"))
+    n = torch_ops.weight_norm(W0, A, B, 1.5)
+    dn = torch.randn_like(n)
+    torch.library.opcheck(torch_ops.weight_norm_backward, (W0, A, B, n, dn, 1.5),
+                          test_utils=("test_schema", "test_faketensor"))
 
 
 @gpu
@@ -186,3 +193,44 @@ def test_dora_linear_starts_as_base_layer_and_inference_tier():
     ref = (m / n) * (xd @ W.T + layer.s * (xd @ A.T) @ B.T)
     assert _rel(y_inf, ref) < 1e-2 and _rel(y_train, ref) < 1e-2
     assert _rel(y_inf, y_train) < 1e-2
+
+
+def _dense_reference_full(x, W0, A, B, m, s, dy):
+    """float64 CPU, norm NOT detached: n = ||W0 + s B A|| inside the graph."""
+    xd, W0d, Ad, Bd, md = (t.detach().double().cpu().requires_grad_() for t in (x, W0, A, B, m))
+    W0d.requires_grad_(False)
+    n = torch.linalg.vector_norm(W0d + s * (Bd @ Ad), dim=1)
+    g = md / n
+    base = xd @ W0d.T
+    y = g * (base + s * ((xd @ Ad.T) @ Bd.T))
+    y.backward(dy.double().cpu())
+    return y.detach(), xd.grad, Ad.grad, Bd.grad, md.grad
+
+
+@gpu
+def test_dora_linear_norm_not_detached():
+    dev = torch.device("cuda:0")
+    torch.manual_seed(3)
+    layer = torch_ops.DoRALinear(256, 192, 16, alpha=32.0, device=dev, detach_norm=False)
+    with torch.no_grad():
+        layer.lora_B.normal_(0.0, 0.05)
+        layer.magnitude.mul_(1.0 + 0.01 * torch.randn_like(layer.magnitude))
+    x = torch.randn(2, 40, 256, device=dev, dtype=torch.bfloat16).requires_grad_()
+    y = layer(x)
+    # dy close to y (the gradient of |y|^2 / 2): the sums over tokens of dy * y
+    # that drive the path through n then add up instead of cancelling
+    dy = (y.detach().float() + 0.1 * torch.randn(y.shape, device=dev)).to(y.dtype)
+    y.backward(dy)
+    y_ref, dx_ref, dA_ref, dB_ref, dm_ref = _dense_reference_full(
+        x.reshape(-1, 256), layer.weight, layer.lora_A, layer.lora_B, layer.magnitude, layer.s, dy.reshape(-1, 192))
+    _, _, dA_det, dB_det, _, _ = _dense_reference(
+        x.reshape(-1, 256), layer.weight, layer.lora_A, layer.lora_B, layer.magnitude, layer.s, dy.reshape(-1, 192))
+    assert _rel(y.reshape(-1, 192), y_ref) < 2e-2
+    assert _rel(x.grad.reshape(-1, 256), dx_ref) < 2e-2
+    assert _rel(layer.magnitude.grad, dm_ref) < 2e-2
+    # the path through n changes the adapter gradients by more than the tolerance,
+    # so these checks tell the two readings apart
+    assert _rel(dA_det, dA_ref) > 0.1 and _rel(dB_det, dB_ref) > 0.1
+    assert _rel(layer.lora_A.grad, dA_ref) < 3e-2
+    assert _rel(layer.lora_B.grad, dB_ref) < 3e-2
+    assert layer.weight.grad is None
