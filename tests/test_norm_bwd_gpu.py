@@ -160,14 +160,18 @@ def test_norm_bwd_degenerate_sizes(lib):
     assert torch.all(d_B == 0)
 
 
-@pytest.mark.parametrize("name", ["attn_proj", "wide_8192_r384"])
-def test_norm_bwd_full_size_sampled(lib, name):
+FULL = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("mlp_up_27648x5120", "bf16"),
+        ("sweep_r16", "bf16"), ("sweep_r768", "fp16")]
+
+
+@pytest.mark.parametrize("name,dtype", FULL, ids=lambda v: str(v))
+def test_norm_bwd_full_size_sampled(lib, name, dtype):
     cfg = synth.CONFIGS[name]
-    log(f"norm_bwd full size {name}: out={cfg.out} in={cfg.in_} r={cfg.r}")
-    W0, A, B = synth.weights(cfg)
+    log(f"norm_bwd full size {name} {dtype}: out={cfg.out} in={cfg.in_} r={cfg.r}")
+    W0, A, B = synth.weights(cfg, dtype)
     rng = np.random.default_rng(4000 + cfg.out + cfg.r)
     d_norm = (rng.standard_normal(cfg.out) * 30).astype(np.float32)
     norm = np.linalg.norm(f64(W0), axis=1).astype(np.float32)
     rows = np.sort(rng.choice(cfg.out, 64, replace=False))
     cols = np.sort(rng.choice(cfg.in_, 64, replace=False))
-    check(lib, W0, A, B, cfg.s, d_norm, norm, "bf16", f"{name} sampled", rows=rows, cols=cols)
+    check(lib, W0, A, B, cfg.s, d_norm, norm, dtype, f"{name} {dtype} sampled", rows=rows, cols=cols)
