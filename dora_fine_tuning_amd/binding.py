@@ -299,6 +299,7 @@ def dora_norm_bwd(W0, A, B, norm, d_norm, s: float, d_A=None, d_B=None, workspac
     out, in_ = W0.shape
     r = A.shape[0]
     dev = W0.device
+    _matrix(W0, "W0", (out, in_), W0.dtype, dev)
     _matrix(A, "A", (r, in_), W0.dtype, dev)
     _matrix(B, "B", (out, r), W0.dtype, dev)
     _matrix(norm, "norm", (out,), torch.float32, dev)

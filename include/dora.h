@@ -214,7 +214,9 @@ DORA_API size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r
  * Needs in and r multiples of 8, in < 2^21, r <= 2^20 and 16-byte aligned
  * matrix and workspace pointers, else DORA_UNSUPPORTED (no general path).
  * In fp16 the lo halves lose bits where |s*c*B| falls below about 2^-3
- * (their values reach fp16's subnormal range).
+ * (their values reach fp16's subnormal range), and s*c*B or the r x r
+ * product beyond fp16's range (65504) overflows: the caller keeps d_norm/norm
+ * in range (bf16 has fp32's exponent range).
  */
 DORA_API int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* norm, const float* d_norm,
                            int64_t out, int64_t in, int64_t r, float s, int dtype, void* d_A, void* d_B, void* ws,

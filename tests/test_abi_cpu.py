@@ -241,3 +241,19 @@ def test_norm_bwd_validation():
     _status(LIB.dora_norm_bwd(*args(d_A=P * 7 + 16)), INVALID, "overlap")
     _status(LIB.dora_norm_bwd(*args(ws=P + 1024)), INVALID, "overlaps")
     assert LIB.dora_norm_bwd(*args(r=0, W0=None, A=None, B=None)) == OK
+
+
+def test_norm_bwd_workspace_is_factored():
+    # O(out*r + in*r + r*r) scratch, well under the dense out x in transient
+    # (V and dV in bf16) at every workload shape.  The row slices of the
+    # contractions are sized for one workgroup per CU (256 CUs, 128-column
+    # blocks), which adds at most 2r * 4 bytes per row of 256 * 128 rows.
+    for c in synth.CONFIGS.values():
+        ws = LIB.dora_norm_bwd_workspace_bytes(c.out, c.in_, c.r, 0)
+        dense = 2 * 2 * c.out * c.in_
+        bound = 24 * (c.out * c.r + c.in_ * c.r + c.r * c.r) + 8 * c.r * 256 * 128 + 4 * c.out + 4096
+        assert 0 < ws <= bound, (c.name, ws, bound)
+        if c.out * c.in_ >= 4096 * 4096:
+            assert ws < dense / 2, (c.name, ws, dense)
+    assert LIB.dora_norm_bwd_workspace_bytes(64, 64, 0, 0) == 0
+    assert LIB.dora_norm_bwd_workspace_bytes(0, 64, 8, 0) == 0
