@@ -78,11 +78,19 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t j = e / r, l = e - j * r;  // l fastest: the reads of E[j][.] are coalesced
+    const float* Ej = E + j * 2 * r + l;
+    // slices in groups of 8, all 16 loads of a group in flight before the
+    // group is added in order
     float m = 0.0f;
-    for (int p = 0; p < nSplit; ++p) {
-      const float* Ep = E + p * slice + j * 2 * r;
-      m += Ep[l] + Ep[r + l];
+    int p = 0;
+    for (; p + 8 <= nSplit; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = Ej[(p + q) * slice] + Ej[(p + q) * slice + r];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m += v[q];
     }
+    for (; p < nSplit; ++p) m += Ej[p * slice] + Ej[p * slice + r];
     const float z = s * m;
     const T hi = Dt<DT>::from_f(z);
     Z[l * 2 * r + j] = hi;
