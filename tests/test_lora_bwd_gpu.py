@@ -135,13 +135,18 @@ def test_lora_bwd_matches_unfused_gradients(lib):
     assert rel(d_mag, d_mag_u) < 1e-2
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_lora_bwd_wide_config(lib, dtype):
-    """The module out = in = 8192, r = 384, T = 8192 tokens, in the benchmark's
-    launch configuration: 64 sampled output columns (all tokens) for d_B and
-    d_mag, 64 sampled token rows of d_base."""
-    cfg = synth.CONFIGS["wide_8192_r384"]
-    log(f"[lora-bwd] wide {dtype}: generating")
+FULL = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("wide_8192_r384", "fp16"),
+        ("mlp_up_27648x5120", "bf16"), ("sweep_r16", "bf16"), ("sweep_r768", "fp16")]
+
+
+@pytest.mark.parametrize("name,dtype", FULL, ids=lambda v: str(v))
+def test_lora_bwd_full_config(lib, name, dtype):
+    """A workload module at full size (the wide one, out = in = 8192, r = 384,
+    T = 8192, is the benchmark's), in the benchmark's launch configuration: 64
+    sampled output columns (all tokens) for d_B and d_mag, 64 sampled token
+    rows of d_base."""
+    cfg = synth.CONFIGS[name]
+    log(f"[lora-bwd] {name} {dtype}: generating")
     W0, A, B = synth.weights(cfg, dtype)
     x, dy = synth.activations(cfg, dtype)
     base, h = synth.base_and_h(x, W0, A, device=DEV)
@@ -151,5 +156,5 @@ def test_lora_bwd_wide_config(lib, dtype):
     rng = np.random.default_rng(cfg.index + 1)
     cols = np.unique(np.concatenate([[0, cfg.out - 1], rng.choice(cfg.out, 62, replace=False)]))
     rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 62, replace=False)]))
-    check(lib, dy, base.cpu(), h.cpu(), B, m, n, cfg.s, dtype, f"wide {dtype}", cols=cols, rows=rows)
-    log(f"[lora-bwd] wide {dtype}: ok")
+    check(lib, dy, base.cpu(), h.cpu(), B, m, n, cfg.s, dtype, f"{name} {dtype}", cols=cols, rows=rows)
+    log(f"[lora-bwd] {name} {dtype}: ok")

@@ -124,14 +124,19 @@ def test_lora_compose_determinism_and_identity(lib):
     assert torch.count_nonzero(y).item() == 0
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_lora_compose_wide_config(lib, dtype):
-    """The module out = in = 8192, r = 384, T = 8192 tokens, in the benchmark's
-    launch configuration: 96 sampled token rows, every column, against the
-    oracle; and the near-unity check (h = 0: the correction alone, nonzero
-    wherever the oracle's is and the dtype can hold it)."""
-    cfg = synth.CONFIGS["wide_8192_r384"]
-    log(f"[lora-fused] wide {dtype}: generating")
+FULL = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("wide_8192_r384", "fp16"),
+        ("mlp_up_27648x5120", "bf16"), ("sweep_r16", "bf16"), ("sweep_r768", "fp16")]
+
+
+@pytest.mark.parametrize("name,dtype", FULL, ids=lambda v: str(v))
+def test_lora_compose_full_config(lib, name, dtype):
+    """A workload module at full size (the wide one, out = in = 8192, r = 384,
+    T = 8192, is the benchmark's), in the benchmark's launch configuration: 96
+    sampled token rows, every column, against the oracle; and the near-unity
+    check (h = 0: the correction alone, nonzero wherever the oracle's is and
+    the dtype can hold it)."""
+    cfg = synth.CONFIGS[name]
+    log(f"[lora-fused] {name} {dtype}: generating")
     W0, A, B = synth.weights(cfg, dtype)
     x, _ = synth.activations(cfg, dtype)
     base, h = synth.base_and_h(x, W0, A, device=DEV)
@@ -148,8 +153,8 @@ def test_lora_compose_wide_config(lib, dtype):
         y = lib.dora_lora_compose_fwd(base, h, Bd, md, nd, cfg.s, add_base=add_base)
         ref = O.lora_compose_fwd(br, hr, Bf, m, n32, cfg.s, add_base=add_base)
         fo = PU.assert_compose(f64(y[ri]), ref, mass(br, hr, Bf, m, n32, cfg.s, add_base), dtype,
-                               f"wide fused add_base={add_base}", floor_rel(cfg.r))
-        log(f"[lora-fused] wide {dtype} add_base={add_base}: ok ({fo} floor-only elements)")
+                               f"{name} fused add_base={add_base}", floor_rel(cfg.r))
+        log(f"[lora-fused] {name} {dtype} add_base={add_base}: ok ({fo} floor-only elements)")
         del y
     z = torch.zeros_like(h)
     y = f64(lib.dora_lora_compose_fwd(base, z, Bd, md, nd, cfg.s)[ri])
@@ -159,4 +164,4 @@ def test_lora_compose_wide_config(lib, dtype):
     assert near.any()
     want = PU.representable_nonzero(ref, dtype)[:, near]
     assert np.all((y != 0)[:, near] == want)
-    log(f"[lora-fused] wide {dtype}: near-unity correction nonzero in all {int(want.sum())} representable elements")
+    log(f"[lora-fused] {name} {dtype}: near-unity correction nonzero in all {int(want.sum())} representable elements")
