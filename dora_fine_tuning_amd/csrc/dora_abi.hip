@@ -252,7 +252,7 @@ int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const
 
 size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
   if (out < 0 || in < 0 || r < 0 || !valid_dtype(dtype)) return 0;
-  return dora::make_norm_bwd_plan(out, in, r, dtype).bytes;
+  return dora::norm_bwd_workspace_bytes(out, in, r, dtype);
 }
 
 int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* norm, const float* d_norm, int64_t out,
@@ -267,12 +267,10 @@ int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* nor
   if (in > 0 && (!A || !d_A)) return fail(DORA_INVALID_ARG, "%s: A or d_A is NULL", fn);
   if (out > 0 && (!B || !d_B || !norm || !d_norm)) return fail(DORA_INVALID_ARG, "%s: B, d_B, norm or d_norm is NULL", fn);
   if (out > 0 && in > 0 && !W0) return fail(DORA_INVALID_ARG, "%s: W0 is NULL", fn);
-  if (in % 8 != 0 || r % 8 != 0 || in >= (int64_t(1) << 21) || r > (int64_t(1) << 20))
-    return fail(DORA_UNSUPPORTED, "%s: needs in and r multiples of 8, in < 2^21, r <= 2^20 (in=%lld r=%lld)", fn,
-                (long long)in, (long long)r);
-  if (!aligned16(W0) || !aligned16(A) || !aligned16(B) || !aligned16(d_A) || !aligned16(d_B) || !aligned16(ws))
-    return fail(DORA_UNSUPPORTED, "%s: matrix and workspace pointers must be 16-byte aligned", fn);
-  const dora::NormBwdPlan plan = dora::make_norm_bwd_plan(out, in, r, dtype);
+  const bool vec = in % 8 == 0 && r % 8 == 0 && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20) &&
+                   aligned16(W0) && aligned16(A) && aligned16(B) && aligned16(d_A) && aligned16(d_B) &&
+                   aligned16(ws);
+  const dora::NormBwdPlan plan = dora::make_norm_bwd_plan(out, in, r, dtype, vec);
   const size_t need = plan.bytes;
   if (ws_bytes < need) return fail(DORA_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
   if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "%s: workspace is NULL", fn);

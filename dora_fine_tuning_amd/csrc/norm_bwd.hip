@@ -25,6 +25,8 @@
 //                      through LDS into d_A [r x in].
 // The hi/lo pairs carry about 16 (bf16) or 22 (fp16) significant bits of the
 // computed operands Y and Z into the bf16/fp16 MFMAs; W0, A and B enter exactly.
+// Sizes or pointers the 16-byte path cannot take go to a general path of plain
+// fp32 loops (one thread per output element).
 #include <algorithm>
 
 #include "dora_common.hpp"
@@ -147,12 +149,94 @@ hipError_t zero_t(void* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// General path (in or r not a multiple of 8, or unaligned pointers): one
+// thread per output element, every sum in order in fp32, no MFMA.
+
+// c_i = dn_i / n_i (0 where n_i == 0)
+__global__ __launch_bounds__(256) void nbwd_gen_c(const float* norm, const float* d_norm, int64_t out, float* c) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= out) return;
+  const float ni = norm[i];
+  c[i] = ni != 0.0f ? d_norm[i] / ni : 0.0f;
+}
+
+// G[j][l] = sum_k A_jk A_lk and M[j][l] = sum_i c_i B_ij B_il, both [r x r] fp32
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_gen_gm(const void* Av, const void* Bv, const float* c, int64_t out,
+                                                   int64_t in, int64_t r, float* G, float* M) {
+  using T = typename Dt<DT>::T;
+  const T* A = static_cast<const T*>(Av);
+  const T* B = static_cast<const T*>(Bv);
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= r * r) return;
+  const int64_t j = e / r, l = e - j * r;
+  float g = 0.0f, m = 0.0f;
+  for (int64_t k = 0; k < in; ++k) g = __builtin_fmaf(Dt<DT>::to_f(A[j * in + k]), Dt<DT>::to_f(A[l * in + k]), g);
+  for (int64_t i = 0; i < out; ++i)
+    m = __builtin_fmaf(c[i] * Dt<DT>::to_f(B[i * r + j]), Dt<DT>::to_f(B[i * r + l]), m);
+  G[e] = g;
+  M[e] = m;
+}
+
+// d_B[i][j] = s c_i (sum_k W0_ik A_jk + s sum_l B_il G_lj)
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_gen_db(const void* Wv, const void* Av, const void* Bv, const float* c,
+                                                   const float* G, int64_t out, int64_t in, int64_t r, float s,
+                                                   void* dBv) {
+  using T = typename Dt<DT>::T;
+  const T *W = static_cast<const T*>(Wv), *A = static_cast<const T*>(Av), *B = static_cast<const T*>(Bv);
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= out * r) return;
+  const int64_t i = e / r, j = e - i * r;
+  float u = 0.0f, q = 0.0f;
+  for (int64_t k = 0; k < in; ++k) u = __builtin_fmaf(Dt<DT>::to_f(W[i * in + k]), Dt<DT>::to_f(A[j * in + k]), u);
+  for (int64_t l = 0; l < r; ++l) q = __builtin_fmaf(Dt<DT>::to_f(B[i * r + l]), G[l * r + j], q);
+  static_cast<T*>(dBv)[e] = Dt<DT>::from_f((s * c[i]) * __builtin_fmaf(s, q, u));
+}
+
+// d_A[j][k] = s (sum_i c_i B_ij W0_ik + s sum_l M_jl A_lk)
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_gen_da(const void* Wv, const void* Av, const void* Bv, const float* c,
+                                                   const float* M, int64_t out, int64_t in, int64_t r, float s,
+                                                   void* dAv) {
+  using T = typename Dt<DT>::T;
+  const T *W = static_cast<const T*>(Wv), *A = static_cast<const T*>(Av), *B = static_cast<const T*>(Bv);
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= r * in) return;
+  const int64_t j = e / in, k = e - j * in;  // k fastest: the reads of W0 rows are coalesced
+  float a1 = 0.0f, a2 = 0.0f;
+  for (int64_t i = 0; i < out; ++i)
+    a1 = __builtin_fmaf(c[i] * Dt<DT>::to_f(B[i * r + j]), Dt<DT>::to_f(W[i * in + k]), a1);
+  for (int64_t l = 0; l < r; ++l) a2 = __builtin_fmaf(M[j * r + l], Dt<DT>::to_f(A[l * in + k]), a2);
+  static_cast<T*>(dAv)[e] = Dt<DT>::from_f(s * __builtin_fmaf(s, a2, a1));
+}
+
+template <int DT>
+hipError_t launch_norm_bwd_gen_t(const NormBwdPlan& p, const NormBwdArgs& a) {
+  const int64_t out = p.out, in = p.in, r = p.r;
+  char* ws = static_cast<char*>(a.ws);
+  float* c = reinterpret_cast<float*>(ws + p.off_c);
+  float* G = reinterpret_cast<float*>(ws + p.off_y);
+  float* M = reinterpret_cast<float*>(ws + p.off_z);
+  hipLaunchKernelGGL(nbwd_gen_c, dim3(static_cast<unsigned>(ndiv(out, 256))), dim3(256), 0, a.stream, a.norm,
+                     a.d_norm, out, c);
+  hipLaunchKernelGGL((nbwd_gen_gm<DT>), dim3(static_cast<unsigned>(ndiv(r * r, 256))), dim3(256), 0, a.stream, a.A,
+                     a.B, c, out, in, r, G, M);
+  hipLaunchKernelGGL((nbwd_gen_db<DT>), dim3(static_cast<unsigned>(ndiv(out * r, 256))), dim3(256), 0, a.stream,
+                     a.W0, a.A, a.B, c, G, out, in, r, a.s, a.d_B);
+  hipLaunchKernelGGL((nbwd_gen_da<DT>), dim3(static_cast<unsigned>(ndiv(r * in, 256))), dim3(256), 0, a.stream,
+                     a.W0, a.A, a.B, c, M, out, in, r, a.s, a.d_A);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   const int64_t out = p.out, in = p.in, r = p.r;
   if (r == 0) return hipSuccess;
   if (out == 0) return zero_t<DT>(a.d_A, r * in, a.stream);
   if (in == 0) return zero_t<DT>(a.d_B, out * r, a.stream);
+  if (!p.vec) return launch_norm_bwd_gen_t<DT>(p, a);
   char* ws = static_cast<char*>(a.ws);
   float* c = reinterpret_cast<float*>(ws + p.off_c);
   void* Y = ws + p.off_y;
@@ -181,12 +265,22 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
 
 }  // namespace
 
-NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype) {
+NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec) {
   NormBwdPlan p;
   p.out = out;
   p.in = in;
   p.r = r;
+  p.vec = vec;
   if (out <= 0 || in <= 0 || r <= 0) return p;
+  if (!vec) {
+    // c [out], G and M [r x r] fp32 (in the Y and Z slots)
+    p.off_c = 0;
+    p.off_y = al256(static_cast<size_t>(out) * 4);
+    p.off_z = p.off_y + al256(static_cast<size_t>(r) * r * 4);
+    p.bytes = p.off_z + al256(static_cast<size_t>(r) * r * 4);
+    p.max_grid = std::max({ndiv(out, 256), ndiv(r * r, 256), ndiv(out * r, 256), ndiv(r * in, 256)});
+    return p;
+  }
   p.np = make_norm_plan(out, in, r, dtype, true);
   p.rM = row_contract_plan(out, r, 2 * r);
   p.rW = row_contract_plan(out, in, 2 * r, r);
@@ -205,6 +299,13 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype) {
   p.max_grid = std::max({norm_max_grid(p.np), p.rM.grid, p.rW.grid, ndiv(in, 32), ndiv(out * r, 256)});
   p.max_slice_bytes = std::max(p.rM.slice_bytes, p.rW.slice_bytes);
   return p;
+}
+
+size_t norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype) {
+  size_t b = make_norm_bwd_plan(out, in, r, dtype, false).bytes;
+  if (in % 8 == 0 && r % 8 == 0 && in < (int64_t(1) << 21) && r <= (int64_t(1) << 20))
+    b = std::max(b, make_norm_bwd_plan(out, in, r, dtype, true).bytes);
+  return b;
 }
 
 hipError_t launch_norm_bwd(const NormBwdPlan& p, const NormBwdArgs& a) {

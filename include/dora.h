@@ -183,10 +183,11 @@ DORA_API int dora_lora_compose_fwd(const void* base, const void* h, const void* 
                                    int add_base, void* y, hipStream_t stream);
 
 /*
- * Bytes of device workspace dora_norm_bwd needs for these sizes: the Gram
- * scratch of the norm, c [out] fp32, the hi/lo pair of s*c*B [out x 2r] and of
- * an r x r product [r x 2r] in the storage dtype, and one fp32 region of
- * row-slice partials of size O(out*r + in*r) reused by the steps in turn.
+ * Bytes of device workspace dora_norm_bwd needs for these sizes (either
+ * path): on the fast path the Gram scratch of the norm, c [out] fp32, the
+ * hi/lo pair of s*c*B [out x 2r] and of an r x r product [r x 2r] in the
+ * storage dtype, and one fp32 region of row-slice partials of size
+ * O(out*r + in*r) reused by the steps in turn.
  * Returns 0 for negative sizes or an unknown dtype.
  */
 DORA_API size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
@@ -211,8 +212,10 @@ DORA_API size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r
  * (the forward's n) and d_norm: device fp32 [out].  No output overlaps an
  * input, the other output or ws.  ws: at least dora_norm_bwd_workspace_bytes
  * bytes.  r == 0 is a no-op; out == 0 gives d_A = 0; in == 0 gives d_B = 0.
- * Needs in and r multiples of 8, in < 2^21, r <= 2^20 and 16-byte aligned
- * matrix and workspace pointers, else DORA_UNSUPPORTED (no general path).
+ * The fast path needs in and r multiples of 8, in < 2^21, r <= 2^20 and
+ * 16-byte aligned matrix and workspace pointers; other cases take a slow
+ * general path (one thread per output element, every sum in order in fp32,
+ * no hi/lo operands).
  * In fp16 the lo halves lose bits where |s*c*B| falls below about 2^-3
  * (their values reach fp16's subnormal range), and s*c*B or the r x r
  * product beyond fp16's range (65504) overflows: the caller keeps d_norm/norm

@@ -232,9 +232,11 @@ def test_norm_bwd_validation():
     _status(LIB.dora_norm_bwd(*args(A=None)), INVALID, "A or d_A")
     _status(LIB.dora_norm_bwd(*args(d_norm=None)), INVALID, "d_norm")
     _status(LIB.dora_norm_bwd(*args(W0=None)), INVALID, "W0")
-    _status(LIB.dora_norm_bwd(*args(in_=60)), UNSUPPORTED, "multiples of 8")
-    _status(LIB.dora_norm_bwd(*args(r=12)), UNSUPPORTED, "multiples of 8")
-    _status(LIB.dora_norm_bwd(*args(B=P * 3 + 8)), UNSUPPORTED, "aligned")
+    # sizes the 16-byte path cannot take go to the general path, whose (smaller)
+    # workspace is still checked before any launch
+    ws_gen = LIB.dora_norm_bwd_workspace_bytes(64, 60, 12, 0)
+    assert ws_gen > 0
+    _status(LIB.dora_norm_bwd(*args(in_=60, r=12, wsb=3)), INVALID, "workspace")
     _status(LIB.dora_norm_bwd(*args(wsb=ws - 1)), INVALID, "workspace")
     _status(LIB.dora_norm_bwd(*args(ws=None)), INVALID, "workspace is NULL")
     _status(LIB.dora_norm_bwd(*args(d_B=P * 3 + 64)), INVALID, "overlaps")

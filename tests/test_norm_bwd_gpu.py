@@ -61,25 +61,29 @@ def case(out, in_, r, dtype, seed):
     return W0, A, B, s, d_norm
 
 
-def floors(W0, A, B, c, s):
-    """Cancellation floors of d_A [r x in] and d_B [out x r] (see the module docstring)."""
+def floors(W0, A, B, c, s, general=False):
+    """Cancellation floors of d_A [r x in] and d_B [out x r] (see the module
+    docstring).  The general path sums one product at a time: K steps, not K/16."""
     out, in_ = W0.shape
     r = A.shape[0]
+    step = 1 if general else 16
     aW, aA, aB, ac = np.abs(W0), np.abs(A), np.abs(B), np.abs(c)
     G = A @ A.T
     gram_B = s * s * ac[:, None] * (aB @ np.abs(G))
     mass_B = s * ac[:, None] * (aW @ aA.T) + gram_B
-    floor_B = 3.0 * (in_ / 16 + 100) * 2.0**-24 * mass_B + 2.0**-16 * gram_B
+    floor_B = 3.0 * ((in_ + r) / step + 100) * 2.0**-24 * mass_B + 2.0**-16 * gram_B
     Ymass = s * ac[:, None] * aB
     mass_A = Ymass.T @ aW + (s * s * (aB.T @ (ac[:, None] * aB))) @ aA
-    floor_A = (3.0 * ((out + r) / 16 + 100) * 2.0**-24 + 2.0**-16) * mass_A
+    floor_A = (3.0 * ((out + r) / step + 100) * 2.0**-24 + 2.0**-16) * mass_A
     return floor_A, floor_B
 
 
-def check(lib, W0, A, B, s, d_norm, norm, dtype, what, rows=None, cols=None):
+def check(lib, W0, A, B, s, d_norm, norm, dtype, what, rows=None, cols=None, Wd=None):
     out, in_ = W0.shape
     r = A.shape[0]
-    Wd, Ad, Bd = W0.to(DEV), A.to(DEV), B.to(DEV)
+    general = in_ % 8 != 0 or r % 8 != 0 or Wd is not None
+    Wd = W0.to(DEV) if Wd is None else Wd
+    Ad, Bd = A.to(DEV), B.to(DEV)
     nd, dd = torch.from_numpy(norm).to(DEV), torch.from_numpy(d_norm).to(DEV)
     d_A, d_B = lib.dora_norm_bwd(Wd, Ad, Bd, nd, dd, s)
     torch.cuda.synchronize()
@@ -91,8 +95,8 @@ def check(lib, W0, A, B, s, d_norm, norm, dtype, what, rows=None, cols=None):
     _, rB = O.weight_norm_bwd(d_norm[rows], norm[rows], Wf[rows], Af, Bf[rows], s)
     # d_A on the sampled input columns: the columns of V = W0 + s B A are independent
     rA, _ = O.weight_norm_bwd(d_norm, norm, Wf[:, cols], Af[:, cols], Bf, s)
-    fA, _ = floors(Wf[:, cols], Af[:, cols], Bf, c, s)
-    _, fB = floors(Wf[rows], Af, Bf[rows], c[rows], s)
+    fA, _ = floors(Wf[:, cols], Af[:, cols], Bf, c, s, general)
+    _, fB = floors(Wf[rows], Af, Bf[rows], c[rows], s, general)
     nA = PU.assert_compose(f64(d_A)[:, cols], rA, fA, dtype, f"{what} d_A", 1.0)
     nB = PU.assert_compose(f64(d_B)[rows], rB, fB, dtype, f"{what} d_B", 1.0)
     log(f"{what}: d_A {rA.size} and d_B {rB.size} elements within tolerance ({nA} and {nB} on the floor only)")
@@ -118,6 +122,36 @@ def test_norm_bwd_small(lib, shape, dtype):
     W0, A, B, s, d_norm = case(out, in_, r, dtype, sum(shape))
     norm = O.weight_norm(W0, A, B, s).astype(np.float32)
     check(lib, W0, A, B, s, d_norm, norm, dtype, f"{shape} {dtype}")
+
+
+GENERAL = [
+    (37, 29, 5),     # nothing a multiple of 8
+    (100, 66, 12),   # in and r not multiples of 8
+    (64, 60, 8),     # in alone
+    (48, 64, 20),    # r alone
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("shape", GENERAL, ids=lambda s: "x".join(map(str, s)))
+def test_norm_bwd_general_path(lib, shape, dtype):
+    out, in_, r = shape
+    log(f"norm_bwd general path {shape} {dtype}")
+    W0, A, B, s, d_norm = case(out, in_, r, dtype, 50 + sum(shape))
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    check(lib, W0, A, B, s, d_norm, norm, dtype, f"general {shape} {dtype}")
+
+
+def test_norm_bwd_unaligned_takes_general_path(lib):
+    # a 16-byte path shape whose W0 starts 2 bytes past an aligned address
+    log("norm_bwd unaligned W0")
+    W0, A, B, s, d_norm = case(96, 128, 16, "bf16", 61)
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    buf = torch.empty(W0.numel() + 1, dtype=W0.dtype, device=DEV)
+    Wd = buf[1:].view(W0.shape)
+    Wd.copy_(W0.to(DEV))
+    assert Wd.data_ptr() % 16 != 0
+    check(lib, W0, A, B, s, d_norm, norm, "bf16", "unaligned W0", Wd=Wd)
 
 
 def test_norm_bwd_zero_norm_rows_and_determinism(lib):
