@@ -140,7 +140,10 @@ __global__ __launch_bounds__(NTH) void compose_bwd_vec(const Chunk* dy, const Ch
   const int64_t bid = blockIdx.x;
   const int64_t c8 = (bid % ncb) * NTH + threadIdx.x;
   if (c8 >= out8) return;
-  const int64_t rb = bid / ncb;
+  // Token blocks in reverse order: the forward that precedes the backward in a
+  // training step reads base and lora from first row to last, so their last
+  // rows are the ones still in the last-level cache when the backward starts.
+  const int64_t rb = (T + ROWS - 1) / ROWS - 1 - bid / ncb;
   const int64_t t0 = rb * ROWS;
   const int64_t t1 = (t0 + ROWS < T) ? t0 + ROWS : T;
 
