@@ -16,8 +16,9 @@ This module registers:
   is frozen and gets no gradient); ``weight_norm_cached`` has the same formula.
 * ``dora_amd::lora_compose`` -- the compose with the adapter's second
   projection fused in: from h = x A^T and B it forms lora = h B^T inside the
-  kernel and never stores it.  No autograd formula: ``DoRALinear`` uses it on
-  the inference tier, where nothing is saved for a backward.
+  kernel and never stores it.  Its autograd formula is
+  ``dora_amd::lora_compose_backward`` (d_base, d_B and d_mag without lora or
+  d_lora), plus d_h = dy (g s .* B), a GEMM done by torch.
 * ``dora_amd::row_sqnorm`` and ``dora_amd::weight_norm_cached`` -- the cached
   base term the page proposes as future work (W0 is frozen): ||W0_i||^2 once,
   then the norm that takes it instead of re-deriving it from W0.
@@ -32,10 +33,11 @@ This module registers:
   n only through g = m / n; this [out]-sized product is the one step of the
   chain done by torch), and the norm's formula turns it into d_A and d_B.
 
-Tiers: autograd records the compose only when a gradient is needed.  Under
-``torch.no_grad()`` or ``torch.inference_mode()`` (or when no input needs a
-gradient) ``DoRALinear`` runs the compose with the second projection fused in:
-lora = x A^T B^T is never stored. There is no eager fallback. Inputs the kernels
+Tiers: autograd records the compose only when a gradient is needed (training:
+the fused forward, then the fused backward); under ``torch.no_grad()`` or
+``torch.inference_mode()`` the forward kernel runs alone.  ``DoRALinear`` runs
+the compose with the second projection fused in on both tiers, so lora =
+x A^T B^T is never stored. There is no eager fallback. Inputs the kernels
 cannot take raise: CPU tensors, dtypes other than bf16/fp16, and a missing
 library.
 
@@ -195,6 +197,51 @@ def _compose_grad(ctx, dy):
 compose.register_autograd(_compose_grad, setup_context=_compose_setup)
 
 
+@torch.library.custom_op("dora_amd::lora_compose_backward", mutates_args=(), device_types="cuda")
+def lora_compose_backward(dy: Tensor, base: Tensor, h: Tensor, B: Tensor, mag: Tensor, norm: Tensor, s: float,
+                          add_base: bool, want_base: bool) -> tuple[Tensor, Tensor, Tensor]:
+    """(d_base, d_B, d_mag) of ``lora_compose``, lora and d_lora never formed.
+    With want_base false the kernel does not write d_base and an empty tensor
+    stands in for it."""
+    d_base, d_B, d_mag = binding.dora_lora_compose_bwd(dy.contiguous(), base.contiguous(), h.contiguous(),
+                                                       B.contiguous(), mag.contiguous(), norm.contiguous(), s,
+                                                       add_base=add_base, want_d_base=want_base)
+    if d_base is None:
+        d_base = dy.new_empty((0,))
+    return d_base, d_B, d_mag
+
+
+@lora_compose_backward.register_fake
+def _lora_compose_backward_fake(dy, base, h, B, mag, norm, s, add_base, want_base):
+    d_base = torch.empty_like(dy) if want_base else dy.new_empty((0,))
+    return d_base, torch.empty_like(B), mag.new_empty(mag.shape)
+
+
+def _lora_compose_setup(ctx, inputs, output):
+    base, h, B, mag, norm, s, add_base = inputs
+    ctx.save_for_backward(base, h, B, mag, norm)
+    ctx.s = s
+    ctx.add_base = add_base
+
+
+def _lora_compose_grad(ctx, dy):
+    base, h, B, mag, norm = ctx.saved_tensors
+    need = ctx.needs_input_grad
+    d_base, d_B, d_mag = lora_compose_backward(dy, base, h, B, mag, norm, ctx.s, ctx.add_base, bool(need[0]))
+    # the gradient of h through lora = h B^T: d_lora B = dy (g s .* B), the
+    # caller's GEMM (a [T x out] by [out x r] product), with g s folded into B
+    d_h = None
+    if need[1]:
+        gsB = ((mag / norm) * ctx.s)[:, None] * B.float()
+        d_h = (dy @ gsB.to(dy.dtype))
+    d_norm = -(mag / norm) * d_mag if need[4] else None
+    return (d_base if need[0] else None, d_h, d_B if need[2] else None, d_mag if need[3] else None, d_norm,
+            None, None)
+
+
+lora_compose.register_autograd(_lora_compose_grad, setup_context=_lora_compose_setup)
+
+
 # -------------------------------------------------------------------------- layer
 
 
@@ -260,10 +307,8 @@ class DoRALinear(torch.nn.Module):
         x2 = x.reshape(-1, self.in_features)
         base = F.linear(x2, self.weight)
         h = F.linear(x2, self.lora_A)
-        if torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in self.parameters())):
-            lora = F.linear(h, self.lora_B)
-            y = compose(base, lora, self.magnitude, self.weight_norm(), self.s, True)
-        else:
-            # inference tier: lora = h B^T is formed inside the compose kernel
-            y = lora_compose(base, h, self.lora_B, self.magnitude, self.weight_norm(), self.s, True)
+        # lora = h B^T is formed inside the compose kernel on both tiers; on the
+        # training tier autograd records it and its backward (lora_compose_backward)
+        # never forms lora or d_lora either, so nothing T x out is saved for lora
+        y = lora_compose(base, h, self.lora_B, self.magnitude, self.weight_norm(), self.s, True)
         return y.reshape(*lead, self.out_features)

@@ -64,6 +64,41 @@ def test_compose_autograd_matches_oracle(dtype, add_base):
 
 
 @gpu
+@pytest.mark.parametrize("add_base", [False, True])
+def test_lora_compose_autograd_matches_oracle(add_base):
+    # the fused pair through autograd: d_base, d_B and d_mag from the kernels
+    # (lora never formed), d_h = dy (g s .* B) from torch's GEMM
+    dev = torch.device("cuda:0")
+    T, out, r = 300, 264, 24
+    rng = np.random.default_rng(11)
+    to = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    base, h, B, dy = to(rng.normal(0, 0.3, (T, out))), to(rng.normal(0, 1, (T, r))), to(rng.normal(0, 0.05, (out, r))), \
+        to(rng.normal(0, 1, (T, out)))
+    n = torch.from_numpy(rng.uniform(0.5, 2.0, out).astype(np.float32))
+    m = n * (1 + torch.from_numpy(rng.normal(0, 1e-3, out).astype(np.float32)))
+    s = 32 / np.sqrt(r)
+    bg, hg, Bg, mg = (t.to(dev).requires_grad_() for t in (base, h, B, m))
+    y = torch_ops.lora_compose(bg, hg, Bg, mg, n.to(dev), s, add_base)
+    y.backward(dy.to(dev))
+    b64, h64, B64, dy64 = (O.as_f64(t.float().numpy()) for t in (base, h, B, dy))
+    m64, n64 = O.as_f64(m.numpy()), O.as_f64(n.numpy())
+    y_ref = O.lora_compose_fwd(b64, h64, B64, m64, n64, s, add_base)
+    db_ref, dB_ref, dm_ref = O.lora_compose_bwd(dy64, b64, h64, B64, m64, n64, s, add_base)
+    g = m64 / n64
+    dh_ref = (g * s * dy64) @ B64
+    assert _rel(y, torch.from_numpy(y_ref)) < 1e-2
+    assert_compose(bg.grad.float().cpu().numpy(), db_ref, np.abs(db_ref), "bf16", "d_base")
+    assert _rel(Bg.grad, torch.from_numpy(dB_ref)) < 1e-2
+    assert _rel(hg.grad, torch.from_numpy(dh_ref)) < 1e-2
+    # d_mag: 1e-5 of the condition, or the fused path's chain bound (its lora
+    # term is sum_k B (dy^T h), an MFMA sum over the tokens)
+    cond = np.sum(np.abs(dy64 * (b64 + s * (h64 @ B64.T))), axis=0) / n64
+    mass_m = (np.sum(np.abs(dy64 * b64), axis=0) + s * np.sum(np.abs(B64) * (np.abs(dy64).T @ np.abs(h64)), axis=1)) / n64
+    err = np.abs(mg.grad.cpu().double().numpy() - dm_ref)
+    assert np.all((err <= 1e-5 * cond) | (err <= (T / 16 + 96) * 2.0**-24 * mass_m)), "d_mag"
+
+
+@gpu
 def test_compose_grad_base_skipped_when_not_needed():
     dev = torch.device("cuda:0")
     base, lora, dy, m, n, s = _compose_inputs(64, 64, torch.bfloat16, 3)
@@ -87,6 +122,13 @@ def test_opcheck():
     h = torch.randn(64, 16, device=dev, dtype=torch.bfloat16)
     B2 = 0.1 * torch.randn(64, 16, device=dev, dtype=torch.bfloat16)
     torch.library.opcheck(torch_ops.lora_compose, (base.to(dev), h, B2, m.to(dev), n.to(dev), s, True),
+                          test_utils=("test_schema", "test_faketensor"))
+    torch.library.opcheck(torch_ops.lora_compose, (base.to(dev).requires_grad_(), h.clone().requires_grad_(),
+                                                   B2.clone().requires_grad_(), m.to(dev).requires_grad_(),
+                                                   n.to(dev), s, False),
+                          test_utils=("test_schema", "test_autograd_registration", "test_faketensor"))
+    torch.library.opcheck(torch_ops.lora_compose_backward, (dy.to(dev), base.to(dev), h, B2, m.to(dev), n.to(dev), s,
+                                                            False, True),
                           test_utils=("test_schema", "test_faketensor"))
     sq = torch_ops.row_sqnorm(W0)
     torch.library.opcheck(torch_ops.weight_norm_cached, (W0, A, B, sq, 1.5),
