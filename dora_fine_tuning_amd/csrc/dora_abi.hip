@@ -230,7 +230,7 @@ int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const
   }
   const bool vec = T >= 1 && (out % 8 == 0) && (r % 8 == 0) && r >= 8 && r <= (int64_t(1) << 20) && aligned16(dy) &&
                    aligned16(base) && aligned16(h) && aligned16(B) && (d_base == nullptr || aligned16(d_base)) &&
-                   aligned16(mag) && aligned16(norm) && aligned16(ws);
+                   aligned16(d_B) && aligned16(mag) && aligned16(norm) && aligned16(ws);
   if (vec) {
     const size_t need = dora::lora_bwd_workspace_bytes(T, out, r);
     if (ws_bytes < need) return fail(DORA_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);

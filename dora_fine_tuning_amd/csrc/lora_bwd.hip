@@ -20,8 +20,8 @@
 //                     the column sums of dy * base (base loaded one stage
 //                     ahead).  The epilogue forms sum_k B E over its rank block
 //                     and writes its E slice and its column partials;
-//   lora_bwd_finalize_mag   d_mag from the partials, fp64, fixed order;
-//   lora_bwd_finalize_b     d_B = g * s * (sum of the E slices), fixed order;
+//   lora_bwd_finalize  d_mag from the partials (fp64) and d_B = g * s * (sum
+//                      of the E slices), both in a fixed order, one launch;
 //   lora_bwd_general  (general path) one thread per output column, all sums in
 //                     order in fp32, lora per element by its r-term dot product.
 #include <algorithm>
@@ -372,29 +372,32 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   }
 }
 
-// d_mag_j = (sum of the column partials) / n_j in fp64.
-__global__ __launch_bounds__(256) void lora_bwd_finalize_mag(const float* col_part, int parts, int64_t out,
-                                                             const float* norm, float* d_mag) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (j >= out) return;
-  double sum = 0.0;
-  for (int p = 0; p < parts; ++p) sum += static_cast<double>(col_part[static_cast<int64_t>(p) * out + j]);
-  d_mag[j] = static_cast<float>(sum / static_cast<double>(norm[j]));
-}
-
-// d_B[j][k] = (g_j * s) * sum of the E slices, the slices added in order in fp32.
+// One launch finishes both outputs: d_mag_j = (sum of the column partials) /
+// n_j in fp64, and d_B[j][k] = (g_j * s) * (sum of the E slices, added in
+// order in fp32), four elements of a row per thread and step (r % 8 == 0).
 template <int DT>
-__global__ __launch_bounds__(256) void lora_bwd_finalize_b(const float* e_part, int nSplit, int64_t out, int64_t r,
-                                                           const float* mag, const float* norm, float s, void* d_B) {
+__global__ __launch_bounds__(256) void lora_bwd_finalize(const float* col_part, int parts, const float* e_part,
+                                                         int nSplit, int64_t out, int64_t r, const float* mag,
+                                                         const float* norm, float s, float* d_mag, void* d_B) {
   using T16 = typename Dt<DT>::T;
-  const int64_t n = out * r;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t j = e / r;
-    float sum = 0.0f;
-    for (int p = 0; p < nSplit; ++p) sum += e_part[static_cast<int64_t>(p) * n + e];
+  using T4 = T16 __attribute__((ext_vector_type(4)));
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t j = g0; j < out; j += stride) {
+    double sum = 0.0;
+    for (int p = 0; p < parts; ++p) sum += static_cast<double>(col_part[static_cast<int64_t>(p) * out + j]);
+    d_mag[j] = static_cast<float>(sum / static_cast<double>(norm[j]));
+  }
+  const int64_t n = out * r, n4 = n / 4;
+  for (int64_t e = g0; e < n4; e += stride) {
+    f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p < nSplit; ++p) sum += reinterpret_cast<const f32x4*>(e_part + static_cast<int64_t>(p) * n)[e];
+    const int64_t j = (e * 4) / r;
     const float gs = (mag[j] / norm[j]) * s;
-    static_cast<T16*>(d_B)[e] = Dt<DT>::from_f(gs * sum);
+    T4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = Dt<DT>::from_f(gs * sum[q]);
+    reinterpret_cast<T4*>(d_B)[e] = o;
   }
 }
 
@@ -587,18 +590,17 @@ hipError_t launch_lora_bwd(const LoraBwdArgs& p, bool vec) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lora_bwd_finalize_mag, dim3(static_cast<unsigned>(bcdiv(p.out, 256))), dim3(256), 0, p.stream,
-                     a.col_part, plan.nSplit * plan.nTiles, p.out, p.norm, p.d_mag);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.r > 0) {
-    const int64_t blocks = std::min<int64_t>(bcdiv(p.out * p.r, 256), 4096);
+  {
+    // the fast path has r >= 8, so both outputs are non-empty
+    const int64_t blocks = std::min<int64_t>(bcdiv(std::max<int64_t>(p.out * p.r / 4, p.out), 256), 4096);
     if (p.dtype == 0)
-      hipLaunchKernelGGL((lora_bwd_finalize_b<0>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream,
-                         a.e_part, plan.nSplit, p.out, p.r, p.mag, p.norm, p.s, p.d_B);
+      hipLaunchKernelGGL((lora_bwd_finalize<0>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream,
+                         a.col_part, plan.nSplit * plan.nTiles, a.e_part, plan.nSplit, p.out, p.r, p.mag, p.norm,
+                         p.s, p.d_mag, p.d_B);
     else
-      hipLaunchKernelGGL((lora_bwd_finalize_b<1>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream,
-                         a.e_part, plan.nSplit, p.out, p.r, p.mag, p.norm, p.s, p.d_B);
+      hipLaunchKernelGGL((lora_bwd_finalize<1>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, p.stream,
+                         a.col_part, plan.nSplit * plan.nTiles, a.e_part, plan.nSplit, p.out, p.r, p.mag, p.norm,
+                         p.s, p.d_mag, p.d_B);
   }
   return hipGetLastError();
 }
