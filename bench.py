@@ -120,6 +120,69 @@ def cpu_baseline(cfg, W0, A, B, base, lora, dy, chunk_tokens, seconds):
     }
 
 
+SWEEP = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("wide_8192_r384", "fp16"),
+         ("mlp_up_27648x5120", "bf16")] + [(f"sweep_r{r}", dt) for r in (16, 64, 128, 384, 512, 768)
+                                           for dt in ("bf16", "fp16")]
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16
+
+
+def sweep(reps):
+    """One JSON line per workload config: the factored norm and the compose
+    forward and backward, timed in the step's order (norm, fwd, bwd) with HIP
+    events, median over ``reps`` steps after 3 warm-up steps, against their
+    rooflines (norm: max of its HBM and MFMA times; compose: HBM)."""
+    dev = torch.device("cuda:0")
+    for name, dtype in SWEEP:
+        cfg = synth.CONFIGS[name]
+        T, out, in_, r, s = cfg.T, cfg.out, cfg.in_, cfg.r, cfg.s
+        W0c, Ac, Bc = synth.weights(cfg, dtype)
+        xc, dyc = synth.activations(cfg, dtype)
+        W0, A, B = W0c.to(dev), Ac.to(dev), Bc.to(dev)
+        base, lora = synth.base_and_lora(xc, W0c, Ac, Bc, device=dev)
+        dy = dyc.to(dev)
+        del xc, dyc
+        norm = torch.empty(out, dtype=torch.float32, device=dev)
+        ws_n = torch.empty(max(binding.dora_norm_workspace_bytes(out, in_, r, W0.dtype), 1), dtype=torch.uint8,
+                           device=dev)
+        binding.dora_norm_factored(W0, A, B, s, norm_out=norm, workspace=ws_n)
+        mag = torch.from_numpy(synth.magnitude(norm.cpu().numpy(), synth.magnitude_eps(cfg))).to(dev)
+        y, d_lora, d_base = torch.empty_like(base), torch.empty_like(base), torch.empty_like(base)
+        d_mag = torch.empty(out, dtype=torch.float32, device=dev)
+        ws_b = torch.empty(max(binding.dora_compose_bwd_workspace_bytes(T, out), 1), dtype=torch.uint8, device=dev)
+        evs = []
+        for k in range(3 + reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            binding.dora_norm_factored(W0, A, B, s, norm_out=norm, workspace=ws_n)
+            e[1].record()
+            binding.dora_compose_fwd(base, lora, mag, norm, s, y=y)
+            e[2].record()
+            binding.dora_compose_bwd(dy, base, lora, mag, norm, s, d_lora=d_lora, d_base=d_base, d_mag=d_mag,
+                                     workspace=ws_b)
+            e[3].record()
+            if k >= 3:
+                evs.append(e)
+        torch.cuda.synchronize()
+        med = lambda i: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+        n_us, f_us, b_us = med(0), med(1), med(2)
+        nb, nf = norm_work(out, in_, r)
+        fb, bb = compose_bytes(T, out)
+        n_roof_us = max(nb / (HBM_PEAK_GBS * 1e3), nf / (MFMA_PEAK_TFLOPS * 1e6))
+        line = {
+            "config": name, "dtype": dtype, "out": out, "in": in_, "r": r, "T": T,
+            "norm_us": round(n_us, 2), "norm_tflops": round(nf / (n_us * 1e-6) / 1e12, 1),
+            "norm_bound": "mfma" if nf / (MFMA_PEAK_TFLOPS * 1e6) > nb / (HBM_PEAK_GBS * 1e3) else "hbm",
+            "norm_roofline_us": round(n_roof_us, 2), "norm_frac_roofline": round(n_roof_us / n_us, 4),
+            "compose_fwd_us": round(f_us, 2), "compose_fwd_gbs": round(fb / (f_us * 1e-6) / 1e9, 1),
+            "compose_bwd_us": round(b_us, 2), "compose_bwd_gbs": round(bb / (b_us * 1e-6) / 1e9, 1),
+            "compose_frac_hbm_peak": round((fb + bb) / ((f_us + b_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "reps": reps,
+        }
+        print(json.dumps(line), flush=True)
+        del W0, A, B, base, lora, dy, y, d_lora, d_base, ws_n, ws_b
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,10 +202,15 @@ def main():
                     help="compose forward+backward timed through the PyTorch custom operator and autograd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference dispatch for byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: one JSON line per workload config (norm and compose vs rooflines)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(max(args.steps // 5, 5))
+        return
 
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[WORKLOAD]
