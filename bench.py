@@ -126,13 +126,15 @@ SWEEP = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("wide_8192_r384", "
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16
 
 
-def sweep(reps):
+def sweep(reps, only=None):
     """One JSON line per workload config: the factored norm and the compose
     forward and backward, timed in the step's order (norm, fwd, bwd) with HIP
     events, median over ``reps`` steps after 3 warm-up steps, against their
     rooflines (norm: max of its HBM and MFMA times; compose: HBM)."""
     dev = torch.device("cuda:0")
     for name, dtype in SWEEP:
+        if only and name not in only:
+            continue
         cfg = synth.CONFIGS[name]
         T, out, in_, r, s = cfg.T, cfg.out, cfg.in_, cfg.r, cfg.s
         W0c, Ac, Bc = synth.weights(cfg, dtype)
@@ -204,12 +206,13 @@ def main():
                     help="run one 1 GiB device copy first (reference dispatch for byte counters)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: one JSON line per workload config (norm and compose vs rooflines)")
+    ap.add_argument("--sweep-only", default="", help="comma-separated config names to restrict --sweep to")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
-        sweep(max(args.steps // 5, 5))
+        sweep(max(args.steps // 5, 5), [c for c in args.sweep_only.split(",") if c])
         return
 
     dev = torch.device("cuda:0")

@@ -1027,18 +1027,31 @@ __global__ __launch_bounds__(256) void row_sqnorm(const typename Dt<DT>::T* W0, 
   if (lane == 0) sq[row] = static_cast<float>(d);
 }
 
+// sum_{q < n} p[q * stride] in fp64, in order; the loads go out in groups of
+// 8 before the group is added, so a row's partials are fetched in parallel
+// rather than one dependent load at a time.
+__device__ inline double ordered_sum(const float* p, int n, int64_t stride) {
+  double acc = 0.0;
+  int q = 0;
+  for (; q + 8 <= n; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[static_cast<int64_t>(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += static_cast<double>(v[u]);
+  }
+  for (; q < n; ++q) acc += static_cast<double>(p[static_cast<int64_t>(q) * stride]);
+  return acc;
+}
+
 // n_i from the partials; the base term from base_sq[i] when a cache is given.
 __global__ __launch_bounds__(256) void norm_finalize(const float* base_part, const float* cross_part,
                                                      const float* base_sq, int nSplit, int nTiles, int64_t out,
                                                      float s, float* norm_out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= out) return;
-  double b = 0.0, c = 0.0;
-  if (base_sq)
-    b = static_cast<double>(base_sq[i]);
-  else
-    for (int sp = 0; sp < nSplit; ++sp) b += static_cast<double>(base_part[static_cast<int64_t>(sp) * out + i]);
-  for (int q = 0; q < nSplit * nTiles; ++q) c += static_cast<double>(cross_part[static_cast<int64_t>(q) * out + i]);
+  const double b = base_sq ? static_cast<double>(base_sq[i]) : ordered_sum(base_part + i, nSplit, out);
+  const double c = ordered_sum(cross_part + i, nSplit * nTiles, out);
   const double n2 = b + 2.0 * static_cast<double>(s) * c;
   norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
 }
