@@ -276,7 +276,7 @@ __global__ __launch_bounds__(COLS* GRPS) void dmag_finalize(const float* partial
 // Short token blocks: consecutive workgroups then cover adjacent memory and
 // the resident set sweeps HBM compactly (4-row blocks measured about 15%
 // faster than 16-row blocks on data not in the caches).
-constexpr int kFwdThreads = 256, kFwdRows = 4, kFwdUnroll = 4;
+constexpr int kFwdThreads = 256, kFwdRows = 2, kFwdUnroll = 2;
 constexpr bool kFwdNtLoad = false, kFwdNtStore = true;
 constexpr int kBwdThreads = 256, kBwdUnroll = 4;
 constexpr bool kBwdNtLoad = true, kBwdNtStore = true;
