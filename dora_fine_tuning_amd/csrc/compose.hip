@@ -307,25 +307,34 @@ hipError_t launch_compose_fwd_t(const ComposeArgs& a, bool vec) {
   return hipGetLastError();
 }
 
+template <int DT, int ROWS>
+void launch_compose_bwd_rows(const ComposeArgs& a, bool vec, int64_t nrb) {
+  if (vec) {
+    const int64_t out8 = a.out / 8;
+    const int ncb = static_cast<int>(cdiv(out8, kBwdThreads));
+    hipLaunchKernelGGL((compose_bwd_vec<DT, kBwdThreads, ROWS, kBwdUnroll, kBwdNtLoad, kBwdNtStore>),
+                       dim3(ncb * nrb), dim3(kBwdThreads), 0, a.stream, static_cast<const Chunk*>(a.dy),
+                       static_cast<const Chunk*>(a.base), static_cast<const Chunk*>(a.lora), a.mag, a.norm, a.s, a.T,
+                       out8, ncb, a.add_base, static_cast<Chunk*>(a.d_lora), static_cast<Chunk*>(a.d_base), a.partial);
+  } else {
+    using T = typename Dt<DT>::T;
+    const int ncb = static_cast<int>(cdiv(a.out, kThreads));
+    hipLaunchKernelGGL((compose_bwd_gen<DT, ROWS>), dim3(ncb * nrb), dim3(kThreads), 0, a.stream,
+                       static_cast<const T*>(a.dy), static_cast<const T*>(a.base), static_cast<const T*>(a.lora),
+                       a.mag, a.norm, a.s, a.T, a.out, ncb, a.add_base, static_cast<T*>(a.d_lora),
+                       static_cast<T*>(a.d_base), a.partial);
+  }
+}
+
 template <int DT>
 hipError_t launch_compose_bwd_t(const ComposeArgs& a, bool vec) {
-  const int64_t nrb = cdiv(a.T, kBwdRows);
+  const int rows = compose_bwd_rows(a.T, a.out);
+  const int64_t nrb = cdiv(a.T, rows);
   if (nrb > 0) {
-    if (vec) {
-      const int64_t out8 = a.out / 8;
-      const int ncb = static_cast<int>(cdiv(out8, kBwdThreads));
-      hipLaunchKernelGGL((compose_bwd_vec<DT, kBwdThreads, kBwdRows, kBwdUnroll, kBwdNtLoad, kBwdNtStore>),
-                         dim3(ncb * nrb), dim3(kBwdThreads), 0, a.stream, static_cast<const Chunk*>(a.dy), static_cast<const Chunk*>(a.base),
-                         static_cast<const Chunk*>(a.lora), a.mag, a.norm, a.s, a.T, out8, ncb, a.add_base,
-                         static_cast<Chunk*>(a.d_lora), static_cast<Chunk*>(a.d_base), a.partial);
-    } else {
-      using T = typename Dt<DT>::T;
-      const int ncb = static_cast<int>(cdiv(a.out, kThreads));
-      hipLaunchKernelGGL((compose_bwd_gen<DT, kBwdRows>), dim3(ncb * nrb), dim3(kThreads), 0, a.stream,
-                         static_cast<const T*>(a.dy), static_cast<const T*>(a.base), static_cast<const T*>(a.lora),
-                         a.mag, a.norm, a.s, a.T, a.out, ncb, a.add_base, static_cast<T*>(a.d_lora),
-                         static_cast<T*>(a.d_base), a.partial);
-    }
+    if (rows == kBwdRowsWide)
+      launch_compose_bwd_rows<DT, kBwdRowsWide>(a, vec, nrb);
+    else
+      launch_compose_bwd_rows<DT, kBwdRowsNarrow>(a, vec, nrb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -338,10 +347,20 @@ hipError_t launch_compose_fwd(const ComposeArgs& a, bool vec) {
   return a.dtype == 0 ? launch_compose_fwd_t<0>(a, vec) : launch_compose_fwd_t<1>(a, vec);
 }
 
+int compose_bwd_rows(int64_t T, int64_t out) {
+  const int64_t ncb = cdiv(cdiv(out, 8), kBwdThreads);
+  return ncb * cdiv(T, kBwdRowsWide) >= 512 ? kBwdRowsWide : kBwdRowsNarrow;
+}
+
+size_t compose_bwd_workspace(int64_t T, int64_t out) {
+  if (T <= 0 || out <= 0) return 0;
+  return static_cast<size_t>(cdiv(T, compose_bwd_rows(T, out))) * static_cast<size_t>(out) * 4;
+}
+
 int64_t compose_max_grid(int64_t T, int64_t out, bool vec) {
   const int64_t ncb_fwd = vec ? cdiv(out / 8, kFwdThreads) : cdiv(out, kThreads);
   const int64_t ncb_bwd = vec ? cdiv(out / 8, kBwdThreads) : cdiv(out, kThreads);
-  const int64_t fwd = ncb_fwd * cdiv(T, kFwdRows), bwd = ncb_bwd * cdiv(T, kBwdRows);
+  const int64_t fwd = ncb_fwd * cdiv(T, kFwdRows), bwd = ncb_bwd * cdiv(T, compose_bwd_rows(T, out));
   return std::max({fwd, bwd, cdiv(out, kFinCols)});
 }
 

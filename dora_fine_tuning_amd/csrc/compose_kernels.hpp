@@ -7,8 +7,13 @@
 namespace dora {
 
 // Tokens per block of the backward; one fp32 partial of the magnitude gradient
-// per (token block, column) lives in the workspace.
-constexpr int kBwdRows = 64;
+// per (token block, column) lives in the workspace.  64 rows, or 16 when 64-row
+// blocks would give fewer than 512 workgroups (a small module would leave CUs
+// idle).  A function of (T, out) only, so the workspace query and the launch
+// agree whatever path the pointers select.
+constexpr int kBwdRowsWide = 64, kBwdRowsNarrow = 16;
+int compose_bwd_rows(int64_t T, int64_t out);
+size_t compose_bwd_workspace(int64_t T, int64_t out);
 
 struct ComposeArgs {
   int dtype;

@@ -299,7 +299,7 @@ int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* nor
 
 size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out) {
   if (T <= 0 || out <= 0) return 0;
-  return static_cast<size_t>((T + dora::kBwdRows - 1) / dora::kBwdRows) * static_cast<size_t>(out) * 4;
+  return dora::compose_bwd_workspace(T, out);
 }
 
 int dora_compose_bwd(const void* dy, const void* base, const void* lora, const float* mag, const float* norm, float s,

@@ -62,8 +62,13 @@ def test_workspace_queries_invalid():
     assert LIB.dora_norm_workspace_bytes(8, 8, 8, 7) == 0
     assert LIB.dora_norm_workspace_bytes(0, 8, 8, 0) == 0
     assert LIB.dora_compose_bwd_workspace_bytes(0, 8) == 0
-    assert LIB.dora_compose_bwd_workspace_bytes(64, 8) == 8 * 4  # one 64-token block
-    assert LIB.dora_compose_bwd_workspace_bytes(65, 8) == 2 * 8 * 4
+    # 16-token blocks while 64-token blocks would give under 512 workgroups
+    # (256 threads of 8 columns per workgroup), else 64-token blocks
+    assert LIB.dora_compose_bwd_workspace_bytes(64, 8) == 4 * 8 * 4
+    assert LIB.dora_compose_bwd_workspace_bytes(65, 8) == 5 * 8 * 4
+    assert LIB.dora_compose_bwd_workspace_bytes(4096, 4096) == 256 * 4096 * 4  # 2 x 64 = 128 workgroups at 64
+    assert LIB.dora_compose_bwd_workspace_bytes(8192, 8192) == 128 * 8192 * 4  # 4 x 128 = 512 at 64
+    assert LIB.dora_compose_bwd_workspace_bytes(10240, 27648) == 160 * 27648 * 4
 
 
 P = 1 << 20  # fake, never dereferenced: every call below fails validation first
