@@ -197,7 +197,8 @@ def test_compose_identity_invariants(lib):
 
 # ------------------------------------------------------------ full-size adapter configs
 
-FULL = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("mlp_up_27648x5120", "bf16")]
+FULL = [("tiny", "bf16"), ("tiny", "fp16"), ("attn_proj", "bf16"), ("attn_proj", "fp16"),
+        ("wide_8192_r384", "bf16"), ("wide_8192_r384", "fp16"), ("mlp_up_27648x5120", "bf16")]
 FULL += [(f"sweep_r{r}", dt) for r in (16, 64, 128, 384, 512, 768) for dt in ("bf16", "fp16")]
 
 
@@ -266,8 +267,15 @@ def test_full_config(lib, name, dtype):
     log(f"[full] {name} {dtype}: {collapsed.mean():.1%} of columns collapse under a naive {dtype} compose, "
         f"{near.mean():.1%} have |g-1| < 2^-8")
     if name == "wide_8192_r384":
-        assert collapsed.mean() > 0.5
-        assert np.all(y[:, collapsed][Br[:, collapsed] != 0] != 0)
+        # |g - 1| ~ U(0, 2^-8): under RNE g rounds to 1 for |g - 1| up to about
+        # 2^-9 .. 2^-8 in bf16 (most columns) but only up to 2^-12 .. 2^-11 in
+        # fp16 (about 9%); the stable kernel keeps the correction in all of them
+        assert collapsed.mean() > (0.5 if dtype == "bf16" else 0.05)
+        # nonzero wherever the exact correction is representable (fp16 rounds
+        # magnitudes at or below 2^-25 to zero; in bf16 that is every nonzero)
+        want_c = PU.representable_nonzero(ref, dtype)[:, collapsed]
+        assert want_c.mean() > 0.99
+        assert np.all((y != 0)[:, collapsed] == want_c)
 
 
 def test_determinism_and_streams(lib):
