@@ -318,6 +318,7 @@ struct DmaTile {
   static constexpr int RED_OFF = AREA - RED_BYTES;
   static_assert(BK == 32, "K stages of 32: 64-byte DMA row segments, two MFMA K steps");
   static_assert(TM % WM == 0, "row tiles split over the waves");
+  static_assert(TMW <= 4 && TN <= 4, "a stage reads at most four fragments per panel and K step");
   static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(RPP >= 32 && RPP * BN * 2 <= RED_OFF, "epilogue B-tile pass fits beside the row sums");
