@@ -72,28 +72,39 @@ __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* no
 
 // Z[l][j] = s * M'[j][l], M'[j][l] = sum over slices of E[j][l] + E[j][r + l]
 // (E = B^T [Yhi | Ylo], [nSplit][r][2r]), split into hi/lo at [l][j], [l][r + j].
+// An 8 x 32 tile of (j, l) per workgroup, one element per thread: reads
+// coalesced along l, a transpose through LDS, then 16-byte runs along j per
+// row of Z.  The slices go in groups of 8, all 16 loads of a group in flight
+// before the group is added in slice order; lanes past r read a valid
+// address and drop the result, so the loads stay unconditional.
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSplit, int64_t r, float s, void* Zv) {
   using T = typename Dt<DT>::T;
-  T* Z = static_cast<T*>(Zv);
-  const int64_t n = r * r, slice = r * 2 * r;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t j = e / r, l = e - j * r;  // l fastest: the reads of E[j][.] are coalesced
-    const float* Ej = E + j * 2 * r + l;
-    // slices in groups of 8, all 16 loads of a group in flight before the
-    // group is added in order
+  __shared__ float tile[8][33];
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 8, l0 = static_cast<int64_t>(blockIdx.y) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t slice = r * 2 * r;
+  {
+    const int64_t j = j0 + ty, l = l0 + tx;
+    const float* Ej = E + (j < r && l < r ? j * 2 * r + l : 0);
     float m = 0.0f;
     int p = 0;
     for (; p + 8 <= nSplit; p += 8) {
       float v[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = Ej[(p + q) * slice] + Ej[(p + q) * slice + r];
+      for (int u = 0; u < 8; ++u) v[u] = Ej[(p + u) * slice] + Ej[(p + u) * slice + r];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) m += v[q];
+      for (int u = 0; u < 8; ++u) m += v[u];
     }
     for (; p < nSplit; ++p) m += Ej[p * slice] + Ej[p * slice + r];
-    const float z = s * m;
+    tile[ty][tx] = s * m;
+  }
+  __syncthreads();
+  T* Z = static_cast<T*>(Zv);
+  const int jj = threadIdx.x & 7, ll = threadIdx.x >> 3;
+  const int64_t l = l0 + ll, j = j0 + jj;
+  if (l < r && j < r) {
+    const float z = tile[jj][ll];
     const T hi = Dt<DT>::from_f(z);
     Z[l * 2 * r + j] = hi;
     Z[l * 2 * r + r + j] = Dt<DT>::from_f(z - Dt<DT>::to_f(hi));
@@ -252,7 +263,8 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   // M = B^T [Yhi | Ylo] -> Z
   e = launch_row_contract(a.B, Y, out, r, 2 * r, p.np.dtype, big, a.stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((nbwd_finalize_m<DT>), stride_grid(r * r), dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, Z);
+  const dim3 mgrid(static_cast<unsigned>(ndiv(r, 8)), static_cast<unsigned>(ndiv(r, 32)));
+  hipLaunchKernelGGL((nbwd_finalize_m<DT>), mgrid, dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, Z);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // d_A^T slices: the rows of W0 with Y, then (spread over the same slices) the rows of A with Z
