@@ -122,15 +122,28 @@ __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A,
 // entries of the upper tiles, split into G'hi = round(G') and G'lo =
 // round(G' - G'hi) in the storage dtype and written at (a, b) and its mirror
 // (b, a).  G'hi + G'lo carries about 16 (bf16) or 22 (fp16) significant bits.
+// One workgroup per 8-row strip of an upper 32 x 32 tile (tr <= tc), one entry
+// per thread: the direct writes run 64 bytes along a row, the mirror goes
+// through LDS and is written in 16-byte runs.  Loads past r read a valid
+// address and are dropped, so every thread issues the same loads.
 template <int DT>
 __global__ __launch_bounds__(256) void gram_finalize(const float* gpart, int splitG, int64_t r, float half_s,
                                                      typename Dt<DT>::T* ghi, typename Dt<DT>::T* glo) {
   using T = typename Dt<DT>::T;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= r * r) return;
-  const int64_t row = idx / r, col = idx % r;
-  if (row / 32 > col / 32) return;  // written as the mirror of (col, row)
-  const float* src = gpart + idx;
+  __shared__ float tile[8][33];
+  const int nT = static_cast<int>((r + 31) / 32);
+  int u = static_cast<int>(blockIdx.x >> 2);
+  int tr = 0;
+  while (u >= nT - tr) {
+    u -= nT - tr;
+    ++tr;
+  }
+  const int tc = tr + u;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t row0 = static_cast<int64_t>(tr) * 32 + (blockIdx.x & 3) * 8, col0 = static_cast<int64_t>(tc) * 32;
+  const int64_t row = row0 + ty, col = col0 + tx;
+  const bool inside = row < r && col < r;
+  const float* src = gpart + (inside ? row * r + col : 0);
   const int64_t stride = r * r;
   float g = 0.0f;
   // groups of up to kFinSplits partials, all loaded before they are summed
@@ -153,13 +166,21 @@ __global__ __launch_bounds__(256) void gram_finalize(const float* gpart, int spl
     g += a[0];
   }
   const float gp = half_s * g;
-  const T hi = Dt<DT>::from_f(gp);
-  const T lo = Dt<DT>::from_f(gp - Dt<DT>::to_f(hi));
-  ghi[row * r + col] = hi;
-  glo[row * r + col] = lo;
-  if (row / 32 != col / 32) {
-    ghi[col * r + row] = hi;
-    glo[col * r + row] = lo;
+  if (inside) {
+    const T hi = Dt<DT>::from_f(gp);
+    ghi[row * r + col] = hi;
+    glo[row * r + col] = Dt<DT>::from_f(gp - Dt<DT>::to_f(hi));
+  }
+  if (tr == tc) return;  // the diagonal tile holds both halves itself
+  tile[ty][tx] = gp;
+  __syncthreads();
+  const int ii = threadIdx.x & 7, jj = threadIdx.x >> 3;
+  const int64_t mrow = col0 + jj, mcol = row0 + ii;  // mirror of (row0 + ii, col0 + jj)
+  if (mrow < r && mcol < r) {
+    const float z = tile[ii][jj];
+    const T hi = Dt<DT>::from_f(z);
+    ghi[mrow * r + mcol] = hi;
+    glo[mrow * r + mcol] = Dt<DT>::from_f(z - Dt<DT>::to_f(hi));
   }
 }
 
@@ -1111,6 +1132,12 @@ void launch_dma(const WArgs& w, hipStream_t stream) {
   hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTileOf<TN>::NT), 0, stream, w);
 }
 
+// Workgroups of gram_finalize: four 8-row strips per upper 32 x 32 tile.
+int64_t gram_finalize_blocks(int64_t r) {
+  const int64_t nT = cdiv(r, 32);
+  return 2 * nT * (nT + 1);
+}
+
 // G' = scale * A A^T as the pair G'hi + G'lo in the plan's workspace regions.
 template <int DT>
 hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* ws, bool vec, hipStream_t stream) {
@@ -1129,8 +1156,8 @@ hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* w
     hipLaunchKernelGGL((gram_partial<DT>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(cdiv(p.r * p.r, 256))), dim3(256), 0, stream,
-                     gpart, p.splitG, p.r, scale, ghi, glo);
+  hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(gram_finalize_blocks(p.r))), dim3(256), 0,
+                     stream, gpart, p.splitG, p.r, scale, ghi, glo);
   return hipGetLastError();
 }
 
@@ -1243,7 +1270,7 @@ size_t norm_scratch_bound(int64_t out, int64_t r) {
 
 int64_t norm_max_grid(const NormPlan& p) {
   const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
-  const int64_t gram = p.r > 0 ? std::max(cdiv(nUpper * p.splitG, 8) * 8, cdiv(p.r * p.r, 256)) : 0;
+  const int64_t gram = p.r > 0 ? std::max(cdiv(nUpper * p.splitG, 8) * 8, gram_finalize_blocks(p.r)) : 0;
   const int64_t stream = cdiv(p.nRB * p.nTiles * p.nSplit, 8) * 8;
   return std::max({gram, stream, cdiv(p.out, 256)});
 }
