@@ -16,10 +16,13 @@
 //                     (Y panel) go global -> LDS by DMA, and MFMA 32x32x16
 //                     contracts over the tokens, its fragments read with the
 //                     transposing LDS read (ds_read_b64_tr_b16, two per
-//                     fragment).  The same stage's dy rows also give d_base and
-//                     the column sums of dy * base (base loaded one stage
-//                     ahead).  The epilogue forms sum_k B E over its rank block
-//                     and writes its E slice and its column partials;
+//                     fragment).  The base rows matching the dy rows come in
+//                     as a third panel of the same stage, so the stage's dy
+//                     and base give d_base and the column sums of dy * base.
+//                     The epilogue forms sum_k B E over its rank block and
+//                     writes its E slice and its column partials.  The same
+//                     kernel without the base panel is the plain contraction
+//                     X^T Y over the rows of X and Y;
 //   lora_bwd_finalize  d_mag from the partials (fp64) and d_B = g * s * (sum
 //                      of the E slices), both in a fixed order, one launch;
 //   lora_bwd_general  (general path) one thread per output column, all sums in
@@ -44,11 +47,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // receives element i%4 of the source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
 // With source lane L addressing row R0 + L/4 at column F(L%4), lane i gets the
 // 4 elements of column F(i/4) + i%4 in rows R0 .. R0 + 3.
+// Issued as inline assembly, like the other fragment reads (the builtin would
+// make the compiler wait for every DMA in flight before each read); the result
+// is valid after lds_wait() / lds_wait_keep(), and tie2() orders its uses after
+// that wait.
 __device__ inline u32x2 lds_read_tr(uint32_t addr) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(static_cast<uintptr_t>(addr)));
-  return __builtin_bit_cast(u32x2, v);
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
 }
+__device__ inline void tie2(u32x2& v) { asm volatile("" : "+v"(v)); }
 
 // Tile: 128 output columns (X, 32*TM with TM = 4, WM = 2 waves along them) x
 // 128*TN rank columns (Y, WN = 4 waves along them); a wave owns TMW = 2 x TN
@@ -58,19 +66,26 @@ __device__ inline u32x2 lds_read_tr(uint32_t addr) {
 // in slot c ^ (4 * (t % 4)): the transposing reads touch 4 consecutive rows and
 // 2 chunks per row, and the 8 (row, chunk) pairs then fall in 8 distinct bank
 // groups.
-template <int TN_, int NS_>
+// BASE adds the third panel, the base rows of the X panel's tokens and
+// columns, laid out like the X panel; the plain contraction has none.  Every
+// vector-memory load of the stage loop is then a DMA of the ring, which keeps
+// the stage waits exact.
+template <int TN_, int NS_, bool BASE_>
 struct BwdTile {
   static constexpr int TN = TN_, NS = NS_;
+  static constexpr bool BASE = BASE_;
   static constexpr int WM = 2, WN = 4, NW = 8, NT = 512, TM = 4, TMW = 2;
   static constexpr int BM = 128, BN = 128 * TN, BK = 32;
   static constexpr int XROWB = BM * 2, YROWB = BN * 2;  // bytes per token row
-  static constexpr int X_BYTES = BK * XROWB, Y_BYTES = BK * YROWB, STAGE_BYTES = X_BYTES + Y_BYTES;
+  static constexpr int X_BYTES = BK * XROWB, Y_BYTES = BK * YROWB, B_BYTES = BASE ? X_BYTES : 0;
+  static constexpr int B_OFF = X_BYTES + Y_BYTES, STAGE_BYTES = X_BYTES + Y_BYTES + B_BYTES;
   static constexpr int XI = X_BYTES / 1024, YI = Y_BYTES / 1024;  // 1 KiB DMA blocks per stage
-  static constexpr int XQ = XI / NW, YQ = YI / NW, L = XQ + YQ;
+  static constexpr int XQ = XI / NW, YQ = YI / NW, L = XQ + YQ + (BASE ? XQ : 0);
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(NS >= 3 && (NS - 2) * L + 1 < 64, "ring depth and vmcnt range");
+  static_assert(NS >= 3 && (NS - 2) * L < 64, "ring depth and vmcnt range");
+  static_assert(2 * (TMW + TN) < 16, "one K step's fragment reads within the lgkmcnt range");
 };
 
 // slot of logical 16-byte chunk c in token row t (see BwdTile)
@@ -86,7 +101,6 @@ struct BwdArgs {
   int nCB, nTiles, nSplit;
   float* e_part;    // [nSplit][out][r]: the E slices
   float* col_part;  // [nSplit][nTiles][out]: sum_t dy * base (tile 0 only) + s * sum_k B E
-  int pure;         // plain contraction E = dy^T h: no d_base, no column sums, no B or col_part
   // plain contraction only: the contraction axis continues over the rows of
   // other matrices, dy2 [T2 x out] and h2 [T2 x r]; slice sp takes rows
   // [T2 sp / nSplit, T2 (sp + 1) / nSplit) of them after its own rows of dy, h
@@ -95,15 +109,15 @@ struct BwdArgs {
 };
 
 // Wait for the current stage's DMA while the younger loads already issued stay
-// in flight: n younger stages (at most NS-2) of L loads each, plus the one base
-// chunk issued after them.  Younger stores only make the wait longer.
+// in flight: n younger stages (at most NS-2) of L loads each.  Younger stores
+// (d_base) only make the wait longer.
 template <class TL, int N = TL::NS - 2>
 __device__ inline void bwd_wait(int n) {
   if constexpr (N == 0) {
-    wait_vmcnt<1>();
+    wait_vmcnt<0>();
   } else {
     if (n >= N)
-      wait_vmcnt<N * TL::L + 1>();
+      wait_vmcnt<N * TL::L>();
     else
       bwd_wait<TL, N - 1>(n);
   }
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const bool want_base = nt == 0 && !a.pure;  // the elementwise part is done by the first rank block
+  const bool want_base = TL::BASE && nt == 0;  // the elementwise part is done by the first rank block
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
   // buffer resources over the token slice; rows past it read zero
@@ -196,6 +210,11 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < TL::YQ; ++q)
       dma16(ry, so + TL::X_BYTES + (q * TL::NW + wave) * 1024, yok[q] ? yo[q] + ss * ystep : kOob);
+    if constexpr (TL::BASE) {  // never with a second segment
+#pragma unroll
+      for (int q = 0; q < TL::XQ; ++q)
+        dma16(rbase, so + TL::B_OFF + (q * TL::NW + wave) * 1024, want_base && xok[q] ? xo[q] + ss * xstep : kOob);
+    }
   };
 
   // Fragment read addresses (within a stage slot; add the slot's offset).  In a
@@ -243,43 +262,52 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
     }
   }
   T16* dbase = static_cast<T16*>(a.d_base);
-  // One buffer load per wave and stage, always issued (lanes with nothing to
-  // load use an out-of-range offset and read zero), so the vmcnt bookkeeping of
-  // the stage waits holds in every workgroup.
-  auto load_base = [&](int st) {
-    const int64_t t = static_cast<int64_t>(st) * TL::BK + et;  // within the slice
-    const uint32_t off = (eok && t < rows) ? static_cast<uint32_t>((t * out + ecol) * 2) : kOob;
-    return __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b128(rbase, off, 0, 0));
-  };
 
   for (int u = 0; u < TL::NS - 1; ++u)
     if (u < S) issue(u, u);
-  Chunk bnext = load_base(0);
 
   int slot = 0;
   for (int st = 0; st < S; ++st) {
     bwd_wait<TL>(S - 1 - st);
     __builtin_amdgcn_s_barrier();
     if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, slot == 0 ? TL::NS - 1 : slot - 1);
-    const Chunk bcur = bnext;
-    if (st + 1 < S) bnext = load_base(st + 1);
     const uint32_t xp = lds0 + static_cast<uint32_t>(slot * TL::STAGE_BYTES);
     const uint32_t yp = xp + TL::X_BYTES;
+    // both K steps' fragment reads in flight, then each step's MFMAs after its
+    // reads have landed (the halves of a fragment are joined after the wait)
+    u32x2 xl[2][TL::TMW], xh[2][TL::TMW], yl[2][TL::TN], yh[2][TL::TN];
 #pragma unroll
     for (int step = 0; step < 2; ++step) {
       const int row = 16 * step + rsrc_row;
-      u32x4 fx[TL::TMW], fy[TL::TN];
 #pragma unroll
       for (int i = 0; i < TL::TMW; ++i) {
-        const u32x2 lo = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
-        const u32x2 hi = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
-        fx[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        xl[step][i] = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
+        xh[step][i] = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
       }
 #pragma unroll
       for (int j = 0; j < TL::TN; ++j) {
-        const u32x2 lo = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
-        const u32x2 hi = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
-        fy[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        yl[step][j] = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
+        yh[step][j] = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
+      }
+    }
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      if (step == 0)
+        lds_wait_keep<2 * (TL::TMW + TL::TN)>();
+      else
+        lds_wait();
+      u32x4 fx[TL::TMW], fy[TL::TN];
+#pragma unroll
+      for (int i = 0; i < TL::TMW; ++i) {
+        tie2(xl[step][i]);
+        tie2(xh[step][i]);
+        fx[i] = u32x4{xl[step][i][0], xl[step][i][1], xh[step][i][0], xh[step][i][1]};
+      }
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) {
+        tie2(yl[step][j]);
+        tie2(yh[step][j]);
+        fy[j] = u32x4{yl[step][j][0], yl[step][j][1], yh[step][j][0], yh[step][j][1]};
       }
 #pragma unroll
       for (int i = 0; i < TL::TMW; ++i)
@@ -287,16 +315,19 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
         for (int j = 0; j < TL::TN; ++j)
           acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
     }
-    if (eok) {
+    if (TL::BASE && eok) {
       const int64_t t = ts + static_cast<int64_t>(st) * TL::BK + et;
       if (t < te) {
-        const u32x4 w = lds_read16(xp + static_cast<uint32_t>(et * TL::XROWB + bwd_slot(ec, et) * 16));
+        // this thread's chunk of dy and of base, at the same place in their panels
+        const uint32_t ce = xp + static_cast<uint32_t>(et * TL::XROWB + bwd_slot(ec, et) * 16);
+        u32x4 wd = lds_read16(ce);
+        u32x4 wb = lds_read16(ce + TL::B_OFF);
         lds_wait();
-        u32x4 wt = w;
-        tie(wt);
+        tie(wd);
+        tie(wb);
         float dyv[8], bv[8], o[8];
-        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wt), dyv);
-        chunk_to_f32<DT>(bcur, bv);
+        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wd), dyv);
+        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wb), bv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           o[e] = gb[e] * dyv[e];
@@ -328,7 +359,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
         // k + 16 <= r: r % 8 == 0 and k % 16 == 0 give whole 8-column chunks;
         // the second chunk is checked on its own
         const bool hi = k + 8 < r;
-        if (!a.pure) {
+        if constexpr (TL::BASE) {
         const Chunk b0 = *reinterpret_cast<const Chunk*>(Bp + j * r + k);
         const Chunk b1 = hi ? *reinterpret_cast<const Chunk*>(Bp + j * r + k + 8) : zero_chunk();
         float bf[16];
@@ -356,7 +387,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
     bsum += __shfl_xor(bsum, 32, 64);
     if (fh == 0) red[32 * 128 + wn * 128 + jl] = bsum;
   }
-  if (a.pure) return;  // uniform: the whole workgroup leaves together
+  if constexpr (!TL::BASE) return;  // the plain contraction has no column sums
   // (2) the column sums of dy * base over the slice: thread tid holds row tid/16
   // of each stage and 8 columns
 #pragma unroll
@@ -471,9 +502,11 @@ BwdPlan bwd_plan(int64_t T, int64_t out, int64_t r, bool vec) {
   return p;
 }
 
-template <int DT, int TN>
+// Ring depth: the 40 KB stages of the rank-384 tile with the base panel fit
+// four times in the 160 KB of LDS, every other stage five times.
+template <int DT, int TN, bool BASE = true>
 void launch_bwd_dma(const BwdArgs& a, hipStream_t stream) {
-  using TL = BwdTile<TN, TN == 3 ? 4 : 5>;
+  using TL = BwdTile<TN, (TN == 3 && BASE) ? 4 : 5, BASE>;
   const int64_t total = static_cast<int64_t>(a.nCB) * a.nTiles * a.nSplit;
   hipLaunchKernelGGL((lora_bwd_dma<DT, TL>), dim3(static_cast<unsigned>(bcdiv(total, 8) * 8)), dim3(TL::NT), 0,
                      stream, a);
@@ -515,7 +548,6 @@ hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t 
   const BwdPlan plan = bwd_plan(T, nx, ny, true);
   BwdArgs a{};
   a.dy = X;
-  a.base = X;  // never read: in a plain contraction every base load is out of range
   a.h = Y;
   a.T = T;
   a.out = nx;
@@ -524,7 +556,6 @@ hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t 
   a.nTiles = plan.nTiles;
   a.nSplit = plan.nSplit;
   a.e_part = e_part;
-  a.pure = 1;
   if (T2 > 0) {
     a.dy2 = X2;
     a.h2 = Y2;
@@ -532,15 +563,15 @@ hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t 
   }
   if (dtype == 0) {
     switch (plan.tn) {
-      case 1: launch_bwd_dma<0, 1>(a, stream); break;
-      case 2: launch_bwd_dma<0, 2>(a, stream); break;
-      default: launch_bwd_dma<0, 3>(a, stream); break;
+      case 1: launch_bwd_dma<0, 1, false>(a, stream); break;
+      case 2: launch_bwd_dma<0, 2, false>(a, stream); break;
+      default: launch_bwd_dma<0, 3, false>(a, stream); break;
     }
   } else {
     switch (plan.tn) {
-      case 1: launch_bwd_dma<1, 1>(a, stream); break;
-      case 2: launch_bwd_dma<1, 2>(a, stream); break;
-      default: launch_bwd_dma<1, 3>(a, stream); break;
+      case 1: launch_bwd_dma<1, 1, false>(a, stream); break;
+      case 2: launch_bwd_dma<1, 2, false>(a, stream); break;
+      default: launch_bwd_dma<1, 3, false>(a, stream); break;
     }
   }
   return hipGetLastError();
