@@ -126,11 +126,14 @@ SWEEP = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("wide_8192_r384", "
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16
 
 
-def sweep(reps, only=None):
+def sweep(reps, only=None, cpu_seconds=0.0):
     """One JSON line per workload config: the factored norm and the compose
     forward and backward, timed in the step's order (norm, fwd, bwd) with HIP
     events, median over ``reps`` steps after 3 warm-up steps, against their
-    rooflines (norm: max of its HBM and MFMA times; compose: HBM)."""
+    rooflines (norm: max of its HBM and MFMA times; compose: HBM).  With
+    ``cpu_seconds`` > 0 the line also carries the CPU oracle timed on the same
+    config (``cpu_baseline``: the norm over all rows, and about ``cpu_seconds``
+    of compose work)."""
     dev = torch.device("cuda:0")
     for name, dtype in SWEEP:
         if only and name not in only:
@@ -180,6 +183,11 @@ def sweep(reps, only=None):
             "compose_frac_hbm_peak": round((fb + bb) / ((f_us + b_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "reps": reps,
         }
+        if cpu_seconds > 0:
+            cb = cpu_baseline(cfg, W0c, Ac, Bc, base, lora, dy, 2048, cpu_seconds)
+            line["cpu_oracle"] = {"norm_us": round(cb["norm_us"], 1), "norm_threads": cb["norm_threads"],
+                                  "compose_gbs": round(cb["value"], 3), "compose_cores": cb["cores"],
+                                  "sample": cb["sample"]}
         print(json.dumps(line), flush=True)
         del W0, A, B, base, lora, dy, y, d_lora, d_base, ws_n, ws_b
         torch.cuda.empty_cache()
@@ -207,12 +215,14 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: one JSON line per workload config (norm and compose vs rooflines)")
     ap.add_argument("--sweep-only", default="", help="comma-separated config names to restrict --sweep to")
+    ap.add_argument("--sweep-cpu-seconds", type=float, default=1.0,
+                    help="seconds of oracle compose work per --sweep config (with the oracle norm); 0 skips")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
-        sweep(max(args.steps // 5, 5), [c for c in args.sweep_only.split(",") if c])
+        sweep(max(args.steps // 5, 5), [c for c in args.sweep_only.split(",") if c], args.sweep_cpu_seconds)
         return
 
     dev = torch.device("cuda:0")
