@@ -478,6 +478,10 @@ def main():
         "norm_us": round(float(norm_ms.mean()) * 1e3, 2),
         "norm_tflops": round(nf / (norm_ms.mean() * 1e-3) / 1e12, 1),
         "norm_frac_mfma_peak": round(nf / (norm_ms.mean() * 1e-3) / 2.5e15, 4),
+        # the factored norm's scratch against its O(out r + r^2) bound and the dense fp32 transient it avoids
+        "norm_workspace": {"bytes": ws_norm.numel(), "bound_bytes": 4 * (out * r + r * r) + 64 * out,
+                           "dense_fp32_bytes": 4 * out * in_},
+        "compose_bwd_workspace_bytes": ws_bwd.numel(),
         "norm_cached_base": cached,
         "lora_fused_fwd": fused,
         "norm_bwd": norm_bwd,
