@@ -59,6 +59,10 @@ bool any_overlap(const void* p, size_t n, const void* q, size_t m) {
 
 bool valid_dtype(int dtype) { return dtype == DORA_BF16 || dtype == DORA_F16; }
 
+// Longest serial chain (T * r products per thread) the slow path of
+// dora_lora_compose_bwd is allowed to run.
+constexpr int64_t kLoraBwdGeneralMaxSerial = int64_t(1) << 20;
+
 // Validation and launch shared by the two norm entry points (base_sq: the
 // cached base term, or NULL to compute it).
 int norm_call(const char* fn, const void* W0, const void* A, const void* B, const float* base_sq, int64_t out,
@@ -244,6 +248,15 @@ int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const
       return fail(DORA_UNSUPPORTED, "%s: T=%lld out=%lld r=%lld: a token slice spans 2 GiB or more", fn,
                   (long long)T, (long long)out, (long long)r);
   }
+  // The slow path gives each output column to one thread, which walks all T x r
+  // products of its d_B row in order: refuse shapes where that serial chain
+  // would be long (a cliff of orders of magnitude against the fast path), so
+  // the caller can take another route (the PyTorch layer's eager tier).
+  if (!vec && T * r > kLoraBwdGeneralMaxSerial)
+    return fail(DORA_UNSUPPORTED,
+                "%s: T=%lld out=%lld r=%lld misses the fast path (out and r multiples of 8, 8 <= r, 16-byte aligned "
+                "pointers and workspace) and T*r exceeds the slow path's limit of %lld",
+                fn, (long long)T, (long long)out, (long long)r, (long long)kLoraBwdGeneralMaxSerial);
   if (dora::lora_bwd_max_grid(T, out, r, vec) > INT32_MAX)
     return fail(DORA_UNSUPPORTED, "%s: out=%lld needs more workgroups than one launch holds", fn, (long long)out);
   dora::LoraBwdArgs a{dtype, T, out, r, s, add_base ? 1 : 0, dy, base, h, B, mag, norm, d_base, d_B, d_mag, ws, stream};

@@ -48,15 +48,35 @@ inline size_t align16(size_t x) { return (x + 15) & ~static_cast<size_t>(15); }
 
 constexpr int kGramU = 8;  // K steps per batch of fragment loads
 
+// One entry g' of G' = scale * G as the storage-dtype pair hi = round(g'),
+// lo = round(g' - hi), written at (row, col) and, for an entry of an
+// off-diagonal tile, at its mirror (col, row).  Used when a single K split
+// covers the whole K axis (no partial sums to add): the Gram kernel then
+// writes G'hi/G'lo itself and the plan holds no fp32 partials.
+template <int DT>
+__device__ inline void gram_store_pair(typename Dt<DT>::T* ghi, typename Dt<DT>::T* glo, int64_t r, int64_t row,
+                                       int64_t col, float gp, bool mirror) {
+  using T = typename Dt<DT>::T;
+  const T hi = Dt<DT>::from_f(gp);
+  const T lo = Dt<DT>::from_f(gp - Dt<DT>::to_f(hi));
+  ghi[row * r + col] = hi;
+  glo[row * r + col] = lo;
+  if (mirror) {
+    ghi[col * r + row] = hi;
+    glo[col * r + row] = lo;
+  }
+}
+
 // Split-K partial products of G on its upper-triangular 32x32 tiles (G is
 // symmetric).  Workgroup (tile, split) = 4 waves; each wave accumulates a
 // quarter of the split's K steps with MFMA 32x32x16, its operand fragments
 // loaded straight from global memory (A is small and L2/MALL resident) in
 // batches of kGramU steps; the four wave partials are summed in LDS in a fixed
 // order and stored as the split's 32x32 tile.
-template <int DT>
+template <int DT, bool DIRECT>
 __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A, int64_t in, int64_t r, int nT,
-                                                    int splitG, float* gpart) {
+                                                    int splitG, float* gpart, float scale, typename Dt<DT>::T* ghi,
+                                                    typename Dt<DT>::T* glo) {
   using T = typename Dt<DT>::T;
   using V8 = typename Dt<DT>::V8;
   __shared__ float red[4][32 * 32];
@@ -114,7 +134,13 @@ __global__ __launch_bounds__(256) void gram_partial(const typename Dt<DT>::T* A,
   float* dst = gpart + static_cast<int64_t>(sp) * r * r;
   for (int e = threadIdx.x; e < 1024; e += 256) {
     const int64_t row = static_cast<int64_t>(ti) * 32 + e / 32, col = static_cast<int64_t>(tj) * 32 + e % 32;
-    if (row < r && col < r) dst[row * r + col] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+    if (row < r && col < r) {
+      const float g = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+      if constexpr (DIRECT)
+        gram_store_pair<DT>(ghi, glo, r, row, col, scale * g, ti != tj);
+      else
+        dst[row * r + col] = g;
+    }
   }
 }
 
@@ -527,9 +553,10 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
 constexpr int kGramStage = 2 * 64 * 128;  // X and Y panels, 64 rows x 128 bytes
 constexpr int kGramL = 4;                 // DMA instructions per wave per stage
 
-template <int DT, int kGramNS>
+template <int DT, int kGramNS, bool DIRECT>
 __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int in, int r, int nB, int splitG,
-                                                float* gpart) {
+                                                float* gpart, float scale, typename Dt<DT>::T* ghi,
+                                                typename Dt<DT>::T* glo) {
   using V8 = typename Dt<DT>::V8;
   static_assert(kGramNS >= 3 && kGramNS <= 8 && (kGramNS - 2) * kGramL < 64, "ring slots");
   __shared__ __attribute__((aligned(1024))) char smem[kGramNS * kGramStage];
@@ -641,7 +668,12 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int row = x0 + wm * 32 + 8 * (q / 4) + 4 * fh + (q % 4);
-    if (row < r && col < r) dst[static_cast<int64_t>(row) * r + col] = acc0[q] + acc1[q];
+    if (row < r && col < r) {
+      if constexpr (DIRECT)
+        gram_store_pair<DT>(ghi, glo, r, row, col, scale * (acc0[q] + acc1[q]), bi != bj);
+      else
+        dst[static_cast<int64_t>(row) * r + col] = acc0[q] + acc1[q];
+    }
   }
 }
 
@@ -1149,11 +1181,21 @@ hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* w
   float* gpart = reinterpret_cast<float*>(ws + p.off_gpart);
   const int nUpper = p.nTg * (p.nTg + 1) / 2;
   const dim3 ggrid(static_cast<unsigned>(cdiv(static_cast<int64_t>(nUpper) * p.splitG, 8) * 8));
+  if (p.gram_direct) {  // one K split: the Gram kernel writes G'hi/G'lo itself
+    if (vec)
+      hipLaunchKernelGGL((gram_dma<DT, 4, true>), ggrid, dim3(256), 0, stream, A, static_cast<int>(p.in),
+                         static_cast<int>(p.r), p.nTg, 1, nullptr, scale, ghi, glo);
+    else
+      hipLaunchKernelGGL((gram_partial<DT, true>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, 1, nullptr,
+                         scale, ghi, glo);
+    return hipGetLastError();
+  }
   if (vec)
-    hipLaunchKernelGGL((gram_dma<DT, 4>), ggrid, dim3(256), 0, stream, A, static_cast<int>(p.in),
-                       static_cast<int>(p.r), p.nTg, p.splitG, gpart);
+    hipLaunchKernelGGL((gram_dma<DT, 4, false>), ggrid, dim3(256), 0, stream, A, static_cast<int>(p.in),
+                       static_cast<int>(p.r), p.nTg, p.splitG, gpart, scale, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((gram_partial<DT>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, p.splitG, gpart);
+    hipLaunchKernelGGL((gram_partial<DT, false>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, p.splitG, gpart,
+                       scale, nullptr, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gram_finalize<DT>), dim3(static_cast<unsigned>(gram_finalize_blocks(p.r))), dim3(256), 0,
@@ -1265,7 +1307,7 @@ hipError_t launch_norm_bwd_db(const NormPlan& p, const void* W0, const void* A, 
 }
 
 size_t norm_scratch_bound(int64_t out, int64_t r) {
-  return static_cast<size_t>(4 * (out * r + r * r) + 64 * out + 256);
+  return static_cast<size_t>(4 * (out * r + r * r) + 64 * out);
 }
 
 int64_t norm_max_grid(const NormPlan& p) {
@@ -1335,7 +1377,7 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
   auto layout = [&]() {
     size_t off = 0;
     p.off_gpart = off;
-    off += align16(static_cast<size_t>(p.splitG) * r * r * 4);
+    if (!p.gram_direct) off += align16(static_cast<size_t>(p.splitG) * r * r * 4);
     p.off_ghi = off;
     off += align16(static_cast<size_t>(r * r * e));
     p.off_glo = off;
@@ -1350,6 +1392,11 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
   const size_t bound = norm_scratch_bound(out, r);
   while (p.bytes > bound && p.splitG > 1) {
     --p.splitG;
+    layout();
+  }
+  if (p.bytes > bound && p.splitG == 1) {
+    // r large against out: no fp32 partials, the Gram kernel writes G'hi/G'lo
+    p.gram_direct = true;
     layout();
   }
   while (p.bytes > bound && p.nSplit > 1) {

@@ -23,6 +23,9 @@ struct NormPlan {
   // Gram: upper-triangular tiles per side (64 rows on the 16-byte path, 32
   // otherwise) x K splits
   int nTg = 0, splitG = 0;
+  // one K split and no fp32 partial region: the Gram kernel writes G'hi/G'lo
+  // directly (chosen when the partials would not fit the scratch bound)
+  bool gram_direct = false;
   // workspace byte offsets
   size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, bytes = 0;
 };
@@ -36,8 +39,8 @@ int64_t norm_max_grid(const NormPlan& p);
 // known only at the call).
 size_t norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
 
-// The factored memory bound 4*(out*r + r*r) + 64*out bytes, plus 256 bytes of
-// region alignment.
+// The factored memory bound 4*(out*r + r*r) + 64*out bytes (region
+// alignment included).
 size_t norm_scratch_bound(int64_t out, int64_t r);
 
 struct NormArgs {

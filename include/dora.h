@@ -77,10 +77,21 @@
 extern "C" {
 #endif
 
+/*
+ * DORA_UNSUPPORTED marks arguments that are valid but that this library does
+ * not take; a caller can route such a call elsewhere (the page's eager tier):
+ *  - an unknown dtype code;
+ *  - sizes whose launch grid would exceed one grid dimension's limit;
+ *  - on the fast paths of dora_lora_compose_bwd and dora_norm_bwd, a token or
+ *    row slice that would span 2 GiB or more;
+ *  - dora_lora_compose_bwd with a shape or pointers its fast path cannot take
+ *    and T * r above 2^20 (its slow path runs T * r products in order in one
+ *    thread per output column).
+ */
 enum dora_status {
   DORA_OK = 0,
   DORA_INVALID_ARG = 1, /* null pointer, negative size, workspace too small, bad alias */
-  DORA_UNSUPPORTED = 2, /* unknown dtype code */
+  DORA_UNSUPPORTED = 2, /* valid arguments this library does not take (listed above) */
   DORA_HIP_ERROR = 3    /* a kernel launch failed (message from the HIP runtime) */
 };
 
@@ -90,10 +101,11 @@ enum dora_dtype { DORA_BF16 = 0, DORA_F16 = 1 };
  * Bytes of device workspace dora_norm_factored needs for these sizes.
  * The scratch is O(out*r + r*r): split-K partial sums of G = A*A^T, the
  * two-term split of (s/2)*G in the storage dtype, and per-split row partials.
- * For r <= out it never exceeds 4*(out*r + r*r) + 64*out + 256 bytes (the
- * factored norm's memory bound, paragraph on the factored norm; 256 bytes of
- * region alignment).  Returns 0 for invalid
- * sizes (negative) or an unknown dtype.
+ * For every shape it stays within 4*(out*r + r*r) + 64*out bytes, region
+ * alignment included (the factored norm's memory bound, paragraph on the
+ * factored norm): where the Gram partials would not fit, one K split writes
+ * the split of (s/2)*G directly.  Returns 0 for invalid sizes (negative) or an
+ * unknown dtype.
  */
 DORA_API size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, int dtype);
 
@@ -247,7 +259,8 @@ DORA_API size_t dora_lora_compose_bwd_workspace_bytes(int64_t T, int64_t out, in
  * dora_lora_compose_bwd_workspace_bytes(T, out, r) bytes on the fast path
  * (out and r multiples of 8, 8 <= r <= 2^20, T >= 1, 16-byte aligned
  * pointers); other cases take a slow path (one thread per output column) and
- * need no workspace.  out == 0 is a no-op; T == 0 gives d_B = 0 and d_mag = 0.
+ * need no workspace; the slow path refuses (DORA_UNSUPPORTED) shapes with
+ * T * r > 2^20.  out == 0 is a no-op; T == 0 gives d_B = 0 and d_mag = 0.
  */
 DORA_API int dora_lora_compose_bwd(const void* dy, const void* base, const void* h, const void* B, const float* mag,
                                    const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype,

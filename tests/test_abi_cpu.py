@@ -33,7 +33,7 @@ def test_version():
 
 
 def bound(out, r):
-    return 4 * (out * r + r * r) + 64 * out + 256
+    return 4 * (out * r + r * r) + 64 * out
 
 
 @pytest.mark.parametrize("name", sorted(synth.CONFIGS))
@@ -48,13 +48,23 @@ def test_norm_workspace_within_factored_bound(name):
 
 
 def test_norm_workspace_bound_over_shapes():
-    for out in (1, 7, 128, 129, 1000, 4096, 27648):
+    # every rank from 1 to 4 * out on small modules (r > out included), and a
+    # spread of ranks on larger ones, in both dtypes and on both paths
+    # (in % 8 selects whether the 16-byte path's plan is also considered)
+    for out in (1, 2, 7, 8, 33, 64):
         for in_ in (0, 8, 100, 4096):
-            for r in (0, 1, 8, 16, 64, 130, 384, 768):
-                if r > out:
-                    continue
+            for r in range(0, 4 * out + 1):
+                for dt in (0, 1):
+                    ws = LIB.dora_norm_workspace_bytes(out, in_, r, dt)
+                    assert ws <= bound(out, r), (out, in_, r, dt, ws, bound(out, r))
+    for out in (128, 129, 1000, 4096, 27648):
+        for in_ in (0, 8, 100, 4096, 8192):
+            for r in (0, 1, 8, 16, 64, 130, 384, 768, 1000, 2048, 4 * out):
                 ws = LIB.dora_norm_workspace_bytes(out, in_, r, 0)
-                assert ws <= bound(out, r), (out, in_, r, ws)
+                assert ws <= bound(out, r), (out, in_, r, ws, bound(out, r))
+    # shapes where r is large against out (the Gram kernel then writes G'hi/G'lo itself)
+    for out, in_, r in ((64, 64, 1000), (33, 64, 200), (8, 8192, 768), (1, 16, 4)):
+        assert LIB.dora_norm_workspace_bytes(out, in_, r, 0) <= bound(out, r)
 
 
 def test_workspace_queries_invalid():
@@ -200,6 +210,24 @@ def test_lora_compose_bwd_validation():
     assert LIB.dora_lora_compose_bwd(None, None, None, None, None, None, 1.0, 8, 0, 8, 0, 0, None, None, None, None, 0,
                                      None) == OK
     assert LIB.dora_lora_compose_bwd_workspace_bytes(0, 8, 8) == 0
+
+
+def test_lora_compose_bwd_slow_path_limit():
+    """Off the fast path (here: an unaligned dy), the slow path runs T * r
+    products in order per output column; above 2^20 the call is refused with
+    UNSUPPORTED before any launch, at or below it the arguments pass validation
+    (checked with far-apart fake pointers and out = 0 would be a no-op, so use
+    a shape whose only failure is the limit)."""
+    out = 8
+
+    def call(T, r):
+        # pointers 2^34 bytes apart: no overlap for any of these sizes
+        p = [(k + 1) << 34 for k in range(10)]
+        return LIB.dora_lora_compose_bwd(p[0] + 2, p[1], p[2], p[3], p[4], p[5], 1.0, T, out, r, 0, 0, p[6], p[7],
+                                         p[8], p[9], 1 << 30, None)
+
+    _status(call(8192, 384), UNSUPPORTED, "slow path")
+    _status(call((1 << 20) // 128 + 1, 128), UNSUPPORTED, "slow path")
 
 
 def test_compose_rejects_grids_beyond_one_launch():
