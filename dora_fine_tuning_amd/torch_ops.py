@@ -33,16 +33,20 @@ This module registers:
   n only through g = m / n; this [out]-sized product is the one step of the
   chain done by torch), and the norm's formula turns it into d_A and d_B.
 
-Tiers: autograd records the compose only when a gradient is needed (training:
-the fused forward, then the fused backward); under ``torch.no_grad()`` or
-``torch.inference_mode()`` the forward kernel runs alone.  ``DoRALinear`` runs
-the compose with the second projection fused in on both tiers, so lora =
-x A^T B^T is never stored. There is no eager fallback. Inputs the kernels
-cannot take raise: CPU tensors, dtypes other than bf16/fp16, and a missing
-library.
+Tiers (paragraph on the dispatch tiers): autograd records the compose only
+when a gradient is needed (training: the fused forward, then the fused
+backward); under ``torch.no_grad()`` or ``torch.inference_mode()`` the forward
+kernel runs alone.  ``DoRALinear`` runs the compose with the second projection
+fused in on both tiers, so lora = x A^T B^T is never stored.  The third tier
+is eager PyTorch for inputs the kernels do not take: tensors on the CPU, matrix
+dtypes other than bf16/fp16 (fp32), and a call the library refuses with
+DORA_UNSUPPORTED.  Those run the plain, unfused torch form of each operator
+(dense B A for the norm, the compose written out elementwise), computed in
+fp32.  Supported inputs on a HIP device always take the kernels; a missing
+library raises on import, it never falls back.
 
-Every operator is argument marshalling around the C ABI (``binding``); the
-arithmetic runs in the HIP kernels.
+On that path every operator is argument marshalling around the C ABI
+(``binding``); the arithmetic runs in the HIP kernels.
 """
 from __future__ import annotations
 
@@ -57,12 +61,88 @@ from . import binding
 Tensor = torch.Tensor
 
 
+# ---------------------------------------------------------------- eager tier
+#
+# The plain PyTorch form of each operator, for inputs the kernels do not take
+# (the page's fallback tier).  fp32 arithmetic, outputs in the matrices' dtype.
+
+
+def _kernels_take(*mats: Tensor) -> bool:
+    """True when the kernels take these matrix arguments: all on a HIP device,
+    in bf16 or fp16."""
+    return all(t.device.type == "cuda" and t.dtype in binding.DTYPE_CODE for t in mats)
+
+
+def _unsupported(e: Exception) -> bool:
+    return isinstance(e, binding.DoraError) and e.status == binding.DORA_UNSUPPORTED
+
+
+def _eager_weight_norm(W0, A, B, s):
+    V = W0.float() + s * (B.float() @ A.float())
+    return torch.linalg.vector_norm(V, dim=1)
+
+
+def _eager_row_sqnorm(W0):
+    W = W0.float()
+    return (W * W).sum(dim=1)
+
+
+def _eager_weight_norm_cached(W0, A, B, base_sq, s):
+    V = B.float() @ A.float()
+    n2 = base_sq.float() + 2.0 * s * (W0.float() * V).sum(dim=1) + (s * s) * (V * V).sum(dim=1)
+    return torch.sqrt(torch.clamp(n2, min=0.0))
+
+
+def _eager_weight_norm_backward(W0, A, B, norm, d_norm, s):
+    n, d = norm.float(), d_norm.float()
+    c = torch.where(n != 0, d / torch.where(n != 0, n, torch.ones_like(n)), torch.zeros_like(n))
+    dV = c[:, None] * (W0.float() + s * (B.float() @ A.float()))
+    return (s * (B.float().t() @ dV)).to(A.dtype), (s * (dV @ A.float().t())).to(B.dtype)
+
+
+def _scales(mag, norm):
+    m, n = mag.float(), norm.float()
+    return m / n, (m - n) / n  # g and g - 1 (the subtraction is exact near g = 1)
+
+
+def _eager_compose(base, lora, mag, norm, s, add_base):
+    g, gm1 = _scales(mag, norm)
+    b = base.float()
+    y = gm1 * b + g * s * lora.float()
+    return (y + b if add_base else y).to(base.dtype)
+
+
+def _eager_compose_backward(dy, base, lora, mag, norm, s, add_base, want_base):
+    g, gm1 = _scales(mag, norm)
+    d = dy.float()
+    d_lora = (g * s * d).to(dy.dtype)
+    d_base = ((g if add_base else gm1) * d).to(dy.dtype) if want_base else dy.new_empty((0,))
+    d_mag = (d * (base.float() + s * lora.float())).sum(dim=0) / norm.float()
+    return d_lora, d_base, d_mag
+
+
+def _eager_lora_compose(base, h, B, mag, norm, s, add_base):
+    return _eager_compose(base, h.float() @ B.float().t(), mag, norm, s, add_base)
+
+
+def _eager_lora_compose_backward(dy, base, h, B, mag, norm, s, add_base, want_base):
+    g, gm1 = _scales(mag, norm)
+    d, hf, Bf = dy.float(), h.float(), B.float()
+    E = d.t() @ hf  # dy^T h
+    d_base = ((g if add_base else gm1) * d).to(dy.dtype) if want_base else dy.new_empty((0,))
+    d_B = ((g * s)[:, None] * E).to(B.dtype)
+    d_mag = ((d * base.float()).sum(dim=0) + s * (Bf * E).sum(dim=1)) / norm.float()
+    return d_base, d_B, d_mag
+
+
 # --------------------------------------------------------------------------- norm
 
 
 @torch.library.custom_op("dora_amd::weight_norm", mutates_args=(), device_types="cuda")
 def weight_norm(W0: Tensor, A: Tensor, B: Tensor, s: float) -> Tensor:
     """||W0_i + s * B_i A||_2 per output row i, fp32, via the factored kernels."""
+    if not _kernels_take(W0, A, B):
+        return _eager_weight_norm(W0, A, B, s)
     return binding.dora_norm_factored(W0.contiguous(), A.contiguous(), B.contiguous(), s)
 
 
@@ -74,6 +154,8 @@ def _weight_norm_fake(W0, A, B, s):
 @torch.library.custom_op("dora_amd::row_sqnorm", mutates_args=(), device_types="cuda")
 def row_sqnorm(W0: Tensor) -> Tensor:
     """||W0_i||^2 per output row, fp32."""
+    if not _kernels_take(W0):
+        return _eager_row_sqnorm(W0)
     return binding.dora_row_sqnorm(W0.contiguous())
 
 
@@ -85,8 +167,10 @@ def _row_sqnorm_fake(W0):
 @torch.library.custom_op("dora_amd::weight_norm_cached", mutates_args=(), device_types="cuda")
 def weight_norm_cached(W0: Tensor, A: Tensor, B: Tensor, base_sq: Tensor, s: float) -> Tensor:
     """The weight norm with the base term ||W0_i||^2 taken from base_sq."""
-    return binding.dora_norm_factored_cached(W0.contiguous(), A.contiguous(), B.contiguous(), base_sq.contiguous(),
-                                             s)
+    if not _kernels_take(W0, A, B):
+        return _eager_weight_norm_cached(W0, A, B, base_sq, s)
+    return binding.dora_norm_factored_cached(W0.contiguous(), A.contiguous(), B.contiguous(),
+                                             base_sq.contiguous().float(), s)
 
 
 @weight_norm_cached.register_fake
@@ -98,7 +182,9 @@ def _weight_norm_cached_fake(W0, A, B, base_sq, s):
 def weight_norm_backward(W0: Tensor, A: Tensor, B: Tensor, norm: Tensor, d_norm: Tensor,
                          s: float) -> tuple[Tensor, Tensor]:
     """(d_A, d_B) of sum(d_norm * n) for n = ||W0 + s*B*A|| (norm: the forward's n)."""
-    return binding.dora_norm_bwd(W0.contiguous(), A.contiguous(), B.contiguous(), norm.contiguous(),
+    if not _kernels_take(W0, A, B):
+        return _eager_weight_norm_backward(W0, A, B, norm, d_norm, s)
+    return binding.dora_norm_bwd(W0.contiguous(), A.contiguous(), B.contiguous(), norm.contiguous().float(),
                                  d_norm.contiguous().float(), s)
 
 
@@ -135,8 +221,10 @@ weight_norm_cached.register_autograd(_norm_grad, setup_context=_norm_setup)
 @torch.library.custom_op("dora_amd::compose", mutates_args=(), device_types="cuda")
 def compose(base: Tensor, lora: Tensor, mag: Tensor, norm: Tensor, s: float, add_base: bool) -> Tensor:
     """(g - 1) * base + g * s * lora, plus base when add_base, with g = mag / norm per column."""
-    return binding.dora_compose_fwd(base.contiguous(), lora.contiguous(), mag.contiguous(), norm.contiguous(), s,
-                                    add_base=add_base)
+    if not _kernels_take(base, lora):
+        return _eager_compose(base, lora, mag, norm, s, add_base)
+    return binding.dora_compose_fwd(base.contiguous(), lora.to(base.dtype).contiguous(), mag.contiguous().float(),
+                                    norm.contiguous().float(), s, add_base=add_base)
 
 
 @compose.register_fake
@@ -149,8 +237,11 @@ def compose_backward(dy: Tensor, base: Tensor, lora: Tensor, mag: Tensor, norm: 
                      want_base: bool) -> tuple[Tensor, Tensor, Tensor]:
     """(d_lora, d_base, d_mag) of the compose.  With want_base false the kernel
     does not write d_base and an empty tensor stands in for it."""
-    d_lora, d_base, d_mag = binding.dora_compose_bwd(dy.contiguous(), base, lora, mag, norm, s, add_base=add_base,
-                                                     want_d_base=want_base)
+    if not _kernels_take(dy, base, lora):
+        return _eager_compose_backward(dy, base, lora, mag, norm, s, add_base, want_base)
+    d_lora, d_base, d_mag = binding.dora_compose_bwd(dy.contiguous(), base.contiguous(), lora.contiguous(),
+                                                     mag.contiguous().float(), norm.contiguous().float(), s,
+                                                     add_base=add_base, want_d_base=want_base)
     if d_base is None:
         d_base = dy.new_empty((0,))
     return d_lora, d_base, d_mag
@@ -165,8 +256,10 @@ def _compose_backward_fake(dy, base, lora, mag, norm, s, add_base, want_base):
 @torch.library.custom_op("dora_amd::lora_compose", mutates_args=(), device_types="cuda")
 def lora_compose(base: Tensor, h: Tensor, B: Tensor, mag: Tensor, norm: Tensor, s: float, add_base: bool) -> Tensor:
     """(g - 1) * base + g * s * (h B^T), plus base when add_base; lora never stored."""
-    return binding.dora_lora_compose_fwd(base.contiguous(), h.contiguous(), B.contiguous(), mag.contiguous(),
-                                         norm.contiguous(), s, add_base=add_base)
+    if not _kernels_take(base, h, B):
+        return _eager_lora_compose(base, h, B, mag, norm, s, add_base)
+    return binding.dora_lora_compose_fwd(base.contiguous(), h.contiguous(), B.contiguous(), mag.contiguous().float(),
+                                         norm.contiguous().float(), s, add_base=add_base)
 
 
 @lora_compose.register_fake
@@ -203,9 +296,17 @@ def lora_compose_backward(dy: Tensor, base: Tensor, h: Tensor, B: Tensor, mag: T
     """(d_base, d_B, d_mag) of ``lora_compose``, lora and d_lora never formed.
     With want_base false the kernel does not write d_base and an empty tensor
     stands in for it."""
-    d_base, d_B, d_mag = binding.dora_lora_compose_bwd(dy.contiguous(), base.contiguous(), h.contiguous(),
-                                                       B.contiguous(), mag.contiguous(), norm.contiguous(), s,
-                                                       add_base=add_base, want_d_base=want_base)
+    if not _kernels_take(dy, base, h, B):
+        return _eager_lora_compose_backward(dy, base, h, B, mag, norm, s, add_base, want_base)
+    try:
+        d_base, d_B, d_mag = binding.dora_lora_compose_bwd(dy.contiguous(), base.contiguous(), h.contiguous(),
+                                                           B.contiguous(), mag.contiguous().float(),
+                                                           norm.contiguous().float(), s, add_base=add_base,
+                                                           want_d_base=want_base)
+    except binding.DoraError as e:
+        if not _unsupported(e):  # a shape the library refuses (its slow path would be too slow): eager tier
+            raise
+        return _eager_lora_compose_backward(dy, base, h, B, mag, norm, s, add_base, want_base)
     if d_base is None:
         d_base = dy.new_empty((0,))
     return d_base, d_B, d_mag
@@ -242,6 +343,17 @@ def _lora_compose_grad(ctx, dy):
 lora_compose.register_autograd(_lora_compose_grad, setup_context=_lora_compose_setup)
 
 
+# The eager tier is also each operator's kernel for CPU tensors.
+weight_norm.register_kernel("cpu")(_eager_weight_norm)
+row_sqnorm.register_kernel("cpu")(_eager_row_sqnorm)
+weight_norm_cached.register_kernel("cpu")(_eager_weight_norm_cached)
+weight_norm_backward.register_kernel("cpu")(_eager_weight_norm_backward)
+compose.register_kernel("cpu")(_eager_compose)
+compose_backward.register_kernel("cpu")(_eager_compose_backward)
+lora_compose.register_kernel("cpu")(_eager_lora_compose)
+lora_compose_backward.register_kernel("cpu")(_eager_lora_compose_backward)
+
+
 # -------------------------------------------------------------------------- layer
 
 
@@ -269,8 +381,8 @@ class DoRALinear(torch.nn.Module):
                  detach_norm: bool = True):
         super().__init__()
         self.detach_norm = detach_norm
-        if dtype not in binding.DTYPE_CODE:
-            raise ValueError(f"unsupported dtype {dtype}; bf16 and fp16 are")
+        if dtype not in (torch.bfloat16, torch.float16, torch.float32):
+            raise ValueError(f"unsupported dtype {dtype}; bf16 and fp16 (HIP kernels) and fp32 (eager tier) are")
         self.in_features, self.out_features, self.r = in_features, out_features, r
         self.s = float(np.float32(alpha / math.sqrt(r)))
         if weight is None:

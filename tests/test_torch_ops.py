@@ -15,19 +15,117 @@ torch_ops = pytest.importorskip("dora_fine_tuning_amd.torch_ops")
 gpu = pytest.mark.gpu
 
 
-def test_ops_reject_host_tensors():
-    x = torch.zeros(4, 8, dtype=torch.bfloat16)
-    v = torch.ones(8, dtype=torch.float32)
-    with pytest.raises((NotImplementedError, RuntimeError, ValueError)):
-        torch_ops.compose(x, x, v, v, 1.0, False)
-    with pytest.raises((NotImplementedError, RuntimeError, ValueError)):
-        torch_ops.weight_norm(torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(2, 8, dtype=torch.bfloat16),
-                              torch.zeros(8, 2, dtype=torch.bfloat16), 1.0)
-
-
 def test_layer_rejects_other_dtypes():
     with pytest.raises(ValueError):
-        torch_ops.DoRALinear(8, 8, 2, dtype=torch.float32)
+        torch_ops.DoRALinear(8, 8, 2, dtype=torch.float64)
+
+
+# ------------------------------------------------------------------ eager tier (CPU)
+
+
+def test_eager_tier_ops_match_oracle():
+    """CPU tensors take the eager tier (plain torch, fp32): every operator
+    against the fp64 oracle.  fp32 arithmetic over bf16 inputs bounds the
+    error well below these tolerances."""
+    rng = np.random.default_rng(21)
+    T, out, in_, r, s = 40, 48, 64, 8, 2.5
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+    W0, A, B = bf(rng.normal(0, 0.02, (out, in_))), bf(rng.normal(0, 0.125, (r, in_))), bf(rng.normal(0, 0.05, (out, r)))
+    n_ref = O.weight_norm(W0, A, B, s)
+    np.testing.assert_allclose(torch_ops.weight_norm(W0, A, B, s).double().numpy(), n_ref, rtol=1e-5)
+    sq = torch_ops.row_sqnorm(W0)
+    np.testing.assert_allclose(sq.double().numpy(), O.row_sqnorm(W0), rtol=1e-5)
+    np.testing.assert_allclose(torch_ops.weight_norm_cached(W0, A, B, sq, s).double().numpy(),
+                               O.weight_norm_cached(sq, W0, A, B, s), rtol=1e-5)
+    n32 = torch.from_numpy(n_ref.astype(np.float32))
+    dn = torch.from_numpy(rng.normal(0, 1, out).astype(np.float32))
+    dA, dB = torch_ops.weight_norm_backward(W0, A, B, n32, dn, s)
+    rA, rB = O.weight_norm_bwd(dn, n32, W0, A, B, s)
+    np.testing.assert_allclose(dA.double().numpy(), rA, rtol=2e-2, atol=2e-2 * np.abs(rA).max())
+    np.testing.assert_allclose(dB.double().numpy(), rB, rtol=2e-2, atol=2e-2 * np.abs(rB).max())
+
+    base, lora, dy = bf(rng.normal(0, 1, (T, out))), bf(rng.normal(0, 0.3, (T, out))), bf(rng.normal(0, 1, (T, out)))
+    m = torch.from_numpy(synth.magnitude(n_ref, rng.uniform(-2**-8, 2**-8, out)))
+    for add_base in (False, True):
+        bg, lg, mg = (t.clone().requires_grad_() for t in (base, lora, m))
+        y = torch_ops.compose(bg, lg, mg, n32, s, add_base)
+        y.backward(dy)
+        y_ref = O.compose_fwd(base, lora, m, n32, s, add_base)
+        dl_ref, db_ref, dm_ref = O.compose_bwd(dy, base, lora, m, n32, s, add_base)
+        g = m.double().numpy() / n32.double().numpy()
+        b64, l64 = O.as_f64(base), O.as_f64(lora)
+        mass = np.abs((g - 1) * b64) + np.abs(g * s * l64) + (np.abs(b64) if add_base else 0)
+        assert_compose(y.detach().float().numpy(), y_ref, mass, "bf16", "eager y")
+        assert_compose(lg.grad.float().numpy(), dl_ref, np.abs(dl_ref), "bf16", "eager d_lora")
+        assert_compose(bg.grad.float().numpy(), db_ref, np.abs(db_ref), "bf16", "eager d_base")
+        cond = np.sum(np.abs(O.as_f64(dy) * (b64 + s * l64)), axis=0) / n32.double().numpy()
+        assert_dmag(mg.grad.numpy(), dm_ref, cond, "eager d_mag")
+    h = bf(rng.normal(0, 1, (T, r)))
+    y = torch_ops.lora_compose(base, h, B, m, n32, s, True)
+    y_ref = O.lora_compose_fwd(base, h, B, m, n32, s, True)
+    np.testing.assert_allclose(y.double().numpy(), y_ref, rtol=2e-2, atol=1e-2)
+    d_base, d_B, d_mag = torch_ops.lora_compose_backward(dy, base, h, B, m, n32, s, False, True)
+    rb, rB2, rm = O.lora_compose_bwd(dy, base, h, B, m, n32, s, False)
+    np.testing.assert_allclose(d_base.double().numpy(), rb, rtol=2e-2, atol=1e-6)
+    np.testing.assert_allclose(d_B.double().numpy(), rB2, rtol=2e-2, atol=2e-2 * np.abs(rB2).max())
+    np.testing.assert_allclose(d_mag.double().numpy(), rm, rtol=1e-4, atol=1e-4 * np.abs(rm).max())
+
+
+def test_eager_tier_layer_matches_dense_reference():
+    """DoRALinear on the CPU (eager tier), forward and backward, against the
+    float64 dense evaluation with the norm detached and not detached."""
+    torch.manual_seed(4)
+    for detach in (True, False):
+        layer = torch_ops.DoRALinear(96, 80, 8, dtype=torch.float32, detach_norm=detach)
+        with torch.no_grad():
+            layer.lora_B.normal_(0.0, 0.05)
+            layer.magnitude.mul_(1.0 + 0.01 * torch.randn_like(layer.magnitude))
+        x = torch.randn(30, 96).requires_grad_()
+        y = layer(x)
+        dy = (y.detach() + 0.1 * torch.randn_like(y))
+        y.backward(dy)
+        ref = _dense_reference if detach else _dense_reference_full
+        out = ref(x, layer.weight, layer.lora_A, layer.lora_B, layer.magnitude, layer.s, dy)
+        y_ref, dx_ref, dA_ref, dB_ref, dm_ref = out[:5]
+        assert _rel(y, y_ref) < 1e-5 and _rel(x.grad, dx_ref) < 1e-5
+        assert _rel(layer.lora_A.grad, dA_ref) < 1e-4 and _rel(layer.lora_B.grad, dB_ref) < 1e-4
+        assert _rel(layer.magnitude.grad, dm_ref) < 1e-5
+
+
+def _compile_check(layer, x):
+    """The layer under torch.compile (fullgraph, aot_eager backend: torch's
+    own autograd-traced graph, no code generation) gives no graph break and
+    the eager layer's outputs and gradients."""
+    import torch._dynamo
+
+    torch._dynamo.reset()
+    y_eager = layer(x)  # fills the base-term cache outside the compiled region
+    explain = torch._dynamo.explain(layer)(x)
+    assert explain.graph_break_count == 0, explain.break_reasons
+    compiled = torch.compile(layer, fullgraph=True, backend="aot_eager")
+    xg = x.detach().clone().requires_grad_()
+    y = compiled(xg)
+    dy = torch.randn_like(y)
+    y.backward(dy)
+    grads = [p.grad.clone() for p in (layer.lora_A, layer.lora_B, layer.magnitude)]
+    for p in (layer.lora_A, layer.lora_B, layer.magnitude):
+        p.grad = None
+    xe = x.detach().clone().requires_grad_()
+    y_eager = layer(xe)
+    y_eager.backward(dy)
+    assert torch.equal(y.detach(), y_eager.detach())
+    assert torch.equal(xg.grad, xe.grad)
+    for g, p in zip(grads, (layer.lora_A, layer.lora_B, layer.magnitude)):
+        assert torch.equal(g, p.grad)
+
+
+def test_compile_without_graph_breaks_cpu():
+    torch.manual_seed(5)
+    for detach in (True, False):
+        layer = torch_ops.DoRALinear(64, 48, 8, dtype=torch.float32, detach_norm=detach)
+        with torch.no_grad():
+            layer.lora_B.normal_(0.0, 0.05)
+        _compile_check(layer, torch.randn(2, 10, 64))
 
 
 def _compose_inputs(T, out, dtype, seed):
@@ -276,3 +374,80 @@ def test_dora_linear_norm_not_detached():
     assert _rel(layer.lora_A.grad, dA_ref) < 3e-2
     assert _rel(layer.lora_B.grad, dB_ref) < 3e-2
     assert layer.weight.grad is None
+
+
+@gpu
+def test_compile_without_graph_breaks_gpu():
+    dev = torch.device("cuda:0")
+    torch.manual_seed(6)
+    for detach in (True, False):
+        layer = torch_ops.DoRALinear(256, 192, 16, device=dev, detach_norm=detach)
+        with torch.no_grad():
+            layer.lora_B.normal_(0.0, 0.05)
+        _compile_check(layer, torch.randn(3, 20, 256, device=dev, dtype=torch.bfloat16))
+
+
+@gpu
+def test_supported_inputs_always_take_the_kernels(monkeypatch):
+    """bf16/fp16 tensors on the GPU reach the C ABI for every operator of the
+    layer's forward and backward (norm not detached, so the norm backward too);
+    the eager tier is not entered (its functions raise if called)."""
+    from dora_fine_tuning_amd import binding
+
+    dev = torch.device("cuda:0")
+    calls = {}
+    for name in ("dora_norm_factored_cached", "dora_row_sqnorm", "dora_lora_compose_fwd", "dora_lora_compose_bwd",
+                 "dora_norm_bwd", "dora_compose_fwd", "dora_compose_bwd", "dora_norm_factored"):
+        fn = getattr(binding, name)
+
+        def counted(*a, _fn=fn, _name=name, **k):
+            calls[_name] = calls.get(_name, 0) + 1
+            return _fn(*a, **k)
+
+        monkeypatch.setattr(binding, name, counted)
+    for name in [n for n in dir(torch_ops) if n.startswith("_eager_")]:
+        def boom(*a, _name=name, **k):
+            raise AssertionError(f"eager tier entered: {_name}")
+
+        monkeypatch.setattr(torch_ops, name, boom)
+    for dtype in (torch.bfloat16, torch.float16):
+        layer = torch_ops.DoRALinear(256, 192, 16, device=dev, dtype=dtype, detach_norm=False)
+        with torch.no_grad():
+            layer.lora_B.normal_(0.0, 0.05)
+        x = torch.randn(40, 256, device=dev, dtype=dtype).requires_grad_()
+        layer(x).backward(torch.randn(40, 192, device=dev, dtype=dtype))
+        base, lora, dy, m, n, s = _compose_inputs(64, 64, dtype, 9)
+        lg = lora.to(dev).requires_grad_()
+        torch_ops.compose(base.to(dev), lg, m.to(dev), n.to(dev), s, False).backward(dy.to(dev))
+        torch_ops.weight_norm(*(t.to(dev) for t in synth.weights(synth.CONFIGS["tiny"], "bf16" if dtype == torch.bfloat16 else "fp16")), 1.5)
+    for name in ("dora_norm_factored_cached", "dora_row_sqnorm", "dora_lora_compose_fwd", "dora_lora_compose_bwd",
+                 "dora_norm_bwd", "dora_compose_fwd", "dora_compose_bwd", "dora_norm_factored"):
+        assert calls.get(name, 0) >= 2, (name, calls)
+
+
+@gpu
+def test_eager_tier_for_fp32_on_the_gpu():
+    """fp32 matrices on the GPU are not a kernel dtype: the operators take the
+    eager tier there and agree with the oracle."""
+    dev = torch.device("cuda:0")
+    base, lora, dy, m, n, s = _compose_inputs(50, 72, torch.float32, 13)
+    y = torch_ops.compose(base.to(dev), lora.to(dev), m.to(dev), n.to(dev), s, True)
+    y_ref = O.compose_fwd(base, lora, m, n, s, True)
+    np.testing.assert_allclose(y.double().cpu().numpy(), y_ref, rtol=1e-5, atol=1e-6)
+
+
+@gpu
+def test_compose_backward_takes_non_contiguous_inputs():
+    """A transposed (non-contiguous) base and lora pass through the forward and
+    the backward alike (the saved originals are made contiguous for the kernel)."""
+    dev = torch.device("cuda:0")
+    base, lora, dy, m, n, s = _compose_inputs(64, 96, torch.bfloat16, 17)
+    bt = base.t().contiguous().to(dev).t()  # [T x out] view of an [out x T] buffer
+    lt = lora.t().contiguous().to(dev).t()
+    assert not bt.is_contiguous() and not lt.is_contiguous()
+    bg, lg = bt.detach().requires_grad_(), lt.detach().requires_grad_()
+    y = torch_ops.compose(bg, lg, m.to(dev), n.to(dev), s, False)
+    y.backward(dy.to(dev))
+    dl_ref, db_ref, _ = O.compose_bwd(dy, base, lora, m, n, s, False)
+    assert_compose(lg.grad.float().cpu().numpy(), dl_ref, np.abs(dl_ref), "bf16", "d_lora non-contiguous")
+    assert_compose(bg.grad.float().cpu().numpy(), db_ref, np.abs(db_ref), "bf16", "d_base non-contiguous")
