@@ -15,7 +15,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdora_hip.so")
+# DORA_HIP_LIB selects another build of the same library (the host-sanitizer
+# build of the CPU validation check); by default the in-tree libdora_hip.so.
+LIB_PATH = os.environ.get("DORA_HIP_LIB") or os.path.join(_HERE, "libdora_hip.so")
 
 DORA_OK, DORA_INVALID_ARG, DORA_UNSUPPORTED, DORA_HIP_ERROR = 0, 1, 2, 3
 DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}

@@ -44,24 +44,36 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libdora_hip.so; returns its path."""
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for a CPU check of
+# the C ABI's validation layer: every -fsanitize= goes to the host compilation
+# only (-Xarch_host); the device code is built exactly as in the product.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+SANITIZED_LIB = os.path.join(HERE, "libdora_hip_hostsan.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every csrc/*.hip and link libdora_hip.so; returns its path.
+    With ``sanitize`` the host code is instrumented (see SANITIZE) and the
+    result goes to libdora_hip_hostsan.so, for CPU tests only."""
     srcs = sources()
+    flags = COMMON + (SANITIZE if sanitize else [])
+    lib = SANITIZED_LIB if sanitize else LIB
     tmp = tempfile.mkdtemp(prefix="dora_build_")
     try:
         objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
         with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-            logs = list(ex.map(lambda so: _run([HIPCC, *COMMON, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
-        tmp_lib = LIB + ".tmp"
-        logs.append(_run([HIPCC, *COMMON, "-shared", "-o", tmp_lib, *objs]))
-        os.replace(tmp_lib, LIB)
+            logs = list(ex.map(lambda so: _run([HIPCC, *flags, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+        tmp_lib = lib + ".tmp"
+        logs.append(_run([HIPCC, *flags, "-shared", "-o", tmp_lib, *objs]))
+        os.replace(tmp_lib, lib)
         if verbose:
             for l in logs:
                 if l.strip():
                     print(l)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
