@@ -158,3 +158,20 @@ def test_lora_bwd_full_config(lib, name, dtype):
     rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 62, replace=False)]))
     check(lib, dy, base.cpu(), h.cpu(), B, m, n, cfg.s, dtype, f"{name} {dtype}", cols=cols, rows=rows)
     log(f"[lora-bwd] {name} {dtype}: ok")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_lora_bwd_all_elements_wide(lib, dtype):
+    """The wide module (out = in = 8192, r = 384, T = 8192) in the benchmark's
+    launch configuration: every element of d_base, every element of d_B and
+    every d_mag column against the oracle."""
+    name = "wide_8192_r384"
+    cfg = synth.CONFIGS[name]
+    W0, A, B = synth.weights(cfg, dtype)
+    x, dy = synth.activations(cfg, dtype)
+    base, h = synth.base_and_h(x, W0, A, device=DEV)
+    del x, W0
+    n = (np.linalg.norm(f64(B), axis=1) + 1.0).astype(np.float32)
+    m = synth.magnitude(n, synth.magnitude_eps(cfg))
+    check(lib, dy, base.cpu(), h.cpu(), B, m, n, cfg.s, dtype, f"{name} {dtype} all elements")
+    log(f"[lora-bwd] {name} {dtype}: every element of d_base and d_B and every d_mag column ok")

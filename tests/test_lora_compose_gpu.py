@@ -165,3 +165,33 @@ def test_lora_compose_full_config(lib, name, dtype):
     want = PU.representable_nonzero(ref, dtype)[:, near]
     assert np.all((y != 0)[:, near] == want)
     log(f"[lora-fused] {name} {dtype}: near-unity correction nonzero in all {int(want.sum())} representable elements")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_lora_compose_all_elements_wide(lib, dtype):
+    """The wide module (out = in = 8192, r = 384, T = 8192) in the benchmark's
+    launch configuration: every element of y, delta and full output, against
+    the oracle, which walks token chunks of 512 rows."""
+    name = "wide_8192_r384"
+    cfg = synth.CONFIGS[name]
+    W0, A, B = synth.weights(cfg, dtype)
+    x, _ = synth.activations(cfg, dtype)
+    base, h = synth.base_and_h(x, W0, A, device=DEV)
+    del x, W0
+    n = np.linalg.norm(f64(B), axis=1) + 1.0
+    n32 = n.astype(np.float32)
+    m = synth.magnitude(n, synth.magnitude_eps(cfg))
+    md, nd, Bd = torch.from_numpy(m).to(DEV), torch.from_numpy(n32).to(DEV), B.to(DEV)
+    Bf = f64(B)
+    for add_base in (False, True):
+        y = lib.dora_lora_compose_fwd(base, h, Bd, md, nd, cfg.s, add_base=add_base)
+        fo = 0
+        for t0 in range(0, cfg.T, 512):
+            t1 = min(t0 + 512, cfg.T)
+            bc, hc = f64(base[t0:t1]), f64(h[t0:t1])
+            ref = O.lora_compose_fwd(bc, hc, Bf, m, n32, cfg.s, add_base=add_base)
+            fo += PU.assert_compose(f64(y[t0:t1]), ref, mass(bc, hc, Bf, m, n32, cfg.s, add_base), dtype,
+                                    f"{name} fused rows {t0}:{t1} add_base={add_base}", floor_rel(cfg.r))
+        log(f"[lora-fused] {name} {dtype} add_base={add_base}: all {cfg.T * cfg.out} elements ok "
+            f"({fo} floor-only elements)")
+        del y

@@ -278,6 +278,97 @@ def test_full_config(lib, name, dtype):
         assert np.all((y != 0)[:, collapsed] == want_c)
 
 
+# ----------------------------------------- every element at the wide module (8192^2, r = 384)
+
+
+def _token_chunks(T, rows=512):
+    for t0 in range(0, T, rows):
+        yield t0, min(t0 + rows, T)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_full_elements_wide(lib, dtype):
+    """The wide module in the benchmark's launch configuration, with every
+    element of y (delta and full output), d_lora and d_base and every d_mag
+    column compared with the oracle; the oracle walks token chunks of 512 rows
+    (d_mag and its condition sum over the chunks in fp64)."""
+    name = "wide_8192_r384"
+    cfg = synth.CONFIGS[name]
+    log(f"[all-elements] {name} {dtype}: generating")
+    W0, A, B = synth.weights(cfg, dtype)
+    n_ref = O.weight_norm(W0, A, B, cfg.s)
+    x, dy = synth.activations(cfg, dtype)
+    base, lora = synth.base_and_lora(x, W0, A, B, device=DEV)
+    del x
+    n32 = n_ref.astype(np.float32)
+    m = synth.magnitude(n_ref, synth.magnitude_eps(cfg))
+    md, nd = torch.from_numpy(m).to(DEV), torch.from_numpy(n32).to(DEV)
+    dyd = dy.to(DEV)
+    g = m.astype(np.float64) / n32.astype(np.float64)
+    s = cfg.s
+    for add_base in (False, True):
+        y = lib.dora_compose_fwd(base, lora, md, nd, s, add_base=add_base)
+        dl, db, dm = lib.dora_compose_bwd(dyd, base, lora, md, nd, s, add_base=add_base)
+        rm = np.zeros(cfg.out)
+        cond = np.zeros(cfg.out)
+        fo = 0
+        for t0, t1 in _token_chunks(cfg.T):
+            Bc, Lc, Dc = f64(base[t0:t1]), f64(lora[t0:t1]), f64(dyd[t0:t1])
+            ref = O.compose_fwd(Bc, Lc, m, n32, s, add_base=add_base)
+            mass = np.abs((g - 1) * Bc) + np.abs(g * s * Lc) + (np.abs(Bc) if add_base else 0)
+            fo += PU.assert_compose(f64(y[t0:t1]), ref, mass, dtype, f"{name} fwd rows {t0}:{t1} add_base={add_base}")
+            rl, rb, rmc = O.compose_bwd(Dc, Bc, Lc, m, n32, s, add_base=add_base)
+            PU.assert_compose(f64(dl[t0:t1]), rl, np.abs(rl), dtype, f"{name} d_lora rows {t0}:{t1}")
+            PU.assert_compose(f64(db[t0:t1]), rb, np.abs(rb), dtype, f"{name} d_base rows {t0}:{t1}")
+            rm += rmc
+            cond += np.sum(np.abs(Dc * (Bc + s * Lc)), axis=0) / n32
+        PU.assert_dmag(f64(dm), rm, cond, f"{name} d_mag (all columns)")
+        log(f"[all-elements] {name} {dtype} add_base={add_base}: all {cfg.T * cfg.out} elements of y, d_lora, d_base "
+            f"and all {cfg.out} d_mag columns within tolerance ({fo} floor-only elements of y)")
+        del y, dl, db, dm
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_naive_vs_stable_peak_error(lib, dtype):
+    """Diagnostic beside the page's account of the stable form (paragraph on
+    stability near g = 1: a 3x lower peak error than the naive form).  At the
+    wide module, whose |g - 1| lies in U(0, 2^-8), the naive compose rounds g
+    to the storage dtype first, then evaluates (g~ - 1) base + g~ s lora in
+    fp32 and rounds once; the kernel keeps g - 1 = (m - n) / n.  Both are
+    measured against the oracle on 256 token rows (every column); the peak
+    absolute errors and their ratio are logged, with lora as drawn and with
+    lora = 0 (the base correction alone).  The kernel's peak error must be the
+    lower one."""
+    name = "wide_8192_r384"
+    cfg = synth.CONFIGS[name]
+    W0, A, B = synth.weights(cfg, dtype)
+    n_ref = O.weight_norm(W0, A, B, cfg.s)
+    x, _ = synth.activations(cfg, dtype)
+    rows = np.random.default_rng(cfg.index + 1).choice(cfg.T, 256, replace=False)
+    base, lora = synth.base_and_lora(x[torch.from_numpy(rows)], W0, A, B, device=DEV)
+    del x
+    n32 = n_ref.astype(np.float32)
+    m = synth.magnitude(n_ref, synth.magnitude_eps(cfg))
+    md, nd = torch.from_numpy(m).to(DEV), torch.from_numpy(n32).to(DEV)
+    s = cfg.s
+    g = m.astype(np.float64) / n32.astype(np.float64)
+    g_lo = synth.to_dtype(g.astype(np.float32), dtype).double().numpy()
+    rat = {}
+    for label, L in (("lora", lora), ("lora=0", torch.zeros_like(lora))):
+        Bf, Lf = f64(base), f64(L)
+        ref = O.compose_fwd(Bf, Lf, m, n32, s)
+        stable = f64(lib.dora_compose_fwd(base, L, md, nd, s))
+        naive32 = ((g_lo - 1.0) * Bf + g_lo * np.float64(np.float32(s)) * Lf).astype(np.float32)
+        naive = synth.to_dtype(naive32, dtype).double().numpy()
+        e_st, e_nv = np.max(np.abs(stable - ref)), np.max(np.abs(naive - ref))
+        rat[label] = e_nv / e_st
+        log(f"[naive-vs-stable] {name} {dtype} {label}: peak |error| naive {e_nv:.3e}, stable {e_st:.3e}, "
+            f"ratio {e_nv / e_st:.1f}x; columns collapsed under the naive form "
+            f"{np.mean((g_lo == 1.0) & (g != 1.0)):.1%}")
+        assert e_st < e_nv
+    assert min(rat.values()) > 1.0
+
+
 def test_determinism_and_streams(lib):
     """Bitwise identical norm and gradients across calls and across streams."""
     cfg = synth.CONFIGS["attn_proj"]
