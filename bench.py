@@ -431,7 +431,7 @@ def main():
                                                              d_mag=dm2, workspace=ws_lb), R)
         ubw_us = timed(lambda: (binding.dora_compose_bwd(dy, base, lora2, mag, norm, s, d_lora=dl2, d_base=db2,
                                                          d_mag=dm2, workspace=ws_bwd),
-                                torch.mm(dl2.t().contiguous(), h, out=dB2)), R)
+                                torch.mm(dl2.t(), h, out=dB2)), R)
         bb = 3 * 2 * T * out + 2 * (T * r + 2 * out * r) + 12 * out
         fused["bwd"] = {"fused_us": round(fbw_us, 2), "unfused_us": round(ubw_us, 2), "algorithmic_bytes": bb,
                         "flops": ff, "fused_gbs": round(bb / (fbw_us * 1e-6) / 1e9, 1),
