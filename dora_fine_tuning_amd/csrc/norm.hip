@@ -896,6 +896,235 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
 #undef DORA_STEP_SQUARES
 
 // ---------------------------------------------------------------------------
+// W stream with 128-byte row segments (rank tiles of 384).
+//
+// The 64-byte row segments of wstream_dma make every L1 -> L2 request 64
+// bytes, and the L1's table of pending requests then bounds the stream (it is
+// full most of the time at the measured L2 latency).  Here a stage is 64 K
+// columns: every DMA row segment is a whole 128-byte line.  The A panel (384
+// rank rows, L2 resident) and the W0 panel (128 rows, streamed from HBM) sit
+// in separate rings: two A slots, three W0 slots.  Stage u issues A(u + 1) and
+// then W0(u + 2); loads of a wave complete in order, so waiting for A(u + 1)
+// at stage u + 1 leaves W0(u + 2) in flight: W0 has two stages to arrive, A
+// one.  Every stage issues the same loads per wave (stages past the slice get
+// out-of-range offsets: zeros into a slot no stage reads again), so one vmcnt
+// value serves every wait.  Tile: 128 rows x 384 ranks, 8 waves (2 along the
+// rows x 4 along the ranks, 64 x 96 each), four MFMA K steps per stage with
+// the next step's fragments read during the current step's MFMAs.
+struct K64Tile {
+  static constexpr int TMW = 2, TN = 3, WM = 2, WN = 4, NW = 8, NT = 512;
+  static constexpr int BM = 32 * TMW * WM, BN = 32 * TN * WN;  // 128 x 384
+  static constexpr int BK = 64, KS = BK / 16, ROWB = BK * 2;   // 128-byte rows
+  static constexpr int RPI = 1024 / ROWB;                      // rows per 1 KiB DMA instruction
+  static constexpr int XI = BM / RPI, YI = BN / RPI, XQ = XI / NW, YQ = YI / NW, L = XQ + YQ;
+  static constexpr int A_BYTES = BN * ROWB, W_BYTES = BM * ROWB;  // one slot of each ring
+  static constexpr int NA = 2, NWS = 3;
+  static constexpr int A_OFF = 0, W_OFF = NA * A_BYTES;
+  static constexpr int AREA = 160 * 1024, LDS_BYTES = AREA;
+  static constexpr int NPAIR = TMW * KS, NP = (NPAIR + WN - 1) / WN;
+  static constexpr int RED_BYTES = 2 * WN * BM * 4, RED_OFF = AREA - RED_BYTES;
+  static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
+  static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
+  static_assert(XI % NW == 0 && YI % NW == 0, "whole DMA groups per wave");
+  static_assert(W_OFF + NWS * W_BYTES <= RED_OFF, "rings below the epilogue's row sums");
+  static_assert(L < 64, "vmcnt range");
+};
+
+template <int DT>
+__global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
+  using TL = K64Tile;
+  using V8 = typename Dt<DT>::V8;
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
+  float(*red)[TL::BM] = reinterpret_cast<float(*)[TL::BM]>(smem + TL::RED_OFF);
+
+  const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
+  if (v >= static_cast<uint32_t>(a.total)) return;
+  const uint32_t nTiles = static_cast<uint32_t>(a.nTiles), nRB = static_cast<uint32_t>(a.nRB);
+  const int nt = static_cast<int>(v % nTiles);
+  const uint32_t rb = (v / nTiles) % nRB;
+  const int sp = static_cast<int>(v / (nTiles * nRB));
+  const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
+  const int S1 = static_cast<int>(a.sm.S1), S12 = S1 + static_cast<int>(a.sm.S2);
+  const int st0 = static_cast<int>(a.S * sp / a.nSplit), st1 = static_cast<int>(a.S * (sp + 1) / a.nSplit);
+  const int in = static_cast<int>(a.sm.in), r = static_cast<int>(a.sm.r);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const bool want_base = (nt == 0) && !a.skip_base;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+
+  auto rsrc = [](const void* base, int64_t row0, int64_t rows, int64_t ld, int64_t max_rows) {
+    const int64_t nrows = std::min<int64_t>(std::max<int64_t>(rows - row0, 0), max_rows);
+    const char* p = static_cast<const char*>(base) + (nrows > 0 ? row0 * ld * 2 : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), static_cast<short>(0),
+                                             static_cast<int>(nrows * ld * 2), kBufferWord3);
+  };
+  const int64_t out = a.sm.out;
+  const __amdgpu_buffer_rsrc_t rxW = rsrc(a.sm.W0, m0, out, in, TL::BM);
+  const __amdgpu_buffer_rsrc_t ryA = rsrc(a.sm.A, n0, r, in, TL::BN);
+  const __amdgpu_buffer_rsrc_t rxB = rsrc(a.sm.B, m0, out, r, TL::BM);
+  const __amdgpu_buffer_rsrc_t ryH = rsrc(a.sm.Ghi, n0, r, r, TL::BN);
+  const __amdgpu_buffer_rsrc_t ryL = rsrc(a.sm.Glo, n0, r, r, TL::BN);
+
+  // DMA geometry: instruction q of wave w moves panel rows 8*(q*NW + w) ..
+  // + 7, 128 bytes each; lane l takes row l/8 of them and the logical chunk
+  // (l%8) ^ ((row/2)%8), which lands in LDS slot l%8 (so the fragment reads
+  // of 16 consecutive rows at one logical chunk hit 16 distinct bank groups).
+  // Group rows start on multiples of 64*q + 8*w: the chunk depends on the lane
+  // and the wave's parity only.  The A panel is fetched in the fragment row
+  // order sigma (rows 16..31 of a 32-row tile hold rank rows sigma(p)).
+  auto sigma = [](int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); };
+  const int prow = wave * TL::RPI + (lane >> 3);       // panel row of instruction 0
+  const int lc = (lane & 7) ^ ((prow >> 1) & 7);      // logical chunk fetched
+  const int kc = lc * 8;                               // its first K element
+  const int yr0 = (prow & ~31) + sigma(prow & 31);
+  const uint32_t ldA = static_cast<uint32_t>(in) * 2u, ldB = static_cast<uint32_t>(r) * 2u;
+  const uint32_t lxA = static_cast<uint32_t>(prow) * ldA + kc * 2u, lxB = static_cast<uint32_t>(prow) * ldB + kc * 2u;
+  const uint32_t lyA = static_cast<uint32_t>(yr0) * ldA + kc * 2u, lyB = static_cast<uint32_t>(yr0) * ldB + kc * 2u;
+
+  // Fragment reads: lane l reads row 32*i + l%32 of its wave's tiles at
+  // logical chunk 2*step + l/32, stored at chunk (2*step + l/32) ^ ((l%32)/2 % 8).
+  const int frow = lane & 31, fh = lane >> 5, fsw = (frow >> 1) & 7;
+  const uint32_t xrow = lds0 + static_cast<uint32_t>(TL::W_OFF + (wm * TL::TMW * 32 + frow) * TL::ROWB);
+  const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::A_OFF + (wn * TL::TN * 32 + frow) * TL::ROWB);
+  uint32_t co[TL::KS];
+#pragma unroll
+  for (int k = 0; k < TL::KS; ++k) co[k] = static_cast<uint32_t>(((2 * k + fh) ^ fsw) * 16);
+
+  f32x16 acc[TL::TMW][TL::TN];
+#pragma unroll
+  for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
+  float bs[TL::NP];
+#pragma unroll
+  for (int t = 0; t < TL::NP; ++t) bs[t] = 0.0f;
+
+  // the segment of stage st: resources, row pitch, per-lane offsets, K offset
+  // and whether this lane's chunk lies past the segment (or the stage past st1)
+#define K64_SEL(ST)                                                                      \
+  const int dst_ = (ST);                                                                 \
+  const bool dw_ = dst_ < S1, dh_ = dst_ < S12;                                          \
+  const __amdgpu_buffer_rsrc_t drx_ = dw_ ? rxW : rxB;                                   \
+  const __amdgpu_buffer_rsrc_t dry_ = dw_ ? ryA : (dh_ ? ryH : ryL);                     \
+  const uint32_t dld_ = dw_ ? ldA : ldB, dlx_ = dw_ ? lxA : lxB, dly_ = dw_ ? lyA : lyB; \
+  const int dkst_ = dst_ - (dw_ ? 0 : (dh_ ? S1 : S12));                                 \
+  const int dkrem_ = (dw_ ? in : r) - dkst_ * TL::BK;                                    \
+  const uint32_t dkb_ = static_cast<uint32_t>(dkst_) * static_cast<uint32_t>(TL::ROWB);  \
+  const bool doob_ = dst_ >= st1 || (dkrem_ < TL::BK && kc >= dkrem_);
+  // DMA of the A (rank-side) panel of stage ST into A slot SA
+#define K64_ISSUE_A(ST, SA)                                                              \
+  {                                                                                      \
+    K64_SEL(ST)                                                                          \
+    _Pragma("unroll") for (int q = 0; q < TL::YQ; ++q) {                                 \
+      const uint32_t o_ = dly_ + static_cast<uint32_t>(q * TL::NW * TL::RPI) * dld_ + dkb_; \
+      dma16(dry_, smem + TL::A_OFF + (SA) * TL::A_BYTES + (q * TL::NW + wave) * 1024, doob_ ? kOob : o_); \
+    }                                                                                    \
+  }
+  // DMA of the W0 (row-side) panel of stage ST into W slot SW
+#define K64_ISSUE_W(ST, SWS)                                                             \
+  {                                                                                      \
+    K64_SEL(ST)                                                                          \
+    _Pragma("unroll") for (int q = 0; q < TL::XQ; ++q) {                                 \
+      const uint32_t o_ = dlx_ + static_cast<uint32_t>(q * TL::NW * TL::RPI) * dld_ + dkb_; \
+      dma16(drx_, smem + TL::W_OFF + (SWS) * TL::W_BYTES + (q * TL::NW + wave) * 1024, doob_ ? kOob : o_); \
+    }                                                                                    \
+  }
+  // fragments of K step K of the stage in A slot SA / W slot SWS
+#define K64_READS(X, Y, SA, SWS, K)                                                      \
+  {                                                                                      \
+    const uint32_t xb_ = xrow + (SWS) * TL::W_BYTES + co[K];                             \
+    const uint32_t yb_ = yrow + (SA) * TL::A_BYTES + co[K];                              \
+    X[0] = lds_read16_at<0>(xb_);                                                        \
+    X[1] = lds_read16_at<32 * TL::ROWB>(xb_);                                            \
+    Y[0] = lds_read16_at<0>(yb_);                                                        \
+    Y[1] = lds_read16_at<32 * TL::ROWB>(yb_);                                            \
+    Y[2] = lds_read16_at<64 * TL::ROWB>(yb_);                                            \
+  }
+#define K64_MFMAS(X, Y)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) \
+      acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, Y[j]), __builtin_bit_cast(V8, X[i]), acc[i][j]);
+#define K64_SQUARES(X, C)                                                                \
+  _Pragma("unroll") for (int t = 0; t < TL::NP; ++t)                                     \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i)                                  \
+      if (wn + TL::WN * t == TL::KS * i + (C)) {                                         \
+        bs[t] = sq2<DT>(X[i][0], bs[t]);                                                 \
+        bs[t] = sq2<DT>(X[i][1], bs[t]);                                                 \
+        bs[t] = sq2<DT>(X[i][2], bs[t]);                                                 \
+        bs[t] = sq2<DT>(X[i][3], bs[t]);                                                 \
+      }
+  // One stage: U is the stage's index within a loop turn of 6 (A slot U % 2,
+  // W slot U % 3).
+#define K64_STAGE(U)                                                                     \
+  {                                                                                      \
+    constexpr int sa = (U) % TL::NA, sws = (U) % TL::NWS;                                \
+    const int st = sb + (U);                                                             \
+    if (st >= st1) break;                                                                \
+    wait_vmcnt<TL::XQ>();                                                                \
+    __builtin_amdgcn_s_barrier();                                                        \
+    const bool base_here = want_base && st < S1;                                         \
+    u32x4 xa[TL::TMW], ya[TL::TN], xn[TL::TMW], yn[TL::TN];                              \
+    K64_READS(xa, ya, sa, sws, 0)                                                        \
+    K64_ISSUE_A(st + 1, ((U) + 1) % TL::NA)                                              \
+    K64_ISSUE_W(st + 2, ((U) + 2) % TL::NWS)                                             \
+    lds_wait();                                                                          \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(xa[i]);                      \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(ya[j]);                       \
+    K64_READS(xn, yn, sa, sws, 1)                                                        \
+    K64_MFMAS(xa, ya)                                                                    \
+    if (base_here) { K64_SQUARES(xa, 0) }                                                \
+    lds_wait();                                                                          \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(xn[i]);                      \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(yn[j]);                       \
+    K64_READS(xa, ya, sa, sws, 2)                                                        \
+    K64_MFMAS(xn, yn)                                                                    \
+    if (base_here) { K64_SQUARES(xn, 1) }                                                \
+    lds_wait();                                                                          \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(xa[i]);                      \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(ya[j]);                       \
+    K64_READS(xn, yn, sa, sws, 3)                                                        \
+    K64_MFMAS(xa, ya)                                                                    \
+    if (base_here) { K64_SQUARES(xa, 2) }                                                \
+    lds_wait();                                                                          \
+    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(xn[i]);                      \
+    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(yn[j]);                       \
+    K64_MFMAS(xn, yn)                                                                    \
+    if (base_here) { K64_SQUARES(xn, 3) }                                                \
+  }
+
+  if (st0 < st1) {
+    // prologue: A(st0), W0(st0), W0(st0 + 1), in that order
+    K64_ISSUE_A(st0, 0)
+    K64_ISSUE_W(st0, 0)
+    K64_ISSUE_W(st0 + 1, 1)
+    for (int sb = st0; sb < st1; sb += 6) {
+      K64_STAGE(0)
+      K64_STAGE(1)
+      K64_STAGE(2)
+      K64_STAGE(3)
+      K64_STAGE(4)
+      K64_STAGE(5)
+    }
+  }
+  // stages past the slice were issued as out-of-range loads: drain them
+  // before the stage area is reused
+  wait_vmcnt<0>();
+#undef K64_STAGE
+#undef K64_SQUARES
+#undef K64_MFMAS
+#undef K64_READS
+#undef K64_ISSUE_W
+#undef K64_ISSUE_A
+#undef K64_SEL
+
+  if (a.acc_part) {  // norm backward: keep U + B G'
+    dma_store_acc<TL>(a, sp, m0, n0, acc);
+    return;
+  }
+  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0, rxB);
+}
+
+// ---------------------------------------------------------------------------
 // W stream, general path (row lengths not multiples of 8, or unaligned
 // pointers): register-staged loads with element-wise bounds, LDS rows padded
 // by 8 elements, double buffered.
@@ -1133,6 +1362,7 @@ int dma_tn(int64_t r) {
 template <int TN> struct DmaShape;
 template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6, WM = 2, BK = 32; };
 template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4, WM = 2, BK = 32; };
+// rank tiles of 384 take wstream_k64 (K64Tile); this shape is not launched
 template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 5, WM = 2, BK = 32; };
 template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3, WM = 2, BK = 32; };
 
@@ -1143,7 +1373,7 @@ int dma_rows(int tn) {
   switch (tn) {
     case 1: return DmaTileOf<1>::BM;
     case 2: return DmaTileOf<2>::BM;
-    case 3: return DmaTileOf<3>::BM;
+    case 3: return K64Tile::BM;
     default: return DmaTileOf<4>::BM;
   }
 }
@@ -1152,7 +1382,7 @@ int dma_bk(int tn) {
   switch (tn) {
     case 1: return DmaTileOf<1>::BK;
     case 2: return DmaTileOf<2>::BK;
-    case 3: return DmaTileOf<3>::BK;
+    case 3: return K64Tile::BK;
     default: return DmaTileOf<4>::BK;
   }
 }
@@ -1161,7 +1391,11 @@ template <int DT, int TN>
 void launch_dma(const WArgs& w, hipStream_t stream) {
   using S = DmaShape<TN>;
   const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
-  hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTileOf<TN>::NT), 0, stream, w);
+  if constexpr (TN == 3) {  // rank tiles of 384: the 128-byte-segment stream
+    hipLaunchKernelGGL((wstream_k64<DT>), grid, dim3(K64Tile::NT), 0, stream, w);
+  } else {
+    hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTileOf<TN>::NT), 0, stream, w);
+  }
 }
 
 // Workgroups of gram_finalize: four 8-row strips per upper 32 x 32 tile.
