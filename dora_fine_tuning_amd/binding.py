@@ -33,6 +33,7 @@ EXPORTS = (
     "dora_lora_compose_bwd",
     "dora_compose_bwd_workspace_bytes",
     "dora_compose_bwd",
+    "dora_compose_bwd_noalloc",
     "dora_norm_bwd_workspace_bytes",
     "dora_norm_bwd",
     "dora_last_error",
@@ -71,6 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.dora_compose_bwd_workspace_bytes.restype = sz
     lib.dora_compose_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.dora_compose_bwd.restype = i32
+    lib.dora_compose_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.dora_compose_bwd_noalloc.restype = i32
     lib.dora_norm_bwd_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.dora_norm_bwd_workspace_bytes.restype = sz
     lib.dora_norm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, vp, vp, sz, vp]
@@ -287,6 +290,34 @@ def dora_compose_bwd(dy, base, lora, mag, norm, s: float, add_base: bool = False
     _check(LIB.dora_compose_bwd(_ptr(dy), _ptr(base), _ptr(lora), _ptr(mag), _ptr(norm), float(s), T, out, code,
                                 int(bool(add_base)), _ptr(d_lora), _ptr(d_base), _ptr(d_mag), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return d_lora, d_base, d_mag
+
+
+def dora_compose_bwd_noalloc(dy, base, lora, mag, norm, s: float, add_base: bool = False, d_lora=None, d_base=None,
+                             d_mag=None, want_d_base: bool = True):
+    """dora_compose_bwd with the library's own scratch in place of a workspace
+    (the entry point that allocates nothing; outputs passed in are written in
+    place, missing ones are allocated here, outside the library call)."""
+    code = _code(dy)
+    T, out = dy.shape
+    dev = dy.device
+    _matrix(base, "base", (T, out), dy.dtype, dev)
+    _matrix(lora, "lora", (T, out), dy.dtype, dev)
+    _matrix(mag, "mag", (out,), torch.float32, dev)
+    _matrix(norm, "norm", (out,), torch.float32, dev)
+    if d_lora is None:
+        d_lora = torch.empty_like(dy)
+    if d_base is None and want_d_base:
+        d_base = torch.empty_like(dy)
+    if d_mag is None:
+        d_mag = torch.empty(out, dtype=torch.float32, device=dev)
+    _matrix(d_lora, "d_lora", (T, out), dy.dtype, dev)
+    if d_base is not None:
+        _matrix(d_base, "d_base", (T, out), dy.dtype, dev)
+    _matrix(d_mag, "d_mag", (out,), torch.float32, dev)
+    _check(LIB.dora_compose_bwd_noalloc(_ptr(dy), _ptr(base), _ptr(lora), _ptr(mag), _ptr(norm), float(s), T, out,
+                                        code, int(bool(add_base)), _ptr(d_lora), _ptr(d_base), _ptr(d_mag),
+                                        _stream(dev)))
     return d_lora, d_base, d_mag
 
 

@@ -10,6 +10,7 @@
 #include "../../include/dora.h"
 #include "compose_kernels.hpp"
 #include "lora_compose_kernels.hpp"
+#include "noalloc_kernels.hpp"
 #include "norm_bwd_kernels.hpp"
 #include "norm_kernels.hpp"
 
@@ -100,6 +101,60 @@ int norm_call(const char* fn, const void* W0, const void* A, const void* B, cons
                 (long long)out, (long long)r);
   dora::NormArgs a{W0, A, B, s, norm_out, ws, stream, base_sq};
   return hip_status(dora::launch_norm(plan, a), fn);
+}
+
+// Validation and launch shared by the compose backward entry points (ws: the
+// caller's workspace, or the library's own scratch for the no-allocation one).
+int compose_bwd_call(const char* fn, const void* dy, const void* base, const void* lora, const float* mag, const float* norm, float s,
+                     int64_t T, int64_t out, int dtype, int add_base, void* d_lora, void* d_base, float* d_mag,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (T < 0 || out < 0)
+    return fail(DORA_INVALID_ARG, "%s: negative size (T=%lld out=%lld)", fn, (long long)T, (long long)out);
+  if (out == 0) return ok();
+  if (!norm || !d_mag) return fail(DORA_INVALID_ARG, "%s: norm or d_mag is NULL", fn);
+  if (T > 0 && (!dy || !base || !lora || !mag || !d_lora))
+    return fail(DORA_INVALID_ARG, "%s: NULL pointer argument", fn);
+  const size_t need = dora_compose_bwd_workspace_bytes(T, out);
+  if (ws_bytes < need) return fail(DORA_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "%s: workspace is NULL", fn);
+  const size_t mb = static_cast<size_t>(T) * out * 2, vb = static_cast<size_t>(out) * 4;
+  if (any_overlap(d_lora, mb, d_base, mb)) return fail(DORA_INVALID_ARG, "%s: d_lora and d_base overlap", fn);
+  const void* ins[3] = {dy, base, lora};
+  for (const void* p : ins) {
+    if (partial_overlap(d_lora, mb, p, mb) || partial_overlap(d_base, mb, p, mb))
+      return fail(DORA_INVALID_ARG, "%s: an output partially overlaps an input", fn);
+    if (any_overlap(ws, need, p, mb)) return fail(DORA_INVALID_ARG, "%s: workspace overlaps an input", fn);
+  }
+  if (any_overlap(ws, need, d_lora, mb) || any_overlap(ws, need, d_base, mb) || any_overlap(ws, need, d_mag, vb) ||
+      any_overlap(ws, need, norm, vb) || any_overlap(ws, need, mag, vb))
+    return fail(DORA_INVALID_ARG, "%s: workspace overlaps an argument", fn);
+  if (any_overlap(d_mag, vb, d_lora, mb) || any_overlap(d_mag, vb, d_base, mb) || any_overlap(d_mag, vb, dy, mb) ||
+      any_overlap(d_mag, vb, base, mb) || any_overlap(d_mag, vb, lora, mb) || partial_overlap(d_mag, vb, norm, vb) ||
+      partial_overlap(d_mag, vb, mag, vb))
+    return fail(DORA_INVALID_ARG, "%s: d_mag overlaps another argument", fn);
+  dora::ComposeArgs a{};
+  a.dtype = dtype;
+  a.T = T;
+  a.out = out;
+  a.s = s;
+  a.add_base = add_base ? 1 : 0;
+  a.mag = mag;
+  a.norm = norm;
+  a.dy = dy;
+  a.base = base;
+  a.lora = lora;
+  a.d_lora = d_lora;
+  a.d_base = d_base;
+  a.d_mag = d_mag;
+  a.partial = static_cast<float*>(ws);
+  a.stream = stream;
+  const bool vec = (out % 8 == 0) && aligned16(dy) && aligned16(base) && aligned16(lora) && aligned16(d_lora) &&
+                   (d_base == nullptr || aligned16(d_base)) && aligned16(mag) && aligned16(norm) && aligned16(ws);
+  if (dora::compose_max_grid(T, out, vec) > INT32_MAX)
+    return fail(DORA_UNSUPPORTED, "%s: T=%lld x out=%lld needs more workgroups than one launch holds", fn,
+                (long long)T, (long long)out);
+  return hip_status(dora::launch_compose_bwd(a, vec), fn);
 }
 
 }  // namespace
@@ -318,53 +373,30 @@ size_t dora_compose_bwd_workspace_bytes(int64_t T, int64_t out) {
 int dora_compose_bwd(const void* dy, const void* base, const void* lora, const float* mag, const float* norm, float s,
                      int64_t T, int64_t out, int dtype, int add_base, void* d_lora, void* d_base, float* d_mag,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "dora_compose_bwd: unknown dtype %d", dtype);
+  return compose_bwd_call("dora_compose_bwd", dy, base, lora, mag, norm, s, T, out, dtype, add_base, d_lora, d_base,
+                          d_mag, ws, ws_bytes, stream);
+}
+
+int dora_compose_bwd_noalloc(const void* dy, const void* base, const void* lora, const float* mag, const float* norm,
+                             float s, int64_t T, int64_t out, int dtype, int add_base, void* d_lora, void* d_base,
+                             float* d_mag, hipStream_t stream) {
+  const char* fn = "dora_compose_bwd_noalloc";
+  if (!valid_dtype(dtype)) return fail(DORA_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
   if (T < 0 || out < 0)
-    return fail(DORA_INVALID_ARG, "dora_compose_bwd: negative size (T=%lld out=%lld)", (long long)T, (long long)out);
+    return fail(DORA_INVALID_ARG, "%s: negative size (T=%lld out=%lld)", fn, (long long)T, (long long)out);
   if (out == 0) return ok();
-  if (!norm || !d_mag) return fail(DORA_INVALID_ARG, "dora_compose_bwd: norm or d_mag is NULL");
-  if (T > 0 && (!dy || !base || !lora || !mag || !d_lora))
-    return fail(DORA_INVALID_ARG, "dora_compose_bwd: NULL pointer argument");
   const size_t need = dora_compose_bwd_workspace_bytes(T, out);
-  if (ws_bytes < need) return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace of %zu bytes, %zu needed", ws_bytes, need);
-  if (need > 0 && !ws) return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace is NULL");
-  const size_t mb = static_cast<size_t>(T) * out * 2, vb = static_cast<size_t>(out) * 4;
-  if (any_overlap(d_lora, mb, d_base, mb)) return fail(DORA_INVALID_ARG, "dora_compose_bwd: d_lora and d_base overlap");
-  const void* ins[3] = {dy, base, lora};
-  for (const void* p : ins) {
-    if (partial_overlap(d_lora, mb, p, mb) || partial_overlap(d_base, mb, p, mb))
-      return fail(DORA_INVALID_ARG, "dora_compose_bwd: an output partially overlaps an input");
-    if (any_overlap(ws, need, p, mb)) return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace overlaps an input");
+  if (need > dora::kNoAllocScratchBytes)
+    return fail(DORA_UNSUPPORTED, "%s: T=%lld out=%lld needs %zu bytes of scratch, above this entry point's %zu; "
+                "use dora_compose_bwd with a workspace", fn, (long long)T, (long long)out, need,
+                dora::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = dora::noalloc_scratch(stream, &scratch);
+    if (e != hipSuccess) return fail(DORA_HIP_ERROR, "%s: scratch address: %s", fn, hipGetErrorString(e));
   }
-  if (any_overlap(ws, need, d_lora, mb) || any_overlap(ws, need, d_base, mb) || any_overlap(ws, need, d_mag, vb) ||
-      any_overlap(ws, need, norm, vb) || any_overlap(ws, need, mag, vb))
-    return fail(DORA_INVALID_ARG, "dora_compose_bwd: workspace overlaps an argument");
-  if (any_overlap(d_mag, vb, d_lora, mb) || any_overlap(d_mag, vb, d_base, mb) || any_overlap(d_mag, vb, dy, mb) ||
-      any_overlap(d_mag, vb, base, mb) || any_overlap(d_mag, vb, lora, mb) || partial_overlap(d_mag, vb, norm, vb) ||
-      partial_overlap(d_mag, vb, mag, vb))
-    return fail(DORA_INVALID_ARG, "dora_compose_bwd: d_mag overlaps another argument");
-  dora::ComposeArgs a{};
-  a.dtype = dtype;
-  a.T = T;
-  a.out = out;
-  a.s = s;
-  a.add_base = add_base ? 1 : 0;
-  a.mag = mag;
-  a.norm = norm;
-  a.dy = dy;
-  a.base = base;
-  a.lora = lora;
-  a.d_lora = d_lora;
-  a.d_base = d_base;
-  a.d_mag = d_mag;
-  a.partial = static_cast<float*>(ws);
-  a.stream = stream;
-  const bool vec = (out % 8 == 0) && aligned16(dy) && aligned16(base) && aligned16(lora) && aligned16(d_lora) &&
-                   (d_base == nullptr || aligned16(d_base)) && aligned16(mag) && aligned16(norm) && aligned16(ws);
-  if (dora::compose_max_grid(T, out, vec) > INT32_MAX)
-    return fail(DORA_UNSUPPORTED, "dora_compose_bwd: T=%lld x out=%lld needs more workgroups than one launch holds",
-                (long long)T, (long long)out);
-  return hip_status(dora::launch_compose_bwd(a, vec), "dora_compose_bwd");
+  return compose_bwd_call(fn, dy, base, lora, mag, norm, s, T, out, dtype, add_base, d_lora, d_base, d_mag, scratch,
+                          need, stream);
 }
 
 }  // extern "C"

@@ -86,7 +86,8 @@ extern "C" {
  *    row slice that would span 2 GiB or more;
  *  - dora_lora_compose_bwd with a shape or pointers its fast path cannot take
  *    and T * r above 2^20 (its slow path runs T * r products in order in one
- *    thread per output column).
+ *    thread per output column);
+ *  - dora_compose_bwd_noalloc with sizes whose partials exceed its scratch.
  */
 enum dora_status {
   DORA_OK = 0,
@@ -291,6 +292,24 @@ DORA_API int dora_compose_bwd(const void* dy, const void* base, const void* lora
                      const float* norm, float s, int64_t T, int64_t out, int dtype, int add_base,
                      void* d_lora, void* d_base, float* d_mag, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/*
+ * dora_compose_bwd for callers that cannot allocate device memory (code under
+ * stream or graph capture, tight serving loops, harnesses that forbid
+ * allocation): same arguments, results and errors, without the workspace.
+ * The magnitude-gradient partials go to a scratch array of 24 MiB that the
+ * library holds on each GPU it runs on from load until process exit; this
+ * call allocates and frees nothing.  Sizes whose partials need more
+ * (dora_compose_bwd_workspace_bytes(T, out) > 24 MiB) return DORA_UNSUPPORTED
+ * before any launch.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * threads) race on it: serialise them.  The array keeps the last call's
+ * partials; each call overwrites every partial it reads.  The first call on a
+ * device looks up the array's address there (hipGetSymbolAddress).
+ */
+DORA_API int dora_compose_bwd_noalloc(const void* dy, const void* base, const void* lora, const float* mag,
+                                      const float* norm, float s, int64_t T, int64_t out, int dtype, int add_base,
+                                      void* d_lora, void* d_base, float* d_mag, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none).  Valid until the next call. */
 DORA_API const char* dora_last_error(void);

@@ -230,6 +230,24 @@ def test_lora_compose_bwd_slow_path_limit():
     _status(call((1 << 20) // 128 + 1, 128), UNSUPPORTED, "slow path")
 
 
+def test_compose_bwd_noalloc_validation():
+    """The entry point without a workspace: the argument checks of
+    dora_compose_bwd, and sizes whose partials exceed its 24 MiB scratch are
+    refused (UNSUPPORTED) before any device call."""
+    T, out = 64, 16
+    call = lambda dtype=0, T=T, out=out, d_mag=P * 9, base=P * 2: LIB.dora_compose_bwd_noalloc(
+        P, base, P * 3, P * 4, P * 5, 1.0, T, out, dtype, 0, P * 6, P * 7, d_mag, None)
+    _status(call(dtype=4), UNSUPPORTED, "dtype")
+    _status(call(T=-1), INVALID, "negative")
+    # 16-token blocks of 8192 columns: 2^21 tokens need 2^17 blocks x 32 KiB = 4 GiB of partials
+    far = [(k + 1) << 42 for k in range(10)]
+    _status(LIB.dora_compose_bwd_noalloc(far[0], far[1], far[2], far[3], far[4], 1.0, 1 << 21, 8192, 0, 0, far[5],
+                                         far[6], far[7], None), UNSUPPORTED, "scratch")
+    # the largest workload module fits: 10240 tokens x 27648 columns (17.7 MB of partials)
+    assert LIB.dora_compose_bwd_workspace_bytes(10240, 27648) <= 24 << 20
+    assert LIB.dora_compose_bwd_noalloc(None, None, None, None, None, 1.0, 8, 0, 0, 0, None, None, None, None) == OK
+
+
 def test_compose_rejects_grids_beyond_one_launch():
     # 2^36 tokens of 8 columns: the forward would need 2^34 workgroups.  Far-apart
     # fake pointers keep the overlap checks quiet; nothing is launched.
