@@ -253,7 +253,35 @@ struct WArgs {
   float* cross_part;  // [nSplit][nTiles][out]
   int skip_base;      // the base term comes from a cache: no squares, no base partials
   float* acc_part = nullptr;  // [nSplit][out][r]: store the accumulators U + B G' instead of reducing them
+  // Norm finalize in the epilogue: the last workgroup of each row block (a
+  // counter per row block, zeroed by the Gram kernel of the same call) sums
+  // the partials and writes the norm.  Null: a separate norm_finalize launch.
+  unsigned* fin_count = nullptr;
+  float* norm_out = nullptr;
+  const float* base_sq = nullptr;
+  float s = 0.0f;
 };
+
+// sum_{q < n} p[q * stride] in fp64, in order, each load at device scope (it
+// reads through this XCD's L2 to the device-coherent level, so it sees the
+// partials that workgroups on other XCDs wrote through with device-scope
+// stores); loads go out in groups of 8 before the group is added.
+__device__ inline double ordered_sum_device(const float* p, int n, int64_t stride) {
+  double acc = 0.0;
+  int q = 0;
+  for (; q + 8 <= n; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __hip_atomic_load(p + static_cast<int64_t>(q + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += static_cast<double>(v[u]);
+  }
+  for (; q < n; ++q)
+    acc += static_cast<double>(
+        __hip_atomic_load(p + static_cast<int64_t>(q) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return acc;
+}
 
 // Epilogue shared by both W-stream kernels.  The MFMAs take the rank-side
 // fragment as their first operand, so acc[i][j] is the transposed 32x32 tile:
@@ -528,17 +556,48 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     }
   }
   __syncthreads();
+  const bool fused = a.fin_count != nullptr;
   if (tid < TL::BM && m0 + tid < out) {
     float c = 0.0f;
 #pragma unroll
     for (int w = 0; w < TL::WN; ++w) c += red[w][tid];
-    a.cross_part[(static_cast<int64_t>(sp) * a.nTiles + nt) * out + m0 + tid] = c;
+    float* cp = a.cross_part + (static_cast<int64_t>(sp) * a.nTiles + nt) * out + m0 + tid;
+    if (fused)  // written through to the device-coherent level
+      __hip_atomic_store(cp, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *cp = c;
     if (want_base) {
       float b = 0.0f;
 #pragma unroll
       for (int w = 0; w < TL::WN; ++w) b += red[TL::WN + w][tid];
-      a.base_part[static_cast<int64_t>(sp) * out + m0 + tid] = b;
+      float* bp = a.base_part + static_cast<int64_t>(sp) * out + m0 + tid;
+      if (fused)
+        __hip_atomic_store(bp, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *bp = b;
     }
+  }
+  if (!fused) return;
+  // The last of the row block's nSplit * nTiles workgroups computes its norms
+  // (the sums of norm_finalize, in the same order).  Every thread's partial
+  // stores are complete before the workgroup's counter increment; the loads of
+  // the last workgroup follow its increment.
+  wait_vmcnt<0>();
+  __syncthreads();
+  int* flag = reinterpret_cast<int*>(&red[0][0]);
+  if (tid == 0) {
+    const unsigned total = static_cast<unsigned>(a.nSplit) * static_cast<unsigned>(a.nTiles);
+    const unsigned old = __hip_atomic_fetch_add(a.fin_count + m0 / TL::BM, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == total - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag && tid < TL::BM && m0 + tid < out) {
+    const int64_t i = m0 + tid;
+    const double b = a.base_sq ? static_cast<double>(a.base_sq[i]) : ordered_sum_device(a.base_part + i, a.nSplit, out);
+    const double c = ordered_sum_device(a.cross_part + i, a.nSplit * a.nTiles, out);
+    const double n2 = b + 2.0 * static_cast<double>(a.s) * c;
+    a.norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
   }
 }
 
@@ -556,7 +615,7 @@ constexpr int kGramL = 4;                 // DMA instructions per wave per stage
 template <int DT, int kGramNS, bool DIRECT>
 __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int in, int r, int nB, int splitG,
                                                 float* gpart, float scale, typename Dt<DT>::T* ghi,
-                                                typename Dt<DT>::T* glo) {
+                                                typename Dt<DT>::T* glo, unsigned* fin_count, int n_count) {
   using V8 = typename Dt<DT>::V8;
   static_assert(kGramNS >= 3 && kGramNS <= 8 && (kGramNS - 2) * kGramL < 64, "ring slots");
   __shared__ __attribute__((aligned(1024))) char smem[kGramNS * kGramStage];
@@ -564,6 +623,9 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
   // XCD-aware: consecutive logical indices share a K split, so each XCD's L2
   // holds one K slice of A
   const int v = static_cast<int>(xcd_logical_index());
+  // the W stream's per-row-block counters of this call start at zero
+  if (v == 0 && fin_count)
+    for (int i = threadIdx.x; i < n_count; i += 256) fin_count[i] = 0u;
   if (v >= nUpper * splitG) return;
   int u = v % nUpper;
   const int sp = v / nUpper;
@@ -1406,7 +1468,8 @@ int64_t gram_finalize_blocks(int64_t r) {
 
 // G' = scale * A A^T as the pair G'hi + G'lo in the plan's workspace regions.
 template <int DT>
-hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* ws, bool vec, hipStream_t stream) {
+hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* ws, bool vec, hipStream_t stream,
+                         unsigned* fin_count = nullptr) {
   using T = typename Dt<DT>::T;
   if (p.r <= 0) return hipSuccess;
   T* ghi = reinterpret_cast<T*>(ws + p.off_ghi);
@@ -1418,7 +1481,8 @@ hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* w
   if (p.gram_direct) {  // one K split: the Gram kernel writes G'hi/G'lo itself
     if (vec)
       hipLaunchKernelGGL((gram_dma<DT, 4, true>), ggrid, dim3(256), 0, stream, A, static_cast<int>(p.in),
-                         static_cast<int>(p.r), p.nTg, 1, nullptr, scale, ghi, glo);
+                         static_cast<int>(p.r), p.nTg, 1, nullptr, scale, ghi, glo, fin_count,
+                         static_cast<int>(p.nRB));
     else
       hipLaunchKernelGGL((gram_partial<DT, true>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, 1, nullptr,
                          scale, ghi, glo);
@@ -1426,7 +1490,8 @@ hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* w
   }
   if (vec)
     hipLaunchKernelGGL((gram_dma<DT, 4, false>), ggrid, dim3(256), 0, stream, A, static_cast<int>(p.in),
-                       static_cast<int>(p.r), p.nTg, p.splitG, gpart, scale, nullptr, nullptr);
+                       static_cast<int>(p.r), p.nTg, p.splitG, gpart, scale, nullptr, nullptr, fin_count,
+                       static_cast<int>(p.nRB));
   else
     hipLaunchKernelGGL((gram_partial<DT, false>), ggrid, dim3(256), 0, stream, A, p.in, p.r, p.nTg, p.splitG, gpart,
                        scale, nullptr, nullptr);
@@ -1443,8 +1508,12 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   using T = typename Dt<DT>::T;
   T* ghi = reinterpret_cast<T*>(ws + p.off_ghi);
   T* glo = reinterpret_cast<T*>(ws + p.off_glo);
+  // 16-byte path with an adapter: the W stream's epilogue finalizes the norm
+  // (per-row-block counters in the workspace, zeroed by the Gram kernel)
+  const bool fuse = vec && p.r > 0 && p.in > 0;
+  unsigned* fin_count = fuse ? reinterpret_cast<unsigned*>(ws + p.off_count) : nullptr;
   {
-    const hipError_t e = launch_gram_t<DT>(p, a.A, a.s * 0.5f, ws, vec, a.stream);
+    const hipError_t e = launch_gram_t<DT>(p, a.A, a.s * 0.5f, ws, vec, a.stream, fin_count);
     if (e != hipSuccess) return e;
   }
   WArgs w;
@@ -1457,6 +1526,10 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
   w.base_part = reinterpret_cast<float*>(ws + p.off_base);
   w.cross_part = reinterpret_cast<float*>(ws + p.off_cross);
   w.skip_base = a.base_sq != nullptr;
+  w.fin_count = fin_count;
+  w.norm_out = a.norm_out;
+  w.base_sq = a.base_sq;
+  w.s = a.s;
   if (vec) {
     switch (p.tn) {
       case 1: launch_dma<DT, 1>(w, a.stream); break;
@@ -1469,7 +1542,7 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
     hipLaunchKernelGGL((wstream_general<DT>), grid, dim3(TileW::NT), 0, a.stream, w);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fuse) return e;
   hipLaunchKernelGGL(norm_finalize, dim3(static_cast<unsigned>(cdiv(p.out, 256))), dim3(256), 0, a.stream,
                      w.base_part, w.cross_part, a.base_sq, p.nSplit, p.nTiles, p.out, a.s, a.norm_out);
   return hipGetLastError();
@@ -1619,7 +1692,9 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
     p.off_base = off;
     off += align16(static_cast<size_t>(p.nSplit) * out * 4);
     p.off_cross = off;
-    off += align16(static_cast<size_t>(p.nSplit) * p.nTiles * out * 4);
+    off += static_cast<size_t>(p.nSplit) * p.nTiles * out * 4;
+    p.off_count = off;  // the fused finalize's counter per row block, right after the cross partials
+    off = align16(off + static_cast<size_t>(p.nRB) * 4);
     p.bytes = off;
   };
   layout();

@@ -27,7 +27,7 @@ struct NormPlan {
   // directly (chosen when the partials would not fit the scratch bound)
   bool gram_direct = false;
   // workspace byte offsets
-  size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, bytes = 0;
+  size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, off_count = 0, bytes = 0;
 };
 
 NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec);

@@ -100,6 +100,28 @@ def test_norm_exact_cancellation(lib):
     np.testing.assert_allclose(n_gpu[::3], np.sqrt(in_ * 2.0**-6), rtol=1e-6)
 
 
+@pytest.mark.parametrize("shape", [(8192, 8192, 384), (4096, 4096, 64), (1000, 520, 136), (300, 264, 296)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_norm_reused_workspace_alternating_inputs(lib, shape):
+    """One workspace, two different adapters, called in turn many times: every
+    call's norms equal that adapter's first result bit for bit.  The norm's
+    last step reads the partials other workgroups wrote earlier in the same
+    call; reading a previous call's partials instead would show here."""
+    out, in_, r = shape
+    cfgs = [synth.custom("reuse_a", out, in_, r, 1, index=610), synth.custom("reuse_b", out, in_, r, 1, index=611)]
+    inputs = [tuple(t.to(DEV) for t in synth.weights(c)) for c in cfgs]
+    ws = torch.empty(lib.dora_norm_workspace_bytes(out, in_, r), dtype=torch.uint8, device=DEV)
+    first = [lib.dora_norm_factored(*inp, c.s, workspace=ws).clone() for inp, c in zip(inputs, cfgs)]
+    assert not torch.equal(first[0], first[1])
+    for k in range(24):
+        j = k % 2
+        n = lib.dora_norm_factored(*inputs[j], cfgs[j].s, workspace=ws)
+        assert torch.equal(n, first[j]), f"call {k}"
+    ref = O.weight_norm(*synth.weights(cfgs[1]), cfgs[1].s)
+    W, Af, Bf = (f64(t) for t in inputs[1])
+    PU.assert_norm(f64(first[1]), ref, PU.norm_term_mass(W, Af, Bf, cfgs[1].s), f"reuse {shape}")
+
+
 def test_norm_b_zero_is_plain_row_norm(lib):
     cfg = synth.custom("bzero", 300, 1024, 32, 1)
     W0, A, B = synth.weights(cfg)
