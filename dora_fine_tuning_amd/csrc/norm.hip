@@ -473,6 +473,9 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int h = lane >> 5, frow = lane & 31;
   const int64_t out = a.sm.out, r = a.sm.r;
+  // waves past the NW tile waves (DMA-only waves) hold no accumulators: they
+  // take part in the barriers only
+  const bool worker = wave < TL::NW;
   const int cols_here = static_cast<int>(std::min<int64_t>(std::max<int64_t>(r - n0, 0), TL::BN));
   // byte offsets within a row of the lane's chunks (tile j, chunk k of two)
   uint32_t cofs[TL::TN][2];
@@ -492,7 +495,7 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   for (int pass = 0; pass < NPASS; ++pass) {
     const int row_base = pass * RPP;
     __syncthreads();  // stage buffers (or the previous pass) no longer read
-    if (cols_here > 0) {
+    if (worker && cols_here > 0) {
       for (int q = wave; q < INSTR; q += TL::NW) {
         const int sl = q * 64 + lane;
         const int rl = sl / CPR, p = sl % CPR;
@@ -505,7 +508,7 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
     }
     wait_vmcnt<0>();
     __syncthreads();
-    if (cols_here > 0) {
+    if (worker && cols_here > 0) {
 #pragma unroll
       for (int i = 0; i < TL::TMW; ++i) {
         const int r32 = wm * TL::TMW * 32 + i * 32;  // first tile row within the workgroup tile
@@ -540,7 +543,7 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   for (int i = 0; i < TL::TMW; ++i) {
     float v = rs[i][0] + rs[i][1];
     v += __shfl_xor(v, 32, 64);
-    if (h == 0) red[wn][wm * TL::TMW * 32 + i * 32 + frow] = v;
+    if (worker && h == 0) red[wn][wm * TL::TMW * 32 + i * 32 + frow] = v;
   }
   if (want_base) {
     // wave wn holds the squares of pairs p = wn + WN*t (tile p/KS); at most one
@@ -552,7 +555,7 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
       for (int t = 0; t < TL::NP; ++t)
         if ((wn + TL::WN * t) / TL::KS == i) b = bs[t];
       b += __shfl_xor(b, 32, 64);
-      if (h == 0) red[TL::WN + wn][wm * TL::TMW * 32 + i * 32 + frow] = b;
+      if (worker && h == 0) red[TL::WN + wn][wm * TL::TMW * 32 + i * 32 + frow] = b;
     }
   }
   __syncthreads();
@@ -965,20 +968,27 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
 // full most of the time at the measured L2 latency).  Here a stage is 64 K
 // columns: every DMA row segment is a whole 128-byte line.  The A panel (384
 // rank rows, L2 resident) and the W0 panel (128 rows, streamed from HBM) sit
-// in separate rings: two A slots, three W0 slots.  Stage u issues A(u + 1) and
-// then W0(u + 2); loads of a wave complete in order, so waiting for A(u + 1)
-// at stage u + 1 leaves W0(u + 2) in flight: W0 has two stages to arrive, A
-// one.  Every stage issues the same loads per wave (stages past the slice get
-// out-of-range offsets: zeros into a slot no stage reads again), so one vmcnt
-// value serves every wait.  Tile: 128 rows x 384 ranks, 8 waves (2 along the
-// rows x 4 along the ranks, 64 x 96 each), four MFMA K steps per stage with
-// the next step's fragments read during the current step's MFMAs.
+// in separate rings: two A slots, three W0 slots.
+//
+// The loads of a stage (64 KiB per workgroup) take the texture path about a
+// thousand cycles to accept, and a wave that issues them cannot issue MFMAs
+// meanwhile.  So the roles are split: 8 tile waves only read LDS and run
+// MFMAs, 4 DMA waves (one per SIMD) only issue loads.  After the barrier
+// that opens stage u, the DMA waves issue A(u + 1) and then W0(u + 2) into
+// the slots stage u - 1 used, and wait for A(u + 1) (their loads complete in
+// order, so W0(u + 2) stays in flight: W0 has two stages to arrive, A one)
+// before the barrier of stage u + 1.  Every stage issues the same loads per
+// DMA wave (stages past the slice get out-of-range offsets: zeros into a slot
+// no stage reads again), so one vmcnt value serves every wait.  Tile: 128
+// rows x 384 ranks, tile waves 2 along the rows x 4 along the ranks (64 x 96
+// each), four MFMA K steps per stage with the next step's fragments read
+// during the current step's MFMAs.
 struct K64Tile {
-  static constexpr int TMW = 2, TN = 3, WM = 2, WN = 4, NW = 8, NT = 512;
+  static constexpr int TMW = 2, TN = 3, WM = 2, WN = 4, NW = 8, NDMA = 4, NT = 64 * (NW + NDMA);
   static constexpr int BM = 32 * TMW * WM, BN = 32 * TN * WN;  // 128 x 384
   static constexpr int BK = 64, KS = BK / 16, ROWB = BK * 2;   // 128-byte rows
   static constexpr int RPI = 1024 / ROWB;                      // rows per 1 KiB DMA instruction
-  static constexpr int XI = BM / RPI, YI = BN / RPI, XQ = XI / NW, YQ = YI / NW, L = XQ + YQ;
+  static constexpr int XI = BM / RPI, YI = BN / RPI, XQ = XI / NDMA, YQ = YI / NDMA, L = 2 * XQ + YQ;
   static constexpr int A_BYTES = BN * ROWB, W_BYTES = BM * ROWB;  // one slot of each ring
   static constexpr int NA = 2, NWS = 3;
   static constexpr int A_OFF = 0, W_OFF = NA * A_BYTES;
@@ -987,7 +997,7 @@ struct K64Tile {
   static constexpr int RED_BYTES = 2 * WN * BM * 4, RED_OFF = AREA - RED_BYTES;
   static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
   static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
-  static_assert(XI % NW == 0 && YI % NW == 0, "whole DMA groups per wave");
+  static_assert(XI % NDMA == 0 && YI % NDMA == 0, "whole DMA groups per DMA wave");
   static_assert(W_OFF + NWS * W_BYTES <= RED_OFF, "rings below the epilogue's row sums");
   static_assert(L < 64, "vmcnt range");
 };
@@ -1011,6 +1021,8 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
   const int in = static_cast<int>(a.sm.in), r = static_cast<int>(a.sm.r);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool dma_wave = wave >= TL::NW;
+  const int dw = dma_wave ? wave - TL::NW : 0;  // index among the DMA waves
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const bool want_base = (nt == 0) && !a.skip_base;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
@@ -1028,15 +1040,16 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
   const __amdgpu_buffer_rsrc_t ryH = rsrc(a.sm.Ghi, n0, r, r, TL::BN);
   const __amdgpu_buffer_rsrc_t ryL = rsrc(a.sm.Glo, n0, r, r, TL::BN);
 
-  // DMA geometry: instruction q of wave w moves panel rows 8*(q*NW + w) ..
-  // + 7, 128 bytes each; lane l takes row l/8 of them and the logical chunk
-  // (l%8) ^ ((row/2)%8), which lands in LDS slot l%8 (so the fragment reads
-  // of 16 consecutive rows at one logical chunk hit 16 distinct bank groups).
-  // Group rows start on multiples of 64*q + 8*w: the chunk depends on the lane
-  // and the wave's parity only.  The A panel is fetched in the fragment row
-  // order sigma (rows 16..31 of a 32-row tile hold rank rows sigma(p)).
+  // DMA geometry: instruction q of DMA wave d moves panel rows
+  // 8*(q*NDMA + d) .. + 7, 128 bytes each; lane l takes row l/8 of them and the
+  // logical chunk (l%8) ^ ((row/2)%8), which lands in LDS slot l%8 (so the
+  // fragment reads of 16 consecutive rows at one logical chunk hit 16 distinct
+  // bank groups).  Group rows start on multiples of 32*q + 8*d: the chunk
+  // depends on the lane and the wave's parity only.  The A panel is fetched in
+  // the fragment row order sigma (rows 16..31 of a 32-row tile hold rank rows
+  // sigma(p)); 32*q keeps a row's place within its 32-row tile.
   auto sigma = [](int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); };
-  const int prow = wave * TL::RPI + (lane >> 3);       // panel row of instruction 0
+  const int prow = dw * TL::RPI + (lane >> 3);         // panel row of instruction 0
   const int lc = (lane & 7) ^ ((prow >> 1) & 7);      // logical chunk fetched
   const int kc = lc * 8;                               // its first K element
   const int yr0 = (prow & ~31) + sigma(prow & 31);
@@ -1079,8 +1092,8 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
   {                                                                                      \
     K64_SEL(ST)                                                                          \
     _Pragma("unroll") for (int q = 0; q < TL::YQ; ++q) {                                 \
-      const uint32_t o_ = dly_ + static_cast<uint32_t>(q * TL::NW * TL::RPI) * dld_ + dkb_; \
-      dma16(dry_, smem + TL::A_OFF + (SA) * TL::A_BYTES + (q * TL::NW + wave) * 1024, doob_ ? kOob : o_); \
+      const uint32_t o_ = dly_ + static_cast<uint32_t>(q * TL::NDMA * TL::RPI) * dld_ + dkb_; \
+      dma16(dry_, smem + TL::A_OFF + (SA) * TL::A_BYTES + (q * TL::NDMA + dw) * 1024, doob_ ? kOob : o_); \
     }                                                                                    \
   }
   // DMA of the W0 (row-side) panel of stage ST into W slot SW
@@ -1088,8 +1101,8 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
   {                                                                                      \
     K64_SEL(ST)                                                                          \
     _Pragma("unroll") for (int q = 0; q < TL::XQ; ++q) {                                 \
-      const uint32_t o_ = dlx_ + static_cast<uint32_t>(q * TL::NW * TL::RPI) * dld_ + dkb_; \
-      dma16(drx_, smem + TL::W_OFF + (SWS) * TL::W_BYTES + (q * TL::NW + wave) * 1024, doob_ ? kOob : o_); \
+      const uint32_t o_ = dlx_ + static_cast<uint32_t>(q * TL::NDMA * TL::RPI) * dld_ + dkb_; \
+      dma16(drx_, smem + TL::W_OFF + (SWS) * TL::W_BYTES + (q * TL::NDMA + dw) * 1024, doob_ ? kOob : o_); \
     }                                                                                    \
   }
   // fragments of K step K of the stage in A slot SA / W slot SWS
@@ -1115,20 +1128,27 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
         bs[t] = sq2<DT>(X[i][2], bs[t]);                                                 \
         bs[t] = sq2<DT>(X[i][3], bs[t]);                                                 \
       }
-  // One stage: U is the stage's index within a loop turn of 6 (A slot U % 2,
-  // W slot U % 3).
+  // One stage of a DMA wave: U is the stage's index within a loop turn of 6
+  // (A slot U % 2, W slot U % 3).
+#define K64_DMA_STAGE(U)                                                                 \
+  {                                                                                      \
+    const int st = sb + (U);                                                             \
+    if (st >= st1) break;                                                                \
+    __builtin_amdgcn_s_barrier();                                                        \
+    K64_ISSUE_A(st + 1, ((U) + 1) % TL::NA)                                              \
+    K64_ISSUE_W(st + 2, ((U) + 2) % TL::NWS)                                             \
+    wait_vmcnt<TL::XQ>();                                                                \
+  }
+  // One stage of a tile wave
 #define K64_STAGE(U)                                                                     \
   {                                                                                      \
     constexpr int sa = (U) % TL::NA, sws = (U) % TL::NWS;                                \
     const int st = sb + (U);                                                             \
     if (st >= st1) break;                                                                \
-    wait_vmcnt<TL::XQ>();                                                                \
     __builtin_amdgcn_s_barrier();                                                        \
     const bool base_here = want_base && st < S1;                                         \
     u32x4 xa[TL::TMW], ya[TL::TN], xn[TL::TMW], yn[TL::TN];                              \
     K64_READS(xa, ya, sa, sws, 0)                                                        \
-    K64_ISSUE_A(st + 1, ((U) + 1) % TL::NA)                                              \
-    K64_ISSUE_W(st + 2, ((U) + 2) % TL::NWS)                                             \
     lds_wait();                                                                          \
     _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(xa[i]);                      \
     _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(ya[j]);                       \
@@ -1154,23 +1174,38 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
     if (base_here) { K64_SQUARES(xn, 3) }                                                \
   }
 
+  // Both roles pass one barrier per stage of the slice.
   if (st0 < st1) {
-    // prologue: A(st0), W0(st0), W0(st0 + 1), in that order
-    K64_ISSUE_A(st0, 0)
-    K64_ISSUE_W(st0, 0)
-    K64_ISSUE_W(st0 + 1, 1)
-    for (int sb = st0; sb < st1; sb += 6) {
-      K64_STAGE(0)
-      K64_STAGE(1)
-      K64_STAGE(2)
-      K64_STAGE(3)
-      K64_STAGE(4)
-      K64_STAGE(5)
+    if (dma_wave) {
+      // prologue: A(st0), W0(st0), W0(st0 + 1), in that order; stage st0's
+      // panels have landed before its barrier
+      K64_ISSUE_A(st0, 0)
+      K64_ISSUE_W(st0, 0)
+      K64_ISSUE_W(st0 + 1, 1)
+      wait_vmcnt<TL::XQ>();
+      for (int sb = st0; sb < st1; sb += 6) {
+        K64_DMA_STAGE(0)
+        K64_DMA_STAGE(1)
+        K64_DMA_STAGE(2)
+        K64_DMA_STAGE(3)
+        K64_DMA_STAGE(4)
+        K64_DMA_STAGE(5)
+      }
+    } else {
+      for (int sb = st0; sb < st1; sb += 6) {
+        K64_STAGE(0)
+        K64_STAGE(1)
+        K64_STAGE(2)
+        K64_STAGE(3)
+        K64_STAGE(4)
+        K64_STAGE(5)
+      }
     }
   }
   // stages past the slice were issued as out-of-range loads: drain them
-  // before the stage area is reused
+  // before the stage area is reused (the epilogue's first barrier)
   wait_vmcnt<0>();
+#undef K64_DMA_STAGE
 #undef K64_STAGE
 #undef K64_SQUARES
 #undef K64_MFMAS
@@ -1179,8 +1214,8 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
 #undef K64_ISSUE_A
 #undef K64_SEL
 
-  if (a.acc_part) {  // norm backward: keep U + B G'
-    dma_store_acc<TL>(a, sp, m0, n0, acc);
+  if (a.acc_part) {  // norm backward: keep U + B G' (DMA waves hold no accumulators)
+    if (!dma_wave) dma_store_acc<TL>(a, sp, m0, n0, acc);
     return;
   }
   dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0, rxB);
