@@ -19,6 +19,8 @@
 //                     fragment).  The base rows matching the dy rows come in
 //                     as a third panel of the same stage, so the stage's dy
 //                     and base give d_base and the column sums of dy * base.
+//                     Eight tile waves run the fragment reads, the MFMAs and
+//                     the elementwise part; four DMA waves issue the loads.
 //                     The epilogue forms sum_k B E over its rank block and
 //                     writes its E slice and its column partials.  The same
 //                     kernel without the base panel is the plain contraction
@@ -67,22 +69,29 @@ __device__ inline void tie2(u32x2& v) { asm volatile("" : "+v"(v)); }
 // 2 chunks per row, and the 8 (row, chunk) pairs then fall in 8 distinct bank
 // groups.
 // BASE adds the third panel, the base rows of the X panel's tokens and
-// columns, laid out like the X panel; the plain contraction has none.  Every
-// vector-memory load of the stage loop is then a DMA of the ring, which keeps
-// the stage waits exact.
+// columns, laid out like the X panel; the plain contraction has none.
+// Roles: NW = 8 tile waves read fragments, run MFMAs and (with BASE) do the
+// stage's elementwise part; NDMA = 4 DMA waves (one per SIMD) only issue the
+// ring's loads, so the tile waves never stall on the texture path that takes
+// a stage's loads.  Every vector-memory instruction of a DMA wave's stage
+// loop is a DMA of the ring, which keeps the stage waits exact.
 template <int TN_, int NS_, bool BASE_>
 struct BwdTile {
   static constexpr int TN = TN_, NS = NS_;
   static constexpr bool BASE = BASE_;
-  static constexpr int WM = 2, WN = 4, NW = 8, NT = 512, TM = 4, TMW = 2;
+  static constexpr int WM = 2, WN = 4, NW = 8, NDMA = 4, NT = 64 * (NW + NDMA), TM = 4, TMW = 2;
   static constexpr int BM = 128, BN = 128 * TN, BK = 32;
   static constexpr int XROWB = BM * 2, YROWB = BN * 2;  // bytes per token row
   static constexpr int X_BYTES = BK * XROWB, Y_BYTES = BK * YROWB, B_BYTES = BASE ? X_BYTES : 0;
   static constexpr int B_OFF = X_BYTES + Y_BYTES, STAGE_BYTES = X_BYTES + Y_BYTES + B_BYTES;
   static constexpr int XI = X_BYTES / 1024, YI = Y_BYTES / 1024;  // 1 KiB DMA blocks per stage
-  static constexpr int XQ = XI / NW, YQ = YI / NW, L = XQ + YQ + (BASE ? XQ : 0);
+  static constexpr int XQ = XI / NDMA, YQ = YI / NDMA, L = XQ + YQ + (BASE ? XQ : 0);  // per DMA wave
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
-  static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
+  // the widest tile with the elementwise part reads one K step's fragments at
+  // a time: both steps' would not fit the registers of three waves per SIMD
+  static constexpr bool ONE_STEP = BASE && TN == 3;
+  static_assert(XI % NDMA == 0 && YI % NDMA == 0, "panels split into whole DMA groups per DMA wave");
+  static_assert(NW * 64 == BK * 16, "one 16-byte chunk of a stage's dy and base rows per tile-wave thread");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(NS >= 3 && (NS - 2) * L < 64, "ring depth and vmcnt range");
   static_assert(2 * (TMW + TN) < 16, "one K step's fragment reads within the lgkmcnt range");
@@ -145,253 +154,308 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   const int S = S1 + static_cast<int>(bcdiv(te2 - ts2, TL::BK));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool dma_wave = wave >= TL::NW;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const bool want_base = TL::BASE && nt == 0;  // the elementwise part is done by the first rank block
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+  // epilogue: [32][128] column sums, then [WN][128] rank-block sums
+  float* red = reinterpret_cast<float*>(smem);
 
-  // buffer resources over the token slice; rows past it read zero
-  const int64_t rows = te - ts;
-  const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(a.dy) + ts * out * 2), static_cast<short>(0),
-      static_cast<int>(rows * out * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rbase = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(a.base) + ts * out * 2), static_cast<short>(0),
-      static_cast<int>(rows * out * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(a.h) + ts * r * 2), static_cast<short>(0),
-      static_cast<int>(rows * r * 2), kBufferWord3);
-  const int64_t rows2 = te2 - ts2;
-  const __amdgpu_buffer_rsrc_t rdy2 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.dy2) + ts2 * out * 2 : nullptr), static_cast<short>(0),
-      static_cast<int>(rows2 * out * 2), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rh2 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.h2) + ts2 * r * 2 : nullptr), static_cast<short>(0),
-      static_cast<int>(rows2 * r * 2), kBufferWord3);
+  if (dma_wave) {
+    // ---- DMA waves: the ring's loads, and (with the base panel) the
+    // elementwise part of each stage
+    const int dw = wave - TL::NW;
+    // buffer resources over the token slice; rows past it read zero
+    const int64_t rows = te - ts;
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(a.dy) + ts * out * 2), static_cast<short>(0),
+        static_cast<int>(rows * out * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rbase = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(TL::BASE ? static_cast<const char*>(a.base) + ts * out * 2 : nullptr), static_cast<short>(0),
+        static_cast<int>(TL::BASE ? rows * out * 2 : 0), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(a.h) + ts * r * 2), static_cast<short>(0),
+        static_cast<int>(rows * r * 2), kBufferWord3);
+    const int64_t rows2 = te2 - ts2;
+    const __amdgpu_buffer_rsrc_t rdy2 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.dy2) + ts2 * out * 2 : nullptr),
+        static_cast<short>(0), static_cast<int>(rows2 * out * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rh2 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.h2) + ts2 * r * 2 : nullptr), static_cast<short>(0),
+        static_cast<int>(rows2 * r * 2), kBufferWord3);
 
-  // Per-lane DMA offsets (stage 0).  Wave instruction q moves 1 KiB block
-  // b = q*NW + wave of its panel, lane l writing bytes 16l .. 16l + 15.  X: a
-  // block is 4 dy rows of 256 bytes, so lane l fills slot l%16 of row 4b + l/16
-  // and fetches the logical chunk that slot holds (bwd_slot is its own inverse
-  // within a 16-chunk group).  Y: linear 16-byte slot b*64 + l of the 32 x BN
-  // panel, row (b*64 + l) / (BN/8).
-  uint32_t xo[TL::XQ], yo[TL::YQ];
-  bool xok[TL::XQ], yok[TL::YQ];
+    // Per-lane DMA offsets (stage 0).  Instruction q of DMA wave d moves 1 KiB
+    // block b = q*NDMA + d of its panel, lane l writing bytes 16l .. 16l + 15.
+    // X: a block is 4 dy rows of 256 bytes, so lane l fills slot l%16 of row
+    // 4b + l/16 and fetches the logical chunk that slot holds (bwd_slot is its
+    // own inverse within a 16-chunk group).  Y: linear 16-byte slot b*64 + l of
+    // the 32 x BN panel, row (b*64 + l) / (BN/8).
+    uint32_t xo[TL::XQ], yo[TL::YQ];
+    bool xok[TL::XQ], yok[TL::YQ];
 #pragma unroll
-  for (int q = 0; q < TL::XQ; ++q) {
-    const int b = q * TL::NW + wave;
-    const int t = 4 * b + (lane >> 4), sl = lane & 15;
-    const int c = bwd_slot(sl, t);  // the slot map is its own inverse within a group
-    const int64_t col = j0 + 8 * c;
-    xok[q] = col < out;
-    xo[q] = static_cast<uint32_t>((t * out + col) * 2);
-  }
+    for (int q = 0; q < TL::XQ; ++q) {
+      const int b = q * TL::NDMA + dw;
+      const int t = 4 * b + (lane >> 4), sl = lane & 15;
+      const int c = bwd_slot(sl, t);
+      const int64_t col = j0 + 8 * c;
+      xok[q] = col < out;
+      xo[q] = static_cast<uint32_t>((t * out + col) * 2);
+    }
 #pragma unroll
-  for (int q = 0; q < TL::YQ; ++q) {
-    const int b = q * TL::NW + wave;
-    const int lin = b * 64 + lane;
-    const int t = lin / (TL::BN / 8), sl = lin % (TL::BN / 8);
-    const int c = bwd_slot(sl, t);
-    const int64_t col = k0 + 8 * c;
-    yok[q] = col < r;
-    yo[q] = static_cast<uint32_t>((t * r + col) * 2);
-  }
-  const uint32_t xstep = static_cast<uint32_t>(TL::BK * out * 2), ystep = static_cast<uint32_t>(TL::BK * r * 2);
-  // stages [0, S1) read the slice's rows of dy and h, stages [S1, S) those of
-  // dy2 and h2 (same row pitches, so the same per-lane offsets); a segment's
-  // last stage reads zeros past its rows
-  auto issue = [&](int st, int slot) {
-    char* so = smem + slot * TL::STAGE_BYTES;
-    const bool seg2 = st >= S1;
-    const __amdgpu_buffer_rsrc_t rx = seg2 ? rdy2 : rdy, ry = seg2 ? rh2 : rh;
-    const uint32_t ss = static_cast<uint32_t>(seg2 ? st - S1 : st);
-#pragma unroll
-    for (int q = 0; q < TL::XQ; ++q)
-      dma16(rx, so + (q * TL::NW + wave) * 1024, xok[q] ? xo[q] + ss * xstep : kOob);
-#pragma unroll
-    for (int q = 0; q < TL::YQ; ++q)
-      dma16(ry, so + TL::X_BYTES + (q * TL::NW + wave) * 1024, yok[q] ? yo[q] + ss * ystep : kOob);
-    if constexpr (TL::BASE) {  // never with a second segment
+    for (int q = 0; q < TL::YQ; ++q) {
+      const int b = q * TL::NDMA + dw;
+      const int lin = b * 64 + lane;
+      const int t = lin / (TL::BN / 8), sl = lin % (TL::BN / 8);
+      const int c = bwd_slot(sl, t);
+      const int64_t col = k0 + 8 * c;
+      yok[q] = col < r;
+      yo[q] = static_cast<uint32_t>((t * r + col) * 2);
+    }
+    const uint32_t xstep = static_cast<uint32_t>(TL::BK * out * 2), ystep = static_cast<uint32_t>(TL::BK * r * 2);
+    // stages [0, S1) read the slice's rows of dy and h, stages [S1, S) those of
+    // dy2 and h2 (same row pitches, so the same per-lane offsets); a segment's
+    // last stage reads zeros past its rows
+    auto issue = [&](int st, int slot) {
+      char* so = smem + slot * TL::STAGE_BYTES;
+      const bool seg2 = st >= S1;
+      const __amdgpu_buffer_rsrc_t rx = seg2 ? rdy2 : rdy, ry = seg2 ? rh2 : rh;
+      const uint32_t ss = static_cast<uint32_t>(seg2 ? st - S1 : st);
 #pragma unroll
       for (int q = 0; q < TL::XQ; ++q)
-        dma16(rbase, so + TL::B_OFF + (q * TL::NW + wave) * 1024, want_base && xok[q] ? xo[q] + ss * xstep : kOob);
-    }
-  };
-
-  // Fragment read addresses (within a stage slot; add the slot's offset).  In a
-  // 16-lane group g = l/16 (i = l%16), a read covers tokens R0 .. R0 + 3 with
-  // R0 = 16*step + 8*(g/2) (+ 4 for the second read of a fragment).  Y side
-  // (MFMA operand A, rank columns): result lane i must get rank column
-  // 32*kt + sigma(16*(g%2) + i), sigma(p) = 16*((p/4)%2) + 4*(p/8) + p%4, so that
-  // accumulator register q of lane l holds rank column 16*(l/32) + q; source
-  // lane L therefore addresses column 32*kt + 16*((L%4)%2) + 8*(g%2) + 4*((L%4)/2).
-  // X side (operand B, output columns): lane i gets column 32*jt + 16*(g%2) + i,
-  // so source lane L addresses column 32*jt + 16*(g%2) + 4*(L%4).
-  const int g = lane >> 4, L = lane & 15;
-  const int rsrc_row = 8 * (g >> 1) + (L >> 2);  // token row within a K step, first read
-  auto tr_addr = [&](uint32_t panel, int rowb, int row, int col) {
-    const int c = col >> 3;
-    return panel + static_cast<uint32_t>(row * rowb + bwd_slot(c, row) * 16 + (col & 7) * 2);
-  };
-  // per (step, read) the row differs; the column part is per tile
-  int ycol[TL::TN], xcol[TL::TMW];
+        dma16(rx, so + (q * TL::NDMA + dw) * 1024, xok[q] ? xo[q] + ss * xstep : kOob);
 #pragma unroll
-  for (int j = 0; j < TL::TN; ++j)
-    ycol[j] = 32 * (wn * TL::TN + j) + 16 * ((L & 3) & 1) + 8 * (g & 1) + 4 * ((L & 3) >> 1);
+      for (int q = 0; q < TL::YQ; ++q)
+        dma16(ry, so + TL::X_BYTES + (q * TL::NDMA + dw) * 1024, yok[q] ? yo[q] + ss * ystep : kOob);
+      if constexpr (TL::BASE) {  // never with a second segment
 #pragma unroll
-  for (int i = 0; i < TL::TMW; ++i) xcol[i] = 32 * (wm * TL::TMW + i) + 16 * (g & 1) + 4 * (L & 3);
-
-  f32x16 acc[TL::TMW][TL::TN];
-#pragma unroll
-  for (int i = 0; i < TL::TMW; ++i)
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
-
-  // Elementwise part: thread tid takes token row tid/16 of each stage and the
-  // 8 output columns of chunk tid%16.
-  const int et = tid >> 4, ec = tid & 15;
-  const int64_t ecol = j0 + 8 * ec;
-  const bool eok = want_base && ecol < out;
-  float gb[8], colsum[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    colsum[e] = 0.0f;
-    gb[e] = 0.0f;
-    if (eok) {
-      const float m = a.mag[ecol + e], n = a.norm[ecol + e];
-      gb[e] = a.add_base ? m / n : (m - n) / n;
-    }
-  }
-  T16* dbase = static_cast<T16*>(a.d_base);
-
-  for (int u = 0; u < TL::NS - 1; ++u)
-    if (u < S) issue(u, u);
-
-  int slot = 0;
-  for (int st = 0; st < S; ++st) {
-    bwd_wait<TL>(S - 1 - st);
-    __builtin_amdgcn_s_barrier();
-    if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, slot == 0 ? TL::NS - 1 : slot - 1);
-    const uint32_t xp = lds0 + static_cast<uint32_t>(slot * TL::STAGE_BYTES);
-    const uint32_t yp = xp + TL::X_BYTES;
-    // both K steps' fragment reads in flight, then each step's MFMAs after its
-    // reads have landed (the halves of a fragment are joined after the wait)
-    u32x2 xl[2][TL::TMW], xh[2][TL::TMW], yl[2][TL::TN], yh[2][TL::TN];
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const int row = 16 * step + rsrc_row;
-#pragma unroll
-      for (int i = 0; i < TL::TMW; ++i) {
-        xl[step][i] = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
-        xh[step][i] = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
+        for (int q = 0; q < TL::XQ; ++q)
+          dma16(rbase, so + TL::B_OFF + (q * TL::NDMA + dw) * 1024,
+                want_base && xok[q] ? xo[q] + ss * xstep : kOob);
       }
+    };
+
+    for (int u = 0; u < TL::NS - 1; ++u)
+      if (u < S) issue(u, u);
+    int slot = 0;
+    for (int st = 0; st < S; ++st) {
+      bwd_wait<TL>(S - 1 - st);
+      __builtin_amdgcn_s_barrier();
+      if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, slot == 0 ? TL::NS - 1 : slot - 1);
+      slot = slot == TL::NS - 1 ? 0 : slot + 1;
+    }
+    // Epilogue.  The ring is free once every wave is past its last read.
+    __syncthreads();
+  } else {
+    // ---- tile waves: fragment reads and MFMAs
+    // Fragment read addresses (within a stage slot; add the slot's offset).  In a
+    // 16-lane group g = l/16 (i = l%16), a read covers tokens R0 .. R0 + 3 with
+    // R0 = 16*step + 8*(g/2) (+ 4 for the second read of a fragment).  Y side
+    // (MFMA operand A, rank columns): result lane i must get rank column
+    // 32*kt + sigma(16*(g%2) + i), sigma(p) = 16*((p/4)%2) + 4*(p/8) + p%4, so that
+    // accumulator register q of lane l holds rank column 16*(l/32) + q; source
+    // lane L therefore addresses column 32*kt + 16*((L%4)%2) + 8*(g%2) + 4*((L%4)/2).
+    // X side (operand B, output columns): lane i gets column 32*jt + 16*(g%2) + i,
+    // so source lane L addresses column 32*jt + 16*(g%2) + 4*(L%4).
+    const int g = lane >> 4, L = lane & 15;
+    const int rsrc_row = 8 * (g >> 1) + (L >> 2);  // token row within a K step, first read
+    auto tr_addr = [&](uint32_t panel, int rowb, int row, int col) {
+      const int c = col >> 3;
+      return panel + static_cast<uint32_t>(row * rowb + bwd_slot(c, row) * 16 + (col & 7) * 2);
+    };
+    // per (step, read) the row differs; the column part is per tile
+    int ycol[TL::TN], xcol[TL::TMW];
 #pragma unroll
-      for (int j = 0; j < TL::TN; ++j) {
-        yl[step][j] = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
-        yh[step][j] = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
+    for (int j = 0; j < TL::TN; ++j)
+      ycol[j] = 32 * (wn * TL::TN + j) + 16 * ((L & 3) & 1) + 8 * (g & 1) + 4 * ((L & 3) >> 1);
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) xcol[i] = 32 * (wm * TL::TMW + i) + 16 * (g & 1) + 4 * (L & 3);
+
+    f32x16 acc[TL::TMW][TL::TN];
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
+
+    // Elementwise part: tile-wave thread tid takes token row tid/16 of each
+    // stage and the 8 output columns of chunk tid%16.
+    const int et = tid >> 4, ec = tid & 15;
+    const int64_t ecol = j0 + 8 * ec;
+    const bool eok = want_base && ecol < out;
+    float gb[8], colsum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      colsum[e] = 0.0f;
+      gb[e] = 0.0f;
+      if (eok) {
+        const float m = a.mag[ecol + e], n = a.norm[ecol + e];
+        gb[e] = a.add_base ? m / n : (m - n) / n;
       }
     }
+    T16* dbase = static_cast<T16*>(a.d_base);
+
+    int slot = 0;
+    for (int st = 0; st < S; ++st) {
+      __builtin_amdgcn_s_barrier();  // the DMA waves' loads of stage st have landed
+      const uint32_t xp = lds0 + static_cast<uint32_t>(slot * TL::STAGE_BYTES);
+      const uint32_t yp = xp + TL::X_BYTES;
+      if constexpr (!TL::ONE_STEP) {
+        // both K steps' fragment reads in flight, then each step's MFMAs after its
+        // reads have landed (the halves of a fragment are joined after the wait)
+        u32x2 xl[2][TL::TMW], xh[2][TL::TMW], yl[2][TL::TN], yh[2][TL::TN];
 #pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      if (step == 0)
-        lds_wait_keep<2 * (TL::TMW + TL::TN)>();
-      else
-        lds_wait();
-      u32x4 fx[TL::TMW], fy[TL::TN];
+        for (int step = 0; step < 2; ++step) {
+          const int row = 16 * step + rsrc_row;
 #pragma unroll
-      for (int i = 0; i < TL::TMW; ++i) {
-        tie2(xl[step][i]);
-        tie2(xh[step][i]);
-        fx[i] = u32x4{xl[step][i][0], xl[step][i][1], xh[step][i][0], xh[step][i][1]};
-      }
+          for (int i = 0; i < TL::TMW; ++i) {
+            xl[step][i] = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
+            xh[step][i] = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
+          }
 #pragma unroll
-      for (int j = 0; j < TL::TN; ++j) {
-        tie2(yl[step][j]);
-        tie2(yh[step][j]);
-        fy[j] = u32x4{yl[step][j][0], yl[step][j][1], yh[step][j][0], yh[step][j][1]};
-      }
-#pragma unroll
-      for (int i = 0; i < TL::TMW; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::TN; ++j)
-          acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
-    }
-    if (TL::BASE && eok) {
-      const int64_t t = ts + static_cast<int64_t>(st) * TL::BK + et;
-      if (t < te) {
-        // this thread's chunk of dy and of base, at the same place in their panels
-        const uint32_t ce = xp + static_cast<uint32_t>(et * TL::XROWB + bwd_slot(ec, et) * 16);
-        u32x4 wd = lds_read16(ce);
-        u32x4 wb = lds_read16(ce + TL::B_OFF);
-        lds_wait();
-        tie(wd);
-        tie(wb);
-        float dyv[8], bv[8], o[8];
-        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wd), dyv);
-        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wb), bv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          o[e] = gb[e] * dyv[e];
-          colsum[e] = __builtin_fmaf(dyv[e], bv[e], colsum[e]);
+          for (int j = 0; j < TL::TN; ++j) {
+            yl[step][j] = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
+            yh[step][j] = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
+          }
         }
-        if (dbase) *reinterpret_cast<u32x4*>(dbase + t * out + ecol) = __builtin_bit_cast(u32x4, f32_to_chunk<DT>(o));
-      }
-    }
-    slot = slot == TL::NS - 1 ? 0 : slot + 1;
-  }
-
-  // Epilogue.  The ring is free once every wave is past its last read.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);  // [32][128] column sums, then [WN][128] rank-block sums
-  // (1) s * sum_k B_jk E_jk over this rank block, per output column: lane l holds
-  // output column 32*(wm*TMW + i) + l%32 and rank columns 32*(wn*TN + j) + 16*(l/32) + q
-  const T16* Bp = static_cast<const T16*>(a.B);
-  const int frow = lane & 31, fh = lane >> 5;
-  float* ep = a.e_part + static_cast<int64_t>(sp) * out * r;
 #pragma unroll
-  for (int i = 0; i < TL::TMW; ++i) {
-    const int jl = 32 * (wm * TL::TMW + i) + frow;
-    const int64_t j = j0 + jl;
-    float bsum = 0.0f;
+        for (int step = 0; step < 2; ++step) {
+          if (step == 0)
+            lds_wait_keep<2 * (TL::TMW + TL::TN)>();
+          else
+            lds_wait();
+          u32x4 fx[TL::TMW], fy[TL::TN];
 #pragma unroll
-    for (int jj = 0; jj < TL::TN; ++jj) {
-      const int64_t k = k0 + 32 * (wn * TL::TN + jj) + 16 * fh;
-      if (j < out && k < r) {
-        // k + 16 <= r: r % 8 == 0 and k % 16 == 0 give whole 8-column chunks;
-        // the second chunk is checked on its own
-        const bool hi = k + 8 < r;
-        if constexpr (TL::BASE) {
-        const Chunk b0 = *reinterpret_cast<const Chunk*>(Bp + j * r + k);
-        const Chunk b1 = hi ? *reinterpret_cast<const Chunk*>(Bp + j * r + k + 8) : zero_chunk();
-        float bf[16];
-        chunk_to_f32<DT>(b0, *reinterpret_cast<float(*)[8]>(bf));
-        chunk_to_f32<DT>(b1, *reinterpret_cast<float(*)[8]>(bf + 8));
-        float u0 = 0.0f, u1 = 0.0f;
+          for (int i = 0; i < TL::TMW; ++i) {
+            tie2(xl[step][i]);
+            tie2(xh[step][i]);
+            fx[i] = u32x4{xl[step][i][0], xl[step][i][1], xh[step][i][0], xh[step][i][1]};
+          }
 #pragma unroll
-        for (int q = 0; q < 16; q += 2) {
-          u0 = __builtin_fmaf(bf[q], acc[i][jj][q], u0);
-          u1 = __builtin_fmaf(bf[q + 1], acc[i][jj][q + 1], u1);
+          for (int j = 0; j < TL::TN; ++j) {
+            tie2(yl[step][j]);
+            tie2(yh[step][j]);
+            fy[j] = u32x4{yl[step][j][0], yl[step][j][1], yh[step][j][0], yh[step][j][1]};
+          }
+#pragma unroll
+          for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+            for (int j = 0; j < TL::TN; ++j)
+              acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
         }
-        bsum += u0 + u1;
-        }
-        // this slice of E for d_B
-        float* dst = ep + j * r + k;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[i][jj][4], acc[i][jj][5], acc[i][jj][6], acc[i][jj][7]};
-        if (hi) {
-          *reinterpret_cast<f32x4*>(dst + 8) = f32x4{acc[i][jj][8], acc[i][jj][9], acc[i][jj][10], acc[i][jj][11]};
-          *reinterpret_cast<f32x4*>(dst + 12) =
-              f32x4{acc[i][jj][12], acc[i][jj][13], acc[i][jj][14], acc[i][jj][15]};
+      } else {
+        // one K step's fragments at a time (fewer registers)
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+          const int row = 16 * step + rsrc_row;
+          u32x2 xl[TL::TMW], xh[TL::TMW], yl[TL::TN], yh[TL::TN];
+#pragma unroll
+          for (int i = 0; i < TL::TMW; ++i) {
+            xl[i] = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
+            xh[i] = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
+          }
+#pragma unroll
+          for (int j = 0; j < TL::TN; ++j) {
+            yl[j] = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
+            yh[j] = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
+          }
+          lds_wait();
+          u32x4 fx[TL::TMW], fy[TL::TN];
+#pragma unroll
+          for (int i = 0; i < TL::TMW; ++i) {
+            tie2(xl[i]);
+            tie2(xh[i]);
+            fx[i] = u32x4{xl[i][0], xl[i][1], xh[i][0], xh[i][1]};
+          }
+#pragma unroll
+          for (int j = 0; j < TL::TN; ++j) {
+            tie2(yl[j]);
+            tie2(yh[j]);
+            fy[j] = u32x4{yl[j][0], yl[j][1], yh[j][0], yh[j][1]};
+          }
+#pragma unroll
+          for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+            for (int j = 0; j < TL::TN; ++j)
+              acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
         }
       }
+      if (TL::BASE && eok) {
+        const int64_t t = ts + static_cast<int64_t>(st) * TL::BK + et;
+        if (t < te) {
+          // this thread's chunk of dy and of base, at the same place in their panels
+          const uint32_t ce = xp + static_cast<uint32_t>(et * TL::XROWB + bwd_slot(ec, et) * 16);
+          u32x4 wd = lds_read16(ce);
+          u32x4 wb = lds_read16(ce + TL::B_OFF);
+          lds_wait();
+          tie(wd);
+          tie(wb);
+          float dyv[8], bv[8], o[8];
+          chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wd), dyv);
+          chunk_to_f32<DT>(__builtin_bit_cast(Chunk, wb), bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            o[e] = gb[e] * dyv[e];
+            colsum[e] = __builtin_fmaf(dyv[e], bv[e], colsum[e]);
+          }
+          if (dbase) *reinterpret_cast<u32x4*>(dbase + t * out + ecol) = __builtin_bit_cast(u32x4, f32_to_chunk<DT>(o));
+        }
+      }
+      slot = slot == TL::NS - 1 ? 0 : slot + 1;
     }
-    bsum += __shfl_xor(bsum, 32, 64);
-    if (fh == 0) red[32 * 128 + wn * 128 + jl] = bsum;
+
+    // Epilogue.  The ring is free once every wave is past its last read.
+    __syncthreads();
+    // (1) s * sum_k B_jk E_jk over this rank block, per output column: lane l holds
+    // output column 32*(wm*TMW + i) + l%32 and rank columns 32*(wn*TN + j) + 16*(l/32) + q
+    const T16* Bp = static_cast<const T16*>(a.B);
+    const int frow = lane & 31, fh = lane >> 5;
+    float* ep = a.e_part + static_cast<int64_t>(sp) * out * r;
+#pragma unroll
+    for (int i = 0; i < TL::TMW; ++i) {
+      const int jl = 32 * (wm * TL::TMW + i) + frow;
+      const int64_t j = j0 + jl;
+      float bsum = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < TL::TN; ++jj) {
+        const int64_t k = k0 + 32 * (wn * TL::TN + jj) + 16 * fh;
+        if (j < out && k < r) {
+          // k + 16 <= r: r % 8 == 0 and k % 16 == 0 give whole 8-column chunks;
+          // the second chunk is checked on its own
+          const bool hi = k + 8 < r;
+          if constexpr (TL::BASE) {
+            const Chunk b0 = *reinterpret_cast<const Chunk*>(Bp + j * r + k);
+            const Chunk b1 = hi ? *reinterpret_cast<const Chunk*>(Bp + j * r + k + 8) : zero_chunk();
+            float bf[16];
+            chunk_to_f32<DT>(b0, *reinterpret_cast<float(*)[8]>(bf));
+            chunk_to_f32<DT>(b1, *reinterpret_cast<float(*)[8]>(bf + 8));
+            float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; q += 2) {
+              u0 = __builtin_fmaf(bf[q], acc[i][jj][q], u0);
+              u1 = __builtin_fmaf(bf[q + 1], acc[i][jj][q + 1], u1);
+            }
+            bsum += u0 + u1;
+          }
+          // this slice of E for d_B
+          float* dst = ep + j * r + k;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[i][jj][4], acc[i][jj][5], acc[i][jj][6], acc[i][jj][7]};
+          if (hi) {
+            *reinterpret_cast<f32x4*>(dst + 8) = f32x4{acc[i][jj][8], acc[i][jj][9], acc[i][jj][10], acc[i][jj][11]};
+            *reinterpret_cast<f32x4*>(dst + 12) =
+                f32x4{acc[i][jj][12], acc[i][jj][13], acc[i][jj][14], acc[i][jj][15]};
+          }
+        }
+      }
+      bsum += __shfl_xor(bsum, 32, 64);
+      if (fh == 0) red[32 * 128 + wn * 128 + jl] = bsum;
+    }
+    if constexpr (TL::BASE) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[et * 128 + 8 * ec + e] = colsum[e];
+    }
   }
   if constexpr (!TL::BASE) return;  // the plain contraction has no column sums
-  // (2) the column sums of dy * base over the slice: thread tid holds row tid/16
-  // of each stage and 8 columns
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[et * 128 + 8 * ec + e] = colsum[e];
+  // (2) the column sums of dy * base over the slice and the rank-block sums
   __syncthreads();
   if (tid < TL::BM && j0 + tid < out) {
     float bs = 0.0f, cs = 0.0f;
@@ -402,6 +466,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
     a.col_part[(static_cast<int64_t>(sp) * nTl + nt) * out + j0 + tid] = cs + a.s * bs;
   }
 }
+
 
 // One launch finishes both outputs: d_mag_j = (sum of the column partials) /
 // n_j in fp64, and d_B[j][k] = (g_j * s) * (sum of the E slices, added in
