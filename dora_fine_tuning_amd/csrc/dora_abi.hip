@@ -247,8 +247,9 @@ int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const 
   if (any_overlap(y, mb, h, hb) || any_overlap(y, mb, B, bb) || any_overlap(y, mb, mag, vb) ||
       any_overlap(y, mb, norm, vb))
     return fail(DORA_INVALID_ARG, "%s: y overlaps h, B, mag or norm", fn);
-  const bool vec = (out % 8 == 0) && (r % 8 == 0) && r <= (int64_t(1) << 20) && aligned16(base) &&
-                   (r == 0 || (aligned16(h) && aligned16(B))) && aligned16(mag) && aligned16(norm) && aligned16(y);
+  const bool vec = (out % 8 == 0) && out < (int64_t(1) << 22) && (r % 8 == 0) && r <= (int64_t(1) << 20) &&
+                   aligned16(base) && (r == 0 || (aligned16(h) && aligned16(B))) && aligned16(mag) &&
+                   aligned16(norm) && aligned16(y);
   if (dora::lora_fwd_max_grid(T, out, vec) > INT32_MAX)
     return fail(DORA_UNSUPPORTED, "%s: T=%lld x out=%lld needs more workgroups than one launch holds", fn,
                 (long long)T, (long long)out);

@@ -13,10 +13,11 @@
 //                     go global -> LDS by DMA into an NS-slot ring (h rows as
 //                     the X panel, B rows as the Y panel in the fragment row
 //                     order), MFMA 32x32x16 with fp32 accumulation, then an
-//                     epilogue straight from the accumulators: a lane holds one
-//                     token row and 16 consecutive output columns per 32x32
-//                     tile, so it reads base and writes y as two 16-byte chunks
-//                     per tile;
+//                     epilogue straight from the accumulators: the tile's base
+//                     block comes into the freed ring by DMA, and a lane,
+//                     holding one token row and 16 consecutive output columns
+//                     per 32x32 tile, reads its base from LDS and writes y as
+//                     two 16-byte chunks per tile;
 //   lora_fwd_general  (general path) one thread per output element, the r-term
 //                     dot product in order in fp32.
 #include <algorithm>
@@ -51,7 +52,8 @@ struct LoraTile {
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static_assert(TM % WM == 0, "token tiles split over the waves");
   static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "panels split into whole DMA groups per wave");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(LDS_BYTES + 2 * BN * 4 <= 160 * 1024, "LDS: ring and column scales");
+  static_assert(BM * BN * 2 <= LDS_BYTES, "the epilogue's base block fits the ring");
   static_assert(NS >= 3 && NS <= 8 && (NS - 2) * L < 64, "ring depth and vmcnt range");
 };
 
@@ -90,7 +92,7 @@ __device__ inline void lora_wait_younger(int n) {
 template <int DT, class TL>
 __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   using V8 = typename Dt<DT>::V8;
-  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES + 2 * TL::BN * 4];
 
   const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
   const uint32_t total = static_cast<uint32_t>(a.nRB) * static_cast<uint32_t>(a.nTiles);
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
-  // Buffer resources of the two panels, rebased to the tile's first row; rows
-  // past the operand lie beyond num_records and read zero.  Offsets stay below
-  // 2^31 (at most 256 rows of r <= 2^20 elements).
+  // Buffer resources, rebased to the tile's first row; rows past the operand
+  // lie beyond num_records and read zero.  Offsets stay below 2^31 (at most
+  // 256 rows of r <= 2^20 or out < 2^22 elements).
   auto rsrc = [](const void* base, int64_t row0, int64_t rows, int64_t ld, int64_t max_rows) {
     const int64_t nrows = std::min<int64_t>(std::max<int64_t>(rows - row0, 0), max_rows);
     const char* p = static_cast<const char*>(base) + (nrows > 0 ? row0 * ld * 2 : 0);
@@ -212,34 +214,36 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
     }
   }
 
-  // Epilogue.  The column scales (g - 1, g*s) of the tile's BN columns are
-  // formed once, by the first BN threads, into LDS (the ring is free after the
-  // barrier).  A lane then walks its TMW token rows; for each it needs 2*TN
-  // chunks of 8 columns (16 consecutive columns c0 .. c0 + 15 per column tile j,
-  // whole chunks since out % 8 == 0).  The chunks of row i + 1 are loaded
-  // before the stores of row i (y may be base, so the compiler keeps loads
-  // after earlier stores), and the four stores that complete a row's 128-byte
-  // line of y follow each other, so the L2 merges them before any write-back.
-  // Plain stores: nontemporal stores of these 16-byte pieces took 107 instead
-  // of 62 us for the epilogue alone at T = out = 8192.
+  // Epilogue.  The ring is free once every wave is past its last fragment
+  // read; the tile's base block (BM rows x BN columns, 2 bytes each) then goes
+  // global -> LDS by DMA, all of it in flight at once (a lane loading its own
+  // rows of base one at a time leaves too few loads in flight to cover the
+  // memory latency).  Row t of the block is BN*2 bytes, its logical 16-byte
+  // chunk c in slot c ^ (t % 32): the reads below, 32 rows at one logical
+  // chunk, then spread over the banks.  Columns past out read zero.  The
+  // column scales (g - 1, g*s) sit after the ring.  A lane then walks its
+  // TMW token rows; per row it needs 2*TN chunks of 8 columns (16 consecutive
+  // columns c0 .. c0 + 15 per column tile j, whole chunks since out % 8 == 0),
+  // and the four stores that complete a row's 128-byte line of y follow each
+  // other, so the L2 merges them before any write-back.  The whole block is in
+  // LDS before the first store, so y may be base.
   using T16 = typename Dt<DT>::T;
-  const T16* base = static_cast<const T16*>(a.base);
   T16* y = static_cast<T16*>(a.y);
-  float* sc = reinterpret_cast<float*>(smem);  // [2][BN]: g - 1, then g*s
-  Chunk cb[2][TL::TN][2];
-  auto load_row = [&](int i, Chunk (&c)[TL::TN][2]) {
-    const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) {
-      const int64_t c0 = n0 + wn * TL::TN * 32 + j * 32 + 16 * fhalf;
-      const bool ok0 = t < T && c0 < out, ok1 = t < T && c0 + 8 < out;
-      const int64_t idx = ok0 ? t * out + c0 : 0;
-      c[j][0] = ok0 ? *reinterpret_cast<const Chunk*>(base + idx) : zero_chunk();
-      c[j][1] = ok1 ? *reinterpret_cast<const Chunk*>(base + idx + 8) : zero_chunk();
+  float* sc = reinterpret_cast<float*>(smem + TL::LDS_BYTES);  // [2][BN]: g - 1, then g*s
+  constexpr int EROWB = TL::BN * 2, ECPR = EROWB / 16, ERPI = 1024 / EROWB;
+  static_assert(ECPR == 32 && ERPI * EROWB == 1024, "base rows of 32 chunks, two per DMA instruction");
+  __syncthreads();
+  {
+    const __amdgpu_buffer_rsrc_t rb = rsrc(a.base, m0, T, out, TL::BM);
+    const int erow = lane / ECPR, eslot = lane % ECPR;
+#pragma unroll 4
+    for (int q = wave; q < TL::BM / ERPI; q += TL::NW) {
+      const int row = q * ERPI + erow;
+      const int64_t col = n0 + 8 * (eslot ^ (row % ECPR));
+      const uint32_t off = col < out ? static_cast<uint32_t>((static_cast<int64_t>(row) * out + col) * 2) : kOob;
+      dma16(rb, smem + q * 1024, off);
     }
-  };
-  load_row(0, cb[0]);
-  __syncthreads();  // every wave is past its last fragment read
+  }
   if (tid < TL::BN) {
     const int64_t c = n0 + tid;
     float gm1 = 0.0f, gs = 0.0f;
@@ -251,11 +255,21 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
     sc[tid] = gm1;
     sc[TL::BN + tid] = gs;
   }
+  wait_vmcnt<0>();
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < TL::TMW; ++i) {
-    if (i + 1 < TL::TMW) load_row(i + 1, cb[(i + 1) & 1]);
-    const int64_t t = m0 + wm * TL::TMW * 32 + i * 32 + frow;
+    const int rl = wm * TL::TMW * 32 + i * 32 + frow;  // row within the block (rl % 32 == frow)
+    const int64_t t = m0 + rl;
+    u32x4 cb[TL::TN][2];
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = (wn * TL::TN * 32 + j * 32 + 16 * fhalf) / 8 + k;  // logical chunk
+        cb[j][k] = lds_read16(lds0 + static_cast<uint32_t>(rl * EROWB + ((c ^ frow) * 16)));
+      }
+    lds_wait();
     if (t >= T) continue;
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) {
@@ -266,13 +280,14 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         if (k == 1 && c0 + 8 >= out) continue;
+        tie(cb[j][k]);
         // the chunk's 8 column scales, read from LDS where they are used
         const f32x4 g1a = *reinterpret_cast<const f32x4*>(sc + cl + 8 * k);
         const f32x4 g1b = *reinterpret_cast<const f32x4*>(sc + cl + 8 * k + 4);
         const f32x4 g2a = *reinterpret_cast<const f32x4*>(sc + TL::BN + cl + 8 * k);
         const f32x4 g2b = *reinterpret_cast<const f32x4*>(sc + TL::BN + cl + 8 * k + 4);
         float b[8], o[8];
-        chunk_to_f32<DT>(cb[i & 1][j][k], b);
+        chunk_to_f32<DT>(__builtin_bit_cast(Chunk, cb[j][k]), b);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float gm1 = e < 4 ? g1a[e] : g1b[e - 4], gs = e < 4 ? g2a[e] : g2b[e - 4];

@@ -188,8 +188,8 @@ DORA_API int dora_compose_fwd(const void* base, const void* lora, const float* m
  * device fp32 [out].  y may be the same buffer as base; no other overlap with
  * an input.  h and B may be NULL when r == 0 (then y is the compose of
  * lora = 0).  T == 0 or out == 0 is a no-op.  The fast path needs out and r
- * multiples of 8, r <= 2^20 and 16-byte aligned pointers; other cases take a
- * slow path (one thread per output element).
+ * multiples of 8, out < 2^22, r <= 2^20 and 16-byte aligned pointers; other
+ * cases take a slow path (one thread per output element).
  */
 DORA_API int dora_lora_compose_fwd(const void* base, const void* h, const void* B, const float* mag,
                                    const float* norm, float s, int64_t T, int64_t out, int64_t r, int dtype,
