@@ -34,18 +34,20 @@ inline int64_t lcdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile geometry: NW = WM*4 waves in a WM x 4 grid (WM along the tokens, 4 along
 // the output columns); a wave owns TMW = TM/WM token tiles x TN column tiles of
-// 32 and keeps their accumulators in registers.  A K stage holds one 64-byte
-// segment (32 elements) of each panel row; one wave DMA instruction moves 16
-// rows x 64 bytes, lane l taking row l/4 and the logical 16-byte chunk
-// (l%4) ^ ((row/4)%4), which lands in LDS slot l%4; the fragment reads of 16
-// consecutive rows at one logical chunk then hit 16 distinct bank groups.
-template <int TN_, int TM_, int NS_, int WM_>
+// 32 and keeps their accumulators in registers.  A K stage holds one segment of
+// BK elements (ROWB = 2*BK bytes, CPR 16-byte chunks) of each panel row; one
+// wave DMA instruction moves RPI = 1024/ROWB rows, lane l taking row l/CPR and
+// the logical chunk (l%CPR) ^ ((row/SWP)%CPR), SWP = 16/CPR, which lands in LDS
+// slot l%CPR; the fragment reads of 16 consecutive rows at one logical chunk
+// then hit 16 distinct bank groups.
+template <int TN_, int TM_, int NS_, int WM_, int BK_ = 32>
 struct LoraTile {
   static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_;
   static constexpr int WN = 4, NW = WM * WN, NT = NW * 64;
   static constexpr int TMW = TM / WM;
   static constexpr int BM = 32 * TM, BN = 32 * WN * TN;
-  static constexpr int BK = 32, ROWB = 64, CPR = 4, RPI = 16, SWP = 4;
+  static constexpr int BK = BK_, ROWB = 2 * BK, CPR = ROWB / 16, RPI = 1024 / ROWB, SWP = 16 / CPR;
+  static constexpr int KS = BK / 16;  // MFMA K steps per stage, done in pairs
   static constexpr int X_BYTES = BM * ROWB, Y_BYTES = BN * ROWB, STAGE_BYTES = X_BYTES + Y_BYTES;
   static constexpr int XQ = BM / RPI / NW, YQ = BN / RPI / NW;
   static constexpr int L = XQ + YQ;  // DMA instructions per wave and stage
@@ -54,14 +56,14 @@ struct LoraTile {
   static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "panels split into whole DMA groups per wave");
   static_assert(LDS_BYTES + 2 * BN * 4 <= 160 * 1024, "LDS: ring and column scales");
   static_assert(BM * BN * 2 <= LDS_BYTES, "the epilogue's base block fits the ring");
-  static_assert(NS >= 3 && NS <= 8 && (NS - 2) * L < 64, "ring depth and vmcnt range");
+  static_assert(BK == 32 || BK == 64, "64- or 128-byte row segments");
+  static_assert(NS >= 2 && NS <= 8 && (NS - 2) * L < 64, "ring depth and vmcnt range");
 };
 
-// 256 tokens x 256 columns, 8 waves, four ring slots of 32 KB (one workgroup
-// per CU).  Measured against 128 x 256 with 4 waves and two workgroups per CU:
-// 120 against 141 us at T = out = 8192, r = 384; the two workgroups of a CU
-// run their K loops and epilogues in step, so the second brings no overlap.
-using LoraTileMain = LoraTile<2, 8, 4, 2>;
+// 256 tokens x 256 columns, 8 waves, one workgroup per CU.  K stages of 64
+// (128-byte row segments, whole cache lines) in two ring slots of 64 KB: the
+// DMA of stage u + 1 overlaps the MFMAs of stage u.
+using LoraTileMain = LoraTile<2, 8, 2, 2, 64>;
 
 constexpr uint32_t kGroupCols = 4;  // column tiles per group of the tile order
 
@@ -131,7 +133,9 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   // panel is fetched in the row order sigma of the fragment reads, so that
   // accumulator register q of a lane in half h holds column 16h + q of its tile.
   const int lrow = lane / TL::CPR, lslot = lane % TL::CPR;
-  const int lc = lslot ^ ((lrow / TL::SWP) % TL::CPR);
+  // instruction q of the wave starts at row (q*NW + wave)*RPI, and q*NW*RPI is
+  // a multiple of SWP*CPR: the chunk depends on the wave's row of instruction 0
+  const int lc = lslot ^ (((wave * TL::RPI + lrow) / TL::SWP) % TL::CPR);
   const int kc = lc * 8;
   auto sigma = [](int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); };
   const int xr0 = wave * TL::RPI + lrow;
@@ -143,8 +147,10 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow / TL::SWP) % TL::CPR;
   const uint32_t xrow = lds0 + static_cast<uint32_t>((wm * TL::TMW * 32 + frow) * TL::ROWB);
   const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * TL::ROWB);
-  const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), yb0 = yrow + ((fhalf ^ fsw) * 16);
-  const uint32_t xb1 = xrow + (((2 + fhalf) ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
+  // K step k reads logical chunk 2k + fhalf of its rows
+  uint32_t cofs[TL::KS];
+#pragma unroll
+  for (int k = 0; k < TL::KS; ++k) cofs[k] = static_cast<uint32_t>(((2 * k + fhalf) ^ fsw) * 16);
 
   f32x16 acc[TL::TMW][TL::TN];
 #pragma unroll
@@ -182,15 +188,17 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
       __builtin_amdgcn_s_barrier();
       if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, (u + TL::NS - 1) % TL::NS);
       const uint32_t so = static_cast<uint32_t>(u * TL::STAGE_BYTES);
+#pragma unroll
+      for (int kp = 0; kp < TL::KS; kp += 2) {
       u32x4 x0[TL::TMW], y0[TL::TN], x1[TL::TMW], y1[TL::TN];
 #pragma unroll
-      for (int i = 0; i < TL::TMW; ++i) x0[i] = lds_read16(xb0 + so + i * tstep);
+      for (int i = 0; i < TL::TMW; ++i) x0[i] = lds_read16(xrow + cofs[kp] + so + i * tstep);
 #pragma unroll
-      for (int j = 0; j < TL::TN; ++j) y0[j] = lds_read16(yb0 + so + j * tstep);
+      for (int j = 0; j < TL::TN; ++j) y0[j] = lds_read16(yrow + cofs[kp] + so + j * tstep);
 #pragma unroll
-      for (int i = 0; i < TL::TMW; ++i) x1[i] = lds_read16(xb1 + so + i * tstep);
+      for (int i = 0; i < TL::TMW; ++i) x1[i] = lds_read16(xrow + cofs[kp + 1] + so + i * tstep);
 #pragma unroll
-      for (int j = 0; j < TL::TN; ++j) y1[j] = lds_read16(yb1 + so + j * tstep);
+      for (int j = 0; j < TL::TN; ++j) y1[j] = lds_read16(yrow + cofs[kp + 1] + so + j * tstep);
       lds_wait_keep<TL::TMW + TL::TN>();
 #pragma unroll
       for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);
@@ -211,6 +219,7 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
 #pragma unroll
         for (int j = 0; j < TL::TN; ++j)
           acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, y1[j]), __builtin_bit_cast(V8, x1[i]), acc[i][j]);
+      }
     }
   }
 
