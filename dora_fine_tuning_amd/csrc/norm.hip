@@ -961,14 +961,15 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
 #undef DORA_STEP_SQUARES
 
 // ---------------------------------------------------------------------------
-// W stream with 128-byte row segments (rank tiles of 384).
+// W stream with 128-byte row segments (rank tiles of 128, 256 and 384).
 //
 // The 64-byte row segments of wstream_dma make every L1 -> L2 request 64
 // bytes, and the L1's table of pending requests then bounds the stream (it is
 // full most of the time at the measured L2 latency).  Here a stage is 64 K
 // columns: every DMA row segment is a whole 128-byte line.  The A panel (384
 // rank rows, L2 resident) and the W0 panel (128 rows, streamed from HBM) sit
-// in separate rings: two A slots, three W0 slots.
+// in separate rings: two A slots, three W0 slots (the W0 panel is 128 or 256
+// rows, the A panel 32 * TN * 4 rank rows).
 //
 // The loads of a stage (64 KiB per workgroup) take the texture path about a
 // thousand cycles to accept, and a wave that issues them cannot issue MFMAs
@@ -979,12 +980,13 @@ __global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_
 // order, so W0(u + 2) stays in flight: W0 has two stages to arrive, A one)
 // before the barrier of stage u + 1.  Every stage issues the same loads per
 // DMA wave (stages past the slice get out-of-range offsets: zeros into a slot
-// no stage reads again), so one vmcnt value serves every wait.  Tile: 128
-// rows x 384 ranks, tile waves 2 along the rows x 4 along the ranks (64 x 96
-// each), four MFMA K steps per stage with the next step's fragments read
-// during the current step's MFMAs.
+// no stage reads again), so one vmcnt value serves every wait.  Tile: 64 * TMW
+// rows x 128 * TN ranks, tile waves 2 along the rows x 4 along the ranks
+// (32 * TMW x 32 * TN each), four MFMA K steps per stage with the next step's
+// fragments read during the current step's MFMAs.
+template <int TN_, int TMW_>
 struct K64Tile {
-  static constexpr int TMW = 2, TN = 3, WM = 2, WN = 4, NW = 8, NDMA = 4, NT = 64 * (NW + NDMA);
+  static constexpr int TMW = TMW_, TN = TN_, WM = 2, WN = 4, NW = 8, NDMA = 4, NT = 64 * (NW + NDMA);
   static constexpr int BM = 32 * TMW * WM, BN = 32 * TN * WN;  // 128 x 384
   static constexpr int BK = 64, KS = BK / 16, ROWB = BK * 2;   // 128-byte rows
   static constexpr int RPI = 1024 / ROWB;                      // rows per 1 KiB DMA instruction
@@ -997,14 +999,14 @@ struct K64Tile {
   static constexpr int RED_BYTES = 2 * WN * BM * 4, RED_OFF = AREA - RED_BYTES;
   static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
   static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
+  static_assert(TMW <= 4 && TN <= 3, "fragment reads of one K step: at most four W0 and three rank tiles");
   static_assert(XI % NDMA == 0 && YI % NDMA == 0, "whole DMA groups per DMA wave");
   static_assert(W_OFF + NWS * W_BYTES <= RED_OFF, "rings below the epilogue's row sums");
   static_assert(L < 64, "vmcnt range");
 };
 
-template <int DT>
-__global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
-  using TL = K64Tile;
+template <int DT, class TL>
+__global__ __launch_bounds__(TL::NT, 1) void wstream_k64(WArgs a) {
   using V8 = typename Dt<DT>::V8;
   __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
   float(*red)[TL::BM] = reinterpret_cast<float(*)[TL::BM]>(smem + TL::RED_OFF);
@@ -1111,10 +1113,12 @@ __global__ __launch_bounds__(K64Tile::NT, 1) void wstream_k64(WArgs a) {
     const uint32_t xb_ = xrow + (SWS) * TL::W_BYTES + co[K];                             \
     const uint32_t yb_ = yrow + (SA) * TL::A_BYTES + co[K];                              \
     X[0] = lds_read16_at<0>(xb_);                                                        \
-    X[1] = lds_read16_at<32 * TL::ROWB>(xb_);                                            \
+    if constexpr (TL::TMW > 1) X[1 % TL::TMW] = lds_read16_at<32 * TL::ROWB>(xb_);       \
+    if constexpr (TL::TMW > 2) X[2 % TL::TMW] = lds_read16_at<64 * TL::ROWB>(xb_);       \
+    if constexpr (TL::TMW > 3) X[3 % TL::TMW] = lds_read16_at<96 * TL::ROWB>(xb_);       \
     Y[0] = lds_read16_at<0>(yb_);                                                        \
-    Y[1] = lds_read16_at<32 * TL::ROWB>(yb_);                                            \
-    Y[2] = lds_read16_at<64 * TL::ROWB>(yb_);                                            \
+    if constexpr (TL::TN > 1) Y[1 % TL::TN] = lds_read16_at<32 * TL::ROWB>(yb_);         \
+    if constexpr (TL::TN > 2) Y[2 % TL::TN] = lds_read16_at<64 * TL::ROWB>(yb_);         \
   }
 #define K64_MFMAS(X, Y)                                                                  \
   _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) \
@@ -1452,46 +1456,45 @@ int dma_tn(int64_t r) {
   return best;
 }
 
-// Per rank-tile width: W0 rows per tile (32*TM), LDS ring slots, waves along
-// the rows and K depth of a stage.  K stages of 32 give 64-byte row segments
-// per DMA lane group: global -> LDS DMA from L2 runs at about 40 B/clk per CU
-// with 64-byte segments and at about half that with 32-byte ones.
+// Shape of the 64-byte-segment stream (rank tiles of 512): W0 rows per tile
+// (32*TM), LDS ring slots, waves along the rows and K depth of a stage.
 template <int TN> struct DmaShape;
-template <> struct DmaShape<1> { static constexpr int TM = 8, NS = 6, WM = 2, BK = 32; };
-template <> struct DmaShape<2> { static constexpr int TM = 8, NS = 4, WM = 2, BK = 32; };
-// rank tiles of 384 take wstream_k64 (K64Tile); this shape is not launched
-template <> struct DmaShape<3> { static constexpr int TM = 4, NS = 5, WM = 2, BK = 32; };
+// rank tiles of 128, 256 and 384 take wstream_k64: 256 x 128, 128 x 256 and
+// 128 x 384 (W0 rows x ranks); rank tiles of 512 the 64-byte-segment stream
+template <int TN> struct K64Of;
+template <> struct K64Of<1> { using T = K64Tile<1, 4>; };
+template <> struct K64Of<2> { using T = K64Tile<2, 2>; };
+template <> struct K64Of<3> { using T = K64Tile<3, 2>; };
 template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3, WM = 2, BK = 32; };
-
-template <int TN>
-using DmaTileOf = DmaTile<TN, DmaShape<TN>::TM, DmaShape<TN>::NS, DmaShape<TN>::WM, DmaShape<TN>::BK>;
+using DmaTile4 = DmaTile<4, DmaShape<4>::TM, DmaShape<4>::NS, DmaShape<4>::WM, DmaShape<4>::BK>;
 
 int dma_rows(int tn) {
   switch (tn) {
-    case 1: return DmaTileOf<1>::BM;
-    case 2: return DmaTileOf<2>::BM;
-    case 3: return K64Tile::BM;
-    default: return DmaTileOf<4>::BM;
+    case 1: return K64Of<1>::T::BM;
+    case 2: return K64Of<2>::T::BM;
+    case 3: return K64Of<3>::T::BM;
+    default: return DmaTile4::BM;
   }
 }
 
 int dma_bk(int tn) {
   switch (tn) {
-    case 1: return DmaTileOf<1>::BK;
-    case 2: return DmaTileOf<2>::BK;
-    case 3: return K64Tile::BK;
-    default: return DmaTileOf<4>::BK;
+    case 1: return K64Of<1>::T::BK;
+    case 2: return K64Of<2>::T::BK;
+    case 3: return K64Of<3>::T::BK;
+    default: return DmaTile4::BK;
   }
 }
 
 template <int DT, int TN>
 void launch_dma(const WArgs& w, hipStream_t stream) {
-  using S = DmaShape<TN>;
   const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
-  if constexpr (TN == 3) {  // rank tiles of 384: the 128-byte-segment stream
-    hipLaunchKernelGGL((wstream_k64<DT>), grid, dim3(K64Tile::NT), 0, stream, w);
+  if constexpr (TN <= 3) {  // the 128-byte-segment stream
+    using TL = typename K64Of<TN>::T;
+    hipLaunchKernelGGL((wstream_k64<DT, TL>), grid, dim3(TL::NT), 0, stream, w);
   } else {
-    hipLaunchKernelGGL((wstream_dma<DT, TN, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTileOf<TN>::NT), 0, stream, w);
+    using S = DmaShape<4>;
+    hipLaunchKernelGGL((wstream_dma<DT, 4, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTile4::NT), 0, stream, w);
   }
 }
 
