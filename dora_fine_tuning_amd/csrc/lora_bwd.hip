@@ -30,6 +30,7 @@
 //   lora_bwd_general  (general path) one thread per output column, all sums in
 //                     order in fp32, lora per element by its r-term dot product.
 #include <algorithm>
+#include <type_traits>
 
 #include "dma_common.hpp"
 #include "dora_common.hpp"
@@ -75,26 +76,32 @@ __device__ inline void tie2(u32x2& v) { asm volatile("" : "+v"(v)); }
 // ring's loads, so the tile waves never stall on the texture path that takes
 // a stage's loads.  Every vector-memory instruction of a DMA wave's stage
 // loop is a DMA of the ring, which keeps the stage waits exact.
-template <int TN_, int NS_, bool BASE_>
+// DUAL (plain contraction only): the Y rows hold two column blocks that add
+// into the same output, Y[t][c] and Y[t][ny + c] (the hi and lo halves of a
+// value carried as a pair); a stage then holds both Y panels and every
+// accumulator takes one MFMA from each, so X is streamed once for both.
+template <int TN_, int NS_, bool BASE_, bool DUAL_ = false>
 struct BwdTile {
   static constexpr int TN = TN_, NS = NS_;
-  static constexpr bool BASE = BASE_;
+  static constexpr bool BASE = BASE_, DUAL = DUAL_;
+  static constexpr int NYP = DUAL ? 2 : 1;  // Y panels per stage
   static constexpr int WM = 2, WN = 4, NW = 8, NDMA = 4, NT = 64 * (NW + NDMA), TM = 4, TMW = 2;
   static constexpr int BM = 128, BN = 128 * TN, BK = 32;
   static constexpr int XROWB = BM * 2, YROWB = BN * 2;  // bytes per token row
   static constexpr int X_BYTES = BK * XROWB, Y_BYTES = BK * YROWB, B_BYTES = BASE ? X_BYTES : 0;
-  static constexpr int B_OFF = X_BYTES + Y_BYTES, STAGE_BYTES = X_BYTES + Y_BYTES + B_BYTES;
-  static constexpr int XI = X_BYTES / 1024, YI = Y_BYTES / 1024;  // 1 KiB DMA blocks per stage
-  static constexpr int XQ = XI / NDMA, YQ = YI / NDMA, L = XQ + YQ + (BASE ? XQ : 0);  // per DMA wave
+  static constexpr int B_OFF = X_BYTES + NYP * Y_BYTES, STAGE_BYTES = X_BYTES + NYP * Y_BYTES + B_BYTES;
+  static constexpr int XI = X_BYTES / 1024, YI = Y_BYTES / 1024;  // 1 KiB DMA blocks per stage and panel
+  static constexpr int XQ = XI / NDMA, YQ = YI / NDMA, L = XQ + NYP * YQ + (BASE ? XQ : 0);  // per DMA wave
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   // the widest tile with the elementwise part reads one K step's fragments at
   // a time: both steps' would not fit the registers of three waves per SIMD
-  static constexpr bool ONE_STEP = BASE && TN == 3;
+  static constexpr bool ONE_STEP = (BASE && TN == 3) || DUAL;
+  static_assert(!(BASE && DUAL), "the dual Y panels are for the plain contraction");
   static_assert(XI % NDMA == 0 && YI % NDMA == 0, "panels split into whole DMA groups per DMA wave");
   static_assert(NW * 64 == BK * 16, "one 16-byte chunk of a stage's dy and base rows per tile-wave thread");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(NS >= 3 && (NS - 2) * L < 64, "ring depth and vmcnt range");
-  static_assert(2 * (TMW + TN) < 16, "one K step's fragment reads within the lgkmcnt range");
+  static_assert(NS >= 2 && (NS - 2) * L < 64, "ring depth and vmcnt range");
+  static_assert(ONE_STEP || 2 * (TMW + TN) < 16, "one K step's fragment reads within the lgkmcnt range");
 };
 
 // slot of logical 16-byte chunk c in token row t (see BwdTile)
@@ -107,6 +114,7 @@ struct BwdArgs {
   float s;
   int add_base;
   int64_t T, out, r;
+  int64_t ldy;  // row pitch of h (and h2) in elements: r, or 2r with DUAL panels
   int nCB, nTiles, nSplit;
   float* e_part;    // [nSplit][out][r]: the E slices
   float* col_part;  // [nSplit][nTiles][out]: sum_t dy * base (tile 0 only) + s * sum_k B E
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
   const int nt = static_cast<int>(v % nTl);
   const int cb = static_cast<int>((v / nTl) % nCB);
   const int sp = static_cast<int>(v / (nTl * nCB));
-  const int64_t T = a.T, out = a.out, r = a.r;
+  const int64_t T = a.T, out = a.out, r = a.r, ldy = a.ldy;
   const int64_t j0 = static_cast<int64_t>(cb) * TL::BM, k0 = static_cast<int64_t>(nt) * TL::BN;
   const int64_t ts = T * sp / a.nSplit, te = T * (sp + 1) / a.nSplit;
   // second row segment (plain contraction only; empty when T2 == 0)
@@ -174,15 +182,15 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
         const_cast<char*>(TL::BASE ? static_cast<const char*>(a.base) + ts * out * 2 : nullptr), static_cast<short>(0),
         static_cast<int>(TL::BASE ? rows * out * 2 : 0), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(a.h) + ts * r * 2), static_cast<short>(0),
-        static_cast<int>(rows * r * 2), kBufferWord3);
+        const_cast<char*>(static_cast<const char*>(a.h) + ts * ldy * 2), static_cast<short>(0),
+        static_cast<int>(rows * ldy * 2), kBufferWord3);
     const int64_t rows2 = te2 - ts2;
     const __amdgpu_buffer_rsrc_t rdy2 = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.dy2) + ts2 * out * 2 : nullptr),
         static_cast<short>(0), static_cast<int>(rows2 * out * 2), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rh2 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.h2) + ts2 * r * 2 : nullptr), static_cast<short>(0),
-        static_cast<int>(rows2 * r * 2), kBufferWord3);
+        const_cast<char*>(rows2 > 0 ? static_cast<const char*>(a.h2) + ts2 * ldy * 2 : nullptr),
+        static_cast<short>(0), static_cast<int>(rows2 * ldy * 2), kBufferWord3);
 
     // Per-lane DMA offsets (stage 0).  Instruction q of DMA wave d moves 1 KiB
     // block b = q*NDMA + d of its panel, lane l writing bytes 16l .. 16l + 15.
@@ -209,9 +217,9 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
       const int c = bwd_slot(sl, t);
       const int64_t col = k0 + 8 * c;
       yok[q] = col < r;
-      yo[q] = static_cast<uint32_t>((t * r + col) * 2);
+      yo[q] = static_cast<uint32_t>((t * ldy + col) * 2);
     }
-    const uint32_t xstep = static_cast<uint32_t>(TL::BK * out * 2), ystep = static_cast<uint32_t>(TL::BK * r * 2);
+    const uint32_t xstep = static_cast<uint32_t>(TL::BK * out * 2), ystep = static_cast<uint32_t>(TL::BK * ldy * 2);
     // stages [0, S1) read the slice's rows of dy and h, stages [S1, S) those of
     // dy2 and h2 (same row pitches, so the same per-lane offsets); a segment's
     // last stage reads zeros past its rows
@@ -226,6 +234,12 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
 #pragma unroll
       for (int q = 0; q < TL::YQ; ++q)
         dma16(ry, so + TL::X_BYTES + (q * TL::NDMA + dw) * 1024, yok[q] ? yo[q] + ss * ystep : kOob);
+      if constexpr (TL::DUAL) {  // the second Y panel: the same rows, r columns further
+#pragma unroll
+        for (int q = 0; q < TL::YQ; ++q)
+          dma16(ry, so + TL::X_BYTES + TL::Y_BYTES + (q * TL::NDMA + dw) * 1024,
+                yok[q] ? yo[q] + ss * ystep + static_cast<uint32_t>(r * 2) : kOob);
+      }
       if constexpr (TL::BASE) {  // never with a second segment
 #pragma unroll
         for (int q = 0; q < TL::XQ; ++q)
@@ -342,23 +356,26 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
               acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
         }
       } else {
-        // one K step's fragments at a time (fewer registers)
+        // one K step's fragments at a time (fewer registers); with DUAL the
+        // second Y panel's fragments feed the same accumulators
 #pragma unroll
         for (int step = 0; step < 2; ++step) {
           const int row = 16 * step + rsrc_row;
-          u32x2 xl[TL::TMW], xh[TL::TMW], yl[TL::TN], yh[TL::TN];
+          u32x2 xl[TL::TMW], xh[TL::TMW], yl[TL::NYP][TL::TN], yh[TL::NYP][TL::TN];
 #pragma unroll
           for (int i = 0; i < TL::TMW; ++i) {
             xl[i] = lds_read_tr(tr_addr(xp, TL::XROWB, row, xcol[i]));
             xh[i] = lds_read_tr(tr_addr(xp, TL::XROWB, row + 4, xcol[i]));
           }
 #pragma unroll
-          for (int j = 0; j < TL::TN; ++j) {
-            yl[j] = lds_read_tr(tr_addr(yp, TL::YROWB, row, ycol[j]));
-            yh[j] = lds_read_tr(tr_addr(yp, TL::YROWB, row + 4, ycol[j]));
-          }
+          for (int pn = 0; pn < TL::NYP; ++pn)
+#pragma unroll
+            for (int j = 0; j < TL::TN; ++j) {
+              yl[pn][j] = lds_read_tr(tr_addr(yp + pn * TL::Y_BYTES, TL::YROWB, row, ycol[j]));
+              yh[pn][j] = lds_read_tr(tr_addr(yp + pn * TL::Y_BYTES, TL::YROWB, row + 4, ycol[j]));
+            }
           lds_wait();
-          u32x4 fx[TL::TMW], fy[TL::TN];
+          u32x4 fx[TL::TMW];
 #pragma unroll
           for (int i = 0; i < TL::TMW; ++i) {
             tie2(xl[i]);
@@ -366,16 +383,20 @@ __global__ __launch_bounds__(TL::NT, 1) void lora_bwd_dma(BwdArgs a) {
             fx[i] = u32x4{xl[i][0], xl[i][1], xh[i][0], xh[i][1]};
           }
 #pragma unroll
-          for (int j = 0; j < TL::TN; ++j) {
-            tie2(yl[j]);
-            tie2(yh[j]);
-            fy[j] = u32x4{yl[j][0], yl[j][1], yh[j][0], yh[j][1]};
+          for (int pn = 0; pn < TL::NYP; ++pn) {
+            u32x4 fy[TL::TN];
+#pragma unroll
+            for (int j = 0; j < TL::TN; ++j) {
+              tie2(yl[pn][j]);
+              tie2(yh[pn][j]);
+              fy[j] = u32x4{yl[pn][j][0], yl[pn][j][1], yh[pn][j][0], yh[pn][j][1]};
+            }
+#pragma unroll
+            for (int i = 0; i < TL::TMW; ++i)
+#pragma unroll
+              for (int j = 0; j < TL::TN; ++j)
+                acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
           }
-#pragma unroll
-          for (int i = 0; i < TL::TMW; ++i)
-#pragma unroll
-            for (int j = 0; j < TL::TN; ++j)
-              acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, fy[j]), __builtin_bit_cast(V8, fx[i]), acc[i][j]);
         }
       }
       if (TL::BASE && eok) {
@@ -567,11 +588,18 @@ BwdPlan bwd_plan(int64_t T, int64_t out, int64_t r, bool vec) {
   return p;
 }
 
-// Ring depth: the 40 KB stages of the rank-384 tile with the base panel fit
-// four times in the 160 KB of LDS, every other stage five times.
-template <int DT, int TN, bool BASE = true>
+// Ring depth: as many stages as fit in the 160 KB of LDS, at most five (the
+// 40 KB stages of the rank-384 tile with the base panel: four; the 56 KB
+// stages of the rank-384 tile with dual Y panels: two).
+template <int TN, bool BASE, bool DUAL>
+constexpr int bwd_ring() {
+  constexpr int stage = 32 * 256 * (1 + (DUAL ? 2 : 1) * TN + (BASE ? 1 : 0));
+  return 160 * 1024 / stage < 5 ? 160 * 1024 / stage : 5;
+}
+
+template <int DT, int TN, bool BASE = true, bool DUAL = false>
 void launch_bwd_dma(const BwdArgs& a, hipStream_t stream) {
-  using TL = BwdTile<TN, (TN == 3 && BASE) ? 4 : 5, BASE>;
+  using TL = BwdTile<TN, bwd_ring<TN, BASE, DUAL>(), BASE, DUAL>;
   const int64_t total = static_cast<int64_t>(a.nCB) * a.nTiles * a.nSplit;
   hipLaunchKernelGGL((lora_bwd_dma<DT, TL>), dim3(static_cast<unsigned>(bcdiv(total, 8) * 8)), dim3(TL::NT), 0,
                      stream, a);
@@ -596,19 +624,20 @@ int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r) {
   return rows * std::max<int64_t>(out, r) * 2;
 }
 
-RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny, int64_t T2) {
+RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny, int64_t T2, int64_t ldy) {
   RowContractPlan q;
   if (T <= 0 || nx <= 0 || ny <= 0) return q;
   const BwdPlan p = bwd_plan(T, nx, ny, true);
   q.nSplit = p.nSplit;
   q.bytes = static_cast<size_t>(q.nSplit) * nx * ny * 4;
   q.grid = bcdiv(static_cast<int64_t>(p.nCB) * p.nTiles * q.nSplit, 8) * 8;
-  q.slice_bytes = bcdiv(std::max(T, T2), p.nSplit) * std::max(nx, ny) * 2;
+  q.slice_bytes = bcdiv(std::max(T, T2), p.nSplit) * std::max(nx, std::max(ny, ldy)) * 2;
   return q;
 }
 
-hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int dtype,
-                               float* e_part, hipStream_t stream, const void* X2, const void* Y2, int64_t T2) {
+hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int64_t ldy, bool dual,
+                               int dtype, float* e_part, hipStream_t stream, const void* X2, const void* Y2,
+                               int64_t T2) {
   if (T <= 0 || nx <= 0 || ny <= 0) return hipSuccess;
   const BwdPlan plan = bwd_plan(T, nx, ny, true);
   BwdArgs a{};
@@ -617,6 +646,7 @@ hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t 
   a.T = T;
   a.out = nx;
   a.r = ny;
+  a.ldy = ldy;
   a.nCB = plan.nCB;
   a.nTiles = plan.nTiles;
   a.nSplit = plan.nSplit;
@@ -626,19 +656,23 @@ hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t 
     a.h2 = Y2;
     a.T2 = T2;
   }
-  if (dtype == 0) {
+  auto go = [&](auto dt, auto du) {
+    constexpr int DT = decltype(dt)::value;
+    constexpr bool DU = decltype(du)::value;
     switch (plan.tn) {
-      case 1: launch_bwd_dma<0, 1, false>(a, stream); break;
-      case 2: launch_bwd_dma<0, 2, false>(a, stream); break;
-      default: launch_bwd_dma<0, 3, false>(a, stream); break;
+      case 1: launch_bwd_dma<DT, 1, false, DU>(a, stream); break;
+      case 2: launch_bwd_dma<DT, 2, false, DU>(a, stream); break;
+      default: launch_bwd_dma<DT, 3, false, DU>(a, stream); break;
     }
-  } else {
-    switch (plan.tn) {
-      case 1: launch_bwd_dma<1, 1, false>(a, stream); break;
-      case 2: launch_bwd_dma<1, 2, false>(a, stream); break;
-      default: launch_bwd_dma<1, 3, false>(a, stream); break;
-    }
-  }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BF = std::false_type;
+  using BT = std::true_type;
+  if (dtype == 0)
+    dual ? go(I0{}, BT{}) : go(I0{}, BF{});
+  else
+    dual ? go(I1{}, BT{}) : go(I1{}, BF{});
   return hipGetLastError();
 }
 
@@ -656,6 +690,7 @@ hipError_t launch_lora_bwd(const LoraBwdArgs& p, bool vec) {
   a.T = p.T;
   a.out = p.out;
   a.r = p.r;
+  a.ldy = p.r;
   if (!vec) {
     const dim3 grid(static_cast<unsigned>(bcdiv(p.out, 256)));
     if (p.dtype == 0)

@@ -47,21 +47,23 @@ int64_t lora_bwd_max_slice_bytes(int64_t T, int64_t out, int64_t r);
 hipError_t launch_lora_bwd(const LoraBwdArgs& a, bool vec);
 
 // Plain contraction over the row (token) axis of two row-major matrices of the
-// storage dtype, X [T x nx] and Y [T x ny]: E = X^T Y, computed in nSplit row
-// slices whose fp32 partials are written to e_part[nSplit][nx][ny] (the
-// caller adds them).  With T2 > 0 the contraction axis continues over the rows
-// of X2 [T2 x nx] and Y2 [T2 x ny], spread evenly over the same slices.  Needs
-// nx, ny multiples of 8, 16-byte aligned X, Y, X2, Y2 and e_part, and
-// slice_bytes < 2^31.
+// storage dtype, X [T x nx] and Y [T x ny] with row pitch ldy: E = X^T Y,
+// computed in nSplit row slices whose fp32 partials are written to
+// e_part[nSplit][nx][ny] (the caller adds them).  With dual, Y's rows hold a
+// second block of ny columns at column ny (ldy >= 2 ny) that adds into the same
+// E: E = X^T (Y[:, :ny] + Y[:, ny:2ny]).  With T2 > 0 the contraction axis
+// continues over the rows of X2 [T2 x nx] and Y2 [T2 x ny] (pitch ldy), spread
+// evenly over the same slices.  Needs nx, ny, ldy multiples of 8, 16-byte
+// aligned X, Y, X2, Y2 and e_part, and slice_bytes < 2^31.
 struct RowContractPlan {
   int nSplit = 0;            // row slices
   size_t bytes = 0;          // of e_part
   int64_t grid = 0;          // workgroups of the launch
   int64_t slice_bytes = 0;   // largest byte range one slice's buffer resource spans
 };
-RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny, int64_t T2 = 0);
-hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int dtype,
-                               float* e_part, hipStream_t stream, const void* X2 = nullptr,
+RowContractPlan row_contract_plan(int64_t T, int64_t nx, int64_t ny, int64_t T2, int64_t ldy);
+hipError_t launch_row_contract(const void* X, const void* Y, int64_t T, int64_t nx, int64_t ny, int64_t ldy, bool dual,
+                               int dtype, float* e_part, hipStream_t stream, const void* X2 = nullptr,
                                const void* Y2 = nullptr, int64_t T2 = 0);
 
 }  // namespace dora

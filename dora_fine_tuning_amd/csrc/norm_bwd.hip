@@ -13,16 +13,18 @@
 //   d_B                the norm's W stream with G' = s G, its accumulators
 //                      U + s B G stored and then scaled by s c_i (norm.hip);
 //   M                  the token-axis contraction kernel (lora_bwd.hip) over
-//                      the rows of B: B^T [Yhi | Ylo] = s B^T diag(c) B, in
+//                      the rows of B, its two Y panels Yhi and Ylo adding into
+//                      one accumulator: B^T (Yhi + Ylo) = s B^T diag(c) B, in
 //                      row slices;
 //   nbwd_finalize_m    Z = s (that r x r matrix), transposed, as Zhi | Zlo;
 //   d_A                the same contraction kernel, in one launch, over the
-//                      rows of W0 with [Yhi | Ylo] and then over the rows of A
-//                      with [Zhi | Zlo] (each row slice takes its share of
-//                      both): the contraction axis [out rows of W0 ; r rows of
+//                      rows of W0 with Yhi + Ylo and then over the rows of A
+//                      with Zhi + Zlo (each row slice takes its share of both;
+//                      each stage's W0 rows meet both halves, so W0 is read
+//                      once): the contraction axis [out rows of W0 ; r rows of
 //                      A] gives d_A^T in row slices;
-//   nbwd_finalize_a    sum of the slices and of the hi/lo halves, transposed
-//                      through LDS into d_A [r x in].
+//   nbwd_finalize_a    sum of the slices, transposed through LDS into
+//                      d_A [r x in].
 // The hi/lo pairs carry about 16 (bf16) or 22 (fp16) significant bits of the
 // computed operands Y and Z into the bf16/fp16 MFMAs; W0, A and B enter exactly.
 // Sizes or pointers the 16-byte path cannot take go to a general path of plain
@@ -70,8 +72,8 @@ __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* no
   }
 }
 
-// Z[l][j] = s * M'[j][l], M'[j][l] = sum over slices of E[j][l] + E[j][r + l]
-// (E = B^T [Yhi | Ylo], [nSplit][r][2r]), split into hi/lo at [l][j], [l][r + j].
+// Z[l][j] = s * M'[j][l], M'[j][l] = sum over slices of E[j][l]
+// (E = B^T (Yhi + Ylo), [nSplit][r][r]), split into hi/lo at [l][j], [l][r + j].
 // An 8 x 32 tile of (j, l) per workgroup, one element per thread: reads
 // coalesced along l, a transpose through LDS, then 16-byte runs along j per
 // row of Z.  The slices go in groups of 8, all 16 loads of a group in flight
@@ -83,20 +85,20 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
   __shared__ float tile[8][33];
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 8, l0 = static_cast<int64_t>(blockIdx.y) * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t slice = r * 2 * r;
+  const int64_t slice = r * r;
   {
     const int64_t j = j0 + ty, l = l0 + tx;
-    const float* Ej = E + (j < r && l < r ? j * 2 * r + l : 0);
+    const float* Ej = E + (j < r && l < r ? j * r + l : 0);
     float m = 0.0f;
     int p = 0;
     for (; p + 8 <= nSplit; p += 8) {
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = Ej[(p + u) * slice] + Ej[(p + u) * slice + r];
+      for (int u = 0; u < 8; ++u) v[u] = Ej[(p + u) * slice];
 #pragma unroll
       for (int u = 0; u < 8; ++u) m += v[u];
     }
-    for (; p < nSplit; ++p) m += Ej[p * slice] + Ej[p * slice + r];
+    for (; p < nSplit; ++p) m += Ej[p * slice];
     tile[ty][tx] = s * m;
   }
   __syncthreads();
@@ -111,8 +113,8 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
   }
 }
 
-// d_A[j][k] = sum over the slices of E[k][j] + E[k][r + j] (E [nParts][in][2r],
-// the slices added in order, each slice's hi and lo halves first), rounded once.
+// d_A[j][k] = sum over the slices of E[k][j] (E [nParts][in][r], the slices
+// added in order), rounded once.
 // A 32 x 32 tile of (k, j) per workgroup: coalesced reads along j, a transpose
 // through LDS, coalesced writes along k.
 template <int DT>
@@ -121,15 +123,15 @@ __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nPart
   __shared__ float tile[32][33];
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 32, j0 = static_cast<int64_t>(blockIdx.y) * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t slice = in * 2 * r;
+  const int64_t slice = in * r;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int kk = ty + 8 * q;
     const int64_t k = k0 + kk, j = j0 + tx;
     float v = 0.0f;
     if (k < in && j < r) {
-      const float* Ep = E + k * 2 * r + j;
-      for (int p = 0; p < nParts; ++p) v += Ep[p * slice] + Ep[p * slice + r];
+      const float* Ep = E + k * r + j;
+      for (int p = 0; p < nParts; ++p) v += Ep[p * slice];
     }
     tile[kk][tx] = v;
   }
@@ -260,15 +262,15 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   // d_B (the W stream's partials live in the big region until its finalize)
   e = launch_norm_bwd_db(p.np, a.W0, a.A, a.B, a.s, c, a.d_B, ws + p.off_np, big, a.stream);
   if (e != hipSuccess) return e;
-  // M = B^T [Yhi | Ylo] -> Z
-  e = launch_row_contract(a.B, Y, out, r, 2 * r, p.np.dtype, big, a.stream);
+  // M = B^T (Yhi + Ylo) -> Z
+  e = launch_row_contract(a.B, Y, out, r, r, 2 * r, true, p.np.dtype, big, a.stream);
   if (e != hipSuccess) return e;
   const dim3 mgrid(static_cast<unsigned>(ndiv(r, 8)), static_cast<unsigned>(ndiv(r, 32)));
   hipLaunchKernelGGL((nbwd_finalize_m<DT>), mgrid, dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, Z);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // d_A^T slices: the rows of W0 with Y, then (spread over the same slices) the rows of A with Z
-  e = launch_row_contract(a.W0, Y, out, in, 2 * r, p.np.dtype, big, a.stream, a.A, Z, r);
+  e = launch_row_contract(a.W0, Y, out, in, r, 2 * r, true, p.np.dtype, big, a.stream, a.A, Z, r);
   if (e != hipSuccess) return e;
   const dim3 fgrid(static_cast<unsigned>(ndiv(in, 32)), static_cast<unsigned>(ndiv(r, 32)));
   hipLaunchKernelGGL((nbwd_finalize_a<DT>), fgrid, dim3(256), 0, a.stream, big, p.rW.nSplit, in, r, a.d_A);
@@ -294,8 +296,8 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype, bo
     return p;
   }
   p.np = make_norm_plan(out, in, r, dtype, true);
-  p.rM = row_contract_plan(out, r, 2 * r);
-  p.rW = row_contract_plan(out, in, 2 * r, r);
+  p.rM = row_contract_plan(out, r, r, 0, 2 * r);
+  p.rW = row_contract_plan(out, in, r, r, 2 * r);
   size_t off = 0;
   p.off_np = off;
   off += al256(p.np.bytes);
