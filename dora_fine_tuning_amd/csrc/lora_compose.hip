@@ -174,6 +174,25 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
             tail ? kOob : ly + static_cast<uint32_t>(q * TL::NW * TL::RPI) * ld + kb);
   };
 
+  // The epilogue's base block: BM rows of BN*2 bytes, row t's logical 16-byte
+  // chunk c in slot c ^ (t % 32) (see the epilogue); DMA of rows [h*R, h*R + R),
+  // R = BM / NS, which land in ring slot h.
+  constexpr int EROWB = TL::BN * 2, ECPR = EROWB / 16, ERPI = 1024 / EROWB;
+  static_assert(ECPR == 32 && ERPI * EROWB == 1024, "base rows of 32 chunks, two per DMA instruction");
+  static_assert(TL::BM * EROWB == TL::NS * TL::STAGE_BYTES, "the base block fills the ring, one part per slot");
+  const __amdgpu_buffer_rsrc_t rbase = rsrc(a.base, m0, T, out, TL::BM);
+  auto issue_base = [&](int h) {
+    constexpr int QH = TL::BM / ERPI / TL::NS;  // DMA instructions per slot
+    const int erow = lane / ECPR, eslot = lane % ECPR;
+#pragma unroll
+    for (int q = h * QH + wave; q < (h + 1) * QH; q += TL::NW) {
+      const int row = q * ERPI + erow;
+      const int64_t col = n0 + 8 * (eslot ^ (row % ECPR));
+      const uint32_t off = col < out ? static_cast<uint32_t>((static_cast<int64_t>(row) * out + col) * 2) : kOob;
+      dma16(rbase, smem + q * 1024, off);
+    }
+  };
+
 #pragma unroll
   for (int u = 0; u < TL::NS - 1; ++u)
     if (u < S) issue(u, u);
@@ -187,6 +206,9 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
       lora_wait_younger<TL>(S - 1 - st);
       __builtin_amdgcn_s_barrier();
       if (st + TL::NS - 1 < S) issue(st + TL::NS - 1, (u + TL::NS - 1) % TL::NS);
+      // last stage: the slot of the one before it is free; its part of the
+      // base block comes in during this stage's MFMAs
+      if (TL::NS == 2 && st == S - 1 && S >= 2) issue_base((u + 1) % 2);
       const uint32_t so = static_cast<uint32_t>(u * TL::STAGE_BYTES);
 #pragma unroll
       for (int kp = 0; kp < TL::KS; kp += 2) {
@@ -227,9 +249,11 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   // read; the tile's base block (BM rows x BN columns, 2 bytes each) then goes
   // global -> LDS by DMA, all of it in flight at once (a lane loading its own
   // rows of base one at a time leaves too few loads in flight to cover the
-  // memory latency).  Row t of the block is BN*2 bytes, its logical 16-byte
-  // chunk c in slot c ^ (t % 32): the reads below, 32 rows at one logical
-  // chunk, then spread over the banks.  Columns past out read zero.  The
+  // memory latency); with two ring slots the part in the next-to-last stage's
+  // slot was issued during the last stage.  Row t of the block is BN*2 bytes,
+  // its logical 16-byte chunk c in slot c ^ (t % 32): the reads below, 32 rows
+  // at one logical chunk, then spread over the banks.  Columns past out read
+  // zero.  The
   // column scales (g - 1, g*s) sit after the ring.  A lane then walks its
   // TMW token rows; per row it needs 2*TN chunks of 8 columns (16 consecutive
   // columns c0 .. c0 + 15 per column tile j, whole chunks since out % 8 == 0),
@@ -239,19 +263,15 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   using T16 = typename Dt<DT>::T;
   T16* y = static_cast<T16*>(a.y);
   float* sc = reinterpret_cast<float*>(smem + TL::LDS_BYTES);  // [2][BN]: g - 1, then g*s
-  constexpr int EROWB = TL::BN * 2, ECPR = EROWB / 16, ERPI = 1024 / EROWB;
-  static_assert(ECPR == 32 && ERPI * EROWB == 1024, "base rows of 32 chunks, two per DMA instruction");
-  __syncthreads();
+  // every wave is past its last fragment read (each waited for its own LDS
+  // reads): a bare barrier, so the base loads already in flight keep flying
+  __builtin_amdgcn_s_barrier();
   {
-    const __amdgpu_buffer_rsrc_t rb = rsrc(a.base, m0, T, out, TL::BM);
-    const int erow = lane / ECPR, eslot = lane % ECPR;
-#pragma unroll 4
-    for (int q = wave; q < TL::BM / ERPI; q += TL::NW) {
-      const int row = q * ERPI + erow;
-      const int64_t col = n0 + 8 * (eslot ^ (row % ECPR));
-      const uint32_t off = col < out ? static_cast<uint32_t>((static_cast<int64_t>(row) * out + col) * 2) : kOob;
-      dma16(rb, smem + q * 1024, off);
-    }
+    // the parts not issued during the last stage (all of them when S < 2)
+    const int early = (TL::NS == 2 && S >= 2) ? (S - 2) % 2 : -1;
+#pragma unroll
+    for (int h = 0; h < TL::NS; ++h)
+      if (h != early) issue_base(h);
   }
   if (tid < TL::BN) {
     const int64_t c = n0 + tid;
