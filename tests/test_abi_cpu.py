@@ -300,7 +300,8 @@ def test_norm_bwd_workspace_is_factored():
     # O(out*r + in*r + r*r) scratch, well under the dense out x in transient
     # (V and dV in bf16) at every workload shape.  The row slices of the
     # contractions are sized for one workgroup per CU (256 CUs, 128-column
-    # blocks), which adds at most 2r * 4 bytes per row of 256 * 128 rows.
+    # blocks), which adds at most r * 4 bytes per row of 256 * 128 rows (the
+    # bound allows 2r * 4).
     for c in synth.CONFIGS.values():
         ws = LIB.dora_norm_bwd_workspace_bytes(c.out, c.in_, c.r, 0)
         dense = 2 * 2 * c.out * c.in_
