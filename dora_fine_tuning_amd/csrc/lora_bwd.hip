@@ -24,7 +24,8 @@
 //                     The epilogue forms sum_k B E over its rank block and
 //                     writes its E slice and its column partials.  The same
 //                     kernel without the base panel is the plain contraction
-//                     X^T Y over the rows of X and Y;
+//                     X^T Y over the rows of X and Y, optionally with two Y
+//                     column blocks (a hi/lo pair) adding into one accumulator;
 //   lora_bwd_finalize  d_mag from the partials (fp64) and d_B = g * s * (sum
 //                      of the E slices), both in a fixed order, one launch;
 //   lora_bwd_general  (general path) one thread per output column, all sums in

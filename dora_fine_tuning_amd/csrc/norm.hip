@@ -13,17 +13,21 @@
 //   gram_finalize     fixed-order sum of the partials, then G' = (s/2) G split
 //                     into two storage-dtype matrices G'hi + G'lo (written with
 //                     their mirror images);
-//   wstream_dma       (16-byte path) one pass over W0.  A workgroup owns 128 rows
-//   wstream_general   (general path) x a block of rank columns and a slice of the
-//                     augmented K axis
+//   wstream_k64       (16-byte path, rank tiles of 128, 256 and 384; 128-byte
+//   wstream_dma        row segments, DMA waves beside the MFMA waves) one pass
+//                     (16-byte path, rank tiles of 512; 64-byte segments)
+//   wstream_general   (general path) over W0.  A workgroup owns a block of rows
+//                     x a block of rank columns x a slice of the augmented K axis
 //                       [ W0 | B | B ] . [ A | G'hi | G'lo ]^T
 //                     so its accumulator holds U + B G' = U + (s/2) B G for those
 //                     rows and columns.  The epilogue reduces B_ij * acc_ij over
 //                     its columns, since 2s * sum_j B_ij (U + (s/2) B G)_ij =
 //                     cross_i + gram_i, and the W0 elements the waves read for
 //                     the MFMAs are also squared for the base term.  U is never
-//                     written to memory;
-//   norm_finalize     n_i = sqrt(max(sum of partials, 0)) in fp64, rounded to fp32.
+//                     written to memory.  On the 16-byte path the last
+//                     workgroup of each row block also finalizes its norms;
+//   norm_finalize     (general path) n_i = sqrt(max(sum of partials, 0)) in
+//                     fp64, rounded to fp32.
 //
 // All reductions are in fixed order, so the result is bitwise reproducible.
 #include <algorithm>
