@@ -8,8 +8,10 @@
 //   d_A   = s (c*B)^T W0 + s^2 (B^T diag(c) B) A
 //
 // and the out x in matrix B A is never formed.  Steps, in launch order:
-//   nbwd_prep          c_i (0 where n_i = 0) and Y = s c*B [out x r] as the
-//                      storage-dtype pair Yhi | Ylo [out x 2r];
+//   nbwd_absmax        (fp16 only) max |s c_i B_ij| for the operand scale
+//                      sigma, a power of two;
+//   nbwd_prep          c_i (0 where n_i = 0) and Y = sigma s c*B [out x r] as
+//                      the storage-dtype pair Yhi | Ylo [out x 2r];
 //   d_B                the norm's W stream with G' = s G, its accumulators
 //                      U + s B G stored and then scaled by s c_i (norm.hip);
 //   M                  the token-axis contraction kernel (lora_bwd.hip) over
@@ -23,8 +25,8 @@
 //                      each stage's W0 rows meet both halves, so W0 is read
 //                      once): the contraction axis [out rows of W0 ; r rows of
 //                      A] gives d_A^T in row slices;
-//   nbwd_finalize_a    sum of the slices, transposed through LDS into
-//                      d_A [r x in].
+//   nbwd_finalize_a    sum of the slices over sigma, transposed through LDS
+//                      into d_A [r x in].
 // The hi/lo pairs carry about 16 (bf16) or 22 (fp16) significant bits of the
 // computed operands Y and Z into the bf16/fp16 MFMAs; W0, A and B enter exactly.
 // Sizes or pointers the 16-byte path cannot take go to a general path of plain
@@ -43,13 +45,73 @@ namespace {
 __host__ __device__ inline int64_t ndiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// c_i = dn_i / n_i (0 where n_i == 0); Y_ij = s c_i B_ij split into
+// fp16 only (its exponent range is narrow): the operand Y = s c B is stored
+// times a power of two sigma that brings max |Y| into [1/2, 1), so a small
+// upstream gradient or an early-training B does not push the hi/lo pair into
+// fp16's subnormal range.  M' and Z then carry sigma too, and the d_A
+// finalize divides it out (exactly).  bf16 has fp32's exponent range and
+// takes sigma = 1.
+constexpr int kAbsMaxParts = 256;
+
+// max |s c_i B_ij| over a grid-stride share of the chunks, one value per
+// workgroup into part[blockIdx.x] (every workgroup writes its own slot).
+template <int DT>
+__global__ __launch_bounds__(256) void nbwd_absmax(const void* Bv, const float* norm, const float* d_norm, int64_t out,
+                                                   int64_t r, float s, float* part) {
+  __shared__ float red[256];
+  const Chunk* B = static_cast<const Chunk*>(Bv);
+  const int64_t n = out * r / 8;
+  float m = 0.0f;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t i = (e * 8) / r;
+    const float ni = norm[i];
+    const float ci = ni != 0.0f ? d_norm[i] / ni : 0.0f;
+    float f[8];
+    chunk_to_f32<DT>(B[e], f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf((s * ci) * f[q]));
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// sigma = 2^-e for max = f 2^e, f in [1/2, 1), e clamped to [-64, 64]; 1 for a
+// zero or non-finite max
+__device__ inline float operand_scale(float mx) {
+  if (!(mx > 0.0f) || !isfinite(mx)) return 1.0f;
+  int e;
+  frexpf(mx, &e);
+  return ldexpf(1.0f, -std::min(64, std::max(-64, e)));  // 2^-64 .. 2^64 keeps d_A sigma finite in fp32
+}
+
+// c_i = dn_i / n_i (0 where n_i == 0); Y_ij = sigma s c_i B_ij split into
 // hi = round(Y), lo = round(Y - hi), stored at [i][j] and [i][r + j].  One
 // 16-byte chunk (8 elements of one row, r % 8 == 0) per thread and step.
+// sigma comes from the nparts workgroup maxima in part (nparts == 0:
+// sigma = 1); the first workgroup stores it in sigma_out.
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* norm, const float* d_norm, int64_t out,
-                                                 int64_t r, float s, float* c, void* Yv) {
+                                                 int64_t r, float s, const float* part, int nparts, float* sigma_out,
+                                                 float* c, void* Yv) {
   using T = typename Dt<DT>::T;
+  __shared__ float red[256];
+  float sigma = 1.0f;
+  if (nparts > 0) {  // every workgroup reduces the (at most 256) maxima itself
+    red[threadIdx.x] = static_cast<int>(threadIdx.x) < nparts ? part[threadIdx.x] : 0.0f;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+      __syncthreads();
+    }
+    sigma = operand_scale(red[0]);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) sigma_out[0] = sigma;
   const Chunk* B = static_cast<const Chunk*>(Bv);
   T* Y = static_cast<T*>(Yv);
   const int64_t n = out * r / 8;
@@ -63,7 +125,7 @@ __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* no
     chunk_to_f32<DT>(B[e], f);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float y = (s * ci) * f[q];
+      const float y = ((s * ci) * f[q]) * sigma;  // sigma is a power of two: exact
       hi[q] = Dt<DT>::to_f(Dt<DT>::from_f(y));
       lo[q] = y - hi[q];
     }
@@ -113,12 +175,13 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
   }
 }
 
-// d_A[j][k] = sum over the slices of E[k][j] (E [nParts][in][r], the slices
-// added in order), rounded once.
+// d_A[j][k] = (sum over the slices of E[k][j]) / sigma (E [nParts][in][r],
+// the slices added in order; sigma a power of two), rounded once.
 // A 32 x 32 tile of (k, j) per workgroup: coalesced reads along j, a transpose
 // through LDS, coalesced writes along k.
 template <int DT>
-__global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nParts, int64_t in, int64_t r, void* dAv) {
+__global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nParts, int64_t in, int64_t r,
+                                                       const float* sigma, void* dAv) {
   using T = typename Dt<DT>::T;
   __shared__ float tile[32][33];
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 32, j0 = static_cast<int64_t>(blockIdx.y) * 32;
@@ -132,6 +195,7 @@ __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nPart
     if (k < in && j < r) {
       const float* Ep = E + k * r + j;
       for (int p = 0; p < nParts; ++p) v += Ep[p * slice];
+      v /= sigma[0];
     }
     tile[kk][tx] = v;
   }
@@ -255,8 +319,18 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   void* Y = ws + p.off_y;
   void* Z = ws + p.off_z;
   float* big = reinterpret_cast<float*>(ws + p.off_big);
+  float* part = reinterpret_cast<float*>(ws + p.off_sigma);  // kAbsMaxParts maxima, then sigma
+  float* sigma = part + kAbsMaxParts;
+  int nparts = 0;
+  if (DT == 1) {
+    nparts = static_cast<int>(std::min<int64_t>(kAbsMaxParts, ndiv(out * r / 8, 256)));
+    hipLaunchKernelGGL((nbwd_absmax<DT>), dim3(static_cast<unsigned>(nparts)), dim3(256), 0, a.stream, a.B, a.norm,
+                       a.d_norm, out, r, a.s, part);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL((nbwd_prep<DT>), stride_grid(out * r / 8), dim3(256), 0, a.stream, a.B, a.norm, a.d_norm, out, r,
-                     a.s, c, Y);
+                     a.s, part, nparts, sigma, c, Y);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // d_B (the W stream's partials live in the big region until its finalize)
@@ -273,7 +347,7 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   e = launch_row_contract(a.W0, Y, out, in, r, 2 * r, true, p.np.dtype, big, a.stream, a.A, Z, r);
   if (e != hipSuccess) return e;
   const dim3 fgrid(static_cast<unsigned>(ndiv(in, 32)), static_cast<unsigned>(ndiv(r, 32)));
-  hipLaunchKernelGGL((nbwd_finalize_a<DT>), fgrid, dim3(256), 0, a.stream, big, p.rW.nSplit, in, r, a.d_A);
+  hipLaunchKernelGGL((nbwd_finalize_a<DT>), fgrid, dim3(256), 0, a.stream, big, p.rW.nSplit, in, r, sigma, a.d_A);
   return hipGetLastError();
 }
 
@@ -303,6 +377,8 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype, bo
   off += al256(p.np.bytes);
   p.off_c = off;
   off += al256(static_cast<size_t>(out) * 4);
+  p.off_sigma = off;  // the operand scale's workgroup maxima and the scale itself
+  off += al256(static_cast<size_t>(kAbsMaxParts + 1) * 4);
   p.off_y = off;
   off += al256(static_cast<size_t>(out) * 2 * r * 2);
   p.off_z = off;

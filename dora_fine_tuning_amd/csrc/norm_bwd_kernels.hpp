@@ -19,7 +19,7 @@ struct NormBwdPlan {
   bool vec = true;  // 16-byte MFMA path; else the general path (c, G, M in the workspace)
   NormPlan np;
   RowContractPlan rM, rW;  // B^T Y; [W0 ; A]^T [Y ; Z]
-  size_t off_np = 0, off_c = 0, off_y = 0, off_z = 0, off_big = 0, bytes = 0;
+  size_t off_np = 0, off_c = 0, off_sigma = 0, off_y = 0, off_z = 0, off_big = 0, bytes = 0;
   int64_t max_grid = 0, max_slice_bytes = 0;
 };
 

@@ -167,6 +167,27 @@ def test_norm_bwd_zero_norm_rows_and_determinism(lib):
     assert torch.equal(d_A, d_A2) and torch.equal(d_B, d_B2), "repeated calls differ"
 
 
+@pytest.mark.parametrize("w0_sd, b_sd, dn_sd", [(0.02, 1e-3, 1e-4), (0.1, 1e-3, 4e-3)],
+                         ids=["small_dnorm", "subnormal_Y_normal_dA"])
+def test_norm_bwd_fp16_small_operands(lib, w0_sd, b_sd, dn_sd):
+    """fp16 with a small upstream gradient and an early-training B: s*c*B lies
+    in fp16's subnormal range (|s c B| ~ 1e-6 .. 1e-5), where a hi/lo pair of
+    the unscaled value keeps only a few bits.  In the second case d_A stays in
+    fp16's normal range, so a loss of the operand's bits shows in the output."""
+    out, in_, r = 4096, 264, 64
+    rng = np.random.default_rng(3900)
+    to = lambda a: synth.to_dtype(a.astype(np.float32), "fp16")
+    W0 = to(rng.normal(0, w0_sd, (out, in_)))
+    A = to(rng.normal(0, 1 / np.sqrt(in_), (r, in_)))
+    B = to(rng.normal(0, b_sd, (out, r)))
+    s = float(np.float32(32.0 / np.sqrt(r)))
+    d_norm = (rng.standard_normal(out) * dn_sd).astype(np.float32)
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    c = d_norm.astype(np.float64) / norm
+    log(f"norm_bwd fp16 small operands: max |s c B| {np.max(np.abs(s * c[:, None] * f64(B))):.2e}")
+    check(lib, W0, A, B, s, d_norm, norm, "fp16", f"fp16 small operands w0 {w0_sd} B {b_sd} dn {dn_sd}")
+
+
 def test_norm_bwd_b_zero(lib):
     # B = 0 (DoRA's initialisation): d_A = 0 exactly, d_B = s c W0 A^T
     log("norm_bwd B = 0")
