@@ -1062,6 +1062,15 @@ __global__ __launch_bounds__(TL::NT, 1) void wstream_k64(WArgs a) {
   const uint32_t ldA = static_cast<uint32_t>(in) * 2u, ldB = static_cast<uint32_t>(r) * 2u;
   const uint32_t lxA = static_cast<uint32_t>(prow) * ldA + kc * 2u, lxB = static_cast<uint32_t>(prow) * ldB + kc * 2u;
   const uint32_t lyA = static_cast<uint32_t>(yr0) * ldA + kc * 2u, lyB = static_cast<uint32_t>(yr0) * ldB + kc * 2u;
+  // smallest rank (within the tile) among the eight panel rows of A-panel
+  // instruction q: rows 8m .. 8m + 7 of a 32-row tile hold ranks 4m .. 4m + 3
+  // and 16 + 4m .. 16 + 4m + 3
+  int a_rank0[TL::YQ];
+#pragma unroll
+  for (int q = 0; q < TL::YQ; ++q) {
+    const int p0 = 8 * (q * TL::NDMA + dw);
+    a_rank0[q] = (p0 & ~31) + 4 * ((p0 & 31) >> 3);
+  }
 
   // Fragment reads: lane l reads row 32*i + l%32 of its wave's tiles at
   // logical chunk 2*step + l/32, stored at chunk (2*step + l/32) ^ ((l%32)/2 % 8).
@@ -1093,11 +1102,14 @@ __global__ __launch_bounds__(TL::NT, 1) void wstream_k64(WArgs a) {
   const int dkrem_ = (dw_ ? in : r) - dkst_ * TL::BK;                                    \
   const uint32_t dkb_ = static_cast<uint32_t>(dkst_) * static_cast<uint32_t>(TL::ROWB);  \
   const bool doob_ = dst_ >= st1 || (dkrem_ < TL::BK && kc >= dkrem_);
-  // DMA of the A (rank-side) panel of stage ST into A slot SA
+  // DMA of the A (rank-side) panel of stage ST into A slot SA; an instruction
+  // whose eight panel rows all hold ranks past r is not issued (its LDS rows
+  // only feed accumulator columns past r, which no epilogue reads)
 #define K64_ISSUE_A(ST, SA)                                                              \
   {                                                                                      \
     K64_SEL(ST)                                                                          \
     _Pragma("unroll") for (int q = 0; q < TL::YQ; ++q) {                                 \
+      if (n0 + a_rank0[q] >= r) continue;                                                \
       const uint32_t o_ = dly_ + static_cast<uint32_t>(q * TL::NDMA * TL::RPI) * dld_ + dkb_; \
       dma16(dry_, smem + TL::A_OFF + (SA) * TL::A_BYTES + (q * TL::NDMA + dw) * 1024, doob_ ? kOob : o_); \
     }                                                                                    \
@@ -1546,6 +1558,7 @@ hipError_t launch_gram_t(const NormPlan& p, const void* Av, float scale, char* w
 
 template <int DT>
 hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
+  if (vec && p.strip) return launch_norm_strip(p, a);
   char* ws = static_cast<char*>(a.ws);
   using T = typename Dt<DT>::T;
   T* ghi = reinterpret_cast<T*>(ws + p.off_ghi);
@@ -1663,7 +1676,7 @@ int64_t norm_max_grid(const NormPlan& p) {
   const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
   const int64_t gram = p.r > 0 ? std::max(cdiv(nUpper * p.splitG, 8) * 8, gram_finalize_blocks(p.r)) : 0;
   const int64_t stream = cdiv(p.nRB * p.nTiles * p.nSplit, 8) * 8;
-  return std::max({gram, stream, cdiv(p.out, 256)});
+  return std::max({gram, stream, cdiv(p.out, 256), p.strip ? cdiv_strip(p.out) : int64_t(0)});
 }
 
 NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec) {
@@ -1754,6 +1767,7 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
     --p.nSplit;
     layout();
   }
+  p.strip = vec && norm_strip_fits(out, in, r);
   return p;
 }
 

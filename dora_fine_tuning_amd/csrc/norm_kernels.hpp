@@ -26,11 +26,22 @@ struct NormPlan {
   // one K split and no fp32 partial region: the Gram kernel writes G'hi/G'lo
   // directly (chosen when the partials would not fit the scratch bound)
   bool gram_direct = false;
+  // small adapter (r <= kStripMaxRank, enough row strips): one launch of the
+  // strip kernel, each workgroup taking 32 rows over the whole input axis and
+  // forming the Gram matrix itself; no workspace is used
+  bool strip = false;
   // workspace byte offsets
   size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, off_count = 0, bytes = 0;
 };
 
 NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec);
+
+// The strip kernel (16-byte path): ranks up to 32, at least kStripMinBlocks
+// strips of 32 rows, panels within 32-bit buffer offsets.
+constexpr int64_t kStripMaxRank = 32;
+constexpr int64_t kStripMinBlocks = 128;
+inline int64_t cdiv_strip(int64_t out) { return (out + 31) / 32; }
+bool norm_strip_fits(int64_t out, int64_t in, int64_t r);
 
 // Largest grid (workgroups in one dimension) the launches of this plan use.
 int64_t norm_max_grid(const NormPlan& p);
@@ -55,6 +66,7 @@ struct NormArgs {
 };
 
 hipError_t launch_norm(const NormPlan& p, const NormArgs& a);
+hipError_t launch_norm_strip(const NormPlan& p, const NormArgs& a);
 
 // sq[i] = ||W0_i||^2 in fp32 (vec: in % 8 == 0 and W0 16-byte aligned); grid cdiv(out, 4).
 hipError_t launch_row_sqnorm(const void* W0, int64_t out, int64_t in, int dtype, bool vec, float* sq,
