@@ -92,11 +92,12 @@ def test_norm_strip_large_adapter(lib, dtype):
     PU.assert_norm(n_gpu, ref, PU.norm_term_mass(W, Af, Bf, cfg.s), f"strip big B {dtype}")
 
 
-def test_norm_strip_exact_cancellation(lib):
+@pytest.mark.parametrize("r", [24, 40])
+def test_norm_strip_exact_cancellation(lib, r):
     """W0 = -s B A with dyadic entries (every product and sum exact): n = 0 on
     those rows and the known residual on every third row."""
-    rng = np.random.default_rng(17)
-    out, in_, r, s = 4101, 136, 40, 2.0
+    rng = np.random.default_rng(17 + r)
+    out, in_, s = 4101, 136, 2.0
     A = rng.choice([-1.0, -0.5, 0.0, 0.5, 1.0], size=(r, in_))
     B = rng.choice([-0.25, 0.0, 0.25, 0.5], size=(out, r))
     W0 = -s * (B @ A)
@@ -106,12 +107,13 @@ def test_norm_strip_exact_cancellation(lib):
     n_gpu = f64(lib.dora_norm_factored(t(W0).to(DEV), t(A).to(DEV), t(B).to(DEV), s))
     ref = O.weight_norm(W0, A, B, s)
     np.testing.assert_array_equal(ref[1::3], 0.0)
-    PU.assert_norm(n_gpu, ref, PU.norm_term_mass(W0, A, B, s), "strip cancellation")
+    PU.assert_norm(n_gpu, ref, PU.norm_term_mass(W0, A, B, s), f"strip cancellation r {r}")
     np.testing.assert_allclose(n_gpu[::3], np.sqrt(in_ * 2.0**-6), rtol=1e-6)
 
 
-def test_norm_strip_b_zero_is_plain_row_norm(lib):
-    cfg = synth.custom("strip_bzero", 4096, 1024, 64, 1)
+@pytest.mark.parametrize("r", [16, 64])
+def test_norm_strip_b_zero_is_plain_row_norm(lib, r):
+    cfg = synth.custom("strip_bzero", 4096, 1024, r, 1)
     W0, A, B = synth.weights(cfg)
     n_gpu = f64(lib.dora_norm_factored(W0.to(DEV), A.to(DEV), torch.zeros_like(B).to(DEV), cfg.s))
     np.testing.assert_allclose(n_gpu, np.linalg.norm(f64(W0), axis=1), rtol=1e-6)
