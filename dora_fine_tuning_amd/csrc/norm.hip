@@ -1024,6 +1024,12 @@ __global__ __launch_bounds__(TL::NT, 1) void wstream_k64(WArgs a) {
   const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
   const int S1 = static_cast<int>(a.sm.S1), S12 = S1 + static_cast<int>(a.sm.S2);
   const int st0 = static_cast<int>(a.S * sp / a.nSplit), st1 = static_cast<int>(a.S * (sp + 1) / a.nSplit);
+  // The W0 stages of the slice go in a rotated order, by a different amount
+  // for each row block: the row blocks of a split then read different column
+  // offsets at any moment rather than all the same one (which cost about a
+  // quarter of the stream's rate).  The Gram stages stay last, in order.
+  const int nW = std::max(0, std::min(st1, S1) - st0);
+  const int rot = nW > 0 ? static_cast<int>((rb * 37u) % static_cast<uint32_t>(nW)) : 0;
   const int in = static_cast<int>(a.sm.in), r = static_cast<int>(a.sm.r);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1093,7 +1099,9 @@ __global__ __launch_bounds__(TL::NT, 1) void wstream_k64(WArgs a) {
   // the segment of stage st: resources, row pitch, per-lane offsets, K offset
   // and whether this lane's chunk lies past the segment (or the stage past st1)
 #define K64_SEL(ST)                                                                      \
-  const int dst_ = (ST);                                                                 \
+  const int dstep_ = (ST);                                                               \
+  const int drw_ = dstep_ - st0 + rot;                                                   \
+  const int dst_ = dstep_ - st0 < nW ? st0 + (drw_ < nW ? drw_ : drw_ - nW) : dstep_;    \
   const bool dw_ = dst_ < S1, dh_ = dst_ < S12;                                          \
   const __amdgpu_buffer_rsrc_t drx_ = dw_ ? rxW : rxB;                                   \
   const __amdgpu_buffer_rsrc_t dry_ = dw_ ? ryA : (dh_ ? ryH : ryL);                     \
@@ -1101,7 +1109,7 @@ __global__ __launch_bounds__(TL::NT, 1) void wstream_k64(WArgs a) {
   const int dkst_ = dst_ - (dw_ ? 0 : (dh_ ? S1 : S12));                                 \
   const int dkrem_ = (dw_ ? in : r) - dkst_ * TL::BK;                                    \
   const uint32_t dkb_ = static_cast<uint32_t>(dkst_) * static_cast<uint32_t>(TL::ROWB);  \
-  const bool doob_ = dst_ >= st1 || (dkrem_ < TL::BK && kc >= dkrem_);
+  const bool doob_ = dstep_ >= st1 || (dkrem_ < TL::BK && kc >= dkrem_);
   // DMA of the A (rank-side) panel of stage ST into A slot SA; an instruction
   // whose eight panel rows all hold ranks past r is not issued (its LDS rows
   // only feed accumulator columns past r, which no epilogue reads)
