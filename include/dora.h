@@ -120,7 +120,10 @@ DORA_API size_t dora_norm_workspace_bytes(int64_t out, int64_t in, int64_t r, in
  * (summary page, paragraph on the factored norm).  U and G are dense MFMA
  * contractions with fp32 accumulation; U never leaves the registers.  A
  * negative sum from rounding is clamped to 0.  The norm is a plain value: the
- * backward of the compose treats it as a constant.
+ * backward of the compose treats it as a constant.  With in and r multiples of
+ * 8, 16-byte aligned matrices, r <= 32 and out >= 4065 the call is a single
+ * launch that forms G itself and leaves ws untouched; the workspace query
+ * does not depend on this.
  *
  * W0, A, B: device, dtype.  A and B may be NULL when r == 0.  norm_out: device
  * fp32 [out].  ws: device scratch of at least dora_norm_workspace_bytes(...)
