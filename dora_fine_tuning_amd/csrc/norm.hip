@@ -1453,13 +1453,35 @@ __device__ inline double ordered_sum(const float* p, int n, int64_t stride) {
 }
 
 // n_i from the partials; the base term from base_sq[i] when a cache is given.
+// Up to kFinParts partials of each sum are loaded before either is added (one
+// memory round trip for both sums); the additions keep split order.
+constexpr int kFinParts = 16;
 __global__ __launch_bounds__(256) void norm_finalize(const float* base_part, const float* cross_part,
                                                      const float* base_sq, int nSplit, int nTiles, int64_t out,
                                                      float s, float* norm_out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= out) return;
-  const double b = base_sq ? static_cast<double>(base_sq[i]) : ordered_sum(base_part + i, nSplit, out);
-  const double c = ordered_sum(cross_part + i, nSplit * nTiles, out);
+  const int nc = nSplit * nTiles;
+  double b, c;
+  if (nSplit <= kFinParts && nc <= kFinParts) {
+    float vb[kFinParts], vc[kFinParts];
+    const float bq = base_sq ? base_sq[i] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < kFinParts; ++q) {
+      vb[q] = !base_sq && q < nSplit ? base_part[i + static_cast<int64_t>(q) * out] : 0.0f;
+      vc[q] = q < nc ? cross_part[i + static_cast<int64_t>(q) * out] : 0.0f;
+    }
+    b = static_cast<double>(bq);
+    c = 0.0;
+#pragma unroll
+    for (int q = 0; q < kFinParts; ++q) {
+      if (q < nSplit) b += static_cast<double>(vb[q]);
+      if (q < nc) c += static_cast<double>(vc[q]);
+    }
+  } else {
+    b = base_sq ? static_cast<double>(base_sq[i]) : ordered_sum(base_part + i, nSplit, out);
+    c = ordered_sum(cross_part + i, nc, out);
+  }
   const double n2 = b + 2.0 * static_cast<double>(s) * c;
   norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
 }
