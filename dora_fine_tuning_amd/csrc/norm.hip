@@ -266,6 +266,9 @@ struct WArgs {
   float s = 0.0f;
 };
 
+// Partials per sum that the finalizes load all at once before adding them.
+constexpr int kFinParts = 8;
+
 // sum_{q < n} p[q * stride] in fp64, in order, each load at device scope (it
 // reads through this XCD's L2 to the device-coherent level, so it sees the
 // partials that workgroups on other XCDs wrote through with device-scope
@@ -601,8 +604,34 @@ __device__ inline void dma_cross_epilogue(const WArgs& a, int sp, int nt, int64_
   __syncthreads();
   if (*flag && tid < TL::BM && m0 + tid < out) {
     const int64_t i = m0 + tid;
-    const double b = a.base_sq ? static_cast<double>(a.base_sq[i]) : ordered_sum_device(a.base_part + i, a.nSplit, out);
-    const double c = ordered_sum_device(a.cross_part + i, a.nSplit * a.nTiles, out);
+    const int nc = a.nSplit * a.nTiles;
+    double b, c;
+    if (a.nSplit <= kFinParts && nc <= kFinParts) {
+      // every partial of both sums in flight before the first addition (one
+      // round trip to the device-coherent level); the additions keep split order
+      // (unconditional loads of clamped indices: a load under a condition
+      // would be waited for on its own)
+      float vb[kFinParts], vc[kFinParts];
+      const float* bp = a.base_sq ? a.base_sq + i : a.base_part + i;
+      const int nb = a.base_sq ? 1 : a.nSplit;
+#pragma unroll
+      for (int q = 0; q < kFinParts; ++q) {
+        vb[q] = __hip_atomic_load(bp + static_cast<int64_t>(q < nb ? q : nb - 1) * out, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        vc[q] = __hip_atomic_load(a.cross_part + i + static_cast<int64_t>(q < nc ? q : nc - 1) * out,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      b = 0.0;
+      c = 0.0;
+#pragma unroll
+      for (int q = 0; q < kFinParts; ++q) {
+        b += q < nb ? static_cast<double>(vb[q]) : 0.0;
+        c += q < nc ? static_cast<double>(vc[q]) : 0.0;
+      }
+    } else {
+      b = a.base_sq ? static_cast<double>(a.base_sq[i]) : ordered_sum_device(a.base_part + i, a.nSplit, out);
+      c = ordered_sum_device(a.cross_part + i, nc, out);
+    }
     const double n2 = b + 2.0 * static_cast<double>(a.s) * c;
     a.norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
   }
@@ -1455,7 +1484,6 @@ __device__ inline double ordered_sum(const float* p, int n, int64_t stride) {
 // n_i from the partials; the base term from base_sq[i] when a cache is given.
 // Up to kFinParts partials of each sum are loaded before either is added (one
 // memory round trip for both sums); the additions keep split order.
-constexpr int kFinParts = 16;
 __global__ __launch_bounds__(256) void norm_finalize(const float* base_part, const float* cross_part,
                                                      const float* base_sq, int nSplit, int nTiles, int64_t out,
                                                      float s, float* norm_out) {
