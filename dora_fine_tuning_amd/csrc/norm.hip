@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void gram_finalize(const float* gpart, int spl
   float g = 0.0f;
   // groups of up to kFinSplits partials, all loaded before they are summed
   // pairwise; the groups are added in order
-  constexpr int kFinSplits = 16;
+  constexpr int kFinSplits = 32;
   for (int s0 = 0; s0 < splitG; s0 += kFinSplits) {
     float a[kFinSplits];
 #pragma unroll
@@ -1784,13 +1784,15 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
   }
   if (r > 0) {
     // Gram: upper tiles (64x64 on the 16-byte path, 32x32 otherwise) x K
-    // splits; about 512 workgroups, at least 4 K stages of
-    // 64 (general path: 8 K steps of 16 per wave) per workgroup
+    // splits; about 512 workgroups, at most 32 splits with at least 2 K
+    // stages of 64 per workgroup (general path: 16 splits, 8 K steps of 16
+    // per wave).  At small r the few upper tiles need the splits: r = 64 and
+    // 128 at in = 8192 take 32 splits (1.4 us faster than 16).
     const int64_t tile = vec ? 64 : 32;
     p.nTg = static_cast<int>(cdiv(r, tile));
     const int64_t nUpper = static_cast<int64_t>(p.nTg) * (p.nTg + 1) / 2;
-    const int64_t max_split = std::max<int64_t>(1, vec ? cdiv(in, 64) / 4 : cdiv(in, 16) / (4 * 8));
-    int64_t sg = std::max<int64_t>(1, std::min<int64_t>({cdiv(512, nUpper), 16, max_split}));
+    const int64_t max_split = std::max<int64_t>(1, vec ? cdiv(in, 64) / 2 : cdiv(in, 16) / (4 * 8));
+    int64_t sg = std::max<int64_t>(1, std::min<int64_t>({cdiv(512, nUpper), vec ? 32 : 16, max_split}));
     if (sg >= 8) sg = sg / 8 * 8;  // whole K splits per XCD
     p.splitG = static_cast<int>(sg);
   }
