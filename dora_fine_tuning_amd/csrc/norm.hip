@@ -14,9 +14,9 @@
 //                     into two storage-dtype matrices G'hi + G'lo (written with
 //                     their mirror images);
 //   wstream_k64       (16-byte path, rank tiles of 128, 256 and 384; 128-byte
-//   wstream_dma        row segments, DMA waves beside the MFMA waves) one pass
-//                     (16-byte path, rank tiles of 512; 64-byte segments)
-//   wstream_general   (general path) over W0.  A workgroup owns a block of rows
+//   wstream_general    row segments, DMA waves beside the MFMA waves; general
+//                     path: register-staged loads) one pass per rank tile
+//                     over W0.  A workgroup owns a block of rows
 //                     x a block of rank columns x a slice of the augmented K axis
 //                       [ W0 | B | B ] . [ A | G'hi | G'lo ]^T
 //                     so its accumulator holds U + B G' = U + (s/2) B G for those
@@ -356,71 +356,7 @@ __device__ inline void cross_epilogue(const WArgs& a, int sp, int nt, int64_t m0
 }
 
 // ---------------------------------------------------------------------------
-// W stream, 16-byte path: direct global -> LDS loads through buffer resources.
-//
-// Workgroup tile: 32*TM W0 rows x 128*TN rank columns, K stages of 32.  The
-// NW = WM*4 waves form a WM x 4 grid (WM along the rows, 4 along the rank
-// axis); a wave owns TMW = TM/WM row tiles x TN rank tiles of 32 and keeps
-// their accumulators in registers.  Every workgroup reads the whole rank panel
-// once per K stage; the taller the tile, the fewer times that panel is re-read
-// from L2 for the same W0 rows.  A stage holds one 64-byte segment of each
-// panel row; one wave instruction moves 16 rows x 64 bytes, lane l writing
-// bytes [16l, 16l + 16) of that 1 KiB block.  Lane l fetches the logical
-// 16-byte chunk (l%4) ^ ((row>>2)&3) of its row, so the LDS slot of logical
-// chunk c in row m is c ^ ((m>>2)&3): the fragment reads of 16 consecutive
-// rows then hit 16 distinct bank groups.  Rows past the operand lie beyond the
-// buffer resource's range and K chunks past its end get an out-of-range
-// offset; the hardware writes zeros to LDS for both.  NS stages rotate through
-// LDS; a stage is waited for with s_waitcnt vmcnt once the loads of the NS-2
-// younger stages are in flight.
-template <int TN_, int TM_, int NS_, int WM_, int BK_>
-struct DmaTile {
-  static constexpr int TN = TN_, TM = TM_, NS = NS_, WM = WM_, BK = BK_;
-  static constexpr int WN = 4, NW = WM * WN, NT = NW * 64;
-  static constexpr int TMW = TM / WM;  // 32-row W0 tiles per wave
-  static constexpr int BM = 32 * TM, BN = 128 * TN;
-  static constexpr int KS = BK / 16;    // MFMA K steps per stage
-  static constexpr int CPR = BK / 8;    // 16-byte chunks per LDS row
-  static constexpr int ROWB = BK * 2;   // bytes per LDS row
-  static constexpr int RPI = 64 / CPR;  // rows per 1 KiB DMA instruction
-  static constexpr int SWP = 16 / CPR;  // consecutive rows sharing one chunk swizzle
-  static constexpr int X_BYTES = BM * ROWB, Y_BYTES = BN * ROWB;
-  static constexpr int STAGE_BYTES = X_BYTES + Y_BYTES;
-  static constexpr int XI = BM / RPI, YI = BN / RPI;   // DMA instructions per stage and panel
-  static constexpr int XQ = XI / NW, YQ = YI / NW;     // per wave
-  static constexpr int L = XQ + YQ;
-  static constexpr int NPAIR = TMW * KS;               // (tile, K step) fragment pairs per stage
-  static constexpr int NP = (NPAIR + WN - 1) / WN;     // pairs each rank-axis wave squares
-  // epilogue: B tile passes of RPP rows in the stage area, row sums after them
-  static constexpr int AREA = NS * STAGE_BYTES;
-  static constexpr int LDS_BYTES = AREA;
-  static constexpr int RED_BYTES = 2 * WN * BM * 4;    // cross and base row sums per rank-axis wave
-  static constexpr int RPP_FIT = (AREA - RED_BYTES) / (BN * 2) / 32 * 32;
-  static constexpr int RPP = RPP_FIT < BM ? RPP_FIT : BM;
-  static constexpr int RED_OFF = AREA - RED_BYTES;
-  static_assert(BK == 32, "K stages of 32: 64-byte DMA row segments, two MFMA K steps");
-  static_assert(TM % WM == 0, "row tiles split over the waves");
-  static_assert(TMW <= 4 && TN <= 4, "a stage reads at most four fragments per panel and K step");
-  static_assert(XI % NW == 0 && YI % NW == 0, "panels split into whole DMA groups per wave");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(RPP >= 32 && RPP * BN * 2 <= RED_OFF, "epilogue B-tile pass fits beside the row sums");
-  static_assert(NS >= 3 && NS <= 8 && (NS - 2) * L < 64, "ring depth and vmcnt range");
-};
-
-
-// Wait for a stage's DMA while the n younger stages already issued (at most
-// NS-2, each L loads per wave) stay in flight; n is wave-uniform.
-template <class TL, int N = TL::NS - 2>
-__device__ inline void wait_younger(int n) {
-  if constexpr (N == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (n >= N)
-      wait_vmcnt<N * TL::L>();
-    else
-      wait_younger<TL, N - 1>(n);
-  }
-}
+// Epilogues shared by the W stream's 16-byte path (wstream_k64, below).
 
 // Epilogue of the 16-byte path for the norm backward: the workgroup's split-K
 // partial of U + B G' itself, written to acc_part[sp][row][col] in fp32.  Lane
@@ -775,231 +711,14 @@ __global__ __launch_bounds__(256) void gram_dma(const typename Dt<DT>::T* A, int
   }
 }
 
-// MFMAs of one K step, rank fragments as the first operand.
-#define DORA_STEP_MFMAS(X, Y)                                                                           \
-  _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) \
-      acc[i][j] = Dt<DT>::mfma32(__builtin_bit_cast(V8, Y[j]), __builtin_bit_cast(V8, X[i]), acc[i][j]);
-
-// Base-term squares of K step C.  The TMW*KS (row tile, K step) fragment pairs
-// of a stage are dealt to the WN waves that share them: wave wn squares pair
-// p = wn + WN*t into bs[t] (pair p is tile p/KS, step p%KS).  wn is
-// wave-uniform, so the selection is a scalar branch.
-#define DORA_STEP_SQUARES(X, C)                                            \
-  _Pragma("unroll") for (int t = 0; t < TL::NP; ++t)                       \
-    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i)                    \
-      if (wn + TL::WN * t == TL::KS * i + (C)) {                           \
-        bs[t] = sq2<DT>(X[i][0], bs[t]);                                   \
-        bs[t] = sq2<DT>(X[i][1], bs[t]);                                   \
-        bs[t] = sq2<DT>(X[i][2], bs[t]);                                   \
-        bs[t] = sq2<DT>(X[i][3], bs[t]);                                   \
-      }
-
-// N fragment reads from one base register at compile-time offsets SI + STEP*i.
-#define DORA_READS(V, BASE, SI, STEP, N)                                        \
-  V[0] = lds_read16_at<(SI)>(BASE);                                             \
-  if constexpr ((N) > 1) V[1] = lds_read16_at<(SI) + (STEP)>(BASE);             \
-  if constexpr ((N) > 2) V[2] = lds_read16_at<(SI) + 2 * (STEP)>(BASE);         \
-  if constexpr ((N) > 3) V[3] = lds_read16_at<(SI) + 3 * (STEP)>(BASE);
-
-// DMA of one stage of one segment into ring slot offset SO: KST is the stage
-// index within the segment, KLEN the segment's K length.  Whole stages add the
-// stage's byte offset to the per-lane row offsets; the last stage of a segment
-// whose K length is not a multiple of BK sends the lanes past KLEN out of range
-// (zeros).
-#define DORA_ISSUE_SEG(RX, RY, LD, LX, LY, KST, KLEN, SO)                                             \
-  {                                                                                                   \
-    const uint32_t kb_ = static_cast<uint32_t>(KST) * static_cast<uint32_t>(TL::ROWB);                \
-    const int krem_ = (KLEN) - (KST) * TL::BK;                                                        \
-    const bool tail_ = krem_ < TL::BK && kc >= krem_;                                                 \
-    _Pragma("unroll") for (int q = 0; q < TL::XQ; ++q) {                                              \
-      const uint32_t o_ = (LX) + static_cast<uint32_t>(q * TL::NW * TL::RPI) * (LD) + kb_;            \
-      dma16(RX, smem + (SO) + (q * TL::NW + wave) * 1024, tail_ ? kOob : o_);                         \
-    }                                                                                                 \
-    _Pragma("unroll") for (int q = 0; q < TL::YQ; ++q) {                                              \
-      const uint32_t o_ = (LY) + static_cast<uint32_t>(q * TL::NW * TL::RPI) * (LD) + kb_;            \
-      dma16(RY, smem + (SO) + TL::X_BYTES + (q * TL::NW + wave) * 1024, tail_ ? kOob : o_);           \
-    }                                                                                                 \
-  }
-
-// DMA of stage ST (of the whole augmented K axis) into ring slot SLOT.
-#define DORA_ISSUE(ST, SLOT)                                                      \
-  {                                                                               \
-    const int st_ = (ST);                                                         \
-    constexpr int so_ = (SLOT) * TL::STAGE_BYTES;                                 \
-    if (st_ < S1)                                                                 \
-      DORA_ISSUE_SEG(rxW, ryA, ldA, lxA, lyA, st_, in, so_)                       \
-    else if (st_ < S12)                                                           \
-      DORA_ISSUE_SEG(rxB, ryH, ldB, lxB, lyB, st_ - S1, r, so_)                   \
-    else                                                                          \
-      DORA_ISSUE_SEG(rxB, ryL, ldB, lxB, lyB, st_ - S12, r, so_)                  \
-  }
-
-#define DORA_PROLOGUE(U)                                                      \
-  if constexpr ((U) < TL::NS - 1) {                                           \
-    if (st0 + (U) < st1) DORA_ISSUE(st0 + (U), (U))                           \
-  }
-
-// One stage in ring slot U: wait for its DMA (this wave's loads; the barrier
-// makes every wave's loads visible and frees the slot read last), hand that
-// slot to the DMA of stage st + NS - 1, then two K steps of 16 from LDS (the
-// second step's fragments are read with the first's, and waited for after the
-// first step's MFMAs).
-#define DORA_STAGE(U)                                                                   \
-  if constexpr ((U) < TL::NS) {                                                         \
-    const int st = sb + (U);                                                            \
-    if (st >= st1) break;                                                               \
-    wait_younger<TL>(st1 - 1 - st);                                                     \
-    __builtin_amdgcn_s_barrier();                                                       \
-    if (st + TL::NS - 1 < st1) DORA_ISSUE(st + TL::NS - 1, ((U) + TL::NS - 1) % TL::NS) \
-    constexpr int so = (U) * TL::STAGE_BYTES;                                           \
-    constexpr int sw = so & ~32767, si = so & 32767;                                    \
-    constexpr int tstep = 32 * TL::ROWB;                                                \
-    const bool base_here = want_base && st < S1;                                        \
-    u32x4 x0[TL::TMW], y0[TL::TN], x1[TL::TMW], y1[TL::TN];                             \
-    const uint32_t xa0 = xb0 + sw, ya0 = yb0 + sw, xa1 = xb1 + sw, ya1 = yb1 + sw;      \
-    DORA_READS(x0, xa0, si, tstep, TL::TMW)                                             \
-    DORA_READS(y0, ya0, si, tstep, TL::TN)                                              \
-    DORA_READS(x1, xa1, si, tstep, TL::TMW)                                             \
-    DORA_READS(y1, ya1, si, tstep, TL::TN)                                              \
-    lds_wait_keep<TL::TMW + TL::TN>();                                                  \
-    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x0[i]);                     \
-    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y0[j]);                      \
-    DORA_STEP_MFMAS(x0, y0)                                                             \
-    if (base_here) {                                                                    \
-      DORA_STEP_SQUARES(x0, 0)                                                          \
-    }                                                                                   \
-    lds_wait();                                                                         \
-    _Pragma("unroll") for (int i = 0; i < TL::TMW; ++i) tie(x1[i]);                     \
-    _Pragma("unroll") for (int j = 0; j < TL::TN; ++j) tie(y1[j]);                      \
-    DORA_STEP_MFMAS(x1, y1)                                                             \
-    if (base_here) {                                                                    \
-      DORA_STEP_SQUARES(x1, 1)                                                          \
-    }                                                                                   \
-  }
-
-template <int DT, int TN, int TM, int NS, int WM, int BK>
-__global__ __launch_bounds__((DmaTile<TN, TM, NS, WM, BK>::NT), 1) void wstream_dma(WArgs a) {
-  using TL = DmaTile<TN, TM, NS, WM, BK>;
-  using V8 = typename Dt<DT>::V8;
-  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS_BYTES];
-  // the epilogue's row sums (cross, then base) live past the B-tile passes, in the dead stage area
-  float(*red)[TL::BM] = reinterpret_cast<float(*)[TL::BM]>(smem + TL::RED_OFF);
-
-  const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
-  if (v >= static_cast<uint32_t>(a.total)) return;
-  const uint32_t nTiles = static_cast<uint32_t>(a.nTiles), nRB = static_cast<uint32_t>(a.nRB);
-  const int nt = static_cast<int>(v % nTiles);
-  const uint32_t rb = (v / nTiles) % nRB;
-  const int sp = static_cast<int>(v / (nTiles * nRB));
-  const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
-  // stage bookkeeping in 32 bits (the augmented K axis has well under 2^31 stages)
-  const int S1 = static_cast<int>(a.sm.S1), S12 = S1 + static_cast<int>(a.sm.S2);
-  const int st0 = static_cast<int>(a.S * sp / a.nSplit), st1 = static_cast<int>(a.S * (sp + 1) / a.nSplit);
-  const int in = static_cast<int>(a.sm.in), r = static_cast<int>(a.sm.r);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const bool want_base = (nt == 0) && !a.skip_base;
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
-
-  // Buffer resources of the five operand panels, each rebased to the
-  // workgroup's first row; rows past the operand lie beyond num_records and
-  // read zero.  Byte offsets stay below 2^31 (at most 512 rows of under 2^21
-  // elements).
-  auto rsrc = [](const void* base, int64_t row0, int64_t rows, int64_t ld, int64_t max_rows) {
-    const int64_t nrows = std::min<int64_t>(std::max<int64_t>(rows - row0, 0), max_rows);
-    const char* p = static_cast<const char*>(base) + (nrows > 0 ? row0 * ld * 2 : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), static_cast<short>(0),
-                                             static_cast<int>(nrows * ld * 2), kBufferWord3);
-  };
-  const int64_t out = a.sm.out;
-  const __amdgpu_buffer_rsrc_t rxW = rsrc(a.sm.W0, m0, out, in, TL::BM);
-  const __amdgpu_buffer_rsrc_t ryA = rsrc(a.sm.A, n0, r, in, TL::BN);
-  const __amdgpu_buffer_rsrc_t rxB = rsrc(a.sm.B, m0, out, r, TL::BM);
-  const __amdgpu_buffer_rsrc_t ryH = rsrc(a.sm.Ghi, n0, r, r, TL::BN);
-  const __amdgpu_buffer_rsrc_t ryL = rsrc(a.sm.Glo, n0, r, r, TL::BN);
-
-  // Per-lane DMA geometry.  One wave instruction moves RPI rows x ROWB bytes;
-  // lane l takes row l/CPR of its group and the logical 16-byte chunk
-  // (l%CPR) ^ ((row/SWP)%CPR), which lands in LDS slot l%CPR (the XOR swizzle
-  // of the fragment reads; a group starts on a multiple of 4*SWP rows, so the
-  // chunk depends on l only).  Wave instruction q < XQ moves X-panel group
-  // NW*q + wave, the others Y-panel group NW*(q - XQ) + wave.  The Y panel is
-  // fetched in the row order sigma of the fragment reads, which maps rows
-  // 16..31 of a 32-row tile to sigma(row - 16) + 8.  A lane's byte offset is
-  // then a per-lane value plus (q's first row) x row pitch + the stage's K
-  // offset, where q's first row is a compile-time multiple of NW*RPI.
-  const int lrow = lane / TL::CPR, lslot = lane % TL::CPR;
-  const int lc = lslot ^ ((lrow / TL::SWP) % TL::CPR);
-  const int kc = lc * 8;
-  auto sigma = [](int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); };
-  // row of this lane within the panel for q = 0 (X) and q = XQ (Y)
-  const int xr0 = wave * TL::RPI + lrow;
-  const int yp = wave * TL::RPI + lrow;  // LDS row
-  const int yr0 = (yp & ~31) + sigma(yp & 31);
-  const uint32_t ldA = static_cast<uint32_t>(in) * 2u, ldB = static_cast<uint32_t>(r) * 2u;
-  const uint32_t lxA = static_cast<uint32_t>(xr0) * ldA + kc * 2u, lxB = static_cast<uint32_t>(xr0) * ldB + kc * 2u;
-  const uint32_t lyA = static_cast<uint32_t>(yr0) * ldA + kc * 2u, lyB = static_cast<uint32_t>(yr0) * ldB + kc * 2u;
-
-  // Fragment reads.  LDS row m of a panel holds logical chunk c at slot
-  // c ^ ((m/SWP)%CPR); a lane reads row 32*i + (l%32) of its wave's tiles,
-  // K chunk 2*step + l/32, so the swizzle depends on l only and tile i is a
-  // fixed step of 32 rows.  Rank-side row p of each 32-row tile holds rank row
-  // sigma(p) = 16*((p/4)%2) + 4*(p/8) + p%4, so accumulator register q of a lane
-  // in half h holds rank column 16h + q.
-  const int frow = lane & 31, fhalf = lane >> 5, fsw = (frow / TL::SWP) % TL::CPR;
-  const uint32_t xrow = lds0 + static_cast<uint32_t>((wm * TL::TMW * 32 + frow) * TL::ROWB);
-  const uint32_t yrow = lds0 + static_cast<uint32_t>(TL::X_BYTES + (wn * TL::TN * 32 + frow) * TL::ROWB);
-  const uint32_t xb0 = xrow + ((fhalf ^ fsw) * 16), yb0 = yrow + ((fhalf ^ fsw) * 16);
-  const uint32_t xb1 = xrow + (((2 + fhalf) ^ fsw) * 16), yb1 = yrow + (((2 + fhalf) ^ fsw) * 16);
-
-  f32x16 acc[TL::TMW][TL::TN];
-#pragma unroll
-  for (int i = 0; i < TL::TMW; ++i)
-#pragma unroll
-    for (int j = 0; j < TL::TN; ++j) acc[i][j] = f32x16{};
-  float bs[TL::NP];
-#pragma unroll
-  for (int t = 0; t < TL::NP; ++t) bs[t] = 0.0f;
-
-  DORA_PROLOGUE(0)
-  DORA_PROLOGUE(1)
-  DORA_PROLOGUE(2)
-  DORA_PROLOGUE(3)
-  DORA_PROLOGUE(4)
-  DORA_PROLOGUE(5)
-  DORA_PROLOGUE(6)
-  for (int sb = st0; sb < st1; sb += TL::NS) {
-    DORA_STAGE(0)
-    DORA_STAGE(1)
-    DORA_STAGE(2)
-    DORA_STAGE(3)
-    DORA_STAGE(4)
-    DORA_STAGE(5)
-    DORA_STAGE(6)
-    DORA_STAGE(7)
-  }
-
-  if (a.acc_part) {  // norm backward: keep U + B G' (every DMA of the ring has been waited for)
-    dma_store_acc<TL>(a, sp, m0, n0, acc);
-    return;
-  }
-  dma_cross_epilogue<DT, TL>(a, sp, nt, m0, n0, acc, bs, want_base, red, smem, lds0, rxB);
-}
-#undef DORA_STAGE
-#undef DORA_PROLOGUE
-#undef DORA_ISSUE
-#undef DORA_ISSUE_SEG
-#undef DORA_READS
-#undef DORA_STEP_SQUARES
 
 // ---------------------------------------------------------------------------
 // W stream with 128-byte row segments (rank tiles of 128, 256 and 384).
 //
-// The 64-byte row segments of wstream_dma make every L1 -> L2 request 64
-// bytes, and the L1's table of pending requests then bounds the stream (it is
-// full most of the time at the measured L2 latency).  Here a stage is 64 K
-// columns: every DMA row segment is a whole 128-byte line.  The A panel (384
+// With 64-byte row segments every L1 -> L2 request is 64 bytes, and the L1's
+// table of pending requests then bounds the stream (it is full most of the
+// time at the measured L2 latency).  Here a stage is 64 K columns: every DMA
+// row segment is a whole 128-byte line.  The A panel (384
 // rank rows, L2 resident) and the W0 panel (128 rows, streamed from HBM) sit
 // in separate rings: two A slots, three W0 slots (the W0 panel is 128 or 256
 // rows, the A panel 32 * TN * 4 rank rows).
@@ -1514,12 +1233,15 @@ __global__ __launch_bounds__(256) void norm_finalize(const float* base_part, con
   norm_out[i] = static_cast<float>(n2 > 0.0 ? sqrt(n2) : 0.0);
 }
 
-// Rank tile width of the 16-byte path: 128*TN columns, TN in 1..4, choosing the
-// least padding of r and then the widest tile (fewest passes over W0).
+// Rank tile width of the 16-byte path: 128*TN columns, TN in 1..3, choosing the
+// least padding of r and then the widest tile (fewest passes over W0).  Tiles
+// of 512 are not used: at r = 512, two passes of 256-wide tiles measured 94 us
+// at 8192^2 against 110-114 us for one pass of a 512-wide tile, whose rank
+// panel does not fit two ring slots beside the W0 ring at 128-byte segments.
 int dma_tn(int64_t r) {
   int best = 1;
   int64_t best_pad = -1;
-  for (int tn = 1; tn <= 4; ++tn) {
+  for (int tn = 1; tn <= 3; ++tn) {
     const int64_t w = 128 * tn;
     const int64_t pad = cdiv(std::max<int64_t>(r, 1), w) * w;
     if (best_pad < 0 || pad <= best_pad) {
@@ -1530,24 +1252,17 @@ int dma_tn(int64_t r) {
   return best;
 }
 
-// Shape of the 64-byte-segment stream (rank tiles of 512): W0 rows per tile
-// (32*TM), LDS ring slots, waves along the rows and K depth of a stage.
-template <int TN> struct DmaShape;
-// rank tiles of 128, 256 and 384 take wstream_k64: 256 x 128, 128 x 256 and
-// 128 x 384 (W0 rows x ranks); rank tiles of 512 the 64-byte-segment stream
+// Rank tiles of 128, 256 and 384: 256 x 128, 128 x 256 and 128 x 384 (W0 rows x ranks).
 template <int TN> struct K64Of;
 template <> struct K64Of<1> { using T = K64Tile<1, 4>; };
 template <> struct K64Of<2> { using T = K64Tile<2, 2>; };
 template <> struct K64Of<3> { using T = K64Tile<3, 2>; };
-template <> struct DmaShape<4> { static constexpr int TM = 4, NS = 3, WM = 2, BK = 32; };
-using DmaTile4 = DmaTile<4, DmaShape<4>::TM, DmaShape<4>::NS, DmaShape<4>::WM, DmaShape<4>::BK>;
 
 int dma_rows(int tn) {
   switch (tn) {
     case 1: return K64Of<1>::T::BM;
     case 2: return K64Of<2>::T::BM;
-    case 3: return K64Of<3>::T::BM;
-    default: return DmaTile4::BM;
+    default: return K64Of<3>::T::BM;
   }
 }
 
@@ -1555,21 +1270,16 @@ int dma_bk(int tn) {
   switch (tn) {
     case 1: return K64Of<1>::T::BK;
     case 2: return K64Of<2>::T::BK;
-    case 3: return K64Of<3>::T::BK;
-    default: return DmaTile4::BK;
+    default: return K64Of<3>::T::BK;
   }
 }
 
 template <int DT, int TN>
 void launch_dma(const WArgs& w, hipStream_t stream) {
+  static_assert(TN >= 1 && TN <= 3, "rank tiles of 128, 256 and 384");
+  using TL = typename K64Of<TN>::T;
   const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
-  if constexpr (TN <= 3) {  // the 128-byte-segment stream
-    using TL = typename K64Of<TN>::T;
-    hipLaunchKernelGGL((wstream_k64<DT, TL>), grid, dim3(TL::NT), 0, stream, w);
-  } else {
-    using S = DmaShape<4>;
-    hipLaunchKernelGGL((wstream_dma<DT, 4, S::TM, S::NS, S::WM, S::BK>), grid, dim3(DmaTile4::NT), 0, stream, w);
-  }
+  hipLaunchKernelGGL((wstream_k64<DT, TL>), grid, dim3(TL::NT), 0, stream, w);
 }
 
 // Workgroups of gram_finalize: four 8-row strips per upper 32 x 32 tile.
@@ -1647,8 +1357,7 @@ hipError_t launch_norm_t(const NormPlan& p, const NormArgs& a, bool vec) {
     switch (p.tn) {
       case 1: launch_dma<DT, 1>(w, a.stream); break;
       case 2: launch_dma<DT, 2>(w, a.stream); break;
-      case 3: launch_dma<DT, 3>(w, a.stream); break;
-      default: launch_dma<DT, 4>(w, a.stream); break;
+      default: launch_dma<DT, 3>(w, a.stream); break;
     }
   } else {
     const dim3 grid(static_cast<unsigned>(cdiv(w.total, 8) * 8));
@@ -1704,8 +1413,7 @@ hipError_t launch_norm_bwd_db_t(const NormPlan& p, const void* W0, const void* A
   switch (p.tn) {
     case 1: launch_dma<DT, 1>(w, stream); break;
     case 2: launch_dma<DT, 2>(w, stream); break;
-    case 3: launch_dma<DT, 3>(w, stream); break;
-    default: launch_dma<DT, 4>(w, stream); break;
+    default: launch_dma<DT, 3>(w, stream); break;
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1737,7 +1445,7 @@ int64_t norm_max_grid(const NormPlan& p) {
   return std::max({gram, stream, cdiv(p.out, 256), p.strip ? cdiv_strip(p.out) : int64_t(0)});
 }
 
-NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec) {
+NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec, bool store_acc) {
   NormPlan p;
   p.out = out;
   p.in = in;
@@ -1781,6 +1489,11 @@ NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec)
       }
     }
     p.nSplit = static_cast<int>(best);
+    // Store mode (the norm backward keeps each split's accumulators, nSplit x
+    // out x r fp32, and reads them back): split K only as far as it takes to
+    // give the 256 CUs a workgroup each, since every split adds a full slice.
+    if (store_acc)
+      p.nSplit = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(maxs, slots / std::max<int64_t>(per, 1))));
   }
   if (r > 0) {
     // Gram: upper tiles (64x64 on the 16-byte path, 32x32 otherwise) x K

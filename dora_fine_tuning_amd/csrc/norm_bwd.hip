@@ -369,7 +369,7 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype, bo
     p.max_grid = std::max({ndiv(out, 256), ndiv(r * r, 256), ndiv(out * r, 256), ndiv(r * in, 256)});
     return p;
   }
-  p.np = make_norm_plan(out, in, r, dtype, true);
+  p.np = make_norm_plan(out, in, r, dtype, true, true);
   p.rM = row_contract_plan(out, r, r, 0, 2 * r);
   p.rW = row_contract_plan(out, in, r, r, 2 * r);
   size_t off = 0;

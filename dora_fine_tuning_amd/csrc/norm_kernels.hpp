@@ -34,7 +34,9 @@ struct NormPlan {
   size_t off_gpart = 0, off_ghi = 0, off_glo = 0, off_base = 0, off_cross = 0, off_count = 0, bytes = 0;
 };
 
-NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec);
+// store_acc: the plan of the norm backward's W stream, which stores every K
+// split's accumulators (fewer splits).
+NormPlan make_norm_plan(int64_t out, int64_t in, int64_t r, int dtype, bool vec, bool store_acc = false);
 
 // The strip kernel (16-byte path): ranks up to 32, at least kStripMinBlocks
 // strips of 32 rows, panels within 32-bit buffer offsets.

@@ -48,8 +48,8 @@ NORM_SMALL = [
     (1, 8, 8),
     (33, 200, 200),   # rank above out
     (200, 264, 296),  # 384-wide rank tile, ragged
-    (150, 128, 504),  # 512-wide rank tile
-    (260, 392, 1000),  # two 512-wide rank tiles
+    (150, 128, 504),  # two 256-wide rank tiles, the second partly filled
+    (260, 392, 1000),  # four 256-wide rank tiles, the last partly filled
     (140, 136, 776),  # seven 128-wide rank tiles
     (90, 100, 300),   # general path, rank above 128
 ]
