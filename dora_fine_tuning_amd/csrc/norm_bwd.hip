@@ -179,6 +179,9 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
 // the slices added in order; sigma a power of two), rounded once.
 // A 32 x 32 tile of (k, j) per workgroup: coalesced reads along j, a transpose
 // through LDS, coalesced writes along k.
+// Slices the finalize of d_A loads all at once before adding them.
+constexpr int kFinA = 8;
+
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nParts, int64_t in, int64_t r,
                                                        const float* sigma, void* dAv) {
@@ -187,17 +190,41 @@ __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nPart
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 32, j0 = static_cast<int64_t>(blockIdx.y) * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int64_t slice = in * r;
+  if (nParts <= kFinA) {
+    // every slice of the thread's four elements in flight before the first
+    // addition (clamped indices keep the loads unconditional); the sums keep
+    // slice order
+    float e[4][kFinA];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int kk = ty + 8 * q;
-    const int64_t k = k0 + kk, j = j0 + tx;
-    float v = 0.0f;
-    if (k < in && j < r) {
+    for (int q = 0; q < 4; ++q) {
+      const int64_t k = std::min<int64_t>(k0 + ty + 8 * q, in - 1), j = std::min<int64_t>(j0 + tx, r - 1);
       const float* Ep = E + k * r + j;
-      for (int p = 0; p < nParts; ++p) v += Ep[p * slice];
-      v /= sigma[0];
+#pragma unroll
+      for (int p = 0; p < kFinA; ++p) e[q][p] = Ep[static_cast<int64_t>(p < nParts ? p : nParts - 1) * slice];
     }
-    tile[kk][tx] = v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = ty + 8 * q;
+      const int64_t k = k0 + kk, j = j0 + tx;
+      float v = 0.0f;
+#pragma unroll
+      for (int p = 0; p < kFinA; ++p)
+        if (p < nParts) v += e[q][p];
+      tile[kk][tx] = (k < in && j < r) ? v / sigma[0] : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = ty + 8 * q;
+      const int64_t k = k0 + kk, j = j0 + tx;
+      float v = 0.0f;
+      if (k < in && j < r) {
+        const float* Ep = E + k * r + j;
+        for (int p = 0; p < nParts; ++p) v += Ep[p * slice];
+        v /= sigma[0];
+      }
+      tile[kk][tx] = v;
+    }
   }
   __syncthreads();
   T* dA = static_cast<T*>(dAv);
