@@ -134,6 +134,9 @@ __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* no
   }
 }
 
+// Slices the finalize of d_A loads all at once before adding them.
+constexpr int kFinA = 8;
+
 // Z[l][j] = s * M'[j][l], M'[j][l] = sum over slices of E[j][l]
 // (E = B^T (Yhi + Ylo), [nSplit][r][r]), split into hi/lo at [l][j], [l][r + j].
 // An 8 x 32 tile of (j, l) per workgroup, one element per thread: reads
@@ -179,9 +182,6 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
 // the slices added in order; sigma a power of two), rounded once.
 // A 32 x 32 tile of (k, j) per workgroup: coalesced reads along j, a transpose
 // through LDS, coalesced writes along k.
-// Slices the finalize of d_A loads all at once before adding them.
-constexpr int kFinA = 8;
-
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nParts, int64_t in, int64_t r,
                                                        const float* sigma, void* dAv) {
