@@ -8,25 +8,26 @@
 //   d_A   = s (c*B)^T W0 + s^2 (B^T diag(c) B) A
 //
 // and the out x in matrix B A is never formed.  Steps, in launch order:
-//   nbwd_absmax        (fp16 only) max |s c_i B_ij| for the operand scale
-//                      sigma, a power of two;
-//   nbwd_prep          c_i (0 where n_i = 0) and Y = sigma s c*B [out x r] as
-//                      the storage-dtype pair Yhi | Ylo [out x 2r];
+//   nbwd_colmax,       (fp16 only) per rank j, max_i |s c_i B_ij| and from it
+//   nbwd_colscale      the operand scale sigma_j, a power of two;
+//   nbwd_prep          c_i (0 where n_i = 0) and Y_ij = sigma_j s c_i B_ij
+//                      [out x r] as the storage-dtype pair Yhi | Ylo [out x 2r];
 //   d_B                the norm's W stream with G' = s G, its accumulators
 //                      U + s B G stored and then scaled by s c_i (norm.hip);
 //   M                  the token-axis contraction kernel (lora_bwd.hip) over
 //                      the rows of B, its two Y panels Yhi and Ylo adding into
 //                      one accumulator: B^T (Yhi + Ylo) = s B^T diag(c) B, in
 //                      row slices;
-//   nbwd_finalize_m    Z = s (that r x r matrix), transposed, as Zhi | Zlo;
+//   nbwd_finalize_m    Z = s (that r x r matrix), transposed, rescaled to
+//                      carry sigma_j on its column j, as Zhi | Zlo;
 //   d_A                the same contraction kernel, in one launch, over the
 //                      rows of W0 with Yhi + Ylo and then over the rows of A
 //                      with Zhi + Zlo (each row slice takes its share of both;
 //                      each stage's W0 rows meet both halves, so W0 is read
 //                      once): the contraction axis [out rows of W0 ; r rows of
 //                      A] gives d_A^T in row slices;
-//   nbwd_finalize_a    sum of the slices over sigma, transposed through LDS
-//                      into d_A [r x in].
+//   nbwd_finalize_a    sum of the slices, row j over sigma_j, transposed
+//                      through LDS into d_A [r x in].
 // The hi/lo pairs carry about 16 (bf16) or 22 (fp16) significant bits of the
 // computed operands Y and Z into the bf16/fp16 MFMAs; W0, A and B enter exactly.
 // Sizes or pointers the 16-byte path cannot take go to a general path of plain
@@ -45,73 +46,82 @@ namespace {
 __host__ __device__ inline int64_t ndiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// fp16 only (its exponent range is narrow): the operand Y = s c B is stored
-// times a power of two sigma that brings max |Y| into [1/2, 1), so a small
-// upstream gradient or an early-training B does not push the hi/lo pair into
-// fp16's subnormal range.  M' and Z then carry sigma too, and the d_A
-// finalize divides it out (exactly).  bf16 has fp32's exponent range and
-// takes sigma = 1.
-constexpr int kAbsMaxParts = 256;
+// fp16 only (its exponent range is narrow): column j of the operand Y = s c B
+// is stored times a power of two sigma_j that brings max_i |Y_ij| into
+// [1/2, 1), so a small upstream gradient, an early-training B or a single small
+// column of B does not push the hi/lo pair into fp16's subnormal range.  Every
+// operand column that feeds rank j of d_A carries sigma_j: column j of Y, and
+// column j of Z (its finalize rescales s M' by sigma_j / sigma_l, exactly, since
+// M' = B^T Y carries sigma_l on its column l).  The d_A finalize divides row j
+// by sigma_j (exactly).  One scale for all of Y left a column of B that is small
+// on every row (rank 87 of a 2 x 320, r = 216 module) with subnormal Z entries
+// and ~2^-10 relative error in its row of d_A.  bf16 has fp32's exponent range
+// and takes sigma = 1 (no scale kernels run).
+constexpr int kColMaxParts = 64;
 
-// max |s c_i B_ij| over a grid-stride share of the chunks, one value per
-// workgroup into part[blockIdx.x] (every workgroup writes its own slot).
+// Per-column maxima of |s c_i B_ij| over a share of the rows: workgroup p takes
+// rows [out p / nparts, out (p + 1) / nparts) and leaves max_i in part[p][j],
+// as the bits of a non-negative float (whose order is that of the values).
+// With rc = r / 8 chunks of 8 columns per row, thread t keeps the running
+// maxima of chunk t % rc (t + 256 k for rc > 256) over every (256 / rc)-th row
+// of the share, then merges them into the workgroup's own row of part with
+// atomicMax, which gives the same result in any order; the workgroup zeroes
+// that row first (no other workgroup touches it).
 template <int DT>
-__global__ __launch_bounds__(256) void nbwd_absmax(const void* Bv, const float* norm, const float* d_norm, int64_t out,
-                                                   int64_t r, float s, float* part) {
-  __shared__ float red[256];
+__global__ __launch_bounds__(256) void nbwd_colmax(const void* Bv, const float* norm, const float* d_norm, int64_t out,
+                                                   int64_t r, float s, int nparts, unsigned* part) {
   const Chunk* B = static_cast<const Chunk*>(Bv);
-  const int64_t n = out * r / 8;
-  float m = 0.0f;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t i = (e * 8) / r;
-    const float ni = norm[i];
-    const float ci = ni != 0.0f ? d_norm[i] / ni : 0.0f;
-    float f[8];
-    chunk_to_f32<DT>(B[e], f);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf((s * ci) * f[q]));
-  }
-  red[threadIdx.x] = m;
+  const int p = static_cast<int>(blockIdx.x), t = static_cast<int>(threadIdx.x);
+  const int64_t i0 = out * p / nparts, i1 = out * (p + 1) / nparts;
+  const int64_t rc = r / 8;
+  unsigned* row = part + static_cast<int64_t>(p) * r;
+  for (int64_t j = t; j < r; j += 256) row[j] = 0u;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-    __syncthreads();
+  const int lanes = rc < 256 ? static_cast<int>(256 / rc) : 1;  // rows handled side by side
+  const int lane = rc < 256 ? static_cast<int>(t / rc) : 0;
+  if (lane >= lanes) return;
+  for (int64_t jc = rc < 256 ? t % rc : t; jc < rc; jc += 256) {
+    float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = i0 + lane; i < i1; i += lanes) {
+      const float ni = norm[i];
+      const float ci = ni != 0.0f ? d_norm[i] / ni : 0.0f;
+      float f[8];
+      chunk_to_f32<DT>(B[i * rc + jc], f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m[q] = fmaxf(m[q], fabsf((s * ci) * f[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) atomicMax(row + jc * 8 + q, __float_as_uint(m[q]));
+    if (rc < 256) break;
   }
-  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
 }
 
-// sigma = 2^-e for max = f 2^e, f in [1/2, 1), e clamped to [-64, 64]; 1 for a
+// sigma = 2^-e for max = f 2^e, f in [1/2, 1), e clamped to [-60, 60]; 1 for a
 // zero or non-finite max
 __device__ inline float operand_scale(float mx) {
   if (!(mx > 0.0f) || !isfinite(mx)) return 1.0f;
   int e;
   frexpf(mx, &e);
-  return ldexpf(1.0f, -std::min(64, std::max(-64, e)));  // 2^-64 .. 2^64 keeps d_A sigma finite in fp32
+  return ldexpf(1.0f, -std::min(60, std::max(-60, e)));  // 2^-60 .. 2^60: sigma_j / sigma_l stays finite in fp32
 }
 
-// c_i = dn_i / n_i (0 where n_i == 0); Y_ij = sigma s c_i B_ij split into
+// sigma_j = operand_scale(max over the nparts row shares of part[p][j])
+__global__ __launch_bounds__(256) void nbwd_colscale(const unsigned* part, int nparts, int64_t r, float* sigma) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= r) return;
+  unsigned m = 0u;
+  for (int p = 0; p < nparts; ++p) m = std::max(m, part[static_cast<int64_t>(p) * r + j]);
+  sigma[j] = operand_scale(__uint_as_float(m));
+}
+
+// c_i = dn_i / n_i (0 where n_i == 0); Y_ij = sigma_j s c_i B_ij split into
 // hi = round(Y), lo = round(Y - hi), stored at [i][j] and [i][r + j].  One
 // 16-byte chunk (8 elements of one row, r % 8 == 0) per thread and step.
-// sigma comes from the nparts workgroup maxima in part (nparts == 0:
-// sigma = 1); the first workgroup stores it in sigma_out.
+// sigma == nullptr: sigma_j = 1.
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* norm, const float* d_norm, int64_t out,
-                                                 int64_t r, float s, const float* part, int nparts, float* sigma_out,
-                                                 float* c, void* Yv) {
+                                                 int64_t r, float s, const float* sigma, float* c, void* Yv) {
   using T = typename Dt<DT>::T;
-  __shared__ float red[256];
-  float sigma = 1.0f;
-  if (nparts > 0) {  // every workgroup reduces the (at most 256) maxima itself
-    red[threadIdx.x] = static_cast<int>(threadIdx.x) < nparts ? part[threadIdx.x] : 0.0f;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-      __syncthreads();
-    }
-    sigma = operand_scale(red[0]);
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) sigma_out[0] = sigma;
   const Chunk* B = static_cast<const Chunk*>(Bv);
   T* Y = static_cast<T*>(Yv);
   const int64_t n = out * r / 8;
@@ -121,11 +131,23 @@ __global__ __launch_bounds__(256) void nbwd_prep(const void* Bv, const float* no
     const float ni = norm[i];
     const float ci = ni != 0.0f ? d_norm[i] / ni : 0.0f;
     if (j == 0) c[i] = ci;
+    float sg[8];
+    if (sigma) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sigma + j), s1 = *reinterpret_cast<const f32x4*>(sigma + j + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sg[q] = s0[q];
+        sg[q + 4] = s1[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sg[q] = 1.0f;
+    }
     float f[8], hi[8], lo[8];
     chunk_to_f32<DT>(B[e], f);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float y = ((s * ci) * f[q]) * sigma;  // sigma is a power of two: exact
+      const float y = ((s * ci) * f[q]) * sg[q];  // sigma_j is a power of two: exact
       hi[q] = Dt<DT>::to_f(Dt<DT>::from_f(y));
       lo[q] = y - hi[q];
     }
@@ -145,7 +167,8 @@ constexpr int kFinA = 8;
 // before the group is added in slice order; lanes past r read a valid
 // address and drop the result, so the loads stay unconditional.
 template <int DT>
-__global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSplit, int64_t r, float s, void* Zv) {
+__global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSplit, int64_t r, float s,
+                                                       const float* sigma, void* Zv) {
   using T = typename Dt<DT>::T;
   __shared__ float tile[8][33];
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 8, l0 = static_cast<int64_t>(blockIdx.y) * 32;
@@ -164,6 +187,9 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
       for (int u = 0; u < 8; ++u) m += v[u];
     }
     for (; p < nSplit; ++p) m += Ej[p * slice];
+    // M' carries sigma_l on its column l; Z's column j is to carry sigma_j
+    // (powers of two: both rescalings are exact)
+    if (sigma && j < r && l < r) m = (m / sigma[l]) * sigma[j];
     tile[ty][tx] = s * m;
   }
   __syncthreads();
@@ -178,13 +204,14 @@ __global__ __launch_bounds__(256) void nbwd_finalize_m(const float* E, int nSpli
   }
 }
 
-// d_A[j][k] = (sum over the slices of E[k][j]) / sigma (E [nParts][in][r],
-// the slices added in order; sigma a power of two), rounded once.
+// d_A[j][k] = (sum over the slices of E[k][j]) / sigma_j (E [nParts][in][r],
+// the slices added in order; sigma_j a power of two), rounded once.
 // A 32 x 32 tile of (k, j) per workgroup: coalesced reads along j, a transpose
 // through LDS, coalesced writes along k.
 template <int DT>
 __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nParts, int64_t in, int64_t r,
                                                        const float* sigma, void* dAv) {
+  // sigma == nullptr: sigma_j = 1
   using T = typename Dt<DT>::T;
   __shared__ float tile[32][33];
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 32, j0 = static_cast<int64_t>(blockIdx.y) * 32;
@@ -210,7 +237,7 @@ __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nPart
 #pragma unroll
       for (int p = 0; p < kFinA; ++p)
         if (p < nParts) v += e[q][p];
-      tile[kk][tx] = (k < in && j < r) ? v / sigma[0] : 0.0f;
+      tile[kk][tx] = (k < in && j < r) ? (sigma ? v / sigma[j] : v) : 0.0f;
     }
   } else {
 #pragma unroll
@@ -221,7 +248,7 @@ __global__ __launch_bounds__(256) void nbwd_finalize_a(const float* E, int nPart
       if (k < in && j < r) {
         const float* Ep = E + k * r + j;
         for (int p = 0; p < nParts; ++p) v += Ep[p * slice];
-        v /= sigma[0];
+        if (sigma) v /= sigma[j];
       }
       tile[kk][tx] = v;
     }
@@ -346,18 +373,23 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   void* Y = ws + p.off_y;
   void* Z = ws + p.off_z;
   float* big = reinterpret_cast<float*>(ws + p.off_big);
-  float* part = reinterpret_cast<float*>(ws + p.off_sigma);  // kAbsMaxParts maxima, then sigma
-  float* sigma = part + kAbsMaxParts;
-  int nparts = 0;
+  // fp16: the per-rank operand scales sigma [r] (after kColMaxParts x r partial maxima)
+  float* sigma = nullptr;
   if (DT == 1) {
-    nparts = static_cast<int>(std::min<int64_t>(kAbsMaxParts, ndiv(out * r / 8, 256)));
-    hipLaunchKernelGGL((nbwd_absmax<DT>), dim3(static_cast<unsigned>(nparts)), dim3(256), 0, a.stream, a.B, a.norm,
-                       a.d_norm, out, r, a.s, part);
-    const hipError_t e0 = hipGetLastError();
+    unsigned* part = reinterpret_cast<unsigned*>(ws + p.off_sigma);
+    sigma = reinterpret_cast<float*>(part + static_cast<int64_t>(kColMaxParts) * r);
+    const int nparts = static_cast<int>(std::min<int64_t>(kColMaxParts, ndiv(out, 64)));
+    hipLaunchKernelGGL((nbwd_colmax<DT>), dim3(static_cast<unsigned>(nparts)), dim3(256), 0, a.stream, a.B, a.norm,
+                       a.d_norm, out, r, a.s, nparts, part);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    hipLaunchKernelGGL(nbwd_colscale, dim3(static_cast<unsigned>(ndiv(r, 256))), dim3(256), 0, a.stream, part, nparts,
+                       r, sigma);
+    e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
   hipLaunchKernelGGL((nbwd_prep<DT>), stride_grid(out * r / 8), dim3(256), 0, a.stream, a.B, a.norm, a.d_norm, out, r,
-                     a.s, part, nparts, sigma, c, Y);
+                     a.s, sigma, c, Y);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // d_B (the W stream's partials live in the big region until its finalize)
@@ -367,7 +399,7 @@ hipError_t launch_norm_bwd_t(const NormBwdPlan& p, const NormBwdArgs& a) {
   e = launch_row_contract(a.B, Y, out, r, r, 2 * r, true, p.np.dtype, big, a.stream);
   if (e != hipSuccess) return e;
   const dim3 mgrid(static_cast<unsigned>(ndiv(r, 8)), static_cast<unsigned>(ndiv(r, 32)));
-  hipLaunchKernelGGL((nbwd_finalize_m<DT>), mgrid, dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, Z);
+  hipLaunchKernelGGL((nbwd_finalize_m<DT>), mgrid, dim3(256), 0, a.stream, big, p.rM.nSplit, r, a.s, sigma, Z);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // d_A^T slices: the rows of W0 with Y, then (spread over the same slices) the rows of A with Z
@@ -404,8 +436,8 @@ NormBwdPlan make_norm_bwd_plan(int64_t out, int64_t in, int64_t r, int dtype, bo
   off += al256(p.np.bytes);
   p.off_c = off;
   off += al256(static_cast<size_t>(out) * 4);
-  p.off_sigma = off;  // the operand scale's workgroup maxima and the scale itself
-  off += al256(static_cast<size_t>(kAbsMaxParts + 1) * 4);
+  p.off_sigma = off;  // fp16: the operand scales' partial maxima [kColMaxParts x r] and the scales [r]
+  off += al256(static_cast<size_t>(kColMaxParts + 1) * r * 4);
   p.off_y = off;
   off += al256(static_cast<size_t>(out) * 2 * r * 2);
   p.off_z = off;

@@ -232,12 +232,14 @@ DORA_API size_t dora_norm_bwd_workspace_bytes(int64_t out, int64_t in, int64_t r
  * 16-byte aligned matrix and workspace pointers; other cases take a slow
  * general path (one thread per output element, every sum in order in fp32,
  * no hi/lo operands).
- * In fp16 the fast path stores s*c*B times a power of two sigma that puts
- * its largest magnitude in [1/2, 1) (sigma within 2^-64 .. 2^64; one extra
- * reduction launch), and divides sigma out of d_A in fp32, so a small d_norm
- * or B does not push the operand into fp16's subnormal range.  The r x r
- * product s*B^T*(sigma*s*c*B) beyond fp16's range (65504) still overflows.
- * bf16 has fp32's exponent range and takes sigma = 1.
+ * In fp16 the fast path stores column j of s*c*B times a power of two
+ * sigma_j that puts that column's largest magnitude in [1/2, 1) (sigma_j
+ * within 2^-60 .. 2^60; two extra small launches), carries sigma_j on every
+ * operand column that feeds row j of d_A, and divides it out of that row in
+ * fp32, so a small d_norm, a small B or a single small column of B does not
+ * push the operands into fp16's subnormal range.  Entries of the r x r product
+ * s*B^T*(c*B) beyond fp16's range (65504) after that scaling still overflow.
+ * bf16 has fp32's exponent range and takes sigma_j = 1.
  */
 DORA_API int dora_norm_bwd(const void* W0, const void* A, const void* B, const float* norm, const float* d_norm,
                            int64_t out, int64_t in, int64_t r, float s, int dtype, void* d_A, void* d_B, void* ws,

@@ -188,6 +188,23 @@ def test_norm_bwd_fp16_small_operands(lib, w0_sd, b_sd, dn_sd):
     check(lib, W0, A, B, s, d_norm, norm, "fp16", f"fp16 small operands w0 {w0_sd} B {b_sd} dn {dn_sd}")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("out", [2, 300])
+def test_norm_bwd_small_columns_of_b(lib, out, dtype):
+    """A few columns of B a thousand times smaller than the rest, on every row:
+    the rows of d_A for those ranks are formed from operand columns (of Y and of
+    Z = s B^T diag(c) B) far below the largest ones.  One scale for all of Y
+    left them in fp16's subnormal range, with ~2^-10 relative error in those
+    rows of d_A; per-rank scales keep them normal."""
+    in_, r = 320, 216
+    W0, A, B, s, d_norm = case(out, in_, r, dtype, 4100 + out)
+    Bs = f64(B)
+    Bs[:, [3, 87, 150]] *= 1e-3
+    B = synth.to_dtype(Bs.astype(np.float32), dtype)
+    norm = O.weight_norm(W0, A, B, s).astype(np.float32)
+    check(lib, W0, A, B, s, d_norm, norm, dtype, f"small columns of B, out {out} {dtype}")
+
+
 def test_norm_bwd_b_zero(lib):
     # B = 0 (DoRA's initialisation): d_A = 0 exactly, d_B = s c W0 A^T
     log("norm_bwd B = 0")
