@@ -1,10 +1,16 @@
 """Tolerances of the parity tests, derived from the arithmetic.
 
-* Norm (fp32 output): relative 1e-5 of the oracle's fp64 value.  Where the three
-  terms cancel (n^2 much smaller than base + |cross| + Gram) fp32 cannot hold a
-  relative bound, so an element also passes when |n_gpu^2 - n^2| is within
-  2^-16 of the term mass base + |cross| + Gram (about 2^8 fp32 ulps of the mass:
-  the split-K fp32 partials and the 16-bit two-term split of G).
+* Norm (fp32 output): relative 1e-5 of the oracle's fp64 value.  Where the terms
+  cancel, fp32 arithmetic cannot hold a relative bound, so an element also
+  passes when |n_gpu^2 - n^2| is within 2^-16 of the term mass (about 2^8 fp32
+  ulps of it: the split-K fp32 partials, and the two-term split of G, whose
+  ~16 significant bits per element bound the Gram term's error by 2^-16 of
+  its absolute sum).  The mass adds the absolute values of every product
+  inside each term: base + 2s sum_j |B_ij| (|W0_i| |A_j|^T) +
+  s^2 |B_i| |A A^T| |B_i|^T.  The values |cross| and Gram alone understate it
+  where the terms of the quadratic form B_i G B_i^T cancel (a row of B with
+  mixed signs against a G with large off-diagonal entries, as for a short
+  input axis).
 * Compose outputs and gradients (stored bf16/fp16): within 2 bf16 ulps of the
   oracle value (bf16) or 1e-3 relative (fp16).  fp32 intermediates bound the
   absolute error by a few fp32 ulps of the term mass, not of the result, so an
@@ -87,8 +93,11 @@ def assert_dmag(gpu, ref, cond, what):
 
 
 def norm_term_mass(W0, A, B, s):
-    """base + |cross| + Gram per row, in fp64 (scale of the cancellation floor)."""
+    """Absolute mass of the three terms per row, in fp64 (scale of the
+    cancellation floor): base + the absolute sums of the cross and Gram terms'
+    products."""
+    aW, aA, aB = np.abs(W0), np.abs(A), np.abs(B)
     base = np.sum(W0 * W0, axis=1)
-    cross = 2.0 * s * np.sum(B * (W0 @ A.T), axis=1)
-    gram = s * s * np.sum((B @ (A @ A.T)) * B, axis=1)
-    return base + np.abs(cross) + np.abs(gram)
+    cross = 2.0 * s * np.sum(aB * (aW @ aA.T), axis=1)
+    gram = s * s * np.sum((aB @ np.abs(A @ A.T)) * aB, axis=1)
+    return base + cross + gram

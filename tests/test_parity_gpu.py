@@ -122,6 +122,38 @@ def test_norm_reused_workspace_alternating_inputs(lib, shape):
     PU.assert_norm(f64(first[1]), ref, PU.norm_term_mass(W, Af, Bf, cfgs[1].s), f"reuse {shape}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("in_r", [(8, 8), (16, 16)], ids=["in8_r8", "in16_r16"])
+def test_norm_gram_cancellation(lib, in_r, dtype):
+    """B_i G B_i^T cancelling inside: A's last row is nearly A_0 - A_1, and half
+    the rows of B run along (e_0 - e_1 - e_last), so B_i A is small while
+    |B_i| |A| is not; the other rows are spread over 10^-4 .. 2.  The hi/lo pair
+    of G' (~16 significant bits per element) errs by up to 2^-16 of the Gram
+    term's absolute sum, far above 1e-5 of n^2 on those rows: they must pass on
+    the absolute-mass floor, the others on the relative bound."""
+    in_, r = in_r
+    out = 1491
+    rng = np.random.default_rng(4242 + in_)
+    to = lambda a: synth.to_dtype(a.astype(np.float32), dtype)
+    A = rng.normal(0, 1 / np.sqrt(in_), (r, in_))
+    A[r - 1] = A[0] - A[1] + rng.normal(0, 1e-3 / np.sqrt(in_), in_)
+    Bv = rng.normal(0, 1, (out, r)) * (10.0 ** rng.uniform(-4, 0.35, r))[None, :]
+    d = np.zeros(r)
+    d[0], d[1], d[r - 1] = 1.0, -1.0, -1.0
+    half = np.arange(0, out, 2)
+    Bv[half] = rng.normal(0, 1, (half.size, 1)) * d[None, :] + rng.normal(0, 1e-3, (half.size, r))
+    W0, A, B = to(rng.normal(0, 0.55, (out, in_))), to(A), to(Bv)
+    s = float(np.float32(32.0 / np.sqrt(r)))
+    W, Af, Bf = f64(W0), f64(A), f64(B)
+    gram = s * s * np.sum((Bf @ (Af @ Af.T)) * Bf, axis=1)
+    gram_abs = s * s * np.sum((np.abs(Bf) @ np.abs(Af @ Af.T)) * np.abs(Bf), axis=1)
+    assert np.median((gram_abs / np.maximum(gram, 1e-30))[half]) > 100.0  # those rows cancel
+    n_gpu = f64(lib.dora_norm_factored(W0.to(DEV), A.to(DEV), B.to(DEV), s))
+    ref = O.weight_norm(W0, A, B, s)
+    floor_rows = PU.assert_norm(n_gpu, ref, PU.norm_term_mass(W, Af, Bf, s), f"Gram cancellation {in_r} {dtype}")
+    log(f"Gram cancellation {in_r} {dtype}: {floor_rows} rows pass on the mass floor only")
+
+
 def test_norm_b_zero_is_plain_row_norm(lib):
     cfg = synth.custom("bzero", 300, 1024, 32, 1)
     W0, A, B = synth.weights(cfg)
