@@ -120,7 +120,10 @@ def test_lora_bwd_no_d_base_empty_tokens_determinism(lib):
 
 def test_lora_bwd_matches_unfused_gradients(lib):
     """Against the unfused chain on the GPU: compose backward on a stored lora,
-    then d_B = d_lora^T h.  Equal within the roundings of lora and d_lora."""
+    then d_B = d_lora^T h.  The unfused chain rounds lora and d_lora to bf16
+    (relative error at most 2^-9 per element, round to nearest), which moves
+    its d_B and d_mag by at most 2^-9 of their absolute sums; the fused path
+    keeps both in fp32.  So the two agree to 2^-8 in the Frobenius norm."""
     T, out, r = 512, 512, 64
     dy, base, h, B, m, n, s = case(T, out, r, "bf16", 11)
     dyd, bd, hd, Bd = dy.to(DEV), base.to(DEV), h.to(DEV), B.to(DEV)
@@ -131,8 +134,9 @@ def test_lora_bwd_matches_unfused_gradients(lib):
     d_base, d_B, d_mag = lib.dora_lora_compose_bwd(dyd, bd, hd, Bd, md, nd, s)
     assert torch.equal(d_base, d_base_u)
     rel = lambda a, b: float((a.float() - b.float()).norm() / b.float().norm())
-    assert rel(d_B, dB_u) < 1e-2
-    assert rel(d_mag, d_mag_u) < 1e-2
+    print(f"fused against unfused: d_B {rel(d_B, dB_u):.2e}, d_mag {rel(d_mag, d_mag_u):.2e}", flush=True)
+    assert rel(d_B, dB_u) < 2.0**-8
+    assert rel(d_mag, d_mag_u) < 2.0**-8
 
 
 FULL = [("attn_proj", "bf16"), ("wide_8192_r384", "bf16"), ("wide_8192_r384", "fp16"),

@@ -247,3 +247,16 @@ def test_norm_bwd_full_size_sampled(lib, name, dtype):
     rows = np.sort(rng.choice(cfg.out, 64, replace=False))
     cols = np.sort(rng.choice(cfg.in_, 64, replace=False))
     check(lib, W0, A, B, cfg.s, d_norm, norm, dtype, f"{name} {dtype} sampled", rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_norm_bwd_all_elements_wide(lib, dtype):
+    """The wide module (out = in = 8192, r = 384) in the benchmark's launch
+    configuration: every element of d_A and of d_B against the oracle."""
+    cfg = synth.CONFIGS["wide_8192_r384"]
+    log(f"norm_bwd every element {cfg.name} {dtype}")
+    W0, A, B = synth.weights(cfg, dtype)
+    rng = np.random.default_rng(4100 + cfg.out + cfg.r)
+    d_norm = (rng.standard_normal(cfg.out) * 30).astype(np.float32)
+    norm = O.weight_norm(W0, A, B, cfg.s).astype(np.float32)
+    check(lib, W0, A, B, cfg.s, d_norm, norm, dtype, f"{cfg.name} {dtype} every element")
