@@ -2,12 +2,15 @@
 
 Every source under csrc/ is compiled to an object in parallel and linked into
 one shared library next to this file.  Packed fp32 instructions are disabled
-(-packed-fp32-ops) for all device code.
+(-packed-fp32-ops) for all device code.  The build fails if any kernel spills
+registers to scratch memory (read from the compiler's resource-usage remarks):
+a spill in a streaming kernel costs far more than the registers it saves.
 """
 from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 import tempfile
@@ -34,6 +37,26 @@ COMMON = [
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+_FUNC = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def _spills(log: str) -> tuple[list[str], str]:
+    """(kernels with scratch > 0, the log without the resource remarks)."""
+    bad, kept, func = [], [], None
+    for line in log.splitlines():
+        m = _FUNC.search(line)
+        if m:
+            func = m.group(1)
+        m = _SCRATCH.search(line)
+        if m and int(m.group(1)) > 0:
+            bad.append(f"{func}: {m.group(1)} bytes/lane")
+        if "kernel-resource-usage" not in line:
+            kept.append(line)
+    return bad, "\n".join(kept)
 
 
 def _run(cmd):
@@ -63,7 +86,14 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     try:
         objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
         with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-            logs = list(ex.map(lambda so: _run([HIPCC, *flags, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+            logs = list(ex.map(lambda so: _run([HIPCC, *flags, *RESOURCE_REMARKS, "-c", so[0], "-o", so[1]]),
+                               zip(srcs, objs)))
+        spilled = []
+        for i, l in enumerate(logs):
+            bad, logs[i] = _spills(l)
+            spilled += bad
+        if spilled:
+            raise RuntimeError("kernels spill to scratch memory:\n  " + "\n  ".join(spilled))
         tmp_lib = lib + ".tmp"
         logs.append(_run([HIPCC, *flags, "-shared", "-o", tmp_lib, *objs]))
         os.replace(tmp_lib, lib)
