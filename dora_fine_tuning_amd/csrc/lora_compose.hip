@@ -65,7 +65,19 @@ struct LoraTile {
 // DMA of stage u + 1 overlaps the MFMAs of stage u.
 using LoraTileMain = LoraTile<2, 8, 2, 2, 64>;
 
-constexpr uint32_t kGroupCols = 4;  // column tiles per group of the tile order
+// Column tiles per group of the tile order (below): the largest power of two
+// from 4 to 16 whose B slice (group x 256 rows x r) stays within 1.5 MiB, well
+// inside an XCD's 4 MiB L2.  Wider groups make the concurrent tiles of an XCD
+// cover longer runs of each base row.  Measured at T x out (r), warm / cold us:
+// 4096^2 (64) 19.6 / 21.6 with 16 against 22.9 / 24.3 with 4; 8192^2 (384)
+// 93.2 / 100.8 with 8 against 95.0 / 103.2; at 10240 x 27648 (512), whose
+// B slice of 16 tiles is 4 MiB, 16 and 8 were 7-19 us slower cold than 4.
+inline uint32_t lora_group_cols(int64_t r) {
+  const int64_t slice = 256 * std::max<int64_t>(r, 1) * 2;  // bytes of B per column tile
+  uint32_t g = 16;
+  while (g > 4 && static_cast<int64_t>(g) * slice > (int64_t(3) << 19)) g /= 2;
+  return g;
+}
 
 struct LoraArgs {
   const void *base, *h, *B;
@@ -75,6 +87,7 @@ struct LoraArgs {
   int add_base;
   int64_t T, out, r;
   int nRB, nTiles, S;
+  uint32_t group;  // column tiles per group of the tile order
 };
 
 // Wait for the current stage's DMA while the n younger stages already issued
@@ -99,16 +112,17 @@ __global__ __launch_bounds__(TL::NT, 2) void lora_fwd_dma(LoraArgs a) {
   const uint32_t v = static_cast<uint32_t>(xcd_logical_index());
   const uint32_t total = static_cast<uint32_t>(a.nRB) * static_cast<uint32_t>(a.nTiles);
   if (v >= total) return;
-  // Tile order: groups of kGroupCols column tiles, token blocks within a group.
+  // Tile order: groups of a.group column tiles, token blocks within a group.
   // With the XCD-contiguous numbering an XCD then works on one group's B slice
-  // (kGroupCols x 256 rows of B stay in its L2) while it sweeps the token
+  // (a.group x 256 rows of B stay in its L2) while it sweeps the token
   // blocks, instead of streaming all of B once per token block.
   const uint32_t nRB = static_cast<uint32_t>(a.nRB), nTl = static_cast<uint32_t>(a.nTiles);
-  const uint32_t grp = v / (kGroupCols * nRB);
-  const uint32_t gn = std::min<uint32_t>(kGroupCols, nTl - grp * kGroupCols);
-  const uint32_t loc = v - grp * kGroupCols * nRB;
+  const uint32_t G = a.group;
+  const uint32_t grp = v / (G * nRB);
+  const uint32_t gn = std::min<uint32_t>(G, nTl - grp * G);
+  const uint32_t loc = v - grp * G * nRB;
   const int rb = static_cast<int>(loc / gn);
-  const int nt = static_cast<int>(grp * kGroupCols + loc % gn);
+  const int nt = static_cast<int>(grp * G + loc % gn);
   const int64_t m0 = static_cast<int64_t>(rb) * TL::BM, n0 = static_cast<int64_t>(nt) * TL::BN;
   const int64_t T = a.T, out = a.out;
   const int r = static_cast<int>(a.r), S = a.S;
@@ -379,6 +393,7 @@ hipError_t launch_lora_fwd(const LoraFwdArgs& p, bool vec) {
   if (vec) {
     a.nRB = static_cast<int>(lcdiv(p.T, TL::BM));
     a.nTiles = static_cast<int>(lcdiv(p.out, TL::BN));
+    a.group = lora_group_cols(p.r);
     a.S = static_cast<int>(lcdiv(p.r, TL::BK));
     const dim3 grid(static_cast<unsigned>(lora_fwd_max_grid(p.T, p.out, true)));
     if (p.dtype == 0)
