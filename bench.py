@@ -266,7 +266,7 @@ def main():
                     help="seconds of oracle compose work per --sweep config (with the oracle norm); 0 skips")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         sweep(max(args.steps // 5, 5), [c for c in args.sweep_only.split(",") if c], args.sweep_cpu_seconds)
